@@ -1,0 +1,191 @@
+// C ABI of libgdr (declared in include/gdr.h): metadata validation on the host,
+// then kernel launches on the caller's stream.  No allocation, no synchronisation.
+#include <atomic>
+#include <cstring>
+
+#include "../../include/gdr.h"
+#include "gdr_internal.h"
+
+namespace {
+
+using gdr::RecurrentArgs;
+
+bool head_dim_ok(int32_t d) { return d == 64 || d == 128; }
+
+bool dtype_ok(int d) { return d == GDR_F32 || d == GDR_BF16; }
+
+// gfx950 check, cached per device (written once, idempotent).
+std::atomic<int> g_arch_ok[64];
+
+gdr_status check_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return GDR_ERROR_NOT_SUPPORTED;
+    if (dev < 0 || dev >= 64) return GDR_ERROR_NOT_SUPPORTED;
+    int cached = g_arch_ok[dev].load(std::memory_order_relaxed);
+    if (cached == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GDR_ERROR_NOT_SUPPORTED;
+        cached = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+        g_arch_ok[dev].store(cached, std::memory_order_relaxed);
+    }
+    return cached == 1 ? GDR_SUCCESS : GDR_ERROR_NOT_SUPPORTED;
+}
+
+// Metadata shared by every entry point.
+gdr_status check_problem(const gdr_problem* p) {
+    if (!p) return GDR_ERROR_INVALID_VALUE;
+    if (p->total_tokens < 0 || p->num_seqs < 0) return GDR_ERROR_INVALID_VALUE;
+    if (p->num_k_heads <= 0 || p->num_v_heads <= 0) return GDR_ERROR_INVALID_VALUE;
+    if (p->num_v_heads % p->num_k_heads != 0) return GDR_ERROR_INVALID_VALUE;
+    if (p->gate != GDR_GATE_SCALAR && p->gate != GDR_GATE_PER_K) return GDR_ERROR_INVALID_VALUE;
+    if (!dtype_ok(p->io_dtype)) return GDR_ERROR_INVALID_VALUE;
+    if (p->head_dim_k <= 0 || p->head_dim_v <= 0) return GDR_ERROR_INVALID_VALUE;
+    if (!head_dim_ok(p->head_dim_k) || !head_dim_ok(p->head_dim_v)) return GDR_ERROR_NOT_SUPPORTED;
+    return GDR_SUCCESS;
+}
+
+bool token_inputs_ok(const gdr_problem* p, const void* q, const void* k, const void* v, const float* g,
+                     const void* beta) {
+    if (p->total_tokens == 0) return true;
+    return q && k && v && g && beta;
+}
+
+gdr_status status_of(hipError_t e) { return e == hipSuccess ? GDR_SUCCESS : GDR_ERROR_LAUNCH_FAILED; }
+
+}  // namespace
+
+extern "C" {
+
+const char* gdr_status_string(gdr_status s) {
+    switch (s) {
+        case GDR_SUCCESS: return "GDR_SUCCESS";
+        case GDR_ERROR_INVALID_VALUE: return "GDR_ERROR_INVALID_VALUE";
+        case GDR_ERROR_NOT_SUPPORTED: return "GDR_ERROR_NOT_SUPPORTED";
+        case GDR_ERROR_LAUNCH_FAILED: return "GDR_ERROR_LAUNCH_FAILED";
+        default: return "GDR_ERROR_UNKNOWN";
+    }
+}
+
+gdr_status gdr_recurrent_fwd(const gdr_problem* p, const void* q, const void* k, const void* v, const float* g,
+                             const void* beta, const int32_t* cu_seqlens, const float* initial_state, void* o,
+                             float* final_state, void* hip_stream) {
+    gdr_status st = check_problem(p);
+    if (st != GDR_SUCCESS) return st;
+    if (!token_inputs_ok(p, q, k, v, g, beta)) return GDR_ERROR_INVALID_VALUE;
+    if (p->total_tokens > 0 && !o) return GDR_ERROR_INVALID_VALUE;
+    if (p->num_seqs > 1 && !cu_seqlens) return GDR_ERROR_INVALID_VALUE;
+    if (p->num_seqs == 0 && p->total_tokens > 0) return GDR_ERROR_INVALID_VALUE;
+    if (p->num_seqs == 0) return GDR_SUCCESS;
+    // all sequences empty and no final state requested: nothing to compute
+    if (p->total_tokens == 0 && !final_state) return GDR_SUCCESS;
+    if ((st = check_device()) != GDR_SUCCESS) return st;
+
+    RecurrentArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.o = o;
+    a.cu_seqlens = cu_seqlens;
+    a.one_token_per_seq = 0;
+    a.T = p->total_tokens;
+    a.src = initial_state;
+    a.dst = final_state;
+    a.slots = nullptr;
+    a.ibuf = nullptr; a.ibuf_idx = nullptr; a.cache_steps = 0;
+    a.N = p->num_seqs; a.HK = p->num_k_heads; a.HV = p->num_v_heads; a.V = p->head_dim_v;
+    a.scale = p->scale;
+    return status_of(gdr::launch_recurrent(a, p->head_dim_k, p->io_dtype, GDR_F32, -1,
+                                           p->gate == GDR_GATE_PER_K, static_cast<hipStream_t>(hip_stream)));
+}
+
+gdr_status gdr_decode_paged(const gdr_problem* p, int32_t max_q_len, const void* q, const void* k, const void* v,
+                            const float* g, const void* beta, const int32_t* cu_seqlens, void* pool,
+                            gdr_dtype pool_dtype, int32_t num_slots, const int32_t* state_indices, int32_t commit,
+                            void* inter_states, gdr_dtype inter_dtype, int32_t num_cache_slots,
+                            int32_t cache_steps, const int32_t* inter_state_indices, void* o, void* hip_stream) {
+    gdr_status st = check_problem(p);
+    if (st != GDR_SUCCESS) return st;
+    if (max_q_len < 1 || max_q_len > 12) return GDR_ERROR_INVALID_VALUE;
+    if (!pool || num_slots <= 0 || !state_indices) return GDR_ERROR_INVALID_VALUE;
+    if (!dtype_ok(pool_dtype)) return GDR_ERROR_INVALID_VALUE;
+    if (commit != 0 && commit != 1) return GDR_ERROR_INVALID_VALUE;
+    if (!token_inputs_ok(p, q, k, v, g, beta)) return GDR_ERROR_INVALID_VALUE;
+    if (p->total_tokens > 0 && !o) return GDR_ERROR_INVALID_VALUE;
+    if (!cu_seqlens && p->total_tokens != p->num_seqs) return GDR_ERROR_INVALID_VALUE;
+    if (p->total_tokens > (int64_t)p->num_seqs * max_q_len) return GDR_ERROR_INVALID_VALUE;
+    if (inter_states) {
+        if (!inter_state_indices || num_cache_slots <= 0 || cache_steps < max_q_len) return GDR_ERROR_INVALID_VALUE;
+        if (!dtype_ok(inter_dtype)) return GDR_ERROR_INVALID_VALUE;
+    }
+    if (p->num_seqs == 0 || p->total_tokens == 0) return GDR_SUCCESS;
+    if ((st = check_device()) != GDR_SUCCESS) return st;
+
+    RecurrentArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.o = o;
+    a.cu_seqlens = cu_seqlens;
+    a.one_token_per_seq = cu_seqlens ? 0 : 1;
+    a.T = p->total_tokens;
+    a.src = pool;
+    a.dst = commit ? pool : nullptr;
+    a.slots = state_indices;
+    a.ibuf = inter_states;
+    a.ibuf_idx = inter_state_indices;
+    a.cache_steps = cache_steps;
+    a.N = p->num_seqs; a.HK = p->num_k_heads; a.HV = p->num_v_heads; a.V = p->head_dim_v;
+    a.scale = p->scale;
+    return status_of(gdr::launch_recurrent(a, p->head_dim_k, p->io_dtype, pool_dtype,
+                                           inter_states ? (int)inter_dtype : -1, p->gate == GDR_GATE_PER_K,
+                                           static_cast<hipStream_t>(hip_stream)));
+}
+
+size_t gdr_chunk_workspace_size(const gdr_problem* p, int32_t chunk_size) {
+    if (check_problem(p) != GDR_SUCCESS || chunk_size != 64) return 0;
+    return gdr::chunk_workspace_layout(p->total_tokens, p->num_seqs, p->num_v_heads, p->head_dim_k,
+                                       p->head_dim_v, p->io_dtype == GDR_BF16 ? 2 : 4,
+                                       p->gate == GDR_GATE_PER_K)
+        .total;
+}
+
+gdr_status gdr_chunk_fwd(const gdr_problem* p, int32_t chunk_size, const void* q, const void* k, const void* v,
+                         const float* g, const void* beta, const int32_t* cu_seqlens, const float* initial_state,
+                         void* o, float* final_state, void* workspace, size_t workspace_bytes, void* hip_stream) {
+    gdr_status st = check_problem(p);
+    if (st != GDR_SUCCESS) return st;
+    if (chunk_size != 64) return GDR_ERROR_INVALID_VALUE;
+    if (!token_inputs_ok(p, q, k, v, g, beta)) return GDR_ERROR_INVALID_VALUE;
+    if (p->total_tokens > 0 && !o) return GDR_ERROR_INVALID_VALUE;
+    if (p->num_seqs > 1 && !cu_seqlens) return GDR_ERROR_INVALID_VALUE;
+    if (p->num_seqs == 0 && p->total_tokens > 0) return GDR_ERROR_INVALID_VALUE;
+    const size_t need = gdr_chunk_workspace_size(p, chunk_size);
+    if (!workspace || workspace_bytes < need) return GDR_ERROR_INVALID_VALUE;
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return GDR_ERROR_INVALID_VALUE;
+    if (p->num_seqs == 0) return GDR_SUCCESS;
+    if (p->total_tokens == 0) {
+        // every sequence is empty: final state = initial state
+        return gdr_recurrent_fwd(p, q, k, v, g, beta, cu_seqlens, initial_state, o, final_state, hip_stream);
+    }
+    if ((st = check_device()) != GDR_SUCCESS) return st;
+
+    const bool per_k = p->gate == GDR_GATE_PER_K;
+    const int io_bytes = p->io_dtype == GDR_BF16 ? 2 : 4;
+    const gdr::ChunkWorkspaceLayout L = gdr::chunk_workspace_layout(p->total_tokens, p->num_seqs, p->num_v_heads,
+                                                                   p->head_dim_k, p->head_dim_v, io_bytes, per_k);
+    char* ws = static_cast<char*>(workspace);
+    gdr::ChunkArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+    a.cu_seqlens = cu_seqlens;
+    a.h0 = initial_state;
+    a.o = o;
+    a.ht = final_state;
+    a.T = p->total_tokens;
+    a.N = p->num_seqs; a.HK = p->num_k_heads; a.HV = p->num_v_heads; a.K = p->head_dim_k; a.V = p->head_dim_v;
+    a.scale = p->scale;
+    a.max_chunks = (int32_t)(p->total_tokens / 64 + p->num_seqs);
+    a.chunk_seq = reinterpret_cast<int32_t*>(ws + L.chunk_seq);
+    a.chunk_first = reinterpret_cast<int32_t*>(ws + L.chunk_first);
+    a.gcum = reinterpret_cast<float*>(ws + L.gcum);
+    a.w = ws + L.w;
+    a.u = ws + L.u;
+    a.vnew = ws + L.vnew;
+    a.hc = ws + L.hc;
+    return status_of(gdr::launch_chunk(a, p->io_dtype, per_k, static_cast<hipStream_t>(hip_stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,133 @@
+// Device-side helpers shared by the gfx950 kernels of libgdr: element types,
+// vector loads/stores with fp32 <-> bf16 conversion, and 16-lane DPP reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdr {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Storage tags: fp32 is `float`, bf16 is carried as its 16-bit pattern.
+struct bf16_t {
+    uint16_t bits;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t u) { return __uint_as_float((uint32_t)u << 16); }
+
+// Two floats -> two bf16 (round to nearest even; v_cvt_pk_bf16_f32), packed lo|hi<<16.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    f32x2_t x = {lo, hi};
+    bf16x2_t y = __builtin_convertvector(x, bf16x2_t);
+    return __builtin_bit_cast(uint32_t, y);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+    return (uint16_t)(pack_bf16x2(x, 0.0f) & 0xFFFFu);
+}
+
+// ---- scalar element access -------------------------------------------------
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    static constexpr int bytes = 4;
+    __device__ __forceinline__ static float load(const void* p, int64_t i) { return static_cast<const float*>(p)[i]; }
+    __device__ __forceinline__ static void store(void* p, int64_t i, float x) { static_cast<float*>(p)[i] = x; }
+};
+template <> struct Elem<bf16_t> {
+    static constexpr int bytes = 2;
+    __device__ __forceinline__ static float load(const void* p, int64_t i) {
+        return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
+    }
+    __device__ __forceinline__ static void store(void* p, int64_t i, float x) {
+        static_cast<uint16_t*>(p)[i] = f32_to_bf16(x);
+    }
+};
+
+// ---- vector access: N consecutive elements (N*bytes in {8, 16, 32}) ----------
+template <typename T, int N> struct Vec;
+
+template <int N> struct Vec<float, N> {
+    static_assert(N % 4 == 0, "fp32 vectors are whole float4s");
+    __device__ __forceinline__ static void load(const void* p, int64_t i, float* out) {
+        const f32x4_t* src = reinterpret_cast<const f32x4_t*>(static_cast<const float*>(p) + i);
+#pragma unroll
+        for (int j = 0; j < N / 4; ++j) {
+            f32x4_t x = src[j];
+            out[4 * j + 0] = x[0];
+            out[4 * j + 1] = x[1];
+            out[4 * j + 2] = x[2];
+            out[4 * j + 3] = x[3];
+        }
+    }
+    __device__ __forceinline__ static void store(void* p, int64_t i, const float* in) {
+        f32x4_t* dst = reinterpret_cast<f32x4_t*>(static_cast<float*>(p) + i);
+#pragma unroll
+        for (int j = 0; j < N / 4; ++j) dst[j] = f32x4_t{in[4 * j], in[4 * j + 1], in[4 * j + 2], in[4 * j + 3]};
+    }
+};
+
+template <int N> struct Vec<bf16_t, N> {
+    static_assert(N == 4 || N == 8, "bf16 vectors are 8 or 16 bytes");
+    __device__ __forceinline__ static void load(const void* p, int64_t i, float* out) {
+        const uint16_t* base = static_cast<const uint16_t*>(p) + i;
+        if constexpr (N == 8) {
+            uint4 w = *reinterpret_cast<const uint4*>(base);
+            uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                out[2 * j] = __uint_as_float(ws[j] << 16);
+                out[2 * j + 1] = __uint_as_float(ws[j] & 0xFFFF0000u);
+            }
+        } else {
+            uint2 w = *reinterpret_cast<const uint2*>(base);
+            out[0] = __uint_as_float(w.x << 16);
+            out[1] = __uint_as_float(w.x & 0xFFFF0000u);
+            out[2] = __uint_as_float(w.y << 16);
+            out[3] = __uint_as_float(w.y & 0xFFFF0000u);
+        }
+    }
+    __device__ __forceinline__ static void store(void* p, int64_t i, const float* in) {
+        uint16_t* base = static_cast<uint16_t*>(p) + i;
+        if constexpr (N == 8) {
+            uint4 w;
+            w.x = pack_bf16x2(in[0], in[1]);
+            w.y = pack_bf16x2(in[2], in[3]);
+            w.z = pack_bf16x2(in[4], in[5]);
+            w.w = pack_bf16x2(in[6], in[7]);
+            *reinterpret_cast<uint4*>(base) = w;
+        } else {
+            uint2 w;
+            w.x = pack_bf16x2(in[0], in[1]);
+            w.y = pack_bf16x2(in[2], in[3]);
+            *reinterpret_cast<uint2*>(base) = w;
+        }
+    }
+};
+
+// ---- 16-lane reductions through DPP ----------------------------------------
+// Lanes are grouped in DPP rows of 16.  After the four steps every lane of the row
+// holds the same, bitwise-identical sum (each step adds the same two operands in
+// both partner lanes).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+__device__ __forceinline__ float row16_sum(float x) {
+    x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]: partner lane ^1
+    x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]: partner lane ^2
+    x += dpp_mov<0x141>(x);  // row_half_mirror: lane i <-> 7-i within each half row
+    x += dpp_mov<0x140>(x);  // row_mirror: lane i <-> 15-i within the row
+    return x;
+}
+
+__device__ __forceinline__ float exp_f32(float x) {
+    // e^x = 2^(x * log2(e)); v_exp_f32 evaluates 2^y.
+    return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+}
+
+}  // namespace gdr

@@ -1,0 +1,71 @@
+// Internal (non-exported) declarations shared by the host side of libgdr:
+// kernel argument blocks and launchers.  Not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <type_traits>
+
+namespace gdr {
+
+// Token-loop kernel (dense recurrent, paged decode, verify).
+struct RecurrentArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* g;
+    const void* beta;
+    void* o;
+    const int32_t* cu_seqlens;   // NULL: see one_token_per_seq
+    int32_t one_token_per_seq;   // with cu_seqlens NULL: 1 -> sequence n is token n; 0 -> one sequence of T tokens
+    int64_t T;
+    const void* src;             // state source [*, HV, V, K] (pool or initial state), NULL = zeros
+    void* dst;                   // state destination (pool on commit, final state), NULL = none
+    const int32_t* slots;        // state_indices (paged) or NULL (dense: slot = sequence)
+    void* ibuf;                  // per-token states [*, cache_steps, HV, V, K] or NULL
+    const int32_t* ibuf_idx;
+    int32_t cache_steps;
+    int32_t N, HK, HV, V;
+    float scale;
+};
+
+// dtype codes: 0 = fp32, 1 = bf16; ib_dtype -1 = no intermediate buffer
+hipError_t launch_recurrent(const RecurrentArgs& a, int K, int io_dtype, int st_dtype, int ib_dtype,
+                            bool per_k, hipStream_t stream);
+
+// Chunked path (64-token chunks).
+struct ChunkArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* g;
+    const void* beta;
+    const int32_t* cu_seqlens;   // NULL only when N == 1
+    const float* h0;             // [N, HV, V, K] or NULL
+    void* o;
+    float* ht;                   // [N, HV, V, K] or NULL
+    int64_t T;
+    int32_t N, HK, HV, K, V;
+    float scale;
+    int32_t max_chunks;          // upper bound on the number of chunks: T/64 + N
+    // workspace views
+    int32_t* chunk_seq;          // [max_chunks] sequence of each chunk, -1 unused
+    int32_t* chunk_first;        // [N + 1] index of each sequence's first chunk
+    float* gcum;                 // [T, HV] or [T, HV, K] chunk-local cumulative gate
+    void* w;                     // [T, HV, K] io dtype
+    void* u;                     // [T, HV, V] io dtype
+    void* vnew;                  // [T, HV, V] io dtype
+    void* hc;                    // [max_chunks, HV, V, K] io dtype: state at each chunk start
+};
+
+struct ChunkWorkspaceLayout {
+    size_t chunk_seq, chunk_first, gcum, w, u, vnew, hc, total;
+};
+
+ChunkWorkspaceLayout chunk_workspace_layout(int64_t T, int32_t N, int32_t HV, int32_t K, int32_t V,
+                                            int io_bytes, bool per_k);
+
+hipError_t launch_chunk(const ChunkArgs& a, int io_dtype, bool per_k, hipStream_t stream);
+
+}  // namespace gdr

@@ -1,0 +1,188 @@
+// H1: token-by-token gated delta rule for gfx950 -- dense recurrent forward, paged
+// decode (commit) and speculative verify (per-token intermediate states, no commit).
+//
+// Method: FlashQLA PR #1 "Fused recurrent GDN decode + SGLang DFlash verify kernel"
+// (core decode-kernel commit: decay -> kS -> v_new -> rank-1 -> o, post-update read;
+// verify-kernel commit: paged gather/scatter through state_indices, -1 skips the
+// sequence, V-major pool, per-token intermediate states, no-commit mode).
+//
+// Design (MI355X, wave64):
+//  * one workgroup = 256 threads = 4 waves owns BV = 16*SLOTS consecutive state rows
+//    of one (sequence, value head); V-rows are independent, so V-tiles never talk;
+//  * 16 lanes share a row: lane j holds K/16 key channels of it in fp32 registers
+//    (whole 16-byte vectors; in fp32 the two halves of a 128-wide row go to lanes
+//    j and j+16-units so every load instruction reads 256 contiguous bytes per row);
+//  * a thread owns SLOTS consecutive rows; the two row GEMVs (S.k and S.q) are
+//    in-register FMAs followed by a 4-step DPP reduction over the 16 lanes;
+//  * the state is read once, kept in registers for all tokens of the sequence and
+//    written once (commit / final state), V-major, no transpose; the verify mode
+//    streams each post-update state out as it is produced.
+#include "gdr_device.h"
+#include "gdr_internal.h"
+
+namespace gdr {
+
+template <int K, typename IO, typename ST, typename DT, typename IB, bool PER_K, int SLOTS>
+__global__ __launch_bounds__(256) void recurrent_kernel(const RecurrentArgs a) {
+    constexpr int EPL = K / 16;                                  // key channels per lane
+    constexpr int VW = (16 / Elem<ST>::bytes) < EPL ? (16 / Elem<ST>::bytes) : EPL;
+    constexpr int UNITS = EPL / VW;                              // vectors per lane per row
+    constexpr int BV = 16 * SLOTS;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int j = lane & 15;                                     // lane within the row group
+    const int rg = (tid >> 6) * 4 + (lane >> 4);                 // row group 0..15
+    const int vt = blockIdx.x, h = blockIdx.y, n = blockIdx.z;
+    const int hk = h / (a.HV / a.HK);
+    const int row0 = vt * BV + rg * SLOTS;                       // first of this thread's rows
+
+    const int slot = a.slots ? a.slots[n] : n;
+    if (slot < 0) return;                                        // padded sequence: skip all
+
+    int64_t bos, eos;
+    if (a.cu_seqlens) {
+        bos = a.cu_seqlens[n];
+        eos = a.cu_seqlens[n + 1];
+    } else if (a.one_token_per_seq) {
+        bos = n;
+        eos = n + 1;
+    } else {
+        bos = 0;
+        eos = a.T;
+    }
+
+    int cols[UNITS];
+#pragma unroll
+    for (int u = 0; u < UNITS; ++u) cols[u] = (u * 16 + j) * VW;
+
+    float S[SLOTS][EPL];
+    const int64_t sbase = (((int64_t)slot * a.HV + h) * a.V + row0) * K;
+    if (a.src) {
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s)
+#pragma unroll
+            for (int u = 0; u < UNITS; ++u) Vec<ST, VW>::load(a.src, sbase + (int64_t)s * K + cols[u], &S[s][u * VW]);
+    } else {
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) S[s][e] = 0.0f;
+    }
+
+    const int64_t ib_row = a.ibuf ? (int64_t)a.ibuf_idx[n] * a.cache_steps : 0;
+
+    for (int64_t t = bos; t < eos; ++t) {
+        float kk[EPL], qq[EPL], al[EPL];
+        const int64_t qk_off = (t * a.HK + hk) * K;
+#pragma unroll
+        for (int u = 0; u < UNITS; ++u) {
+            Vec<IO, VW>::load(a.k, qk_off + cols[u], &kk[u * VW]);
+            Vec<IO, VW>::load(a.q, qk_off + cols[u], &qq[u * VW]);
+        }
+        const int64_t th = t * a.HV + h;
+        if constexpr (PER_K) {
+#pragma unroll
+            for (int u = 0; u < UNITS; ++u) Vec<float, VW>::load(a.g, th * K + cols[u], &al[u * VW]);
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) al[e] = exp_f32(al[e]);
+        } else {
+            const float alpha = exp_f32(a.g[th]);
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) al[e] = alpha;
+        }
+        const float bt = Elem<IO>::load(a.beta, th);
+        float vv[SLOTS];
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s) vv[s] = Elem<IO>::load(a.v, th * a.V + row0 + s);
+
+        float ka[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) ka[e] = al[e] * kk[e];
+
+        float ov[SLOTS];
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s) {
+            float p = 0.0f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) p = fmaf(S[s][e], ka[e], p);   // (decayed S) . k
+            p = row16_sum(p);
+            const float nu = bt * (vv[s] - p);
+            float po = 0.0f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                S[s][e] = fmaf(nu, kk[e], al[e] * S[s][e]);               // decay + rank-1
+                po = fmaf(S[s][e], qq[e], po);
+            }
+            ov[s] = a.scale * row16_sum(po);                              // post-update read
+        }
+        // lane j < SLOTS of each row group writes row (row0 + j)
+        float mine = ov[0];
+#pragma unroll
+        for (int s = 1; s < SLOTS; ++s) mine = (j == s) ? ov[s] : mine;
+        if (j < SLOTS) Elem<IO>::store(a.o, th * a.V + row0 + j, mine);
+
+        if constexpr (!std::is_same<IB, void>::value) {
+            if (a.ibuf) {
+                const int64_t ib = (((ib_row + (t - bos)) * a.HV + h) * a.V + row0) * K;
+#pragma unroll
+                for (int s = 0; s < SLOTS; ++s)
+#pragma unroll
+                    for (int u = 0; u < UNITS; ++u) Vec<IB, VW>::store(a.ibuf, ib + (int64_t)s * K + cols[u], &S[s][u * VW]);
+            }
+        }
+    }
+
+    if (a.dst) {
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s)
+#pragma unroll
+            for (int u = 0; u < UNITS; ++u) Vec<DT, VW>::store(a.dst, sbase + (int64_t)s * K + cols[u], &S[s][u * VW]);
+    }
+}
+
+namespace {
+
+constexpr int kSlots = 4;  // BV = 64 rows per workgroup
+
+template <int K, typename IO, typename ST, typename DT, typename IB, bool PER_K>
+hipError_t launch_t(const RecurrentArgs& a, hipStream_t stream) {
+    dim3 grid(a.V / (16 * kSlots), a.HV, a.N);
+    hipLaunchKernelGGL((recurrent_kernel<K, IO, ST, DT, IB, PER_K, kSlots>), grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int K, typename IO, typename ST, typename DT, bool PER_K>
+hipError_t launch_ib(const RecurrentArgs& a, int ib_dtype, hipStream_t stream) {
+    if (ib_dtype < 0) return launch_t<K, IO, ST, DT, void, PER_K>(a, stream);
+    if (ib_dtype == 0) return launch_t<K, IO, ST, DT, float, PER_K>(a, stream);
+    return launch_t<K, IO, ST, DT, bf16_t, PER_K>(a, stream);
+}
+
+template <int K, typename IO, bool PER_K>
+hipError_t launch_st(const RecurrentArgs& a, int st_dtype, int ib_dtype, hipStream_t stream) {
+    // state source and destination share a dtype (pool) except in the dense mode,
+    // where both are fp32
+    if (st_dtype == 0) return launch_ib<K, IO, float, float, PER_K>(a, ib_dtype, stream);
+    return launch_ib<K, IO, bf16_t, bf16_t, PER_K>(a, ib_dtype, stream);
+}
+
+template <int K, bool PER_K>
+hipError_t launch_io(const RecurrentArgs& a, int io_dtype, int st_dtype, int ib_dtype, hipStream_t stream) {
+    if (io_dtype == 0) return launch_st<K, float, PER_K>(a, st_dtype, ib_dtype, stream);
+    return launch_st<K, bf16_t, PER_K>(a, st_dtype, ib_dtype, stream);
+}
+
+}  // namespace
+
+hipError_t launch_recurrent(const RecurrentArgs& a, int K, int io_dtype, int st_dtype, int ib_dtype,
+                            bool per_k, hipStream_t stream) {
+    if (K == 64) {
+        return per_k ? launch_io<64, true>(a, io_dtype, st_dtype, ib_dtype, stream)
+                     : launch_io<64, false>(a, io_dtype, st_dtype, ib_dtype, stream);
+    }
+    return per_k ? launch_io<128, true>(a, io_dtype, st_dtype, ib_dtype, stream)
+                 : launch_io<128, false>(a, io_dtype, st_dtype, ib_dtype, stream);
+}
+
+}  // namespace gdr

@@ -1,0 +1,237 @@
+"""Thin Python binding of libgdr.so (C ABI in include/gdr.h).
+
+Argument marshalling only: every function checks that the torch tensors it is
+given are contiguous device tensors of the documented shape and dtype, builds the
+``gdr_problem`` struct, passes raw pointers and the current HIP stream, and raises
+``GdrError`` on a non-success status.  All computation happens in the library's
+HIP kernels.  If the library has not been built, loading it raises immediately.
+
+Names follow the C entry points: ``gdr_recurrent_fwd``, ``gdr_chunk_fwd``,
+``gdr_chunk_workspace_size``, ``gdr_decode_paged``, ``gdr_status_string``.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdr.so")
+_lib = None
+
+GDR_SUCCESS, GDR_ERROR_INVALID_VALUE, GDR_ERROR_NOT_SUPPORTED, GDR_ERROR_LAUNCH_FAILED = 0, 1, 2, 3
+GDR_F32, GDR_BF16 = 0, 1
+GDR_GATE_SCALAR, GDR_GATE_PER_K = 0, 1
+
+
+class GdrError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {gdr_status_string(status)} ({status})")
+        self.status = status
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [
+        ("total_tokens", ctypes.c_int64),
+        ("num_seqs", ctypes.c_int32),
+        ("num_k_heads", ctypes.c_int32),
+        ("num_v_heads", ctypes.c_int32),
+        ("head_dim_k", ctypes.c_int32),
+        ("head_dim_v", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("gate", ctypes.c_int),
+        ("io_dtype", ctypes.c_int),
+    ]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """Load libgdr.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing: build it with `python -m gated_delta_rule_63_amd.build`")
+        L = ctypes.CDLL(_LIB_PATH)
+        vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        P = ctypes.POINTER(Problem)
+        L.gdr_status_string.restype = ctypes.c_char_p
+        L.gdr_status_string.argtypes = [ctypes.c_int]
+        L.gdr_recurrent_fwd.restype = ctypes.c_int
+        L.gdr_recurrent_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.gdr_chunk_workspace_size.restype = ctypes.c_size_t
+        L.gdr_chunk_workspace_size.argtypes = [P, i32]
+        L.gdr_chunk_fwd.restype = ctypes.c_int
+        L.gdr_chunk_fwd.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.gdr_decode_paged.restype = ctypes.c_int
+        L.gdr_decode_paged.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, i32, vp, i32,
+                                       vp, ctypes.c_int, i32, i32, vp, vp, vp]
+        _lib = L
+    return _lib
+
+
+def gdr_status_string(status: int) -> str:
+    return lib().gdr_status_string(int(status)).decode()
+
+
+# ---------------------------------------------------------------------------
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return GDR_F32
+    if t == torch.bfloat16:
+        return GDR_BF16
+    raise TypeError(f"unsupported dtype {t}: use float32 or bfloat16")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t: Optional[torch.Tensor], name: str, shape=None, dtype=None, optional=False):
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (the C ABI sees no strides)")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _problem(q, k, v, g, num_seqs: int, scale: Optional[float]) -> Problem:
+    T, HK, K = q.shape
+    HV, V = v.shape[1], v.shape[2]
+    per_k = g.dim() == 3
+    if scale is None:
+        scale = 1.0 / math.sqrt(K)
+    return Problem(T, num_seqs, HK, HV, K, V, float(scale), GDR_GATE_PER_K if per_k else GDR_GATE_SCALAR,
+                   _dtype_code(q.dtype))
+
+
+def _check_tokens(q, k, v, g, beta):
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k are [T, HK, K] and v is [T, HV, V]")
+    T, HK, K = q.shape
+    HV, V = v.shape[1], v.shape[2]
+    _check(q, "q")
+    _check(k, "k", (T, HK, K), q.dtype)
+    _check(v, "v", (T, HV, V), q.dtype)
+    _check(beta, "beta", (T, HV), q.dtype)
+    if g.dim() == 3:
+        _check(g, "g", (T, HV, K), torch.float32)
+    else:
+        _check(g, "g", (T, HV), torch.float32)
+    return T, HK, HV, K, V
+
+
+def _num_seqs(cu_seqlens, default: int) -> int:
+    if cu_seqlens is None:
+        return default
+    _check(cu_seqlens, "cu_seqlens", dtype=torch.int32)
+    return cu_seqlens.shape[0] - 1
+
+
+def _raise(status: int, where: str):
+    if status != GDR_SUCCESS:
+        raise GdrError(status, where)
+
+
+# ---------------------------------------------------------------------------
+def gdr_recurrent_fwd(q, k, v, g, beta, cu_seqlens=None, scale=None, initial_state=None, o=None,
+                      final_state=None, output_final_state: bool = True, stream=None):
+    """Token-by-token recurrence.  Returns (o, final_state or None)."""
+    T, HK, HV, K, V = _check_tokens(q, k, v, g, beta)
+    N = _num_seqs(cu_seqlens, 1)
+    _check(initial_state, "initial_state", (N, HV, V, K), torch.float32, optional=True)
+    if o is None:
+        o = torch.empty((T, HV, V), dtype=q.dtype, device=q.device)
+    _check(o, "o", (T, HV, V), q.dtype)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, HV, V, K), dtype=torch.float32, device=q.device)
+    _check(final_state, "final_state", (N, HV, V, K), torch.float32, optional=True)
+    p = _problem(q, k, v, g, N, scale)
+    st = lib().gdr_recurrent_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                 _ptr(cu_seqlens), _ptr(initial_state), _ptr(o), _ptr(final_state), _stream(stream))
+    _raise(st, "gdr_recurrent_fwd")
+    return o, final_state
+
+
+def gdr_chunk_workspace_size(q, v, g, num_seqs: int, chunk_size: int = 64) -> int:
+    p = _problem(q, q, v, g, num_seqs, 1.0)
+    return int(lib().gdr_chunk_workspace_size(ctypes.byref(p), int(chunk_size)))
+
+
+def gdr_chunk_fwd(q, k, v, g, beta, cu_seqlens=None, scale=None, initial_state=None, o=None,
+                  final_state=None, output_final_state: bool = True, workspace=None, chunk_size: int = 64,
+                  stream=None):
+    """Chunked (64-token) forward.  Returns (o, final_state or None).  ``workspace`` is a
+    uint8 device tensor of at least gdr_chunk_workspace_size bytes (allocated here if absent)."""
+    T, HK, HV, K, V = _check_tokens(q, k, v, g, beta)
+    N = _num_seqs(cu_seqlens, 1)
+    _check(initial_state, "initial_state", (N, HV, V, K), torch.float32, optional=True)
+    if o is None:
+        o = torch.empty((T, HV, V), dtype=q.dtype, device=q.device)
+    _check(o, "o", (T, HV, V), q.dtype)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, HV, V, K), dtype=torch.float32, device=q.device)
+    _check(final_state, "final_state", (N, HV, V, K), torch.float32, optional=True)
+    p = _problem(q, k, v, g, N, scale)
+    need = int(lib().gdr_chunk_workspace_size(ctypes.byref(p), int(chunk_size)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check(workspace, "workspace", dtype=torch.uint8)
+    st = lib().gdr_chunk_fwd(ctypes.byref(p), int(chunk_size), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                             _ptr(cu_seqlens), _ptr(initial_state), _ptr(o), _ptr(final_state), _ptr(workspace),
+                             workspace.numel(), _stream(stream))
+    _raise(st, "gdr_chunk_fwd")
+    return o, final_state
+
+
+def gdr_decode_paged(q, k, v, g, beta, pool, state_indices, cu_seqlens=None, max_q_len: int = 1,
+                     commit: bool = True, inter_states=None, inter_state_indices=None, scale=None, o=None,
+                     stream=None):
+    """Paged decode / speculative verify.  pool [num_slots, HV, V, K] (float32 or bfloat16),
+    state_indices int32 [N] (-1 = padded).  inter_states [num_cache_slots, cache_steps, HV, V, K]
+    or None.  Returns o (rows of padded sequences are left as they were)."""
+    T, HK, HV, K, V = _check_tokens(q, k, v, g, beta)
+    _check(state_indices, "state_indices", dtype=torch.int32)
+    N = state_indices.shape[0]
+    if cu_seqlens is not None:
+        _check(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32)
+    if pool.dim() != 4:
+        raise ValueError("pool is [num_slots, HV, V, K]")
+    _check(pool, "pool", (pool.shape[0], HV, V, K))
+    pool_dt = _dtype_code(pool.dtype)
+    ncs = steps = 0
+    inter_dt = GDR_F32
+    if inter_states is not None:
+        if inter_states.dim() != 5:
+            raise ValueError("inter_states is [num_cache_slots, cache_steps, HV, V, K]")
+        ncs, steps = inter_states.shape[0], inter_states.shape[1]
+        _check(inter_states, "inter_states", (ncs, steps, HV, V, K))
+        inter_dt = _dtype_code(inter_states.dtype)
+        _check(inter_state_indices, "inter_state_indices", (N,), torch.int32)
+    if o is None:
+        o = torch.empty((T, HV, V), dtype=q.dtype, device=q.device)
+    _check(o, "o", (T, HV, V), q.dtype)
+    p = _problem(q, k, v, g, N, scale)
+    st = lib().gdr_decode_paged(ctypes.byref(p), int(max_q_len), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                _ptr(cu_seqlens), _ptr(pool), pool_dt, pool.shape[0], _ptr(state_indices),
+                                1 if commit else 0, _ptr(inter_states), inter_dt, ncs, steps,
+                                _ptr(inter_state_indices), _ptr(o), _stream(stream))
+    _raise(st, "gdr_decode_paged")
+    return o

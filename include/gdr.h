@@ -1,0 +1,180 @@
+/*
+ * gdr.h -- C ABI of libgdr.so: the gated-delta-rule state recurrence on MI355X (gfx950).
+ *
+ * The recurrence (FlashQLA PR #1 "Fused recurrent GDN decode + SGLang DFlash verify
+ * kernel (TileLang, SM90)", core decode-kernel commit): per value head h the state
+ * S[V][K] (fp32, row v over key channels c) takes, for every token t,
+ *
+ *     decay    S[v][c] *= exp(g[t,h])          scalar gate (GDN), or
+ *              S[v][c] *= exp(gk[t,h,c])       per-key-channel gate (KDA)
+ *     read     kS[v]    = sum_c S[v][c] * k[t,hk,c]
+ *     delta    nu[v]    = beta[t,h] * (v[t,h,v] - kS[v])
+ *     write    S[v][c] += nu[v] * k[t,hk,c]
+ *     output   o[t,h,v] = scale * sum_c S[v][c] * q[t,hk,c]    (post-update state)
+ *
+ * with key/query head hk = h / (HV / HK) (grouped-query mapping, same page, review
+ * commit).  q and k arrive l2-normalised per (token, head) and g, beta arrive
+ * already activated (same page, verify-kernel commit); the library never
+ * re-normalises.  g is the natural-log decay and must be finite and <= 0.
+ *
+ * Layouts (all tensors contiguous, row-major, packed variable-length batch):
+ *   q, k           [T, HK, K]          io_dtype
+ *   v, o           [T, HV, V]          io_dtype
+ *   beta           [T, HV]             io_dtype
+ *   g              [T, HV]             fp32 (GDR_GATE_SCALAR)
+ *   gk             [T, HV, K]          fp32 (GDR_GATE_PER_K)
+ *   cu_seqlens     [N + 1]             int32, cu_seqlens[0] = 0, non-decreasing,
+ *                                      cu_seqlens[N] = T; sequence n owns tokens
+ *                                      cu_seqlens[n] .. cu_seqlens[n+1]-1
+ *   states         [.., HV, V, K]      V-major ("state_v_first"): row v contiguous over K
+ * Supported: K, V in {64, 128}; HV % HK == 0; io_dtype fp32 or bf16; every
+ * fp32 -> bf16 store rounds to nearest even.
+ *
+ * Ownership and behaviour common to every entry point:
+ *   - every pointer is device memory owned by the caller; the library never
+ *     allocates, frees, retains or synchronises: it validates metadata on the host,
+ *     enqueues kernels on `hip_stream` (NULL = the legacy default stream) and returns,
+ *     so every call can be captured into a HIP graph;
+ *   - validation covers metadata only (null pointers, sizes, enums) and happens
+ *     before any launch; device contents (slot ids, cu_seqlens values, NaN, g > 0,
+ *     duplicate slots) are NOT checked and are undefined behaviour when invalid;
+ *   - T == 0 or N == 0 returns GDR_SUCCESS without launching anything;
+ *   - outputs must not alias inputs, except where stated;
+ *   - the library keeps no mutable global state and is thread-safe.
+ */
+#ifndef GDR_H_
+#define GDR_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define GDR_API __attribute__((visibility("default")))
+#else
+#define GDR_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gdr_status {
+    GDR_SUCCESS = 0,
+    GDR_ERROR_INVALID_VALUE = 1,   /* bad metadata: null pointer, size, enum, workspace */
+    GDR_ERROR_NOT_SUPPORTED = 2,   /* valid but unsupported: head dim, dtype combo, device */
+    GDR_ERROR_LAUNCH_FAILED = 3    /* hipGetLastError reported a failure after a launch */
+} gdr_status;
+
+typedef enum gdr_dtype { GDR_F32 = 0, GDR_BF16 = 1 } gdr_dtype;
+
+typedef enum gdr_gate {
+    GDR_GATE_SCALAR = 0,  /* g  [T, HV]     one log-decay per token and value head (GDN) */
+    GDR_GATE_PER_K = 1    /* gk [T, HV, K]  one log-decay per key channel (KDA)          */
+} gdr_gate;
+
+typedef struct gdr_problem {
+    int64_t total_tokens;   /* T (host value; equals cu_seqlens[N] on the device)        */
+    int32_t num_seqs;       /* N                                                          */
+    int32_t num_k_heads;    /* HK                                                         */
+    int32_t num_v_heads;    /* HV, a multiple of HK                                       */
+    int32_t head_dim_k;     /* K in {64, 128}                                             */
+    int32_t head_dim_v;     /* V in {64, 128}                                             */
+    float scale;            /* multiplies o only (1/sqrt(K) in the usual setting)         */
+    gdr_gate gate;
+    gdr_dtype io_dtype;     /* dtype of q, k, v, beta, o; gates are always fp32            */
+} gdr_problem;
+
+/*
+ * gdr_recurrent_fwd -- the recurrence token by token over a packed varlen batch.
+ * (FlashQLA PR #1: the fused recurrent decode kernel and its multi-step q_len loop.)
+ *
+ *   cu_seqlens     int32 [N+1]; may be NULL only when N == 1 (one sequence of T tokens)
+ *   initial_state  fp32 [N, HV, V, K] or NULL (zeros)
+ *   o              [T, HV, V] io_dtype (written)
+ *   final_state    fp32 [N, HV, V, K] or NULL (not written); may alias initial_state
+ * Empty sequences are allowed: their final state equals their initial state.
+ */
+GDR_API gdr_status gdr_recurrent_fwd(const gdr_problem* p,
+                             const void* q, const void* k, const void* v,
+                             const float* g, const void* beta,
+                             const int32_t* cu_seqlens,
+                             const float* initial_state,
+                             void* o, float* final_state,
+                             void* hip_stream);
+
+/*
+ * gdr_chunk_workspace_size -- bytes of device workspace gdr_chunk_fwd needs for this
+ * problem (depends on T, N, HV, K, V and io_dtype).  Returns 0 for invalid metadata.
+ */
+GDR_API size_t gdr_chunk_workspace_size(const gdr_problem* p, int32_t chunk_size);
+
+/*
+ * gdr_chunk_fwd -- the same result as gdr_recurrent_fwd computed chunk-parallel: 64-token
+ * chunks counted from each sequence's first token (the last chunk of a sequence may be
+ * short), an intra-chunk WY/UT transform (cumulative gate, A = (I + strictly-lower
+ * beta*KK^T*decay)^-1, w, u), a sequential inter-chunk state pass
+ * (v_new = u - w h, h <- decayed h + (decayed k)^T v_new) and a chunk output stage.
+ * (cuLA PR #113 "[GDN2] Add Hopper SM90 CuTe DSL prefill"; attention-gym PR #344 "Replace
+ * the KDA inter-chunk recurrence with a warp-specialized kernel".)  No factor of the form
+ * exp(-prefix) is ever formed, so every finite g <= 0 is safe (cuLA PR #113 review).
+ *
+ *   chunk_size     must be 64
+ *   cu_seqlens, initial_state, o, final_state: as gdr_recurrent_fwd
+ *   workspace      device buffer of at least gdr_chunk_workspace_size(p, 64) bytes,
+ *                  caller-owned, contents need not be initialised; 256-byte aligned
+ * The result matches gdr_recurrent_fwd to the chunked method's rounding, not bitwise.
+ */
+GDR_API gdr_status gdr_chunk_fwd(const gdr_problem* p, int32_t chunk_size,
+                         const void* q, const void* k, const void* v,
+                         const float* g, const void* beta,
+                         const int32_t* cu_seqlens,
+                         const float* initial_state,
+                         void* o, float* final_state,
+                         void* workspace, size_t workspace_bytes,
+                         void* hip_stream);
+
+/*
+ * gdr_decode_paged -- decode (q_len 1) and speculative verify (q_len up to 12) against a
+ * paged state pool.  (FlashQLA PR #1: verify kernel -- in-kernel paged gather/scatter via
+ * state_indices, V-major pool, per-token intermediate states, no-commit mode, varlen
+ * cu_seqlens; deployment-facts commit -- PAD_SLOT_ID = -1, slot 0 valid, intermediate rows
+ * gated by the pool slot mask.)
+ *
+ *   max_q_len            1..12, an upper bound on every sequence length
+ *   cu_seqlens           int32 [N+1], or NULL: every sequence has exactly one token (T == N)
+ *   pool                 [num_slots, HV, V, K] pool_dtype (fp32 or bf16), updated in place
+ *   state_indices        int32 [N]; sequence b starts from pool[state_indices[b]];
+ *                        a negative index marks a padded sequence, which is skipped
+ *                        entirely: no pool read or write, no intermediate write, and its
+ *                        o rows are left untouched.  Non-negative indices must be distinct
+ *                        and < num_slots.
+ *   commit               1: write the state after the last token back to pool[slot]
+ *                        0: the pool is not written (verify)
+ *   inter_states         NULL, or [num_cache_slots, cache_steps, HV, V, K] inter_dtype:
+ *                        the post-update state after token t (t < len_b) of sequence b goes
+ *                        to [inter_state_indices[b], t]; rows t >= len_b are untouched
+ *   inter_state_indices  int32 [N] (required when inter_states is set), values <
+ *                        num_cache_slots
+ *   cache_steps          >= max_q_len when inter_states is set
+ *   o                    [T, HV, V] io_dtype
+ * The gate must be GDR_GATE_SCALAR or GDR_GATE_PER_K as declared in p.
+ */
+GDR_API gdr_status gdr_decode_paged(const gdr_problem* p, int32_t max_q_len,
+                            const void* q, const void* k, const void* v,
+                            const float* g, const void* beta,
+                            const int32_t* cu_seqlens,
+                            void* pool, gdr_dtype pool_dtype, int32_t num_slots,
+                            const int32_t* state_indices, int32_t commit,
+                            void* inter_states, gdr_dtype inter_dtype,
+                            int32_t num_cache_slots, int32_t cache_steps,
+                            const int32_t* inter_state_indices,
+                            void* o, void* hip_stream);
+
+/* Human-readable name of a status code (static string). */
+GDR_API const char* gdr_status_string(gdr_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDR_H_ */

@@ -1,0 +1,125 @@
+"""CPU-side checks of the C ABI: the library loads, exports every entry point the header
+declares, and rejects bad metadata on the host before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_delta_rule_63_amd import gdr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    with open(os.path.join(ROOT, "include", "gdr.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"GDR_API\s+[\w\s\*]+?\b(gdr_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_three_entry_points():
+    syms = _declared_symbols()
+    for name in ("gdr_recurrent_fwd", "gdr_chunk_fwd", "gdr_decode_paged", "gdr_chunk_workspace_size",
+                 "gdr_status_string"):
+        assert name in syms
+
+
+def test_library_exports_every_declared_symbol():
+    L = gdr.lib()
+    for name in _declared_symbols():
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    assert gdr.gdr_status_string(0) == "GDR_SUCCESS"
+    assert gdr.gdr_status_string(1) == "GDR_ERROR_INVALID_VALUE"
+    assert gdr.gdr_status_string(2) == "GDR_ERROR_NOT_SUPPORTED"
+    assert gdr.gdr_status_string(3) == "GDR_ERROR_LAUNCH_FAILED"
+
+
+def _p(T=8, N=1, HK=1, HV=2, K=128, V=128, gate=0, io=1):
+    return gdr.Problem(T, N, HK, HV, K, V, 0.1, gate, io)
+
+
+DUMMY = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails before any launch
+
+
+def _rec(p, **kw):
+    args = dict(q=DUMMY, k=DUMMY, v=DUMMY, g=DUMMY, beta=DUMMY, cu=None, h0=None, o=DUMMY, ht=None)
+    args.update(kw)
+    return gdr.lib().gdr_recurrent_fwd(ctypes.byref(p) if p is not None else None, args["q"], args["k"], args["v"],
+                                       args["g"], args["beta"], args["cu"], args["h0"], args["o"], args["ht"], None)
+
+
+@pytest.mark.parametrize("field,value,expect", [
+    ("num_v_heads", 3, 1),       # HV % HK != 0 with HK = 2 below
+    ("head_dim_k", 96, 2),
+    ("head_dim_v", 32, 2),
+    ("head_dim_k", 0, 1),
+    ("gate", 7, 1),
+    ("io_dtype", 5, 1),
+    ("total_tokens", -1, 1),
+    ("num_seqs", -1, 1),
+])
+def test_recurrent_rejects_bad_metadata(field, value, expect):
+    p = _p(HK=2, HV=4)
+    setattr(p, field, value)
+    assert _rec(p) == expect
+
+
+def test_recurrent_rejects_null_pointers():
+    assert _rec(None) == 1
+    assert _rec(_p(), q=None) == 1
+    assert _rec(_p(), o=None) == 1
+    assert _rec(_p(N=2)) == 1  # cu_seqlens required for N > 1
+
+
+def test_empty_problems_succeed_without_touching_the_device():
+    assert _rec(_p(T=0, N=0), q=None, k=None, v=None, g=None, beta=None, o=None) == 0
+    assert _rec(_p(T=0, N=3), q=None, k=None, v=None, g=None, beta=None, o=None, cu=DUMMY) == 0
+
+
+def _dec(p, max_q_len=1, **kw):
+    a = dict(cu=None, pool=DUMMY, pool_dt=0, slots=4, idx=DUMMY, commit=1, ib=None, ib_dt=1, ncs=0, steps=0,
+             ibidx=None)
+    a.update(kw)
+    return gdr.lib().gdr_decode_paged(ctypes.byref(p), max_q_len, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, a["cu"],
+                                      a["pool"], a["pool_dt"], a["slots"], a["idx"], a["commit"], a["ib"],
+                                      a["ib_dt"], a["ncs"], a["steps"], a["ibidx"], DUMMY, None)
+
+
+def test_decode_rejects_bad_metadata():
+    assert _dec(_p(T=4, N=4), max_q_len=0) == 1
+    assert _dec(_p(T=4, N=4), max_q_len=13) == 1
+    assert _dec(_p(T=5, N=4)) == 1                       # no cu_seqlens but T != N
+    assert _dec(_p(T=30, N=2), max_q_len=12, cu=DUMMY) == 1  # T > N * max_q_len
+    assert _dec(_p(T=4, N=4), pool=None) == 1
+    assert _dec(_p(T=4, N=4), idx=None) == 1
+    assert _dec(_p(T=4, N=4), slots=0) == 1
+    assert _dec(_p(T=4, N=4), pool_dt=9) == 1
+    assert _dec(_p(T=4, N=4), commit=2) == 1
+    # intermediate buffer: indices, cache slots and cache_steps >= max_q_len are required
+    assert _dec(_p(T=8, N=4), max_q_len=2, cu=DUMMY, ib=DUMMY, ncs=5, steps=2) == 1
+    assert _dec(_p(T=8, N=4), max_q_len=2, cu=DUMMY, ib=DUMMY, ibidx=DUMMY, ncs=5, steps=1) == 1
+    assert _dec(_p(T=8, N=4), max_q_len=2, cu=DUMMY, ib=DUMMY, ibidx=DUMMY, ncs=0, steps=2) == 1
+    assert _dec(_p(T=0, N=4), cu=DUMMY) == 0  # nothing to do
+
+
+def test_chunk_workspace_and_rejections():
+    L = gdr.lib()
+    p = _p(T=1000, N=3, HV=4)
+    need = L.gdr_chunk_workspace_size(ctypes.byref(p), 64)
+    assert need > 0
+    assert L.gdr_chunk_workspace_size(ctypes.byref(p), 32) == 0
+    bad = _p(K=96)
+    assert L.gdr_chunk_workspace_size(ctypes.byref(bad), 64) == 0
+
+    def call(p, cs=64, ws=DUMMY, nbytes=need, cu=DUMMY):
+        return L.gdr_chunk_fwd(ctypes.byref(p), cs, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, cu, None, DUMMY, None,
+                               ws, nbytes, None)
+    assert call(p, cs=32) == 1
+    assert call(p, ws=None) == 1
+    assert call(p, nbytes=need - 1) == 1
+    assert call(p, ws=ctypes.c_void_p(0x1010)) == 1    # not 256-byte aligned
+    assert call(p, cu=None) == 1                        # N > 1 needs cu_seqlens
+    assert call(_p(K=96)) == 2

@@ -1,0 +1,251 @@
+"""H1 through gdr_decode_paged: paged decode (commit) and speculative verify (per-token
+intermediate states, no commit) against the fp64 oracle, with bit-exact slot handling."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from _cmp import TOL, max_rel_l2_tokens, rel_l2
+from _dev import f64, oracle_inputs, to_dev, to_host
+from gated_delta_rule_63_amd import gdr, inputs
+
+pytestmark = pytest.mark.gpu
+
+SENT_O = 0x5A5A        # bf16 / low half of fp32 sentinel patterns
+SENT_IB = 0x1234
+
+
+def _fill_bits(t: torch.Tensor, pattern: int):
+    if t.dtype == torch.bfloat16:
+        t.view(torch.int16).fill_(pattern)
+    else:
+        t.view(torch.int32).fill_(pattern | (pattern << 16))
+
+
+def _run(p, with_ibuf=None, commit=None, pool_dev=None):
+    d = {k: to_dev(getattr(p, k)) for k in ("q", "k", "v", "g", "beta")}
+    cu = to_dev(p.cu_seqlens.astype(np.int32)) if getattr(p, "_use_cu", True) else None
+    pool = to_dev(p.pool) if pool_dev is None else pool_dev
+    idx = to_dev(p.state_indices)
+    o = torch.empty((p.T, p.HV, p.V), dtype=d["q"].dtype, device="cuda")
+    _fill_bits(o, SENT_O)
+    ib = ibi = None
+    if with_ibuf is not None:
+        ib = torch.empty((p.num_cache_slots, p.cache_steps, p.HV, p.V, p.K), dtype=with_ibuf, device="cuda")
+        _fill_bits(ib, SENT_IB)
+        ibi = to_dev(p.inter_state_indices)
+    gdr.gdr_decode_paged(d["q"], d["k"], d["v"], d["g"], d["beta"], pool, idx, cu_seqlens=cu,
+                         max_q_len=p.max_q_len, commit=p.commit if commit is None else commit, inter_states=ib,
+                         inter_state_indices=ibi, scale=p.scale, o=o)
+    torch.cuda.synchronize()
+    return o, pool, ib
+
+
+def _check_o(p, o, ref):
+    """Active rows within tolerance; rows of padded sequences keep the sentinel."""
+    cu = p.cu_seqlens
+    act = [b for b in range(p.N) if p.state_indices[b] >= 0]
+    pad = [b for b in range(p.N) if p.state_indices[b] < 0]
+    oh = to_host(o)
+    for b in pad:
+        rows = oh[cu[b]:cu[b + 1]]
+        if o.dtype == torch.bfloat16:
+            assert np.all(rows == SENT_O)
+        else:
+            assert np.all(rows.view(np.uint32) == (SENT_O | (SENT_O << 16)))
+    of = inputs.widen(oh)
+    worst = 0.0
+    for b in act:
+        s, e = cu[b], cu[b + 1]
+        for h in range(p.HV):
+            worst = max(worst, rel_l2(of[s:e, h], ref["o"][s:e, h]))
+    assert worst <= TOL[p.io_dtype], f"o relL2 {worst}"
+
+
+def _check_pool(p, pool_before: np.ndarray, pool_after: torch.Tensor, ref, committed: bool):
+    after = to_host(pool_after)
+    act = set(int(s) for s in p.state_indices if s >= 0)
+    untouched = np.array(sorted(set(range(pool_before.shape[0])) - (act if committed else set())), dtype=np.int64)
+    assert np.array_equal(after[untouched], pool_before[untouched]), "untouched pool slots changed"
+    if committed:
+        worst = 0.0
+        for s in act:
+            for h in range(p.HV):
+                worst = max(worst, rel_l2(inputs.widen(after[s, h]), ref["final"][s][h]))
+        assert worst <= TOL[p.io_dtype], f"committed state relL2 {worst}"
+
+
+def _check_ibuf(p, ib: torch.Tensor, ref):
+    ibh = to_host(ib)
+    sent = SENT_IB if ib.dtype == torch.bfloat16 else (SENT_IB | (SENT_IB << 16))
+    raw = ibh if ib.dtype == torch.bfloat16 else ibh.view(np.uint32)
+    written = np.zeros(raw.shape[:2], dtype=bool)
+    worst = 0.0
+    cu = p.cu_seqlens
+    for b in range(p.N):
+        if p.state_indices[b] < 0:
+            continue
+        row = int(p.inter_state_indices[b])
+        L = int(cu[b + 1] - cu[b])
+        written[row, :L] = True
+        got = inputs.widen(ibh[row, :L])
+        for t in range(L):
+            for h in range(p.HV):
+                worst = max(worst, rel_l2(got[t, h], ref["states"][b][t, h]))
+    assert worst <= TOL[p.io_dtype], f"intermediate state relL2 {worst}"
+    assert np.all(raw[~written] == sent), "intermediate rows that must stay untouched changed"
+
+
+def test_decode_small_fp32_pool_commit_with_padding():
+    p = inputs.paged_problem(21, B=40, q_len=1, HK=16, HV=32, K=128, V=128, num_slots=64, pool_dtype="f32",
+                             pad_count=4, commit=True)
+    before = p.pool.copy()
+    o, pool, _ = _run(p)
+    q, k, v, g, beta = oracle_inputs(p)
+    ref = oracle.decode_paged(q, k, v, g, beta, p.cu_seqlens, p.scale, inputs.widen(p.pool), p.state_indices)
+    _check_o(p, o, ref)
+    _check_pool(p, before, pool, ref, committed=True)
+
+
+@pytest.mark.parametrize("pool_dt,ib_dt", [("bf16", torch.bfloat16), ("f32", torch.float32), ("f32", torch.bfloat16)])
+def test_verify_ragged_no_commit(pool_dt, ib_dt):
+    p = inputs.paged_problem(22, B=10, q_len=12, HK=4, HV=8, K=128, V=128, num_slots=20, pool_dtype=pool_dt,
+                             pad_count=2, commit=False, inter_dtype="bf16", ragged=True, cache_steps=12)
+    before = p.pool.copy()
+    o, pool, ib = _run(p, with_ibuf=ib_dt)
+    q, k, v, g, beta = oracle_inputs(p)
+    ref = oracle.decode_paged(q, k, v, g, beta, p.cu_seqlens, p.scale, inputs.widen(p.pool), p.state_indices,
+                              want_states=True)
+    _check_o(p, o, ref)
+    _check_pool(p, before, pool, ref, committed=False)
+    _check_ibuf(p, ib, ref)
+
+
+@pytest.mark.parametrize("K", [64, 128])
+def test_decode_k64_and_per_key_gate(K):
+    p = inputs.paged_problem(23, B=12, q_len=3, HK=2, HV=4, K=K, V=K, num_slots=16, pool_dtype="f32",
+                             pad_count=2, commit=True, per_k_gate=True, ragged=True)
+    before = p.pool.copy()
+    o, pool, _ = _run(p)
+    q, k, v, g, beta = oracle_inputs(p)
+    ref = oracle.decode_paged(q, k, v, g, beta, p.cu_seqlens, p.scale, inputs.widen(p.pool), p.state_indices)
+    _check_o(p, o, ref)
+    _check_pool(p, before, pool, ref, committed=True)
+
+
+def test_last_intermediate_row_equals_committed_state_bitwise():
+    p = inputs.paged_problem(24, B=6, q_len=12, HK=2, HV=4, K=128, V=128, num_slots=8, pool_dtype="bf16",
+                             pad_count=1, commit=True, inter_dtype="bf16", ragged=True)
+    o, pool, ib = _run(p, with_ibuf=torch.bfloat16)
+    cu = p.cu_seqlens
+    for b in range(p.N):
+        s = int(p.state_indices[b])
+        if s < 0:
+            continue
+        L = int(cu[b + 1] - cu[b])
+        assert torch.equal(ib[int(p.inter_state_indices[b]), L - 1], pool[s])
+
+
+def test_slot_zero_is_valid():
+    p = inputs.paged_problem(25, B=4, q_len=1, HK=1, HV=2, K=64, V=64, num_slots=4, pool_dtype="f32")
+    p.state_indices = np.array([2, 0, -1, 3], dtype=np.int32)
+    before = p.pool.copy()
+    o, pool, _ = _run(p)
+    q, k, v, g, beta = oracle_inputs(p)
+    ref = oracle.decode_paged(q, k, v, g, beta, p.cu_seqlens, p.scale, inputs.widen(p.pool), p.state_indices)
+    _check_o(p, o, ref)
+    _check_pool(p, before, pool, ref, committed=True)
+    assert not np.array_equal(to_host(pool)[0], before[0])
+
+
+def test_graph_capture_replay_equals_eager():
+    p = inputs.paged_problem(26, B=8, q_len=4, HK=2, HV=4, K=128, V=128, num_slots=16, pool_dtype="bf16",
+                             pad_count=1, commit=False, inter_dtype="bf16")
+    d = {k: to_dev(getattr(p, k)) for k in ("q", "k", "v", "g", "beta")}
+    cu = to_dev(p.cu_seqlens.astype(np.int32))
+    pool = to_dev(p.pool)
+    idx = to_dev(p.state_indices)
+    ibi = to_dev(p.inter_state_indices)
+    ib = torch.zeros((p.num_cache_slots, p.cache_steps, p.HV, p.V, p.K), dtype=torch.bfloat16, device="cuda")
+    o = torch.zeros((p.T, p.HV, p.V), dtype=torch.bfloat16, device="cuda")
+
+    def call():
+        gdr.gdr_decode_paged(d["q"], d["k"], d["v"], d["g"], d["beta"], pool, idx, cu_seqlens=cu, max_q_len=4,
+                             commit=False, inter_states=ib, inter_state_indices=ibi, scale=p.scale, o=o)
+
+    call()
+    torch.cuda.synchronize()
+    o_ref, ib_ref = o.clone(), ib.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for _ in range(3):
+        o.zero_()
+        ib.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(ib, ib_ref)
+
+
+def _sampled_oracle(p, sample):
+    """Oracle on a subset of sequences only (every (sequence, head) is independent)."""
+    cu = p.cu_seqlens
+    sub_idx = np.full(p.N, -1, dtype=np.int32)
+    sub_idx[sample] = p.state_indices[sample]
+    q, k, v, g, beta = oracle_inputs(p)
+    pool = {int(p.state_indices[b]): inputs.widen(p.pool[int(p.state_indices[b])]) for b in sample}
+    return oracle.decode_paged(q, k, v, g, beta, cu, p.scale, pool, sub_idx, want_states=True)
+
+
+def test_decode_full_size_sampled():
+    """256 sequences, 1024-slot fp32 pool, 26 padded, commit: all slot handling checked exactly,
+    values checked against the oracle on a sample of sequences."""
+    p = inputs.decode()
+    before = p.pool
+    o, pool, _ = _run(p)
+    after = to_host(pool)
+    act = sorted(int(s) for s in p.state_indices if s >= 0)
+    untouched = np.array(sorted(set(range(1024)) - set(act)))
+    assert np.array_equal(after[untouched], before[untouched])
+    rng = np.random.default_rng(0)
+    active_b = [b for b in range(p.N) if p.state_indices[b] >= 0]
+    sample = sorted(rng.choice(active_b, size=8, replace=False).tolist())
+    ref = _sampled_oracle(p, sample)
+    oh = f64(o)
+    worst = 0.0
+    for b in sample:
+        s = int(p.state_indices[b])
+        for h in range(p.HV):
+            worst = max(worst, rel_l2(oh[b, h], ref["o"][b, h]), rel_l2(inputs.widen(after[s, h]), ref["final"][s][h]))
+    assert worst <= TOL["bf16"], worst
+    ohb = to_host(o)
+    for b in range(p.N):
+        if p.state_indices[b] < 0:
+            assert np.all(ohb[b] == SENT_O)
+
+
+def test_verify_full_size_sampled():
+    """64 sequences x 12 tokens, bf16 pool, bf16 intermediate buffer [1025, 12, 32, 128, 128], no commit."""
+    p = inputs.verify()
+    o, pool, ib = _run(p, with_ibuf=torch.bfloat16)
+    assert torch.equal(pool, to_dev(p.pool)), "verify must not write the pool"
+    # untouched: cache slot 64 (one past the dense arange) keeps its sentinel
+    assert torch.all(ib[64].view(torch.int16) == SENT_IB)
+    sample = [0, 17, 40, 63]
+    ref = _sampled_oracle(p, sample)
+    oh = f64(o)
+    worst = 0.0
+    for b in sample:
+        s, e = p.cu_seqlens[b], p.cu_seqlens[b + 1]
+        row = f64(ib[b])
+        for h in range(p.HV):
+            worst = max(worst, rel_l2(oh[s:e, h], ref["o"][s:e, h]))
+            for t in range(12):
+                worst = max(worst, rel_l2(row[t, h], ref["states"][b][t, h]))
+    assert worst <= TOL["bf16"], worst
