@@ -41,6 +41,7 @@ gdr_status check_problem(const gdr_problem* p) {
     if (!dtype_ok(p->io_dtype)) return GDR_ERROR_INVALID_VALUE;
     if (p->head_dim_k <= 0 || p->head_dim_v <= 0) return GDR_ERROR_INVALID_VALUE;
     if (!head_dim_ok(p->head_dim_k) || !head_dim_ok(p->head_dim_v)) return GDR_ERROR_NOT_SUPPORTED;
+    if (p->num_seqs > 65535 || p->num_v_heads > 65535) return GDR_ERROR_NOT_SUPPORTED;  // grid y/z limits
     return GDR_SUCCESS;
 }
 
@@ -149,6 +150,7 @@ gdr_status gdr_chunk_fwd(const gdr_problem* p, int32_t chunk_size, const void* q
     gdr_status st = check_problem(p);
     if (st != GDR_SUCCESS) return st;
     if (chunk_size != 64) return GDR_ERROR_INVALID_VALUE;
+    if (p->io_dtype == GDR_F32 && p->head_dim_k != 64) return GDR_ERROR_NOT_SUPPORTED;
     if (!token_inputs_ok(p, q, k, v, g, beta)) return GDR_ERROR_INVALID_VALUE;
     if (p->total_tokens > 0 && !o) return GDR_ERROR_INVALID_VALUE;
     if (p->num_seqs > 1 && !cu_seqlens) return GDR_ERROR_INVALID_VALUE;
