@@ -1,0 +1,249 @@
+"""Benchmark of the gated-delta-rule hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--no-cpu-baseline]
+
+One step is one pass of the whole hot path over one batch of synthetic inputs,
+already resident in HBM:
+
+  prefill  gdr_chunk_fwd     8 ragged sequences, 32768 tokens, 32 heads, K=V=128, bf16,
+                             fp32 initial and final state          (chunked GDN prefill)
+  decode   gdr_decode_paged  256 sequences x 1 token, 16/32 heads, fp32 pool [1024, 32, 128, 128],
+                             26 padded slots, commit               (paged decode)
+  verify   gdr_decode_paged  64 sequences x 12 tokens, bf16 pool, bf16 per-token states
+                             [1025, 12, 32, 128, 128], no commit  (speculative verify)
+
+The JSON line reports prefill tokens/s as ``value`` and the decode state GB/s beside it,
+each leg's time from HIP events recorded on the stream the library launches on, the
+roofline of the decode kernel (HBM-bound, one launch) and of the other legs, and the CPU
+oracle timed on a bounded sample of the prefill workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK = 8.0e12          # B/s
+BF16_MFMA_PEAK = 2.5e15    # dense flop/s
+
+
+def _alg_bytes_prefill(p):
+    """q, k, v, o (io dtype) + g fp32 + beta (io dtype) per token-head, initial + final state, cu_seqlens."""
+    io = 2 if p.io_dtype == "bf16" else 4
+    per_tok = p.HK * p.K * io * 2 + p.HV * p.V * io * 2 + p.HV * 4 + p.HV * io
+    return p.T * per_tok + 2 * p.N * p.HV * p.V * p.K * 4 + 4 * (p.N + 1)
+
+
+def _alg_flops_prefill(p, full_tile=False):
+    """Chunk-algorithm flops per 64-token chunk-head, counted per token (x T x HV / 64).
+    Triangle-exact: K K^T strictly lower, (I+L)^-1 (C^3/3), A.(beta V) and A.(beta e^g K) over the
+    strictly lower part, W.h, (K*)^T v_new, Q.h, Q K^T and P v_new over the lower triangle incl.
+    the diagonal.  Full-tile: every MFMA tile counted whole."""
+    C, K, V = 64, p.K, p.V
+    if full_tile:
+        per_chunk = 2 * C * C * K * 2 + 2 * C * C * (K + V) + 2 * C * K * V * 3 + 2 * C * C * V
+    else:
+        tri_strict = C * (C - 1) // 2
+        tri_incl = C * (C + 1) // 2
+        per_chunk = (2 * tri_strict * K + C ** 3 // 3 + 2 * tri_strict * V + 2 * tri_strict * K
+                     + 2 * C * K * V * 3 + 2 * tri_incl * K + 2 * tri_incl * V)
+    return per_chunk * p.T * p.HV // C
+
+
+def _alg_bytes_paged(p, with_ibuf: bool):
+    """Per active sequence: state read (+ write on commit) per value head, q/k/v/o/g/beta per token,
+    per-token intermediate states; 4 bytes (the index) per padded sequence."""
+    io = 2 if p.io_dtype == "bf16" else 4
+    st = 4 if p.pool_dtype == "f32" else 2
+    lens = p.lengths
+    total = 0
+    for b in range(p.N):
+        if p.state_indices[b] < 0:
+            total += 4
+            continue
+        L = int(lens[b])
+        total += 4 + p.HV * p.V * p.K * st * (2 if p.commit else 1)
+        total += L * (2 * p.HK * p.K * io + 2 * p.HV * p.V * io + p.HV * 4 + p.HV * io)
+        if with_ibuf:
+            ib = 2 if p.inter_dtype == "bf16" else 4
+            total += L * p.HV * p.V * p.K * ib + 4
+    if getattr(p, "_use_cu", True):
+        total += 4 * (p.N + 1)
+    return total
+
+
+def _cpu_baseline(p, target_s: float = 12.0):
+    """The fp64 oracle on the host cores, on the first heads of the prefill workload."""
+    import oracle  # test infrastructure: only this leg of the benchmark loads it
+    from gated_delta_rule_63_amd import inputs
+
+    threads = oracle.default_threads()
+    w = [inputs.widen(x) for x in (p.q, p.k, p.v, p.g, p.beta)]
+    heads_done, secs = 0, 0.0
+    h = 0
+    while secs < target_s and h < p.HV:
+        sel = lambda x: np.ascontiguousarray(x[:, h:h + 1])
+        hk = h // (p.HV // p.HK)
+        t0 = time.perf_counter()
+        oracle.recurrent(np.ascontiguousarray(w[0][:, hk:hk + 1]), np.ascontiguousarray(w[1][:, hk:hk + 1]),
+                         sel(w[2]), sel(w[3]), sel(w[4]), p.cu_seqlens, p.scale,
+                         None if p.initial_state is None else np.ascontiguousarray(p.initial_state[:, h:h + 1]),
+                         threads=threads)
+        secs += time.perf_counter() - t0
+        heads_done += 1
+        h += 1
+    tok_per_s = p.T * heads_done / p.HV / secs
+    return {"value": tok_per_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"prefill workload, all {p.T} tokens of {heads_done} of {p.HV} value heads "
+                      f"({secs:.1f} s), scaled to whole-problem tokens/s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the gated-delta-rule path here is built and timed on a single "
+              "MI355X (every (sequence, head) state is independent; sharding is described, not run). "
+              "Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gated_delta_rule_63_amd import gdr, inputs
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev(x):
+        x = np.ascontiguousarray(x)
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(x).to(dev)
+
+    print("bench: generating inputs", file=sys.stderr, flush=True)
+    pp = inputs.prefill()
+    pd = inputs.decode()
+    pv = inputs.verify()
+
+    P = {k: to_dev(getattr(pp, k)) for k in ("q", "k", "v", "g", "beta")}
+    P["cu"] = to_dev(pp.cu_seqlens.astype(np.int32))
+    P["h0"] = to_dev(pp.initial_state)
+    P["o"] = torch.empty((pp.T, pp.HV, pp.V), dtype=torch.bfloat16, device=dev)
+    P["ht"] = torch.empty((pp.N, pp.HV, pp.V, pp.K), dtype=torch.float32, device=dev)
+    ws_bytes = gdr.gdr_chunk_workspace_size(P["q"], P["v"], P["g"], pp.N)
+    P["ws"] = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
+    D = {k: to_dev(getattr(pd, k)) for k in ("q", "k", "v", "g", "beta")}
+    D["pool"] = to_dev(pd.pool)
+    D["idx"] = to_dev(pd.state_indices)
+    D["o"] = torch.empty((pd.T, pd.HV, pd.V), dtype=torch.bfloat16, device=dev)
+
+    V_ = {k: to_dev(getattr(pv, k)) for k in ("q", "k", "v", "g", "beta")}
+    V_["cu"] = to_dev(pv.cu_seqlens.astype(np.int32))
+    V_["pool"] = to_dev(pv.pool)
+    V_["idx"] = to_dev(pv.state_indices)
+    V_["ibi"] = to_dev(pv.inter_state_indices)
+    V_["ib"] = torch.zeros((pv.num_cache_slots, pv.cache_steps, pv.HV, pv.V, pv.K), dtype=torch.bfloat16, device=dev)
+    V_["o"] = torch.empty((pv.T, pv.HV, pv.V), dtype=torch.bfloat16, device=dev)
+
+    def prefill():
+        gdr.gdr_chunk_fwd(P["q"], P["k"], P["v"], P["g"], P["beta"], P["cu"], pp.scale, P["h0"], o=P["o"],
+                          final_state=P["ht"], workspace=P["ws"])
+
+    def decode():
+        gdr.gdr_decode_paged(D["q"], D["k"], D["v"], D["g"], D["beta"], D["pool"], D["idx"], cu_seqlens=None,
+                             max_q_len=1, commit=True, scale=pd.scale, o=D["o"])
+
+    def verify():
+        gdr.gdr_decode_paged(V_["q"], V_["k"], V_["v"], V_["g"], V_["beta"], V_["pool"], V_["idx"],
+                             cu_seqlens=V_["cu"], max_q_len=12, commit=False, inter_states=V_["ib"],
+                             inter_state_indices=V_["ibi"], scale=pv.scale, o=V_["o"])
+
+    legs = [("prefill", prefill), ("decode", decode), ("verify", verify)]
+    print("bench: warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        for _, fn in legs:
+            fn()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = {name: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+          for name, _ in legs}
+    print(f"bench: timing {K} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        for name, fn in legs:
+            ev[name][i][0].record()
+            fn()
+            ev[name][i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    leg_ms = {name: float(np.mean([a.elapsed_time(b) for a, b in ev[name]])) for name, _ in legs}
+    leg_ms_min = {name: float(np.min([a.elapsed_time(b) for a, b in ev[name]])) for name, _ in legs}
+
+    b_pre = _alg_bytes_prefill(pp)
+    f_pre = _alg_flops_prefill(pp)
+    f_pre_full = _alg_flops_prefill(pp, full_tile=True)
+    b_dec = _alg_bytes_paged(pd, with_ibuf=False)
+    b_ver = _alg_bytes_paged(pv, with_ibuf=True)
+    s_pre, s_dec, s_ver = leg_ms["prefill"] / 1e3, leg_ms["decode"] / 1e3, leg_ms["verify"] / 1e3
+    state_bytes_dec = int(sum(1 for s in pd.state_indices if s >= 0)) * pd.HV * pd.V * pd.K * 4 * 2
+
+    prefill_tps = pp.T / s_pre
+    roof_dec = {"bound": "hbm", "achieved": b_dec / s_dec / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                "frac": b_dec / s_dec / HBM_PEAK, "traffic": None,
+                "kernel": "recurrent_kernel (decode: 256 x 1 token, fp32 pool, commit)",
+                "alg_bytes_per_launch": b_dec}
+    roof_legs = {
+        "prefill": {"bound": "hbm", "achieved_GBps": b_pre / s_pre / 1e9, "frac_hbm": b_pre / s_pre / HBM_PEAK,
+                    "mfma_TFLOPs_triangle_exact": f_pre / s_pre / 1e12,
+                    "frac_bf16_mfma_triangle_exact": f_pre / s_pre / BF16_MFMA_PEAK,
+                    "frac_bf16_mfma_full_tile": f_pre_full / s_pre / BF16_MFMA_PEAK,
+                    "alg_bytes": b_pre, "alg_flops_triangle_exact": f_pre, "alg_flops_full_tile": f_pre_full,
+                    "launches": "chunk_index, chunk_prepare (H2), chunk_state (H3), chunk_output (H4)"},
+        "decode": {"bound": "hbm", "achieved_GBps": b_dec / s_dec / 1e9, "frac_hbm": b_dec / s_dec / HBM_PEAK,
+                   "state_GBps": state_bytes_dec / s_dec / 1e9, "alg_bytes": b_dec},
+        "verify": {"bound": "hbm", "achieved_GBps": b_ver / s_ver / 1e9, "frac_hbm": b_ver / s_ver / HBM_PEAK,
+                   "alg_bytes": b_ver},
+    }
+    out = {
+        "metric": "GDN prefill tokens/s + decode state GB/s (fraction of HBM/MFMA peak), 1 GPU",
+        "value": prefill_tps,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": wall / K * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "prefill: chunked GDN, 8 ragged sequences (incl. 64 and 65) summing to 32768 tokens, "
+                               "32 heads, K=V=128, bf16, fp32 h0/final; decode: 256 seqs x 1 token, HK=16/HV=32, "
+                               "fp32 pool [1024,32,128,128], 26 padded, commit; verify: 64 seqs x 12 tokens, "
+                               "bf16 pool, bf16 per-token states [1025,12,32,128,128], no commit",
+                   "global_batch": pp.N, "seq_len": pp.T, "parallelism": "none (1 GPU)"},
+        "decode_state_GBps": state_bytes_dec / s_dec / 1e9,
+        "leg_ms": leg_ms,
+        "leg_ms_min": leg_ms_min,
+        "roofline": roof_dec,
+        "roofline_legs": roof_legs,
+    }
+    if not args.no_cpu_baseline:
+        print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = _cpu_baseline(pp)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()
