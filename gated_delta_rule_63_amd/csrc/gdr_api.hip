@@ -156,7 +156,7 @@ gdr_status gdr_chunk_fwd(const gdr_problem* p, int32_t chunk_size, const void* q
     if (p->num_seqs > 1 && !cu_seqlens) return GDR_ERROR_INVALID_VALUE;
     if (p->num_seqs == 0 && p->total_tokens > 0) return GDR_ERROR_INVALID_VALUE;
     const size_t need = gdr_chunk_workspace_size(p, chunk_size);
-    if (!workspace || workspace_bytes < need) return GDR_ERROR_INVALID_VALUE;
+    if (need > 0 && (!workspace || workspace_bytes < need)) return GDR_ERROR_INVALID_VALUE;
     if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return GDR_ERROR_INVALID_VALUE;
     if (p->num_seqs == 0) return GDR_SUCCESS;
     if (p->total_tokens == 0) {

@@ -1,29 +1,39 @@
-// Chunked gated delta rule for gfx950: 64-token chunks, WY/UT form.
+// Chunked gated delta rule for gfx950: one fused kernel over 64-token chunks (WY/UT form).
 //
-// Stages (each a kernel, launched back to back on the caller's stream):
-//   index    chunk -> sequence map for a packed varlen batch (one small workgroup)
-//   H2       per (chunk, head): chunk-local cumulative gate gamma, the strictly lower
-//            L = beta * (K K^T) * decay, A = (I + L)^-1, W = A diag(beta) (K * e^gamma),
-//            U = A diag(beta) V                                  -> gamma, W, U to workspace
-//   H3       per (sequence, head, 64-wide V tile), sequential over the sequence's chunks:
-//            v_new = U - W S^T,  S <- S * e^{gamma_last} + v_new^T (K * e^{gamma_last - gamma})
-//            with the state S held in MFMA accumulators    -> chunk-start states, v_new
-//   H4       per (chunk, head): O = scale * ((Q * e^gamma) S0^T + P v_new),
-//            P[r][j] = q_r . k_j * decay(r, j) for j <= r
+// One workgroup owns the whole state S[V][K] of one (sequence, value head) -- or a 64-wide
+// V tile of it -- and walks the sequence's chunks in order.  Wave w keeps the 16 state
+// columns v = 16*w + lane%16 of its tile in MFMA accumulators for the whole sequence.
+// Per chunk (rows r = 0..63 from the chunk start, the last chunk of a sequence may be
+// short; rows past its end are zero):
 //
-// Method: the chunked algorithm that the cuLA PR #113 ("[GDN2] Add Hopper SM90 CuTe DSL
-// prefill") and attention-gym PR #344 ("Replace the KDA inter-chunk recurrence with a
-// warp-specialized kernel") pages build on (kkt/solve/A, w, u, per-chunk h, v_new), written
-// out from the token recurrence.  Overflow: every exponential evaluated here has a
-// non-positive argument -- (later - earlier) prefix differences or a prefix itself --
-// so no exp(-prefix) factor exists (cuLA PR #113 review, finding P1).  For the per-key-channel
-// gate the decay cannot be pulled out of K K^T / Q K^T as a matrix factor; off-diagonal
-// 16x16 blocks use a reference point rho (the prefix at the last row before the block row):
-// exp(g_r - g_j) = exp(g_r - rho) * exp(rho - g_j), both factors <= 1, so they become MFMA
-// operands; the four diagonal 16x16 blocks are evaluated element-wise.
+//   A  raw q, k (and v) rows into LDS; gamma = chunk-local prefix sum of the log-decay
+//   B  L = strictly lower  beta_r (k_r . k_j) e^{gamma_r - gamma_j}      (K K^T on MFMA)
+//      P = lower incl. diag  (q_r . k_j) e^{gamma_r - gamma_j}           (Q K^T on MFMA)
+//   C  A = (I + L)^-1  (fp32: 16x16 diagonal blocks by substitution, the rest on MFMA)
+//   D  W = A diag(beta) (K * e^gamma)   -> LDS;   U = A diag(beta) V  -> each wave's registers
+//   E  v_new = U - W S^T;  O = scale (diag(e^gamma) Q S^T + P v_new);
+//      S <- e^{gamma_last} S + sum_r v_new_r (k_r * e^{gamma_last - gamma_r})^T
 //
-// MFMA: bf16 I/O uses v_mfma_f32_16x16x32_bf16, fp32 I/O uses v_mfma_f32_16x16x4f32
-// (fp32-accurate products).  Accumulation is fp32 throughout.
+// This is the chunked algorithm whose parts (cumulative gate, kkt/solve/A, w, u, the
+// inter-chunk recurrence with per-chunk h and v_new, the chunk output) the cuLA PR #113
+// "[GDN2] Add Hopper SM90 CuTe DSL prefill" and attention-gym PR #344 "Replace the KDA
+// inter-chunk recurrence with a warp-specialized kernel" pages build on, derived here from the
+// token recurrence.  Stages B-D are the intra-chunk WY/UT transform, the S-dependent part of E
+// is the inter-chunk state pass and the rest of E is the chunk output; fusing them keeps W, U,
+// v_new and the per-chunk states out of HBM, which then only sees q, k, v, g, beta, o and
+// the initial/final states.  The next chunk's inputs are loaded into registers while the
+// current chunk computes.
+//
+// Overflow: every exponential evaluated has a non-positive argument -- a prefix gamma or a
+// (later - earlier) prefix difference -- so no exp(-prefix) factor is ever formed (cuLA PR
+// #113 review, finding P1).  With the scalar gate the decays are applied as row factors of
+// MFMA inputs/outputs.  With the per-key-channel gate they cannot be factored out of K K^T
+// and Q K^T: off-diagonal 16x16 blocks use a reference point rho (the prefix at the last
+// row before the block row), exp(g_r - g_j) = exp(g_r - rho) exp(rho - g_j) with both
+// factors <= 1, and the four diagonal blocks are evaluated element-wise.
+//
+// MFMA: bf16 I/O uses v_mfma_f32_16x16x32_bf16 (bf16 operands, fp32 accumulation); fp32 I/O
+// uses v_mfma_f32_16x16x4f32.
 #include "gdr_device.h"
 #include "gdr_internal.h"
 
@@ -32,8 +42,6 @@ namespace gdr {
 namespace {
 
 constexpr int CH = 64;  // chunk length
-
-size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // ---------------------------------------------------------------------------
 // MFMA tile products on LDS operands, "NT" form: C[i][j] += sum_k A[i][k] * Bt[j][k]
@@ -86,22 +94,54 @@ template <> struct MM<float> {
     }
 };
 
-struct ChunkInfo {
-    int64_t bos;
-    int len;
-    int n;
-};
+// Column order inside every 32-wide block of a bf16 LDS operand row: logical column
+// c = 32m + 16h + 4g + e is stored at 32m + 8g + 4h + e.  An MFMA lane group then finds the
+// two 4-element runs it needs (below) in one 16-byte read.  fp32 layouts keep natural order.
+template <typename MT>
+__device__ __forceinline__ int perm(int c) {
+    if constexpr (sizeof(typename MM<MT>::S) == 2)
+        return (c & ~31) | (((c >> 2) & 3) << 3) | (((c >> 4) & 1) << 2) | (c & 3);
+    else
+        return c;
+}
 
-__device__ __forceinline__ bool chunk_info(const ChunkArgs& a, int c, ChunkInfo& ci) {
-    const int n = a.chunk_seq[c];
-    if (n < 0) return false;
-    const int64_t s0 = a.cu_seqlens ? a.cu_seqlens[n] : 0;
-    const int64_t s1 = a.cu_seqlens ? a.cu_seqlens[n + 1] : a.T;
-    ci.n = n;
-    ci.bos = s0 + (int64_t)CH * (c - a.chunk_first[n]);
-    const int64_t rem = s1 - ci.bos;
-    ci.len = rem < CH ? (int)rem : CH;
-    return true;
+__device__ __forceinline__ uint32_t pack_tile_lo(const f32x4_t& t) { return pack_bf16x2(t[0], t[1]); }
+__device__ __forceinline__ uint32_t pack_tile_hi(const f32x4_t& t) { return pack_bf16x2(t[2], t[3]); }
+
+// acc[i] += A[16*i + .., :] B, where B (NP x 16, one column per lane%16) is given as NP/16
+// accumulator tiles Bt[p/16] (lane l holds B[16*t + 4*(l/16) + e][l%16] in Bt[t][e]), i.e.
+// the state or v_new straight from registers.  The reduction index is visited in the order
+// the tiles provide it: for a 32-wide bf16 step m, MFMA position 8*(l/16) + e is index
+// 32m + 4*(l/16) + e (e < 4) or 32m + 16 + 4*(l/16) + e - 4 (e >= 4) -- one 16-byte read of a
+// perm()-ordered A row; for an fp32 step (t, e) position l/16 is index 16t + 4*(l/16) + e.
+template <typename MT, int NP, int NI>
+__device__ __forceinline__ void gemm_regs(f32x4_t* acc, const typename MM<MT>::S* sA, int lda, const f32x4_t* Bt) {
+    const int l = threadIdx.x & 63, g4 = l >> 4, lr = l & 15;
+    if constexpr (sizeof(typename MM<MT>::S) == 2) {
+#pragma unroll
+        for (int m = 0; m < NP / 32; ++m) {
+            const uint4 bw = {pack_tile_lo(Bt[2 * m]), pack_tile_hi(Bt[2 * m]), pack_tile_lo(Bt[2 * m + 1]),
+                              pack_tile_hi(Bt[2 * m + 1])};
+            const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, bw);
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(sA + (16 * i + lr) * lda + 32 * m + 8 * g4);
+                acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[i], 0, 0, 0);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < NP / 16; ++t) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+#pragma unroll
+                for (int i = 0; i < NI; ++i) {
+                    const float av = sA[(16 * i + lr) * lda + 16 * t + 4 * g4 + e];
+                    acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, Bt[t][e], acc[i], 0, 0, 0);
+                }
+            }
+        }
+    }
 }
 
 // Eight consecutive elements held raw in registers, so that a whole tile's worth of
@@ -139,798 +179,659 @@ template <> struct Raw8<float> {
     }
 };
 
-// Ownership of a [64][D] row-major tile by 256 threads in vectors of 8 elements:
-// thread t holds NV = D/32 vectors, all in the same 8-column slot.
-template <int D> struct Tile64 {
-    static constexpr int VPR = D / 8;          // vectors per row
-    static constexpr int NV = D / 32;          // vectors per thread
-    static constexpr int RSTEP = 256 / VPR;    // row step between a thread's vectors
+// Ownership of a [ROWS][D] row-major tile by NTHR threads in vectors of 8 elements:
+// thread t holds NV vectors, all in the same 8-column slot.
+template <int ROWS, int D, int NTHR> struct Tile {
+    static constexpr int VPR = D / 8;
+    static_assert(NTHR % VPR == 0 && (ROWS * VPR) % NTHR == 0, "tile mapping");
+    static constexpr int NV = ROWS * VPR / NTHR;
+    static constexpr int RSTEP = NTHR / VPR;
     __device__ __forceinline__ static int row(int tid, int i) { return tid / VPR + RSTEP * i; }
     __device__ __forceinline__ static int col(int tid) { return (tid % VPR) * 8; }
 };
 
-// Chunk-local cumulative gate into LDS (and optionally to the workspace).
-// Scalar gate: sg[64]; per-K gate: sg[64][K].  Rows >= len repeat the last prefix.
-template <int K, bool PER_K>
-__device__ __forceinline__ void load_gamma(const ChunkArgs& a, const ChunkInfo& ci, int h, float* sg, bool from_ws,
-                                           bool write_ws) {
-    const int tid = threadIdx.x;
-    if constexpr (!PER_K) {
-        if (tid < 64) {
-            const int r = tid;
-            const int rc = r < ci.len ? r : ci.len - 1;
-            const int64_t idx = (ci.bos + rc) * a.HV + h;
-            float x;
-            if (from_ws) {
-                x = a.gcum[idx];
-            } else {
-                x = a.g[idx];
-                x = r < ci.len ? x : 0.0f;
-                // inclusive prefix sum across the 64 lanes of wave 0
-#pragma unroll
-                for (int d = 1; d < 64; d <<= 1) {
-                    const float y = __shfl_up(x, d, 64);
-                    if (r >= d) x += y;
-                }
-                if (write_ws && r < ci.len) a.gcum[idx] = x;
-            }
-            sg[r] = x;
-        }
-    } else {
-        // thread (c, quarter): 16 rows of one channel, loads issued as a batch
-        static_assert(K * 4 >= 256 || K * 4 == 256 || K == 64, "per-K gamma mapping");
-        constexpr int Q = 256 / K;            // row groups per channel (2 for K=128, 4 for K=64)
-        constexpr int RPQ = CH / Q;           // rows per group
-        __shared__ float part[Q][K];
-        const int c = tid % K, qd = tid / K;
-        float vals[RPQ];
-#pragma unroll
-        for (int i = 0; i < RPQ; ++i) {
-            const int r = qd * RPQ + i;
-            const int rc = r < ci.len ? r : ci.len - 1;
-            vals[i] = from_ws ? a.gcum[((ci.bos + rc) * a.HV + h) * K + c] : a.g[((ci.bos + rc) * a.HV + h) * K + c];
-        }
-        if (from_ws) {
-#pragma unroll
-            for (int i = 0; i < RPQ; ++i) sg[(qd * RPQ + i) * K + c] = vals[i];
-        } else {
-            float x = 0.0f;
-#pragma unroll
-            for (int i = 0; i < RPQ; ++i) {
-                const int r = qd * RPQ + i;
-                x += r < ci.len ? vals[i] : 0.0f;
-                vals[i] = x;
-            }
-            part[qd][c] = x;
-            __syncthreads();
-            float off = 0.0f;
-            for (int j = 0; j < qd; ++j) off += part[j][c];
-#pragma unroll
-            for (int i = 0; i < RPQ; ++i) {
-                const int r = qd * RPQ + i;
-                const float y = vals[i] + off;
-                sg[r * K + c] = y;
-                if (write_ws && r < ci.len) a.gcum[((ci.bos + r) * a.HV + h) * K + c] = y;
-            }
-        }
-    }
-}
-
-template <int K, bool PER_K>
-__device__ __forceinline__ float gam(const float* sg, int r, int c) {
-    if constexpr (PER_K) return sg[r * K + c];
-    else return sg[r];
-}
-
-// Decayed dot products for the per-K gate, the 16x16 diagonal blocks of a 64x64 matrix:
-// out[r][j] = sum_c x_r[c] y_j[c] exp(g_r[c] - g_j[c]) for j < r (j <= r when INCL), same block.
-template <int K, typename MT, bool INCL>
-__device__ void diag_blocks_per_k(const typename MM<MT>::S* sX, int ldx, const typename MM<MT>::S* sY, int ldy,
-                                  const float* sg, float* out, int ldo, const float* rowscale) {
-    // 4 blocks x 16 x 16 (r, j) pairs; one thread per pair, masked pairs skipped
-    for (int p = threadIdx.x; p < 4 * 256; p += blockDim.x) {
-        const int b = p >> 8, rr = (p >> 4) & 15, jj = p & 15;
-        const int r = 16 * b + rr, j = 16 * b + jj;
-        if (INCL ? (jj > rr) : (jj >= rr)) continue;
-        float acc = 0.0f;
-        for (int c = 0; c < K; ++c) {
-            const float d = exp_f32(sg[r * K + c] - sg[j * K + c]);
-            acc = fmaf(MM<MT>::back(sX[r * ldx + c]) * MM<MT>::back(sY[j * ldy + c]), d, acc);
-        }
-        out[r * ldo + j] = rowscale ? rowscale[r] * acc : acc;
-    }
-}
-
-// Off-diagonal blocks (I > J) for the per-K gate through MFMA with reference point
-// rho_I = gamma[16*I - 1]:  left = X_I * exp(gamma_I - rho_I), right = Y_{<16I} * exp(rho_I - gamma).
-template <int K, typename MT>
-__device__ void offdiag_blocks_per_k(const typename MM<MT>::S* sX, int ldx, const typename MM<MT>::S* sY, int ldy,
-                                     const float* sg, typename MM<MT>::S* sLft, typename MM<MT>::S* sRgt,
-                                     float* out, int ldo, const float* rowscale) {
-    typedef typename MM<MT>::S S;
-    constexpr int LD = K + MM<MT>::PAD;
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-    for (int I = 1; I < 4; ++I) {
-        const int rho_row = 16 * I - 1;
-        for (int idx = tid; idx < 16 * K; idx += blockDim.x) {
-            const int r = idx / K, c = idx % K;
-            const float rho = sg[rho_row * K + c];
-            const int rr = 16 * I + r;
-            sLft[r * LD + c] = MM<MT>::cvt(MM<MT>::back(sX[rr * ldx + c]) * exp_f32(sg[rr * K + c] - rho));
-        }
-        for (int idx = tid; idx < 16 * I * K; idx += blockDim.x) {
-            const int j = idx / K, c = idx % K;
-            const float rho = sg[rho_row * K + c];
-            sRgt[j * LD + c] = MM<MT>::cvt(MM<MT>::back(sY[j * ldy + c]) * exp_f32(rho - sg[j * K + c]));
-        }
-        __syncthreads();
-        for (int J = w; J < I; J += 4) {
-            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-            MM<MT>::nt(acc, sLft, LD, sRgt + 16 * J * LD, LD, K);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * I + 4 * (l >> 4) + e, j = 16 * J + (l & 15);
-                out[r * ldo + j] = rowscale ? rowscale[r] * acc[e] : acc[e];
-            }
-        }
-        __syncthreads();
-    }
-}
-
-// ---------------------------------------------------------------------------
-// index: chunk_first[n] = first chunk of sequence n; chunk_seq[c] = sequence of chunk c.
-__global__ __launch_bounds__(1024) void chunk_index_kernel(const ChunkArgs a) {
-    __shared__ int32_t part[1024];
-    const int tid = threadIdx.x;
-    const int N = a.N;
-    const int per = (N + 1023) / 1024;
-    const int n0 = tid * per, n1 = min(N, n0 + per);
-    int32_t sum = 0;
-    for (int n = n0; n < n1; ++n) {
-        const int64_t len = a.cu_seqlens ? (int64_t)a.cu_seqlens[n + 1] - a.cu_seqlens[n] : a.T;
-        sum += (int32_t)((len + CH - 1) / CH);
-    }
-    part[tid] = sum;
-    __syncthreads();
-    for (int d = 1; d < 1024; d <<= 1) {  // inclusive scan
-        const int32_t y = tid >= d ? part[tid - d] : 0;
-        __syncthreads();
-        part[tid] += y;
-        __syncthreads();
-    }
-    int32_t first = part[tid] - sum;
-    for (int n = n0; n < n1; ++n) {
-        const int64_t len = a.cu_seqlens ? (int64_t)a.cu_seqlens[n + 1] - a.cu_seqlens[n] : a.T;
-        const int32_t nc = (int32_t)((len + CH - 1) / CH);
-        a.chunk_first[n] = first;
-        for (int j = 0; j < nc; ++j) a.chunk_seq[first + j] = n;
-        first += nc;
-    }
-    const int32_t total = part[1023];
-    if (tid == 0) a.chunk_first[N] = total;
-    for (int c = total + tid; c < a.max_chunks; c += 1024) a.chunk_seq[c] = -1;
-}
-
-// ---------------------------------------------------------------------------
-// H2: intra-chunk WY/UT transform.
-// LDS phases: (1) K rows -> L; (2) A = (I + L)^-1 in fp32; (3) W and U on MFMA.  The
-// K rows (phase 1) and the transposed operands of phase 3 share one region.
-template <int K, int V, typename IO, typename MT, bool PER_K>
-struct PrepSmem {
-    typedef typename MM<MT>::S S;
-    static constexpr int LDK = K + MM<MT>::PAD;     // rows over K
-    static constexpr int LDT = CH + MM<MT>::PAD;    // rows over the 64 chunk positions
-    static constexpr int LDL = CH + 1;              // fp32 L and A
-    static constexpr size_t g_off = 0;                                                // f32 [64] or [64][K]
-    static constexpr size_t b_off = g_off + sizeof(float) * CH * (PER_K ? K : 1);     // f32 [64]
-    static constexpr size_t l_off = b_off + sizeof(float) * CH;                       // f32 [64][LDL]
-    static constexpr size_t a_off = l_off + sizeof(float) * CH * LDL;                 // f32 [64][LDL]
-    static constexpr size_t u_off = a_off + sizeof(float) * CH * LDL;                 // union
-    // phase 1
-    static constexpr size_t k_off = u_off;                                            // S [64][LDK]
-    static constexpr size_t lft_off = k_off + sizeof(S) * CH * LDK;
-    static constexpr size_t rgt_off = lft_off + (PER_K ? sizeof(S) * 16 * LDK : 0);
-    static constexpr size_t ph1_end = rgt_off + (PER_K ? sizeof(S) * 48 * LDK : 0);
-    // phase 3
-    static constexpr size_t am_off = u_off;                                           // S [64][LDT]
-    static constexpr size_t kst_off = am_off + sizeof(S) * CH * LDT;                  // S [K][LDT]
-    static constexpr size_t vst_off = kst_off + sizeof(S) * K * LDT;                  // S [V][LDT]
-    static constexpr size_t ph3_end = vst_off + sizeof(S) * V * LDT;
-    static constexpr size_t total = ph1_end > ph3_end ? ph1_end : ph3_end;
+// Ownership of a [64][D] row-major tile by NTHR threads for transposed LDS builds: thread t
+// holds the row pair p = t % 32 (rows 2p, 2p+1) of the 8-column group cg = t / 32 (+ NTHR/32
+// per pass).  A half-wave then covers all 32 row pairs of one column group, so the transpose
+// is written one 32-bit word (two rows) per column into 32 consecutive words -- no LDS bank
+// conflicts -- without unpacking the bf16 data.  Threads past the last column group (only when
+// NTHR / 32 > D / 8) duplicate group 0's loads and store nothing.
+template <int D, int NTHR> struct PairTile {
+    static constexpr int CG = D / 8;
+    static constexpr int NPASS = (CG * 32 + NTHR - 1) / NTHR;
+    __device__ __forceinline__ static int pair(int tid) { return tid & 31; }
+    __device__ __forceinline__ static int group(int tid, int i) { return (tid >> 5) + (NTHR / 32) * i; }
+    __device__ __forceinline__ static bool valid(int tid, int i) { return group(tid, i) < CG; }
+    __device__ __forceinline__ static int col(int tid, int i) { return valid(tid, i) ? 8 * group(tid, i) : 0; }
 };
 
-// A = (I + L)^-1 for a strictly lower 64x64 L (fp32, row stride LDL) into sA.
-// The four unit-lower 16x16 diagonal blocks are inverted by forward substitution; then
-// row block by row block, A_IJ = -D_I sum_{M=J}^{I-1} L_IM A_MJ on fp32 MFMA, the two
-// products chained in registers (the C layout of the first is the B operand of the
-// second once the reduction index runs over rows 4*(l/16) + e, step e).
-template <int LDL>
-__device__ __forceinline__ void invert_unit_lower_64(const float* sL, float* sA) {
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g4 = l >> 4;
-    for (int idx = tid; idx < CH * CH; idx += 256) {      // zero the strictly upper blocks
-        const int r = idx / CH, j = idx % CH;
-        if ((j >> 4) > (r >> 4)) sA[r * LDL + j] = 0.0f;
+// Element e (0..7) of a raw 8-element vector as a 16-bit pattern / as float.
+__device__ __forceinline__ uint32_t raw16(const Raw8<bf16_t>& x, int e) {
+    const uint32_t w = e < 2 ? x.w.x : e < 4 ? x.w.y : e < 6 ? x.w.z : x.w.w;
+    return (e & 1) ? (w >> 16) : (w & 0xFFFFu);
+}
+
+// Transposed store of a row pair: dst[(c8 + e) * ldt + perm(r0)] = {row r0, row r0 + 1}[e].
+template <typename MT, typename IO>
+__device__ __forceinline__ void st_pair_t(typename MM<MT>::S* dst, int ldt, int c8, int r0, const Raw8<IO>& x0,
+                                          bool v0, const Raw8<IO>& x1, bool v1) {
+    if constexpr (sizeof(typename MM<MT>::S) == 2 && std::is_same<IO, bf16_t>::value) {
+        const int pr = perm<MT>(r0);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t lo = v0 ? raw16(x0, e) : 0u, hi = v1 ? raw16(x1, e) : 0u;
+            *reinterpret_cast<uint32_t*>(dst + (c8 + e) * ldt + pr) = lo | (hi << 16);
+        }
+    } else {
+        float a[8], b[8];
+        x0.get(a, v0);
+        x1.get(b, v1);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            dst[(c8 + e) * ldt + perm<MT>(r0)] = MM<MT>::cvt(a[e]);
+            dst[(c8 + e) * ldt + perm<MT>(r0 + 1)] = MM<MT>::cvt(b[e]);
+        }
     }
-    if (l < 16) {
-        const int b0 = 16 * w, j = l;
+}
+
+// Scaled transposed store of a row pair: dst[(c8 + e) * ldt + perm(r)] = x_r[e] * f(r, c8 + e).
+template <typename MT, typename IO, typename F>
+__device__ __forceinline__ void st_pair_t_scaled(typename MM<MT>::S* dst, int ldt, int c8, int r0,
+                                                 const Raw8<IO>& x0, bool v0, const Raw8<IO>& x1, bool v1, F f) {
+    float a[8], b[8];
+    x0.get(a, v0);
+    x1.get(b, v1);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float ya = a[e] * f(r0, c8 + e), yb = b[e] * f(r0 + 1, c8 + e);
+        if constexpr (sizeof(typename MM<MT>::S) == 2) {
+            *reinterpret_cast<uint32_t*>(dst + (c8 + e) * ldt + perm<MT>(r0)) = pack_bf16x2(ya, yb);
+        } else {
+            dst[(c8 + e) * ldt + r0] = ya;
+            dst[(c8 + e) * ldt + r0 + 1] = yb;
+        }
+    }
+}
+
+// D = (I + N)^-1 for a strictly lower 16x16 N (fp32, stride 17), by forward substitution:
+// lane j < 16 of the calling wave computes column j.  D is written row-major (stride ldd) in
+// the MFMA operand dtype.
+template <typename MT>
+__device__ __forceinline__ void invert_unit_lower_16(const float* sN, typename MM<MT>::S* sD, int ldd) {
+    const int j = threadIdx.x & 63;
+    if (j < 16) {
         float x[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             float acc = (i == j) ? 1.0f : 0.0f;
 #pragma unroll
-            for (int m = 0; m < i; ++m) acc = fmaf(-sL[(b0 + i) * LDL + b0 + m], x[m], acc);
+            for (int m = 0; m < i; ++m) acc = fmaf(-sN[i * 17 + m], x[m], acc);
             x[i] = acc;
         }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sA[(b0 + i) * LDL + b0 + j] = x[i];
-    }
-    __syncthreads();
-    for (int I = 1; I < 4; ++I) {
-        if (w < I) {
-            const int J = w;
-            f32x4_t t = {0.f, 0.f, 0.f, 0.f};
-            for (int M = J; M < I; ++M) {
-#pragma unroll
-                for (int st = 0; st < 4; ++st) {
-                    const float av = sL[(16 * I + (l & 15)) * LDL + 16 * M + 4 * st + g4];
-                    const float bv = sA[(16 * M + 4 * st + g4) * LDL + 16 * J + (l & 15)];
-                    t = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, t, 0, 0, 0);
-                }
-            }
-            f32x4_t x = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float av = sA[(16 * I + (l & 15)) * LDL + 16 * I + 4 * g4 + e];
-                x = __builtin_amdgcn_mfma_f32_16x16x4f32(av, t[e], x, 0, 0, 0);
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sA[(16 * I + 4 * g4 + e) * LDL + 16 * J + (l & 15)] = -x[e];
-        }
-        __syncthreads();
+        for (int i = 0; i < 16; ++i) sD[i * ldd + j] = MM<MT>::cvt(x[i]);
     }
 }
 
-template <int K, int V, typename IO, typename MT, bool PER_K>
-__global__ __launch_bounds__(256) void chunk_prepare_kernel(const ChunkArgs a) {
-    typedef PrepSmem<K, V, IO, MT, PER_K> L;
-    typedef typename MM<MT>::S S;
-    __shared__ __align__(16) char smem[L::total];
-    float* sg = reinterpret_cast<float*>(smem + L::g_off);
-    float* sb = reinterpret_cast<float*>(smem + L::b_off);
-    float* sL = reinterpret_cast<float*>(smem + L::l_off);
-    float* sA = reinterpret_cast<float*>(smem + L::a_off);
-    S* sK = reinterpret_cast<S*>(smem + L::k_off);
-    S* sAm = reinterpret_cast<S*>(smem + L::am_off);
-    S* sKsT = reinterpret_cast<S*>(smem + L::kst_off);
-    S* sVsT = reinterpret_cast<S*>(smem + L::vst_off);
-
-    ChunkInfo ci;
-    if (!chunk_info(a, blockIdx.x, ci)) return;
-    const int h = blockIdx.y;
-    const int hk = h / (a.HV / a.HK);
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-
-    // all global loads of the chunk first: K and V rows, beta
-    typedef Tile64<K> TK;
-    typedef Tile64<V> TV;
-    Raw8<IO> kr[TK::NV], vr[TV::NV];
+// X = (I + L)^-1 B for one 16-column tile of B (64 rows), by blocked forward substitution:
+// X_I = D_I (B_I - sum_{J<I} L_IJ X_J), D_I = (I + L_II)^-1.  L's off-diagonal blocks are read
+// negated from sLo (row-major, stride ldo), the D_I from sD (block I at sD + 16*I*ldd).  Row t
+// of the B tile is sBt[perm(t)] * sc[t] (sBt: the transposed-B row of this lane's column).
+// X stays in registers in C layout; with v_mfma_f32_16x16x16_bf16 the C layout of one block
+// is the B operand layout of the next product, so each wave solves its own columns without
+// synchronising with the others.
+template <typename MT>
+__device__ __forceinline__ void block_solve(f32x4_t* X, const typename MM<MT>::S* sLo, int ldo,
+                                            const typename MM<MT>::S* sD, int ldd,
+                                            const typename MM<MT>::S* sBt, const float* sc) {
+    const int l = threadIdx.x & 63, g4 = l >> 4, lr = l & 15;
 #pragma unroll
-    for (int i = 0; i < TK::NV; ++i) {
-        const int r = TK::row(tid, i), rc = r < ci.len ? r : ci.len - 1;
-        kr[i].load(a.k, ((ci.bos + rc) * a.HK + hk) * K + TK::col(tid));
-    }
+    for (int I = 0; I < 4; ++I) {
+        const int t0 = 16 * I + 4 * g4;
+        f32x4_t R;
+        if constexpr (sizeof(typename MM<MT>::S) == 2) {
+            const uint2 raw = *reinterpret_cast<const uint2*>(sBt + perm<MT>(t0));
+            R[0] = __uint_as_float(raw.x << 16) * sc[t0];
+            R[1] = __uint_as_float(raw.x & 0xFFFF0000u) * sc[t0 + 1];
+            R[2] = __uint_as_float(raw.y << 16) * sc[t0 + 2];
+            R[3] = __uint_as_float(raw.y & 0xFFFF0000u) * sc[t0 + 3];
 #pragma unroll
-    for (int i = 0; i < TV::NV; ++i) {
-        const int r = TV::row(tid, i), rc = r < ci.len ? r : ci.len - 1;
-        vr[i].load(a.v, ((ci.bos + rc) * a.HV + h) * V + TV::col(tid));
-    }
-    float bt = 0.0f;
-    if (tid < CH) {
-        const int rc = tid < ci.len ? tid : ci.len - 1;
-        bt = Elem<IO>::load(a.beta, (ci.bos + rc) * a.HV + h);
-    }
-    load_gamma<K, PER_K>(a, ci, h, sg, false, true);
-    if (tid < CH) sb[tid] = tid < ci.len ? bt : 0.0f;
-#pragma unroll
-    for (int i = 0; i < TK::NV; ++i) {
-        float x[8];
-        kr[i].get(x, TK::row(tid, i) < ci.len);
-        MM<MT>::st8(sK + TK::row(tid, i) * L::LDK + TK::col(tid), x);
-    }
-    __syncthreads();
-
-    // L = strictly lower beta_r * (k_r . k_j) * decay(r, j)
-    if constexpr (!PER_K) {
-        for (int t = w; t < 16; t += 4) {
-            const int I = t >> 2, J = t & 3;
-            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-            if (I >= J) MM<MT>::nt(acc, sK + 16 * I * L::LDK, L::LDK, sK + 16 * J * L::LDK, L::LDK, K);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * I + 4 * (l >> 4) + e, j = 16 * J + (l & 15);
-                sL[r * L::LDL + j] = (r > j) ? sb[r] * exp_f32(sg[r] - sg[j]) * acc[e] : 0.0f;
+            for (int J = 0; J < I; ++J) {
+                const s16x4_t av = *reinterpret_cast<const s16x4_t*>(sLo + (16 * I + lr) * ldo + 16 * J + 4 * g4);
+                const s16x4_t bv = __builtin_bit_cast(s16x4_t, uint2{pack_tile_lo(X[J]), pack_tile_hi(X[J])});
+                R = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, R, 0, 0, 0);
             }
+            const s16x4_t dv = *reinterpret_cast<const s16x4_t*>(sD + (16 * I + lr) * ldd + 4 * g4);
+            const s16x4_t rv = __builtin_bit_cast(s16x4_t, uint2{pack_tile_lo(R), pack_tile_hi(R)});
+            X[I] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(dv, rv, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) R[e] = sBt[t0 + e] * sc[t0 + e];
+#pragma unroll
+            for (int J = 0; J < I; ++J) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    R = __builtin_amdgcn_mfma_f32_16x16x4f32(sLo[(16 * I + lr) * ldo + 16 * J + 4 * g4 + e], X[J][e],
+                                                             R, 0, 0, 0);
+            }
+            f32x4_t x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                x = __builtin_amdgcn_mfma_f32_16x16x4f32(sD[(16 * I + lr) * ldd + 4 * g4 + e], R[e], x, 0, 0, 0);
+            X[I] = x;
         }
+    }
+}
+
+// The 6 strictly lower (I, J) tiles of a 64x64 matrix: (1,0),(2,0),(2,1),(3,0),(3,1),(3,2);
+// and the 10 lower tiles incl. the diagonal: (0,0),(1,0),(1,1),(2,0),...
+__device__ __forceinline__ void strict_tile(int t, int& I, int& J) {
+    I = t >= 3 ? 3 : t >= 1 ? 2 : 1;
+    J = t - I * (I - 1) / 2;
+}
+__device__ __forceinline__ void lower_tile(int t, int& I, int& J) {
+    I = t >= 6 ? 3 : t >= 3 ? 2 : t >= 1 ? 1 : 0;
+    J = t - I * (I + 1) / 2;
+}
+
+// Store the 8 consecutive logical columns c8 .. c8+7 of a row into a perm()-ordered LDS row.
+template <typename MT, typename IO>
+__device__ __forceinline__ void st8_perm(typename MM<MT>::S* row, int c8, const Raw8<IO>& x, bool valid) {
+    if constexpr (sizeof(typename MM<MT>::S) == 2 && std::is_same<IO, bf16_t>::value) {
+        const uint4 w = x.w;
+        const uint2 lo = valid ? uint2{w.x, w.y} : uint2{0u, 0u};
+        const uint2 hi = valid ? uint2{w.z, w.w} : uint2{0u, 0u};
+        *reinterpret_cast<uint2*>(row + perm<MT>(c8)) = lo;
+        *reinterpret_cast<uint2*>(row + perm<MT>(c8 + 4)) = hi;
     } else {
-        S* sLft = reinterpret_cast<S*>(smem + L::lft_off);
-        S* sRgt = reinterpret_cast<S*>(smem + L::rgt_off);
-        for (int idx = tid; idx < CH * CH; idx += 256) {
-            const int r = idx / CH, j = idx % CH;
-            if (j >= r) sL[r * L::LDL + j] = 0.0f;
-        }
-        diag_blocks_per_k<K, MT, false>(sK, L::LDK, sK, L::LDK, sg, sL, L::LDL, sb);
-        offdiag_blocks_per_k<K, MT>(sK, L::LDK, sK, L::LDK, sg, sLft, sRgt, sL, L::LDL, sb);
-    }
-    __syncthreads();
-
-    invert_unit_lower_64<L::LDL>(sL, sA);
-
-    // phase 3 operands: A (MFMA dtype), (beta e^gamma K)^T and (beta V)^T from registers
-    for (int idx = tid; idx < CH * CH; idx += 256) {
-        const int r = idx / CH, j = idx % CH;
-        sAm[r * L::LDT + j] = MM<MT>::cvt(sA[r * L::LDL + j]);
-    }
-#pragma unroll
-    for (int i = 0; i < TK::NV; ++i) {
-        const int r = TK::row(tid, i), c8 = TK::col(tid);
-        float x[8];
-        kr[i].get(x, r < ci.len);
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            sKsT[(c8 + e) * L::LDT + r] = MM<MT>::cvt(x[e] * sb[r] * exp_f32(gam<K, PER_K>(sg, r, c8 + e)));
-    }
-#pragma unroll
-    for (int i = 0; i < TV::NV; ++i) {
-        const int r = TV::row(tid, i), c8 = TV::col(tid);
-        float x[8];
-        vr[i].get(x, r < ci.len);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sVsT[(c8 + e) * L::LDT + r] = MM<MT>::cvt(x[e] * sb[r]);
-    }
-    __syncthreads();
-
-    // W = A (beta e^gamma K), U = A (beta V)
-    constexpr int TW = 4 * (K / 16), TU = 4 * (V / 16);
-    for (int t = w; t < TW + TU; t += 4) {
-        const bool isw = t < TW;
-        const int tt = isw ? t : t - TW;
-        const int D = isw ? K : V;
-        const int I = tt / (D / 16), J = tt % (D / 16);
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-        // A is lower triangular: row block I only needs columns below 16*(I+1)
-        const int kdim = MM<MT>::PAD == 8 ? ((16 * (I + 1) + 31) / 32) * 32 : 16 * (I + 1);
-        MM<MT>::nt(acc, sAm + 16 * I * L::LDT, L::LDT, (isw ? sKsT : sVsT) + 16 * J * L::LDT, L::LDT, kdim);
-        void* dst = isw ? a.w : a.u;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = 16 * I + 4 * (l >> 4) + e, c = 16 * J + (l & 15);
-            if (r < ci.len) Elem<IO>::store(dst, ((ci.bos + r) * a.HV + h) * D + c, acc[e]);
-        }
+        float f[8];
+        x.get(f, valid);
+        MM<MT>::st8(row + c8, f);
     }
 }
 
 // ---------------------------------------------------------------------------
-// H3: inter-chunk state pass.  A workgroup owns BV = 64*NT value columns of one
-// (sequence, head); wave w owns 16*NT of them: v = BV*blockIdx.x + 16*(NT*w + nt) + lane%16.
-// The state S[v][k] of a 16-column slice lives in K/16 accumulator tiles: tile kt,
-// element e of lane l holds S[v][16*kt + 4*(l/16) + e].  That layout is the MFMA B
-// operand of the next product once the reduction index is permuted consistently on the
-// A side, so S and v_new never leave registers.  The next chunk's inputs are loaded into
-// registers while the current chunk computes.
-template <int K, typename MT> struct StateSmem {
+// LDS layout (bytes).  A-operand rows of the MFMA products are perm()-ordered.
+template <int K, int BV, typename MT, bool PER_K>
+struct Layout {
     typedef typename MM<MT>::S S;
-    static constexpr int LDW = K + MM<MT>::PAD;                  // -W rows [64][LDW]
-    static constexpr bool TRANS = sizeof(S) == 2;                // bf16: K_d^T [K][LDT]; fp32: K_d [64][LDW]
-    static constexpr int LDT = CH + MM<MT>::PAD;
-    static constexpr size_t w_off = 0;
-    static constexpr size_t kd_off = w_off + sizeof(S) * CH * LDW;
-    static constexpr size_t dec_off = kd_off + (TRANS ? sizeof(S) * K * LDT : sizeof(S) * CH * LDW);
-    static constexpr size_t u_off = dec_off + sizeof(float) * K;              // U tile f32 [64][BVMAX+1]
-    static constexpr int LDU = 128 + 1;
-    static constexpr size_t total = u_off + sizeof(float) * CH * LDU;
+    static constexpr bool BF = sizeof(S) == 2;
+    static constexpr int LDK = K + MM<MT>::PAD;   // rows over the K channels
+    static constexpr int LDT = CH + MM<MT>::PAD;  // rows over the 64 chunk positions
+    static constexpr int LDO = CH + MM<MT>::PAD;  // -L off-diagonal blocks, natural order
+    static constexpr int LDD = 16 + MM<MT>::PAD;  // diagonal-block inverses
+    static constexpr size_t ROWK = sizeof(S) * CH * LDK;   // [64][LDK]
+    static constexpr size_t ROWT = sizeof(S) * CH * LDT;   // [64][LDT]
+    static constexpr size_t KT_ = sizeof(S) * K * LDT;     // [K][LDT]
+    static constexpr size_t VT_ = sizeof(S) * BV * LDT;    // [BV][LDT]
+    static constexpr size_t LO_ = sizeof(S) * CH * LDO;    // [64][LDO]
+    static constexpr size_t LD_ = sizeof(float) * 4 * 16 * 17;  // diagonal L blocks, fp32
+    static constexpr size_t D_ = sizeof(S) * CH * LDD;     // [4*16][LDD]
+
+    // ---- scalar gate ----
+    static constexpr size_t g_q = 0;              // Q rows
+    static constexpr size_t g_k = g_q + ROWK;     // K rows
+    static constexpr size_t g_w = g_k + ROWK;     // -W rows
+    static constexpr size_t g_kt = g_w + ROWK;    // K^T
+    static constexpr size_t g_vt = g_kt + KT_;    // V^T
+    static constexpr size_t g_lo = g_vt + VT_;
+    static constexpr size_t g_ld = g_lo + LO_;
+    static constexpr size_t g_d = g_ld + LD_;
+    static constexpr size_t g_p = g_d + D_;       // P rows
+    static constexpr size_t g_g = g_p + ROWT;     // gamma [64]
+    static constexpr size_t g_b = g_g + sizeof(float) * CH;    // beta [64]
+    static constexpr size_t g_be = g_b + sizeof(float) * CH;   // beta e^gamma [64]
+    static constexpr size_t g_total = g_be + sizeof(float) * CH;
+
+    // ---- per-K gate: fixed part, then X (phases A-B, then C-E) and Y (B-D), W (D-E) ----
+    static constexpr size_t k_g = 0;                                  // gamma [64][K]
+    static constexpr size_t k_gl = k_g + sizeof(float) * CH * K;      // e^{gamma_last} [K]
+    static constexpr size_t k_b = k_gl + sizeof(float) * K;           // beta [64]
+    static constexpr size_t k_p = k_b + sizeof(float) * CH;           // P rows
+    static constexpr size_t X = k_p + ROWT;
+    static constexpr size_t AB = 2 * ROWK + sizeof(S) * 80 * LDK;     // Q, K rows; 16 + 16 + 48 operand rows
+    static constexpr size_t CE = KT_ + VT_ + ROWK + KT_;              // (K e^g)^T, V^T, Q e^g, (K e^{gl-g})^T
+    static constexpr size_t SX = AB > CE ? AB : CE;
+    static constexpr size_t k_q = X;
+    static constexpr size_t k_k = k_q + ROWK;
+    static constexpr size_t k_lk = k_k + ROWK;                        // K_I e^{gamma - rho}   [16][LDK]
+    static constexpr size_t k_lq = k_lk + sizeof(S) * 16 * LDK;       // Q_I e^{gamma - rho}   [16][LDK]
+    static constexpr size_t k_rg = k_lq + sizeof(S) * 16 * LDK;       // K_<I e^{rho - gamma}  [48][LDK]
+    static constexpr size_t k_kgt = X;
+    static constexpr size_t k_vt = k_kgt + KT_;
+    static constexpr size_t k_qt = k_vt + VT_;
+    static constexpr size_t k_kdt = k_qt + ROWK;
+    static constexpr size_t Y = X + SX;
+    static constexpr size_t k_lo = Y;
+    static constexpr size_t k_ld = k_lo + LO_;
+    static constexpr size_t k_d = k_ld + LD_;
+    static constexpr size_t k_w = k_d + D_;
+    static constexpr size_t k_part = k_w;                             // gamma partial sums (phase A)
+    static constexpr size_t k_total = k_w + ROWK;
+
+    // output tile staging [64][BV] in the IO type, 16-byte granules XOR-swizzled by row.  It is
+    // written at the end of E and flushed at the start of the next iteration; the -L and
+    // diagonal-inverse area it overlays is rewritten only in B/C, after the next phase-A barrier.
+    static constexpr size_t o_stage = PER_K ? k_lo : g_lo;
+    static constexpr size_t total = PER_K ? k_total : g_total;
 };
 
-template <int K, int V, typename IO, typename MT, bool PER_K, int NT>
-__global__ __launch_bounds__(256) void chunk_state_kernel(const ChunkArgs a) {
-    typedef StateSmem<K, MT> L;
-    typedef typename MM<MT>::S S;
-    typedef Tile64<K> TK;
-    constexpr int BV = 64 * NT;
-    __shared__ __align__(16) char smem[L::total];
-    S* sW = reinterpret_cast<S*>(smem + L::w_off);
-    S* sKd = reinterpret_cast<S*>(smem + L::kd_off);
-    float* sDec = reinterpret_cast<float*>(smem + L::dec_off);
-    float* sU = reinterpret_cast<float*>(smem + L::u_off);
-    typedef Tile64<BV> TU;
+template <int BV, typename IO>
+struct OStage {
+    static constexpr int SZ = sizeof(IO) == 4 ? 4 : 2;
+    static constexpr int ROWB = BV * SZ;        // bytes per staged row
+    static constexpr int NG = ROWB / 16;        // 16-byte granules per row
+    static constexpr int EPG = 16 / SZ;         // elements per granule
+    static constexpr size_t bytes = (size_t)CH * ROWB;
+    __device__ __forceinline__ static int off(int r, int c) {
+        const int gr = (c / EPG) ^ (r % NG);
+        return r * ROWB + gr * 16 + (c % EPG) * SZ;
+    }
+};
 
-    const int h = blockIdx.y, n = blockIdx.z;
+template <int K, int BV, typename IO, typename MT, bool PER_K>
+__global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) {
+    constexpr int NW = BV / 16;       // waves; wave w owns value columns 16w .. 16w+15 of the tile
+    constexpr int NTHR = 64 * NW;
+    constexpr int KT = K / 16;
+    typedef MM<MT> M;
+    typedef typename M::S S;
+    typedef Layout<K, BV, MT, PER_K> Lay;
+    constexpr int LDK = Lay::LDK, LDT = Lay::LDT, LDO = Lay::LDO, LDD = Lay::LDD;
+    static_assert(NW >= 4, "four waves invert the diagonal blocks");
+    typedef OStage<BV, IO> OS;
+    static_assert(Lay::total <= 160 * 1024, "LDS budget");
+    static_assert(OS::bytes <= Lay::LO_ + Lay::LD_ + Lay::D_, "output staging overlays -L and the inverses");
+    __shared__ __align__(16) char smem[Lay::total];
+    auto SP = [&](size_t off) { return reinterpret_cast<S*>(smem + off); };
+    auto FP = [&](size_t off) { return reinterpret_cast<float*>(smem + off); };
+
+    const int vt = blockIdx.x, h = blockIdx.y, n = blockIdx.z;
     const int hk = h / (a.HV / a.HK);
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g4 = l >> 4;
-    int vcol[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) vcol[nt] = BV * blockIdx.x + 16 * (NT * w + nt) + (l & 15);
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g4 = l >> 4, lr = l & 15;
+    const int v0 = vt * BV;
+    const int vcol = v0 + 16 * w + lr;
     const int64_t s0 = a.cu_seqlens ? a.cu_seqlens[n] : 0;
     const int64_t s1 = a.cu_seqlens ? a.cu_seqlens[n + 1] : a.T;
     const int nc = (int)((s1 - s0 + CH - 1) / CH);
-    const int c0 = a.chunk_first[n];
-    const int c8 = TK::col(tid);
-    constexpr int GE = PER_K ? 8 : 1;
 
-    constexpr int KT = K / 16;
-    f32x4_t hs[NT][KT];
+    // state tiles: hs[kt][e] = S[vcol][16*kt + 4*(l/16) + e]
+    f32x4_t hs[KT];
+    const int64_t sidx = (((int64_t)n * a.HV + h) * a.V + vcol) * K;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        const int64_t sidx = (((int64_t)n * a.HV + h) * V + vcol[nt]) * K;
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
-            if (a.h0) {
-                hs[nt][kt] = *reinterpret_cast<const f32x4_t*>(a.h0 + sidx + 16 * kt + 4 * g4);
-            } else {
-                hs[nt][kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            }
+    for (int kt = 0; kt < KT; ++kt) {
+        hs[kt] = a.h0 ? *reinterpret_cast<const f32x4_t*>(a.h0 + sidx + 16 * kt + 4 * g4)
+                      : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // strictly upper tiles of P are never written: zero them once
+    {
+        S* sP = SP(PER_K ? Lay::k_p : Lay::g_p);
+        for (int idx = tid; idx < CH * CH; idx += NTHR) {
+            const int r = idx / CH, j = idx % CH;
+            if ((j >> 4) > (r >> 4)) sP[r * LDT + perm<MT>(j)] = M::cvt(0.0f);
         }
     }
 
-    // registers holding the next chunk's inputs (loaded one chunk ahead)
-    Raw8<IO> wr[TK::NV], kr[TK::NV], ur[TU::NV];
-    float gr[TK::NV][GE], gl[GE], gdec = 0.0f;
-    auto prefetch = [&](int ci) {
+    // ---- per-chunk inputs, double-buffered in registers ----
+    typedef Tile<CH, K, NTHR> TQ;           // q rows
+    typedef PairTile<K, NTHR> PK;            // k row pairs
+    typedef PairTile<BV, NTHR> PV;           // v row pairs
+    constexpr int GQ = NTHR / K;                   // per-K gate: row groups per channel
+    constexpr int RPQ = PER_K ? CH / GQ : 1;       // gate values per thread
+    Raw8<IO> qn[TQ::NV], kn[2 * PK::NPASS], vn[2 * PV::NPASS];
+    float gn[RPQ];
+    uint32_t bn = 0;  // beta kept as loaded (bf16 bits or fp32 bits): converting here would wait on the load
+    auto load_chunk = [&](int ci) {
         const int64_t bos = s0 + (int64_t)CH * ci;
         const int len = (s1 - bos) < CH ? (int)(s1 - bos) : CH;
-        const int64_t last = bos + len - 1;
 #pragma unroll
-        for (int i = 0; i < TK::NV; ++i) {
-            const int r = TK::row(tid, i), rc = r < len ? r : len - 1;
-            wr[i].load(a.w, ((bos + rc) * a.HV + h) * K + c8);
-            kr[i].load(a.k, ((bos + rc) * a.HK + hk) * K + c8);
-#pragma unroll
-            for (int e = 0; e < GE; ++e)
-                gr[i][e] = PER_K ? a.gcum[((bos + rc) * a.HV + h) * K + c8 + e] : a.gcum[(bos + rc) * a.HV + h];
+        for (int i = 0; i < TQ::NV; ++i) {
+            const int r = TQ::row(tid, i), rc = r < len ? r : len - 1;
+            qn[i].load(a.q, ((bos + rc) * a.HK + hk) * K + TQ::col(tid));
         }
 #pragma unroll
-        for (int e = 0; e < GE; ++e) gl[e] = PER_K ? a.gcum[(last * a.HV + h) * K + c8 + e] : a.gcum[last * a.HV + h];
-        if (tid < K) gdec = PER_K ? a.gcum[(last * a.HV + h) * K + tid] : a.gcum[last * a.HV + h];
+        for (int i = 0; i < PK::NPASS; ++i) {
 #pragma unroll
-        for (int i = 0; i < TU::NV; ++i) {
-            const int r = TU::row(tid, i), rc = r < len ? r : len - 1;
-            ur[i].load(a.u, ((bos + rc) * a.HV + h) * V + BV * blockIdx.x + TU::col(tid));
+            for (int u = 0; u < 2; ++u) {
+                const int r = 2 * PK::pair(tid) + u, rc = r < len ? r : len - 1;
+                kn[2 * i + u].load(a.k, ((bos + rc) * a.HK + hk) * K + PK::col(tid, i));
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < PV::NPASS; ++i) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int r = 2 * PV::pair(tid) + u, rc = r < len ? r : len - 1;
+                vn[2 * i + u].load(a.v, ((bos + rc) * a.HV + h) * a.V + v0 + PV::col(tid, i));
+            }
+        }
+        if constexpr (PER_K) {
+            const int c = tid % K, qd = tid / K;
+#pragma unroll
+            for (int i = 0; i < RPQ; ++i) {
+                const int r = qd * RPQ + i, rc = r < len ? r : len - 1;
+                gn[i] = a.g[((bos + rc) * a.HV + h) * K + c];
+            }
+        } else {
+            const int rc = (tid & 63) < len ? (tid & 63) : len - 1;
+            gn[0] = a.g[(bos + rc) * a.HV + h];
+        }
+        {
+            const int rc = (tid & 63) < len ? (tid & 63) : len - 1;
+            const int64_t bi = (bos + rc) * a.HV + h;
+            if constexpr (std::is_same<IO, float>::value) bn = __float_as_uint(static_cast<const float*>(a.beta)[bi]);
+            else bn = static_cast<const uint16_t*>(a.beta)[bi];
         }
     };
-    if (nc > 0) prefetch(0);
+    if (nc > 0) load_chunk(0);
+
+    // staged output rows of a chunk -> o, one 16-byte granule per thread and pass
+    char* const so = smem + Lay::o_stage;
+    auto flush_o = [&](int64_t bos, int len) {
+        for (int idx = tid; idx < CH * OS::NG; idx += NTHR) {
+            const int r = idx / OS::NG, gi = idx % OS::NG;
+            if (r < len) {
+                const uint4 x = *reinterpret_cast<const uint4*>(so + OS::off(r, gi * OS::EPG));
+                char* dst = static_cast<char*>(a.o) + (((bos + r) * a.HV + h) * a.V + v0 + gi * OS::EPG) * OS::SZ;
+                *reinterpret_cast<uint4*>(dst) = x;
+            }
+        }
+    };
 
     for (int ci = 0; ci < nc; ++ci) {
         const int64_t bos = s0 + (int64_t)CH * ci;
         const int len = (s1 - bos) < CH ? (int)(s1 - bos) : CH;
-        const int c = c0 + ci;
 
-        // stage -W and the decayed keys K_d = K * e^{gamma_last - gamma} from registers
+        // current chunk <- prefetched registers; start loading the next one
+        Raw8<IO> qr[TQ::NV], kr[2 * PK::NPASS], vr[2 * PV::NPASS];
+        float gr[RPQ];
+        const float br = std::is_same<IO, float>::value ? __uint_as_float(bn) : __uint_as_float(bn << 16);
 #pragma unroll
-        for (int i = 0; i < TK::NV; ++i) {
-            const int r = TK::row(tid, i);
-            const bool ok = r < len;
-            float x[8], kx[8];
-            wr[i].get(x, ok);
+        for (int i = 0; i < TQ::NV; ++i) qr[i] = qn[i];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = -x[e];
-            MM<MT>::st8(sW + r * L::LDW + c8, x);
-            kr[i].get(kx, ok);
+        for (int i = 0; i < 2 * PK::NPASS; ++i) kr[i] = kn[i];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int ge = PER_K ? e : 0;
-                const float kd = kx[e] * exp_f32(gl[ge] - gr[i][ge]);
-                if constexpr (L::TRANS) sKd[(c8 + e) * L::LDT + r] = MM<MT>::cvt(kd);
-                else sKd[r * L::LDW + c8 + e] = MM<MT>::cvt(kd);
+        for (int i = 0; i < 2 * PV::NPASS; ++i) vr[i] = vn[i];
+#pragma unroll
+        for (int i = 0; i < RPQ; ++i) gr[i] = gn[i];
+        if (ci + 1 < nc) load_chunk(ci + 1);
+        if (ci > 0) flush_o(bos - CH, CH);
+
+        S* sQ = SP(PER_K ? Lay::k_q : Lay::g_q);
+        S* sK = SP(PER_K ? Lay::k_k : Lay::g_k);
+        S* sP = SP(PER_K ? Lay::k_p : Lay::g_p);
+        S* sLo = SP(PER_K ? Lay::k_lo : Lay::g_lo);
+        float* sLd = FP(PER_K ? Lay::k_ld : Lay::g_ld);
+        S* sD = SP(PER_K ? Lay::k_d : Lay::g_d);
+        S* sW = SP(PER_K ? Lay::k_w : Lay::g_w);
+        float* sg = FP(PER_K ? Lay::k_g : Lay::g_g);
+        float* sb = FP(PER_K ? Lay::k_b : Lay::g_b);
+
+        // ===== A: raw rows into LDS, gate prefix =====
+        const int pr0 = 2 * PK::pair(tid);
+#pragma unroll
+        for (int i = 0; i < TQ::NV; ++i) {
+            const int r = TQ::row(tid, i);
+            st8_perm<MT, IO>(sQ + r * LDK, TQ::col(tid), qr[i], r < len);
+        }
+#pragma unroll
+        for (int i = 0; i < PK::NPASS; ++i) {
+            if (PK::valid(tid, i)) {
+                const int c8 = PK::col(tid, i);
+                st8_perm<MT, IO>(sK + pr0 * LDK, c8, kr[2 * i], pr0 < len);
+                st8_perm<MT, IO>(sK + (pr0 + 1) * LDK, c8, kr[2 * i + 1], pr0 + 1 < len);
+                if constexpr (!PER_K)
+                    st_pair_t<MT, IO>(SP(Lay::g_kt), LDT, c8, pr0, kr[2 * i], pr0 < len, kr[2 * i + 1], pr0 + 1 < len);
             }
         }
-        if (tid < K) sDec[tid] = exp_f32(gdec);
+        if constexpr (!PER_K) {
 #pragma unroll
-        for (int i = 0; i < TU::NV; ++i) {
-            const int r = TU::row(tid, i), cc = TU::col(tid);
-            float x[8];
-            ur[i].get(x, r < len);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) sU[r * L::LDU + cc + e] = x[e];
-        }
-        if (ci + 1 < nc) prefetch(ci + 1);
-        __syncthreads();
-        f32x4_t nu[NT][4];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    nu[nt][mt][e] = sU[(16 * mt + 4 * g4 + e) * L::LDU + 16 * (NT * w + nt) + (l & 15)];
-
-        // chunk-start state -> workspace (io dtype), V-major
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            const int64_t hb = (((int64_t)c * a.HV + h) * V + vcol[nt]) * K;
-#pragma unroll
-            for (int kt = 0; kt < KT; ++kt) {
-                float x[4] = {hs[nt][kt][0], hs[nt][kt][1], hs[nt][kt][2], hs[nt][kt][3]};
-                Vec<IO, 4>::store(a.hc, hb + 16 * kt + 4 * g4, x);
+            for (int i = 0; i < PV::NPASS; ++i) {
+                if (PV::valid(tid, i))
+                    st_pair_t<MT, IO>(SP(Lay::g_vt), LDT, PV::col(tid, i), pr0, vr[2 * i], pr0 < len, vr[2 * i + 1],
+                                      pr0 + 1 < len);
             }
-        }
-
-        // v_new = U - W S^T
-        if constexpr (sizeof(S) == 2) {
+            if (tid < 64) {  // wave 0: inclusive prefix sum of the 64 gates
+                const int r = tid;
+                float x = r < len ? gr[0] : 0.0f;
 #pragma unroll
-            for (int m = 0; m < K / 32; ++m) {
-                bf16x8_t bv[NT];
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        bv[nt][e] = __builtin_bit_cast(__bf16, f32_to_bf16(hs[nt][2 * m][e]));
-                        bv[nt][4 + e] = __builtin_bit_cast(__bf16, f32_to_bf16(hs[nt][2 * m + 1][e]));
-                    }
+                for (int d = 1; d < 64; d <<= 1) {
+                    const float y = __shfl_up(x, d, 64);
+                    if (r >= d) x += y;
                 }
+                const float bb = r < len ? br : 0.0f;
+                sg[r] = x;
+                sb[r] = bb;
+                FP(Lay::g_be)[r] = bb * exp_f32(x);
+            }
+        } else {
+            // thread (c, qd): prefix over its RPQ rows of channel c, then group offsets
+            const int c = tid % K, qd = tid / K;
+            float* part = FP(Lay::k_part);
+            float x = 0.0f;
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
-                    const S* pa = sW + (16 * mt + (l & 15)) * L::LDW + 32 * m + 4 * g4;
-                    const uint2 lo = *reinterpret_cast<const uint2*>(pa);
-                    const uint2 hi = *reinterpret_cast<const uint2*>(pa + 16);
-                    const bf16x8_t av = __builtin_bit_cast(bf16x8_t, uint4{lo.x, lo.y, hi.x, hi.y});
+            for (int i = 0; i < RPQ; ++i) {
+                x += (qd * RPQ + i) < len ? gr[i] : 0.0f;
+                gr[i] = x;
+            }
+            part[qd * K + c] = x;
+            if (tid < 64) sb[tid] = tid < len ? br : 0.0f;
+            __syncthreads();
+            float off = 0.0f;
+            for (int j = 0; j < qd; ++j) off += part[j * K + c];
 #pragma unroll
-                    for (int nt = 0; nt < NT; ++nt)
-                        nu[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[nt], nu[nt][mt], 0, 0, 0);
+            for (int i = 0; i < RPQ; ++i) sg[(qd * RPQ + i) * K + c] = gr[i] + off;
+        }
+        __syncthreads();
+
+        // ===== B/C: L = beta (K K^T) decay (strictly lower), P = (Q K^T) decay (lower incl. diag);
+        //       waves 0-3 also invert the diagonal block of L they computed =====
+        if constexpr (!PER_K) {
+            if (w < 4) {  // diagonal tile (w, w) of L, then D_w = (I + L_ww)^-1
+                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+                M::nt(acc, sK + 16 * w * LDK, LDK, sK + 16 * w * LDK, LDK, K);
+                float* sN = sLd + w * 16 * 17;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int rr = 4 * g4 + e, r = 16 * w + rr, j = 16 * w + lr;
+                    sN[rr * 17 + lr] = (rr > lr) ? sb[r] * exp_f32(sg[r] - sg[j]) * acc[e] : 0.0f;
+                }
+                // the tile's LDS writes complete before this wave's lanes read other lanes' entries
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                invert_unit_lower_16<MT>(sN, sD + 16 * w * LDD, LDD);
+            }
+            const int w0 = NW > 4 ? 4 : 0, nw = NW > 4 ? NW - 4 : NW;
+            for (int t = w - w0; t >= 0 && t < 16; t += nw) {
+                int I, J;
+                const bool isL = t < 6;
+                if (isL) strict_tile(t, I, J);
+                else lower_tile(t - 6, I, J);
+                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+                M::nt(acc, (isL ? sK : sQ) + 16 * I * LDK, LDK, sK + 16 * J * LDK, LDK, K);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * I + 4 * g4 + e, j = 16 * J + lr;
+                    const float d = exp_f32(sg[r] - sg[j]);
+                    if (isL) sLo[r * LDO + j] = M::cvt(-sb[r] * d * acc[e]);
+                    else sP[r * LDT + perm<MT>(j)] = M::cvt((r >= j) ? d * acc[e] : 0.0f);
                 }
             }
         } else {
-#pragma unroll
-            for (int kt = 0; kt < KT; ++kt) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-#pragma unroll
-                    for (int mt = 0; mt < 4; ++mt) {
-                        const float av = sW[(16 * mt + (l & 15)) * L::LDW + 16 * kt + 4 * g4 + e];
-#pragma unroll
-                        for (int nt = 0; nt < NT; ++nt)
-                            nu[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, hs[nt][kt][e], nu[nt][mt], 0, 0, 0);
+            S* sLK = SP(Lay::k_lk);
+            S* sLQ = SP(Lay::k_lq);
+            S* sRG = SP(Lay::k_rg);
+            // diagonal 16x16 blocks, element-wise: (r, j) in the same block, j <= r
+            for (int p = tid; p < 4 * 256; p += NTHR) {
+                const int b = p >> 8, rr = (p >> 4) & 15, jj = p & 15;
+                const int r = 16 * b + rr, j = 16 * b + jj;
+                float accp = 0.0f, accl = 0.0f;
+                if (jj <= rr) {
+                    for (int c = 0; c < K; ++c) {
+                        const int pc = perm<MT>(c);
+                        const float d = exp_f32(sg[r * K + c] - sg[j * K + c]);
+                        const float kj = M::back(sK[j * LDK + pc]) * d;
+                        accp = fmaf(M::back(sQ[r * LDK + pc]), kj, accp);
+                        accl = fmaf(M::back(sK[r * LDK + pc]), kj, accl);
                     }
                 }
+                sP[r * LDT + perm<MT>(j)] = M::cvt(accp);  // zero above the diagonal
+                sLd[b * 16 * 17 + rr * 17 + jj] = (jj < rr) ? sb[r] * accl : 0.0f;
             }
-        }
-
-        // v_new -> workspace (io dtype)
+            // off-diagonal blocks (I > J) through MFMA, reference point rho = gamma[16I - 1]
+            for (int I = 1; I < 4; ++I) {
+                const int rho_row = 16 * I - 1;
+                for (int idx = tid; idx < 16 * K; idx += NTHR) {
+                    const int r = idx / K, c = idx % K, rr = 16 * I + r, pc = perm<MT>(c);
+                    const float f = exp_f32(sg[rr * K + c] - sg[rho_row * K + c]);
+                    sLK[r * LDK + pc] = M::cvt(M::back(sK[rr * LDK + pc]) * f);
+                    sLQ[r * LDK + pc] = M::cvt(M::back(sQ[rr * LDK + pc]) * f);
+                }
+                for (int idx = tid; idx < 16 * I * K; idx += NTHR) {
+                    const int j = idx / K, c = idx % K, pc = perm<MT>(c);
+                    sRG[j * LDK + pc] =
+                        M::cvt(M::back(sK[j * LDK + pc]) * exp_f32(sg[rho_row * K + c] - sg[j * K + c]));
+                }
+                __syncthreads();
+                for (int t = w; t < 2 * I; t += NW) {
+                    const int J = t >> 1;
+                    const bool isL = (t & 1) == 0;
+                    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+                    M::nt(acc, isL ? sLK : sLQ, LDK, sRG + 16 * J * LDK, LDK, K);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 16 * I + 4 * g4 + e, j = 16 * J + lr;
+                        if (isL) sLo[r * LDO + j] = M::cvt(-sb[r] * acc[e]);
+                        else sP[r * LDT + perm<MT>(j)] = M::cvt(acc[e]);
+                    }
+                }
+                __syncthreads();
+            }
+            if (w < 4) invert_unit_lower_16<MT>(sLd + w * 16 * 17, sD + 16 * w * LDD, LDD);
+            // the transposed / scaled operands of D and E, from this chunk's registers
+            S* sKgT = SP(Lay::k_kgt);
+            S* sVT = SP(Lay::k_vt);
+            S* sQt = SP(Lay::k_qt);
+            S* sKdT = SP(Lay::k_kdt);
+            const float* sgc = sg;
+            auto f_g = [sgc](int r, int c) { return exp_f32(sgc[r * K + c]); };
+            auto f_d = [sgc](int r, int c) { return exp_f32(sgc[(CH - 1) * K + c] - sgc[r * K + c]); };
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 16 * mt + 4 * g4 + e;
-                    if (r < len) Elem<IO>::store(a.vnew, ((bos + r) * a.HV + h) * V + vcol[nt], nu[nt][mt][e]);
+            for (int i = 0; i < PK::NPASS; ++i) {
+                if (PK::valid(tid, i)) {
+                    const int c8 = PK::col(tid, i);
+                    st_pair_t_scaled<MT, IO>(sKgT, LDT, c8, pr0, kr[2 * i], pr0 < len, kr[2 * i + 1], pr0 + 1 < len, f_g);
+                    st_pair_t_scaled<MT, IO>(sKdT, LDT, c8, pr0, kr[2 * i], pr0 < len, kr[2 * i + 1], pr0 + 1 < len, f_d);
                 }
             }
-        }
-
-        // S <- S * e^{gamma_last} + v_new^T K_d
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
+            for (int i = 0; i < PV::NPASS; ++i) {
+                if (PV::valid(tid, i))
+                    st_pair_t<MT, IO>(sVT, LDT, PV::col(tid, i), pr0, vr[2 * i], pr0 < len, vr[2 * i + 1], pr0 + 1 < len);
+            }
+#pragma unroll
+            for (int i = 0; i < TQ::NV; ++i) {
+                const int r = TQ::row(tid, i), c8 = TQ::col(tid);
+                float y[8];
+                qr[i].get(y, r < len);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) y[e] *= exp_f32(sg[r * K + c8 + e]);
+                if constexpr (Lay::BF) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) sQt[r * LDK + perm<MT>(c8 + e)] = M::cvt(y[e]);
+                } else {
+                    M::st8(sQt + r * LDK + c8, y);
+                }
+            }
+            for (int c = tid; c < K; c += NTHR) FP(Lay::k_gl)[c] = exp_f32(sg[(CH - 1) * K + c]);
+        }
+        __syncthreads();
+
+        // ===== D: [W | U] = (I + L)^-1 [beta e^gamma K | beta V] by blocked substitution =====
+        f32x4_t nu[4];
+        {
+            const S* sKb = SP(PER_K ? Lay::k_kgt : Lay::g_kt);
+            const S* sVb = SP(PER_K ? Lay::k_vt : Lay::g_vt);
+            const float* wsc = PER_K ? sb : FP(Lay::g_be);
+            for (int jt = w; jt < KT; jt += NW) {
+                f32x4_t X[4];
+                block_solve<MT>(X, sLo, LDO, sD, LDD, sKb + (16 * jt + lr) * LDT, wsc);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        sW[(16 * i + 4 * g4 + e) * LDK + perm<MT>(16 * jt + lr)] = M::cvt(-X[i][e]);
+            }
+            block_solve<MT>(nu, sLo, LDO, sD, LDD, sVb + (16 * w + lr) * LDT, sb);
+        }
+        __syncthreads();
+
+        // ===== E: v_new, output, state update (wave w: columns 16w .. 16w+15) =====
+        // v_new = U - W S^T  (LDS holds -W)
+        gemm_regs<MT, K, 4>(nu, sW, LDK, hs);
+        // O = scale (diag(e^gamma) Q S^T + P v_new)
+        f32x4_t oa[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) oa[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        gemm_regs<MT, K, 4>(oa, SP(PER_K ? Lay::k_qt : Lay::g_q), LDK, hs);
+        if constexpr (!PER_K) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) oa[i][e] *= exp_f32(sg[16 * i + 4 * g4 + e]);
+        }
+        gemm_regs<MT, CH, 4>(oa, sP, LDT, nu);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float d = sDec[16 * kt + 4 * g4 + e];
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) hs[nt][kt][e] *= d;
+                const int r = 16 * i + 4 * g4 + e, c = 16 * w + lr;
+                if constexpr (std::is_same<IO, float>::value)
+                    *reinterpret_cast<float*>(so + OS::off(r, c)) = a.scale * oa[i][e];
+                else
+                    *reinterpret_cast<uint16_t*>(so + OS::off(r, c)) = f32_to_bf16(a.scale * oa[i][e]);
             }
         }
-        if constexpr (sizeof(S) == 2) {
+        // S <- e^{gamma_last} S + sum_r v_new_r (k_r e^{gamma_last - gamma_r})^T
+        if constexpr (!PER_K) {
+            const float gl = sg[CH - 1];
+            const float dec = exp_f32(gl);
 #pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                bf16x8_t bv[NT];
+            for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
+                for (int e = 0; e < 4; ++e) hs[kt][e] *= dec;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        bv[nt][e] = __builtin_bit_cast(__bf16, f32_to_bf16(nu[nt][2 * m][e]));
-                        bv[nt][4 + e] = __builtin_bit_cast(__bf16, f32_to_bf16(nu[nt][2 * m + 1][e]));
-                    }
-                }
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int kt = 0; kt < KT; ++kt) {
-                    const S* pa = sKd + (16 * kt + (l & 15)) * L::LDT + 32 * m + 4 * g4;
-                    const uint2 lo = *reinterpret_cast<const uint2*>(pa);
-                    const uint2 hi = *reinterpret_cast<const uint2*>(pa + 16);
-                    const bf16x8_t av = __builtin_bit_cast(bf16x8_t, uint4{lo.x, lo.y, hi.x, hi.y});
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt)
-                        hs[nt][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[nt], hs[nt][kt], 0, 0, 0);
-                }
-            }
+                for (int e = 0; e < 4; ++e) nu[i][e] *= exp_f32(gl - sg[16 * i + 4 * g4 + e]);
+            gemm_regs<MT, CH, KT>(hs, SP(Lay::g_kt), LDT, nu);
         } else {
+            const float* sgl = FP(Lay::k_gl);
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
+            for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-#pragma unroll
-                    for (int kt = 0; kt < KT; ++kt) {
-                        const float av = sKd[(16 * mt + 4 * g4 + e) * L::LDW + 16 * kt + (l & 15)];
-#pragma unroll
-                        for (int nt = 0; nt < NT; ++nt)
-                            hs[nt][kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, nu[nt][mt][e], hs[nt][kt], 0, 0, 0);
-                    }
-                }
-            }
+                for (int e = 0; e < 4; ++e) hs[kt][e] *= sgl[16 * kt + 4 * g4 + e];
+            gemm_regs<MT, CH, KT>(hs, SP(Lay::k_kdt), LDT, nu);
         }
         __syncthreads();
+    }
+    if (nc > 0) {
+        const int64_t bos = s0 + (int64_t)CH * (nc - 1);
+        flush_o(bos, (int)(s1 - bos));
     }
 
     if (a.ht) {
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            const int64_t sidx = (((int64_t)n * a.HV + h) * V + vcol[nt]) * K;
-#pragma unroll
-            for (int kt = 0; kt < KT; ++kt)
-                *reinterpret_cast<f32x4_t*>(a.ht + sidx + 16 * kt + 4 * g4) = hs[nt][kt];
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// H4: chunk output.
-template <int K, int V, typename IO, typename MT, bool PER_K>
-struct OutSmem {
-    typedef typename MM<MT>::S S;
-    static constexpr int LDK = K + MM<MT>::PAD;
-    static constexpr int LDT = CH + MM<MT>::PAD;
-    static constexpr int LDP = CH + 1;
-    static constexpr size_t q_off = 0;                                          // S [64][LDK]
-    static constexpr size_t p_off = q_off + sizeof(S) * CH * LDK;               // S [64][LDT]
-    static constexpr size_t g_off = p_off + sizeof(S) * CH * LDT;               // f32 [64] or [64][K]
-    static constexpr size_t pf_off = g_off + sizeof(float) * CH * (PER_K ? K : 1);  // f32 [64][LDP] (per-K only)
-    static constexpr size_t u_off = pf_off + (PER_K ? sizeof(float) * CH * LDP : 0);
-    // union: phase 1 {K rows, left, right}; phase 2 {S0 [V][LDK], v_new^T [V][LDT]}
-    static constexpr size_t k_off = u_off;
-    static constexpr size_t lft_off = k_off + sizeof(S) * CH * LDK;
-    static constexpr size_t rgt_off = lft_off + (PER_K ? sizeof(S) * 16 * LDK : 0);
-    static constexpr size_t ph1_end = rgt_off + (PER_K ? sizeof(S) * 48 * LDK : 0);
-    static constexpr size_t s_off = u_off;
-    static constexpr size_t nt_off = s_off + sizeof(S) * V * LDK;
-    static constexpr size_t ph2_end = nt_off + sizeof(S) * V * LDT;
-    static constexpr size_t total = ph1_end > ph2_end ? ph1_end : ph2_end;
-};
-
-template <int K, int V, typename IO, typename MT, bool PER_K>
-__global__ __launch_bounds__(256) void chunk_output_kernel(const ChunkArgs a) {
-    typedef OutSmem<K, V, IO, MT, PER_K> L;
-    typedef typename MM<MT>::S S;
-    __shared__ __align__(16) char smem[L::total];
-    S* sQ = reinterpret_cast<S*>(smem + L::q_off);
-    S* sP = reinterpret_cast<S*>(smem + L::p_off);
-    float* sg = reinterpret_cast<float*>(smem + L::g_off);
-    S* sK = reinterpret_cast<S*>(smem + L::k_off);
-    S* sS = reinterpret_cast<S*>(smem + L::s_off);
-    S* sNT = reinterpret_cast<S*>(smem + L::nt_off);
-
-    ChunkInfo ci;
-    const int c = blockIdx.x;
-    if (!chunk_info(a, c, ci)) return;
-    const int h = blockIdx.y;
-    const int hk = h / (a.HV / a.HK);
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-
-    // every global load of the chunk is issued first: q, k rows, the chunk-start state, v_new
-    typedef Tile64<K> TK;
-    typedef Tile64<V> TV;
-    constexpr int SNV = (V / 64) * TK::NV;
-    Raw8<IO> qr[TK::NV], kr[TK::NV], sr[SNV], nr[TV::NV];
-#pragma unroll
-    for (int i = 0; i < TK::NV; ++i) {
-        const int r = TK::row(tid, i), rc = r < ci.len ? r : ci.len - 1;
-        const int64_t off = ((ci.bos + rc) * a.HK + hk) * K + TK::col(tid);
-        qr[i].load(a.q, off);
-        kr[i].load(a.k, off);
-    }
-#pragma unroll
-    for (int i = 0; i < SNV; ++i) {
-        const int vv = 64 * (i / TK::NV) + TK::row(tid, i % TK::NV);
-        sr[i].load(a.hc, (((int64_t)c * a.HV + h) * V + vv) * K + TK::col(tid));
-    }
-#pragma unroll
-    for (int i = 0; i < TV::NV; ++i) {
-        const int r = TV::row(tid, i), rc = r < ci.len ? r : ci.len - 1;
-        nr[i].load(a.vnew, ((ci.bos + rc) * a.HV + h) * V + TV::col(tid));
-    }
-    load_gamma<K, PER_K>(a, ci, h, sg, true, false);
-#pragma unroll
-    for (int i = 0; i < TK::NV; ++i) {
-        const int r = TK::row(tid, i), c8 = TK::col(tid);
-        float x[8];
-        qr[i].get(x, r < ci.len);
-        MM<MT>::st8(sQ + r * L::LDK + c8, x);
-        kr[i].get(x, r < ci.len);
-        MM<MT>::st8(sK + r * L::LDK + c8, x);
-    }
-    __syncthreads();
-
-    // P[r][j] = q_r . k_j * decay(r, j), j <= r
-    if constexpr (!PER_K) {
-        for (int t = w; t < 16; t += 4) {
-            const int I = t >> 2, J = t & 3;
-            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-            if (I >= J) MM<MT>::nt(acc, sQ + 16 * I * L::LDK, L::LDK, sK + 16 * J * L::LDK, L::LDK, K);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * I + 4 * (l >> 4) + e, j = 16 * J + (l & 15);
-                sP[r * L::LDT + j] = MM<MT>::cvt((r >= j) ? exp_f32(sg[r] - sg[j]) * acc[e] : 0.0f);
-            }
-        }
-    } else {
-        float* sPf = reinterpret_cast<float*>(smem + L::pf_off);
-        S* sLft = reinterpret_cast<S*>(smem + L::lft_off);
-        S* sRgt = reinterpret_cast<S*>(smem + L::rgt_off);
-        for (int idx = tid; idx < CH * CH; idx += 256) {
-            const int r = idx / CH, j = idx % CH;
-            if (j > r) sPf[r * L::LDP + j] = 0.0f;
-        }
-        diag_blocks_per_k<K, MT, true>(sQ, L::LDK, sK, L::LDK, sg, sPf, L::LDP, nullptr);
-        offdiag_blocks_per_k<K, MT>(sQ, L::LDK, sK, L::LDK, sg, sLft, sRgt, sPf, L::LDP, nullptr);
-        __syncthreads();
-        for (int idx = tid; idx < CH * CH; idx += 256) {
-            const int r = idx / CH, j = idx % CH;
-            sP[r * L::LDT + j] = MM<MT>::cvt(sPf[r * L::LDP + j]);
-        }
-    }
-    __syncthreads();
-
-    // Q~ = Q * e^gamma from registers; S0 and v_new^T into the phase-2 area
-#pragma unroll
-    for (int i = 0; i < TK::NV; ++i) {
-        const int r = TK::row(tid, i), c8 = TK::col(tid);
-        float x[8];
-        qr[i].get(x, r < ci.len);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] *= exp_f32(gam<K, PER_K>(sg, r, c8 + e));
-        MM<MT>::st8(sQ + r * L::LDK + c8, x);
-    }
-#pragma unroll
-    for (int i = 0; i < SNV; ++i) {
-        const int vv = 64 * (i / TK::NV) + TK::row(tid, i % TK::NV);
-        float x[8];
-        sr[i].get(x, true);
-        MM<MT>::st8(sS + vv * L::LDK + TK::col(tid), x);
-    }
-#pragma unroll
-    for (int i = 0; i < TV::NV; ++i) {
-        const int r = TV::row(tid, i), c8 = TV::col(tid);
-        float x[8];
-        nr[i].get(x, r < ci.len);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sNT[(c8 + e) * L::LDT + r] = MM<MT>::cvt(x[e]);
-    }
-    __syncthreads();
-
-    // O = scale * (Q~ S0^T + P v_new)
-    for (int t = w; t < 4 * (V / 16); t += 4) {
-        const int I = t / (V / 16), J = t % (V / 16);
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-        MM<MT>::nt(acc, sQ + 16 * I * L::LDK, L::LDK, sS + 16 * J * L::LDK, L::LDK, K);
-        const int kdim = MM<MT>::PAD == 8 ? ((16 * (I + 1) + 31) / 32) * 32 : 16 * (I + 1);
-        MM<MT>::nt(acc, sP + 16 * I * L::LDT, L::LDT, sNT + 16 * J * L::LDT, L::LDT, kdim);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = 16 * I + 4 * (l >> 4) + e, vv = 16 * J + (l & 15);
-            if (r < ci.len) Elem<IO>::store(a.o, ((ci.bos + r) * a.HV + h) * V + vv, a.scale * acc[e]);
-        }
+        for (int kt = 0; kt < KT; ++kt) *reinterpret_cast<f32x4_t*>(a.ht + sidx + 16 * kt + 4 * g4) = hs[kt];
     }
 }
 
 template <int K, int V, typename IO, bool PER_K>
-hipError_t launch_all(const ChunkArgs& a, hipStream_t stream) {
-    typedef IO MT;
-    hipLaunchKernelGGL(chunk_index_kernel, dim3(1), dim3(1024), 0, stream, a);
-    hipLaunchKernelGGL((chunk_prepare_kernel<K, V, IO, MT, PER_K>), dim3(a.max_chunks, a.HV), dim3(256), 0, stream, a);
-    // the state pass is sequential over chunks: one workgroup per (sequence, head) when that
-    // already gives a wave per SIMD, otherwise 64-column V tiles for more workgroups
-    if (V == 128 && (int64_t)a.N * a.HV >= 128) {
-        hipLaunchKernelGGL((chunk_state_kernel<K, V, IO, MT, PER_K, 2>), dim3(1, a.HV, a.N), dim3(256), 0, stream, a);
-    } else {
-        hipLaunchKernelGGL((chunk_state_kernel<K, V, IO, MT, PER_K, 1>), dim3(V / 64, a.HV, a.N), dim3(256), 0, stream,
-                           a);
-    }
-    hipLaunchKernelGGL((chunk_output_kernel<K, V, IO, MT, PER_K>), dim3(a.max_chunks, a.HV), dim3(256), 0, stream, a);
+hipError_t launch_fused(const ChunkArgs& a, hipStream_t stream) {
+    // bf16: the workgroup owns all V columns; fp32 operands (K = 64 only) use 64-column tiles
+    constexpr int BV = std::is_same<IO, float>::value ? 64 : V;
+    hipLaunchKernelGGL((chunk_fused_kernel<K, BV, IO, IO, PER_K>), dim3(V / BV, a.HV, a.N), dim3(4 * BV), 0, stream,
+                       a);
     return hipGetLastError();
 }
 
@@ -938,27 +839,17 @@ template <int K, int V>
 hipError_t launch_kv(const ChunkArgs& a, int io, bool per_k, hipStream_t s) {
     if (io == 0) {
         // fp32 operands at K = 128 do not fit the 160 KiB of LDS in this design
-        if constexpr (K == 64) return per_k ? launch_all<K, V, float, true>(a, s) : launch_all<K, V, float, false>(a, s);
+        if constexpr (K == 64) return per_k ? launch_fused<K, V, float, true>(a, s) : launch_fused<K, V, float, false>(a, s);
         else return hipErrorNotSupported;
     }
-    return per_k ? launch_all<K, V, bf16_t, true>(a, s) : launch_all<K, V, bf16_t, false>(a, s);
+    return per_k ? launch_fused<K, V, bf16_t, true>(a, s) : launch_fused<K, V, bf16_t, false>(a, s);
 }
 
 }  // namespace
 
-ChunkWorkspaceLayout chunk_workspace_layout(int64_t T, int32_t N, int32_t HV, int32_t K, int32_t V, int io_bytes,
-                                            bool per_k) {
+ChunkWorkspaceLayout chunk_workspace_layout(int64_t, int32_t, int32_t, int32_t, int32_t, int, bool) {
     ChunkWorkspaceLayout L{};
-    const int64_t max_chunks = T / CH + N;
-    size_t off = 0;
-    L.chunk_seq = off; off = align256(off + sizeof(int32_t) * (size_t)max_chunks);
-    L.chunk_first = off; off = align256(off + sizeof(int32_t) * (size_t)(N + 1));
-    L.gcum = off; off = align256(off + sizeof(float) * (size_t)T * HV * (per_k ? K : 1));
-    L.w = off; off = align256(off + (size_t)io_bytes * T * HV * K);
-    L.u = off; off = align256(off + (size_t)io_bytes * T * HV * V);
-    L.vnew = off; off = align256(off + (size_t)io_bytes * T * HV * V);
-    L.hc = off; off = align256(off + (size_t)io_bytes * max_chunks * HV * V * K);
-    L.total = off;
+    L.total = 0;  // the fused path keeps every intermediate on chip
     return L;
 }
 

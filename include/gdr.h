@@ -38,7 +38,8 @@
  *   - validation covers metadata only (null pointers, sizes, enums) and happens
  *     before any launch; device contents (slot ids, cu_seqlens values, NaN, g > 0,
  *     duplicate slots) are NOT checked and are undefined behaviour when invalid;
- *   - T == 0 or N == 0 returns GDR_SUCCESS without launching anything;
+ *   - N == 0 returns GDR_SUCCESS without launching anything; so does T == 0 unless a
+ *     final state is requested (the dense entry points then copy the initial state);
  *   - outputs must not alias inputs, except where stated;
  *   - the library keeps no mutable global state and is thread-safe.
  */
@@ -121,7 +122,9 @@ GDR_API size_t gdr_chunk_workspace_size(const gdr_problem* p, int32_t chunk_size
  *   chunk_size     must be 64
  *   cu_seqlens, initial_state, o, final_state: as gdr_recurrent_fwd
  *   workspace      device buffer of at least gdr_chunk_workspace_size(p, 64) bytes,
- *                  caller-owned, contents need not be initialised; 256-byte aligned
+ *                  caller-owned, contents need not be initialised, 256-byte aligned;
+ *                  may be NULL when that size is 0 (the current kernels keep every
+ *                  intermediate on chip)
  * The result matches gdr_recurrent_fwd to the chunked method's rounding, not bitwise.
  */
 GDR_API gdr_status gdr_chunk_fwd(const gdr_problem* p, int32_t chunk_size,
