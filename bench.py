@@ -13,9 +13,15 @@ already resident in HBM:
                              [1025, 12, 32, 128, 128], no commit  (speculative verify)
 
 The JSON line reports prefill tokens/s as ``value`` and the decode state GB/s beside it,
-each leg's time from HIP events recorded on the stream the library launches on, the
-roofline of the decode kernel (HBM-bound, one launch) and of the other legs, and the CPU
-oracle timed on a bounded sample of the prefill workload.
+each leg's time from HIP events recorded on the stream the library launches on (torch's
+current stream, passed explicitly to every call), the roofline of the step's dominant kernel
+(the longest leg; each leg's own roofline beside it), HBM traffic per launch where the
+rocprofv3 counter passes recorded under profiles/ match the current kernel sources, and the
+CPU oracle timed on a bounded sample of the prefill workload.
+
+Profiling passes: ``--legs prefill`` runs only that leg, ``--calib-copy-mib N`` first runs one
+device copy of N MiB (known traffic, to scale FETCH_SIZE / WRITE_SIZE); both print a short
+JSON line instead of the full report.
 """
 from __future__ import annotations
 
@@ -76,6 +82,36 @@ def _alg_bytes_paged(p, with_ibuf: bool):
     return total
 
 
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_CSRC = os.path.join(_HERE, "gated_delta_rule_63_amd", "csrc")
+_TRAFFIC = os.path.join(_HERE, "profiles", "hbm_traffic.md")
+
+
+def _source_digest(names):
+    """sha256 over the kernel sources a leg runs, so measured traffic is dropped once they change."""
+    import hashlib
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(_CSRC, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def _measured_traffic():
+    """HBM bytes per launch from the rocprofv3 FETCH_SIZE / WRITE_SIZE passes recorded in
+    profiles/hbm_traffic.md (one JSON object per leg on lines starting with '{')."""
+    out = {}
+    if not os.path.exists(_TRAFFIC):
+        return out
+    with open(_TRAFFIC) as f:
+        for line in f:
+            line = line.strip()
+            if line.startswith("{"):
+                rec = json.loads(line)
+                out[rec["leg"]] = rec
+    return out
+
+
 def _cpu_baseline(p, target_s: float = 12.0):
     """The fp64 oracle on the host cores, on the first heads of the prefill workload."""
     import oracle  # test infrastructure: only this leg of the benchmark loads it
@@ -108,6 +144,11 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--legs", default="prefill,decode,verify",
+                    help="comma-separated subset of legs to run (profiling passes); the JSON line needs all three")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="before the legs, run one device-to-device copy of this many MiB (a plain copy kernel of "
+                         "known size, used to scale the HBM byte counters of a profiling pass) and stop after the legs")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the gated-delta-rule path here is built and timed on a single "
@@ -167,7 +208,16 @@ def main():
                              cu_seqlens=V_["cu"], max_q_len=12, commit=False, inter_states=V_["ib"],
                              inter_state_indices=V_["ibi"], scale=pv.scale, o=V_["o"])
 
-    legs = [("prefill", prefill), ("decode", decode), ("verify", verify)]
+    legs = [(n, f) for n, f in (("prefill", prefill), ("decode", decode), ("verify", verify))
+            if n in args.legs.split(",")]
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     print("bench: warmup", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         for _, fn in legs:
@@ -187,6 +237,9 @@ def main():
             ev[name][i][1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if len(legs) < 3 or args.calib_copy_mib:
+        print(json.dumps({"profiling_pass": [n for n, _ in legs], "steps": K}))
+        return
     leg_ms = {name: float(np.mean([a.elapsed_time(b) for a, b in ev[name]])) for name, _ in legs}
     leg_ms_min = {name: float(np.min([a.elapsed_time(b) for a, b in ev[name]])) for name, _ in legs}
 
@@ -199,22 +252,44 @@ def main():
     state_bytes_dec = int(sum(1 for s in pd.state_indices if s >= 0)) * pd.HV * pd.V * pd.K * 4 * 2
 
     prefill_tps = pp.T / s_pre
-    roof_dec = {"bound": "hbm", "achieved": b_dec / s_dec / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                "frac": b_dec / s_dec / HBM_PEAK, "traffic": None,
-                "kernel": "recurrent_kernel (decode: 256 x 1 token, fp32 pool, commit)",
-                "alg_bytes_per_launch": b_dec}
-    roof_legs = {
-        "prefill": {"bound": "hbm", "achieved_GBps": b_pre / s_pre / 1e9, "frac_hbm": b_pre / s_pre / HBM_PEAK,
-                    "mfma_TFLOPs_triangle_exact": f_pre / s_pre / 1e12,
-                    "frac_bf16_mfma_triangle_exact": f_pre / s_pre / BF16_MFMA_PEAK,
-                    "frac_bf16_mfma_full_tile": f_pre_full / s_pre / BF16_MFMA_PEAK,
-                    "alg_bytes": b_pre, "alg_flops_triangle_exact": f_pre, "alg_flops_full_tile": f_pre_full,
-                    "launches": "chunk_index, chunk_prepare (H2), chunk_state (H3), chunk_output (H4)"},
-        "decode": {"bound": "hbm", "achieved_GBps": b_dec / s_dec / 1e9, "frac_hbm": b_dec / s_dec / HBM_PEAK,
-                   "state_GBps": state_bytes_dec / s_dec / 1e9, "alg_bytes": b_dec},
-        "verify": {"bound": "hbm", "achieved_GBps": b_ver / s_ver / 1e9, "frac_hbm": b_ver / s_ver / HBM_PEAK,
-                   "alg_bytes": b_ver},
+    leg_info = {
+        "prefill": {"kernel": "chunk_fused_kernel<128,128,bf16> (one launch per call)", "bytes": b_pre,
+                    "flops": f_pre, "secs": s_pre, "sources": ["gdr_chunk.hip", "gdr_device.h"]},
+        "decode": {"kernel": "recurrent_kernel (256 x 1 token, fp32 pool, commit)", "bytes": b_dec, "flops": None,
+                   "secs": s_dec, "sources": ["gdr_recurrent.hip", "gdr_device.h"]},
+        "verify": {"kernel": "recurrent_kernel (64 x 12 tokens, bf16 pool, bf16 per-token states)", "bytes": b_ver,
+                   "flops": None, "secs": s_ver, "sources": ["gdr_recurrent.hip", "gdr_device.h"]},
     }
+    traffic = _measured_traffic()
+
+    def roofline(leg):
+        li = leg_info[leg]
+        t_hbm = li["bytes"] / HBM_PEAK
+        t_mfma = li["flops"] / BF16_MFMA_PEAK if li["flops"] else 0.0
+        tr = traffic.get(leg)
+        tr_ok = tr is not None and tr.get("source_sha256") == _source_digest(li["sources"])
+        if t_mfma > t_hbm:
+            r = {"bound": "mfma", "achieved": li["flops"] / li["secs"] / 1e12, "peak": BF16_MFMA_PEAK / 1e12,
+                 "unit": "TFLOP/s", "frac": li["flops"] / li["secs"] / BF16_MFMA_PEAK}
+        else:
+            r = {"bound": "hbm", "achieved": li["bytes"] / li["secs"] / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                 "frac": li["bytes"] / li["secs"] / HBM_PEAK}
+        r["traffic"] = tr["bytes_per_launch"] if tr_ok else None
+        r["kernel"] = li["kernel"]
+        r["alg_bytes_per_launch"] = li["bytes"]
+        r["avg_launch_ms"] = li["secs"] * 1e3
+        if li["flops"]:
+            r["alg_flops_per_launch"] = li["flops"]
+            r["frac_bf16_mfma"] = li["flops"] / li["secs"] / BF16_MFMA_PEAK
+            r["frac_hbm"] = li["bytes"] / li["secs"] / HBM_PEAK
+        return r
+
+    dominant = max(leg_info, key=lambda n: leg_info[n]["secs"])
+    roof = roofline(dominant)
+    roof_legs = {n: roofline(n) for n in leg_info}
+    roof_legs["prefill"]["frac_bf16_mfma_full_tile"] = f_pre_full / s_pre / BF16_MFMA_PEAK
+    roof_legs["prefill"]["alg_flops_full_tile"] = f_pre_full
+    roof_legs["decode"]["state_GBps"] = state_bytes_dec / s_dec / 1e9
     out = {
         "metric": "GDN prefill tokens/s + decode state GB/s (fraction of HBM/MFMA peak), 1 GPU",
         "value": prefill_tps,
@@ -236,7 +311,7 @@ def main():
         "decode_state_GBps": state_bytes_dec / s_dec / 1e9,
         "leg_ms": leg_ms,
         "leg_ms_min": leg_ms_min,
-        "roofline": roof_dec,
+        "roofline": roof,
         "roofline_legs": roof_legs,
     }
     if not args.no_cpu_baseline:

@@ -9,8 +9,10 @@
 //   A  raw q, k (and v) rows into LDS; gamma = chunk-local prefix sum of the log-decay
 //   B  L = strictly lower  beta_r (k_r . k_j) e^{gamma_r - gamma_j}      (K K^T on MFMA)
 //      P = lower incl. diag  (q_r . k_j) e^{gamma_r - gamma_j}           (Q K^T on MFMA)
-//   C  A = (I + L)^-1  (fp32: 16x16 diagonal blocks by substitution, the rest on MFMA)
-//   D  W = A diag(beta) (K * e^gamma)   -> LDS;   U = A diag(beta) V  -> each wave's registers
+//   C  D_I = (I + L_II)^-1 for the four 16x16 diagonal blocks (fp32 substitution)
+//   D  [W | U] = (I + L)^-1 [diag(beta e^gamma) K | diag(beta) V] by blocked forward
+//      substitution X_I = D_I (B_I - sum_{J<I} L_IJ X_J) on MFMA;
+//      -W -> LDS, U -> the registers of the wave owning those value columns
 //   E  v_new = U - W S^T;  O = scale (diag(e^gamma) Q S^T + P v_new);
 //      S <- e^{gamma_last} S + sum_r v_new_r (k_r * e^{gamma_last - gamma_r})^T
 //
@@ -32,8 +34,9 @@
 // row before the block row), exp(g_r - g_j) = exp(g_r - rho) exp(rho - g_j) with both
 // factors <= 1, and the four diagonal blocks are evaluated element-wise.
 //
-// MFMA: bf16 I/O uses v_mfma_f32_16x16x32_bf16 (bf16 operands, fp32 accumulation); fp32 I/O
-// uses v_mfma_f32_16x16x4f32.
+// MFMA: bf16 I/O uses v_mfma_f32_16x16x32_bf16 for the products over K and the chunk, and
+// v_mfma_f32_16x16x16_bf16 for the blocked substitution (bf16 operands, fp32 accumulation);
+// fp32 I/O uses v_mfma_f32_16x16x4f32 throughout.
 #include "gdr_device.h"
 #include "gdr_internal.h"
 
