@@ -67,6 +67,25 @@ template <> struct MM<bf16_t> {
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
         }
     }
+    // two independent tiles: every operand read is issued before the first product
+    template <int KD>
+    __device__ __forceinline__ static void nt2(f32x4_t& c0, const S* a0, const S* b0, f32x4_t& c1, const S* a1,
+                                               const S* b1, int ld) {
+        const int l = threadIdx.x & 63, o = (l & 15) * ld + 8 * (l >> 4);
+        bf16x8_t va0[KD / 32], vb0[KD / 32], va1[KD / 32], vb1[KD / 32];
+#pragma unroll
+        for (int s = 0; s < KD / 32; ++s) {
+            va0[s] = *reinterpret_cast<const bf16x8_t*>(a0 + o + 32 * s);
+            vb0[s] = *reinterpret_cast<const bf16x8_t*>(b0 + o + 32 * s);
+            va1[s] = *reinterpret_cast<const bf16x8_t*>(a1 + o + 32 * s);
+            vb1[s] = *reinterpret_cast<const bf16x8_t*>(b1 + o + 32 * s);
+        }
+#pragma unroll
+        for (int s = 0; s < KD / 32; ++s) {
+            c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va0[s], vb0[s], c0, 0, 0, 0);
+            c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va1[s], vb1[s], c1, 0, 0, 0);
+        }
+    }
     // store 8 floats (row-contiguous) into LDS
     __device__ __forceinline__ static void st8(S* p, const float* x) {
         uint4 w;
@@ -89,6 +108,24 @@ template <> struct MM<float> {
         const S* pb = sB + (l & 15) * ldb + (l >> 4);
         for (int k0 = 0; k0 < kdim; k0 += 4)
             acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[k0], pb[k0], acc, 0, 0, 0);
+    }
+    template <int KD>
+    __device__ __forceinline__ static void nt2(f32x4_t& c0, const S* a0, const S* b0, f32x4_t& c1, const S* a1,
+                                               const S* b1, int ld) {
+        const int l = threadIdx.x & 63, o = (l & 15) * ld + (l >> 4);
+        float va0[KD / 4], vb0[KD / 4], va1[KD / 4], vb1[KD / 4];
+#pragma unroll
+        for (int s = 0; s < KD / 4; ++s) {
+            va0[s] = a0[o + 4 * s];
+            vb0[s] = b0[o + 4 * s];
+            va1[s] = a1[o + 4 * s];
+            vb1[s] = b1[o + 4 * s];
+        }
+#pragma unroll
+        for (int s = 0; s < KD / 4; ++s) {
+            c0 = __builtin_amdgcn_mfma_f32_16x16x4f32(va0[s], vb0[s], c0, 0, 0, 0);
+            c1 = __builtin_amdgcn_mfma_f32_16x16x4f32(va1[s], vb1[s], c1, 0, 0, 0);
+        }
     }
     __device__ __forceinline__ static void st8(S* p, const float* x) {
         f32x4_t* q = reinterpret_cast<f32x4_t*>(p);
@@ -147,37 +184,41 @@ __device__ __forceinline__ void gemm_regs(f32x4_t* acc, const typename MM<MT>::S
     }
 }
 
+// Buffer resource over the rows of one chunk: `rows` rows of `row_bytes` starting at `base`.
+// Loads at byte offsets past rows * row_bytes return zeros, so rows past the end of a short
+// chunk read as zero without a clamp, a select or a branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const void* base, int rows, int row_bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, rows * row_bytes, 0x00020000);
+}
+
 // Eight consecutive elements held raw in registers, so that a whole tile's worth of
-// global loads can be issued before any of them is used.  Rows past the end of a chunk
-// are loaded from a clamped (valid) row and zeroed on conversion: a conditional load
-// would be compiled as a branch with an immediate wait on every load.
+// global loads can be issued before any of them is used.
 template <typename IO> struct Raw8;
 template <> struct Raw8<bf16_t> {
     uint4 w;
-    __device__ __forceinline__ void load(const void* p, int64_t off) {
-        w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p) + off);
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int voff) {
+        w = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
     }
-    __device__ __forceinline__ void get(float* x, bool valid) const {
+    __device__ __forceinline__ void get(float* x) const {
         const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            x[2 * j] = valid ? __uint_as_float(ws[j] << 16) : 0.0f;
-            x[2 * j + 1] = valid ? __uint_as_float(ws[j] & 0xFFFF0000u) : 0.0f;
+            x[2 * j] = __uint_as_float(ws[j] << 16);
+            x[2 * j + 1] = __uint_as_float(ws[j] & 0xFFFF0000u);
         }
     }
 };
 template <> struct Raw8<float> {
     f32x4_t a, b;
-    __device__ __forceinline__ void load(const void* p, int64_t off) {
-        const f32x4_t* q = reinterpret_cast<const f32x4_t*>(static_cast<const float*>(p) + off);
-        a = q[0];
-        b = q[1];
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int voff) {
+        a = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+        b = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16, 0, 0));
     }
-    __device__ __forceinline__ void get(float* x, bool valid) const {
+    __device__ __forceinline__ void get(float* x) const {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            x[e] = valid ? a[e] : 0.0f;
-            x[4 + e] = valid ? b[e] : 0.0f;
+            x[e] = a[e];
+            x[4 + e] = b[e];
         }
     }
 };
@@ -193,42 +234,48 @@ template <int ROWS, int D, int NTHR> struct Tile {
     __device__ __forceinline__ static int col(int tid) { return (tid % VPR) * 8; }
 };
 
-// Ownership of a [64][D] row-major tile by NTHR threads for transposed LDS builds: thread t
-// holds the row pair p = t % 32 (rows 2p, 2p+1) of the 8-column group cg = t / 32 (+ NTHR/32
-// per pass).  A half-wave then covers all 32 row pairs of one column group, so the transpose
-// is written one 32-bit word (two rows) per column into 32 consecutive words -- no LDS bank
-// conflicts -- without unpacking the bf16 data.  Threads past the last column group (only when
-// NTHR / 32 > D / 8) duplicate group 0's loads and store nothing.
+// Ownership of a [64][D] row-major tile by NTHR threads for transposed LDS builds, in units
+// of (row pair, 8-column group): a thread holds rows 2p and 2p+1 of 8 consecutive columns, so
+// the transpose is written one 32-bit word (two rows) per column without unpacking bf16 data.
+// The 64 units of one wave-wide pass are 8 row pairs x 8 column groups: each load instruction
+// then reads 8 rows of 128 contiguous bytes (one cache line each), and the transposed stores
+// of a pass fall into 16 distinct bank groups (4-way at most).  Units past the end (only when
+// the tile has fewer units than threads) duplicate unit 0's loads and store nothing.
 template <int D, int NTHR> struct PairTile {
-    static constexpr int CG = D / 8;
-    static constexpr int NPASS = (CG * 32 + NTHR - 1) / NTHR;
-    __device__ __forceinline__ static int pair(int tid) { return tid & 31; }
-    __device__ __forceinline__ static int group(int tid, int i) { return (tid >> 5) + (NTHR / 32) * i; }
-    __device__ __forceinline__ static bool valid(int tid, int i) { return group(tid, i) < CG; }
-    __device__ __forceinline__ static int col(int tid, int i) { return valid(tid, i) ? 8 * group(tid, i) : 0; }
+    static constexpr int CG = D / 8;          // 8-column groups
+    static constexpr int CB = CG / 8;         // blocks of 8 column groups
+    static_assert(CG % 8 == 0, "whole blocks of 8 column groups");
+    static constexpr int UNITS = 32 * CG;
+    static constexpr int NPASS = (UNITS + NTHR - 1) / NTHR;
+    __device__ __forceinline__ static bool valid(int tid, int i) { return tid + NTHR * i < UNITS; }
+    __device__ __forceinline__ static int pair(int tid, int i) {
+        const int u = (tid + NTHR * i) % UNITS;
+        return 8 * ((u >> 6) / CB) + ((u >> 3) & 7);
+    }
+    __device__ __forceinline__ static int col(int tid, int i) {
+        const int u = (tid + NTHR * i) % UNITS;
+        return 8 * (8 * ((u >> 6) % CB) + (u & 7));
+    }
 };
 
-// Element e (0..7) of a raw 8-element vector as a 16-bit pattern / as float.
-__device__ __forceinline__ uint32_t raw16(const Raw8<bf16_t>& x, int e) {
-    const uint32_t w = e < 2 ? x.w.x : e < 4 ? x.w.y : e < 6 ? x.w.z : x.w.w;
-    return (e & 1) ? (w >> 16) : (w & 0xFFFFu);
-}
-
 // Transposed store of a row pair: dst[(c8 + e) * ldt + perm(r0)] = {row r0, row r0 + 1}[e].
+// bf16 rows are interleaved in 32-bit words (v_perm_b32) without unpacking.
 template <typename MT, typename IO>
 __device__ __forceinline__ void st_pair_t(typename MM<MT>::S* dst, int ldt, int c8, int r0, const Raw8<IO>& x0,
-                                          bool v0, const Raw8<IO>& x1, bool v1) {
+                                          const Raw8<IO>& x1) {
     if constexpr (sizeof(typename MM<MT>::S) == 2 && std::is_same<IO, bf16_t>::value) {
         const int pr = perm<MT>(r0);
+        const uint32_t a[4] = {x0.w.x, x0.w.y, x0.w.z, x0.w.w}, b[4] = {x1.w.x, x1.w.y, x1.w.z, x1.w.w};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint32_t lo = v0 ? raw16(x0, e) : 0u, hi = v1 ? raw16(x1, e) : 0u;
-            *reinterpret_cast<uint32_t*>(dst + (c8 + e) * ldt + pr) = lo | (hi << 16);
+        for (int j = 0; j < 4; ++j) {
+            *reinterpret_cast<uint32_t*>(dst + (c8 + 2 * j) * ldt + pr) = __builtin_amdgcn_perm(b[j], a[j], 0x05040100u);
+            *reinterpret_cast<uint32_t*>(dst + (c8 + 2 * j + 1) * ldt + pr) =
+                __builtin_amdgcn_perm(b[j], a[j], 0x07060302u);
         }
     } else {
         float a[8], b[8];
-        x0.get(a, v0);
-        x1.get(b, v1);
+        x0.get(a);
+        x1.get(b);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             dst[(c8 + e) * ldt + perm<MT>(r0)] = MM<MT>::cvt(a[e]);
@@ -240,10 +287,10 @@ __device__ __forceinline__ void st_pair_t(typename MM<MT>::S* dst, int ldt, int 
 // Scaled transposed store of a row pair: dst[(c8 + e) * ldt + perm(r)] = x_r[e] * f(r, c8 + e).
 template <typename MT, typename IO, typename F>
 __device__ __forceinline__ void st_pair_t_scaled(typename MM<MT>::S* dst, int ldt, int c8, int r0,
-                                                 const Raw8<IO>& x0, bool v0, const Raw8<IO>& x1, bool v1, F f) {
+                                                 const Raw8<IO>& x0, const Raw8<IO>& x1, F f) {
     float a[8], b[8];
-    x0.get(a, v0);
-    x1.get(b, v1);
+    x0.get(a);
+    x1.get(b);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const float ya = a[e] * f(r0, c8 + e), yb = b[e] * f(r0 + 1, c8 + e);
@@ -339,16 +386,13 @@ __device__ __forceinline__ void lower_tile(int t, int& I, int& J) {
 
 // Store the 8 consecutive logical columns c8 .. c8+7 of a row into a perm()-ordered LDS row.
 template <typename MT, typename IO>
-__device__ __forceinline__ void st8_perm(typename MM<MT>::S* row, int c8, const Raw8<IO>& x, bool valid) {
+__device__ __forceinline__ void st8_perm(typename MM<MT>::S* row, int c8, const Raw8<IO>& x) {
     if constexpr (sizeof(typename MM<MT>::S) == 2 && std::is_same<IO, bf16_t>::value) {
-        const uint4 w = x.w;
-        const uint2 lo = valid ? uint2{w.x, w.y} : uint2{0u, 0u};
-        const uint2 hi = valid ? uint2{w.z, w.w} : uint2{0u, 0u};
-        *reinterpret_cast<uint2*>(row + perm<MT>(c8)) = lo;
-        *reinterpret_cast<uint2*>(row + perm<MT>(c8 + 4)) = hi;
+        *reinterpret_cast<uint2*>(row + perm<MT>(c8)) = uint2{x.w.x, x.w.y};
+        *reinterpret_cast<uint2*>(row + perm<MT>(c8 + 4)) = uint2{x.w.z, x.w.w};
     } else {
         float f[8];
-        x.get(f, valid);
+        x.get(f);
         MM<MT>::st8(row + c8, f);
     }
 }
@@ -451,7 +495,8 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
 
     const int vt = blockIdx.x, h = blockIdx.y, n = blockIdx.z;
     const int hk = h / (a.HV / a.HK);
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g4 = l >> 4, lr = l & 15;
+    const int tid = threadIdx.x, l = tid & 63, g4 = l >> 4, lr = l & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in a scalar register
     const int v0 = vt * BV;
     const int vcol = v0 + 16 * w + lr;
     const int64_t s0 = a.cu_seqlens ? a.cu_seqlens[n] : 0;
@@ -485,47 +530,39 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
     Raw8<IO> qn[TQ::NV], kn[2 * PK::NPASS], vn[2 * PV::NPASS];
     float gn[RPQ];
     uint32_t bn = 0;  // beta kept as loaded (bf16 bits or fp32 bits): converting here would wait on the load
+    // byte strides of one token row and this thread's byte offsets inside a chunk (fixed)
+    constexpr int ESZ = sizeof(IO) == 4 ? 4 : 2;
+    const int qk_row = a.HK * K * ESZ, v_row = a.HV * a.V * ESZ;
+    const int g_row = (PER_K ? a.HV * K : a.HV) * 4, b_row = a.HV * ESZ;
+    const int gq_c = PER_K ? tid % K : 0, gq_r = PER_K ? (tid / K) * RPQ : (tid & 63);
     auto load_chunk = [&](int ci) {
         const int64_t bos = s0 + (int64_t)CH * ci;
         const int len = (s1 - bos) < CH ? (int)(s1 - bos) : CH;
+        const char* q0 = static_cast<const char*>(a.q) + ((bos * a.HK + hk) * K) * ESZ;
+        const char* k0 = static_cast<const char*>(a.k) + ((bos * a.HK + hk) * K) * ESZ;
+        const char* v0p = static_cast<const char*>(a.v) + ((bos * a.HV + h) * a.V + v0) * ESZ;
+        const __amdgpu_buffer_rsrc_t rq = chunk_rsrc(q0, len, qk_row), rk = chunk_rsrc(k0, len, qk_row);
+        const __amdgpu_buffer_rsrc_t rv = chunk_rsrc(v0p, len, v_row);
 #pragma unroll
-        for (int i = 0; i < TQ::NV; ++i) {
-            const int r = TQ::row(tid, i), rc = r < len ? r : len - 1;
-            qn[i].load(a.q, ((bos + rc) * a.HK + hk) * K + TQ::col(tid));
-        }
+        for (int i = 0; i < TQ::NV; ++i) qn[i].load(rq, TQ::row(tid, i) * qk_row + TQ::col(tid) * ESZ);
 #pragma unroll
-        for (int i = 0; i < PK::NPASS; ++i) {
+        for (int i = 0; i < PK::NPASS; ++i)
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int r = 2 * PK::pair(tid) + u, rc = r < len ? r : len - 1;
-                kn[2 * i + u].load(a.k, ((bos + rc) * a.HK + hk) * K + PK::col(tid, i));
-            }
-        }
+            for (int u = 0; u < 2; ++u) kn[2 * i + u].load(rk, (2 * PK::pair(tid, i) + u) * qk_row + PK::col(tid, i) * ESZ);
 #pragma unroll
-        for (int i = 0; i < PV::NPASS; ++i) {
+        for (int i = 0; i < PV::NPASS; ++i)
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int r = 2 * PV::pair(tid) + u, rc = r < len ? r : len - 1;
-                vn[2 * i + u].load(a.v, ((bos + rc) * a.HV + h) * a.V + v0 + PV::col(tid, i));
-            }
-        }
-        if constexpr (PER_K) {
-            const int c = tid % K, qd = tid / K;
+            for (int u = 0; u < 2; ++u) vn[2 * i + u].load(rv, (2 * PV::pair(tid, i) + u) * v_row + PV::col(tid, i) * ESZ);
+        const float* g0 = a.g + (PER_K ? (bos * a.HV + h) * K : bos * a.HV + h);
+        const __amdgpu_buffer_rsrc_t rg = chunk_rsrc(g0, len, g_row);
 #pragma unroll
-            for (int i = 0; i < RPQ; ++i) {
-                const int r = qd * RPQ + i, rc = r < len ? r : len - 1;
-                gn[i] = a.g[((bos + rc) * a.HV + h) * K + c];
-            }
-        } else {
-            const int rc = (tid & 63) < len ? (tid & 63) : len - 1;
-            gn[0] = a.g[(bos + rc) * a.HV + h];
-        }
-        {
-            const int rc = (tid & 63) < len ? (tid & 63) : len - 1;
-            const int64_t bi = (bos + rc) * a.HV + h;
-            if constexpr (std::is_same<IO, float>::value) bn = __float_as_uint(static_cast<const float*>(a.beta)[bi]);
-            else bn = static_cast<const uint16_t*>(a.beta)[bi];
-        }
+        for (int i = 0; i < RPQ; ++i)
+            gn[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, (gq_r + i) * g_row + gq_c * 4, 0, 0));
+        const __amdgpu_buffer_rsrc_t rb = chunk_rsrc(static_cast<const char*>(a.beta) + (bos * a.HV + h) * ESZ, len, b_row);
+        if constexpr (std::is_same<IO, float>::value)
+            bn = __builtin_amdgcn_raw_buffer_load_b32(rb, (tid & 63) * b_row, 0, 0);
+        else
+            bn = __builtin_amdgcn_raw_buffer_load_b16(rb, (tid & 63) * b_row, 0, 0);
     };
     if (nc > 0) load_chunk(0);
 
@@ -546,7 +583,10 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
         const int64_t bos = s0 + (int64_t)CH * ci;
         const int len = (s1 - bos) < CH ? (int)(s1 - bos) : CH;
 
-        // current chunk <- prefetched registers; start loading the next one
+        // current chunk <- prefetched registers.  The next chunk's loads are issued later, at a
+        // point that differs by wave (after the L/P tiles for the waves that compute them, at the
+        // start of D for the waves that invert the diagonal blocks), so that the workgroup's load
+        // instructions do not all queue for the vector memory pipe at once.
         Raw8<IO> qr[TQ::NV], kr[2 * PK::NPASS], vr[2 * PV::NPASS];
         float gr[RPQ];
         const float br = std::is_same<IO, float>::value ? __uint_as_float(bn) : __uint_as_float(bn << 16);
@@ -558,7 +598,6 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
         for (int i = 0; i < 2 * PV::NPASS; ++i) vr[i] = vn[i];
 #pragma unroll
         for (int i = 0; i < RPQ; ++i) gr[i] = gn[i];
-        if (ci + 1 < nc) load_chunk(ci + 1);
         if (ci > 0) flush_o(bos - CH, CH);
 
         S* sQ = SP(PER_K ? Lay::k_q : Lay::g_q);
@@ -572,41 +611,29 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
         float* sb = FP(PER_K ? Lay::k_b : Lay::g_b);
 
         // ===== A: raw rows into LDS, gate prefix =====
-        const int pr0 = 2 * PK::pair(tid);
 #pragma unroll
-        for (int i = 0; i < TQ::NV; ++i) {
-            const int r = TQ::row(tid, i);
-            st8_perm<MT, IO>(sQ + r * LDK, TQ::col(tid), qr[i], r < len);
-        }
+        for (int i = 0; i < TQ::NV; ++i) st8_perm<MT, IO>(sQ + TQ::row(tid, i) * LDK, TQ::col(tid), qr[i]);
 #pragma unroll
         for (int i = 0; i < PK::NPASS; ++i) {
             if (PK::valid(tid, i)) {
-                const int c8 = PK::col(tid, i);
-                st8_perm<MT, IO>(sK + pr0 * LDK, c8, kr[2 * i], pr0 < len);
-                st8_perm<MT, IO>(sK + (pr0 + 1) * LDK, c8, kr[2 * i + 1], pr0 + 1 < len);
-                if constexpr (!PER_K)
-                    st_pair_t<MT, IO>(SP(Lay::g_kt), LDT, c8, pr0, kr[2 * i], pr0 < len, kr[2 * i + 1], pr0 + 1 < len);
+                const int c8 = PK::col(tid, i), pr0 = 2 * PK::pair(tid, i);
+                st8_perm<MT, IO>(sK + pr0 * LDK, c8, kr[2 * i]);
+                st8_perm<MT, IO>(sK + (pr0 + 1) * LDK, c8, kr[2 * i + 1]);
+                if constexpr (!PER_K) st_pair_t<MT, IO>(SP(Lay::g_kt), LDT, c8, pr0, kr[2 * i], kr[2 * i + 1]);
             }
         }
         if constexpr (!PER_K) {
 #pragma unroll
             for (int i = 0; i < PV::NPASS; ++i) {
                 if (PV::valid(tid, i))
-                    st_pair_t<MT, IO>(SP(Lay::g_vt), LDT, PV::col(tid, i), pr0, vr[2 * i], pr0 < len, vr[2 * i + 1],
-                                      pr0 + 1 < len);
+                    st_pair_t<MT, IO>(SP(Lay::g_vt), LDT, PV::col(tid, i), 2 * PV::pair(tid, i), vr[2 * i], vr[2 * i + 1]);
             }
-            if (tid < 64) {  // wave 0: inclusive prefix sum of the 64 gates
+            if (tid < 64) {  // wave 0: inclusive prefix sum of the 64 gates (rows past the end are 0)
                 const int r = tid;
-                float x = r < len ? gr[0] : 0.0f;
-#pragma unroll
-                for (int d = 1; d < 64; d <<= 1) {
-                    const float y = __shfl_up(x, d, 64);
-                    if (r >= d) x += y;
-                }
-                const float bb = r < len ? br : 0.0f;
+                const float x = wave_inclusive_sum(gr[0]);
                 sg[r] = x;
-                sb[r] = bb;
-                FP(Lay::g_be)[r] = bb * exp_f32(x);
+                sb[r] = br;
+                FP(Lay::g_be)[r] = br * exp_f32(x);
             }
         } else {
             // thread (c, qd): prefix over its RPQ rows of channel c, then group offsets
@@ -615,11 +642,11 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
             float x = 0.0f;
 #pragma unroll
             for (int i = 0; i < RPQ; ++i) {
-                x += (qd * RPQ + i) < len ? gr[i] : 0.0f;
+                x += gr[i];
                 gr[i] = x;
             }
             part[qd * K + c] = x;
-            if (tid < 64) sb[tid] = tid < len ? br : 0.0f;
+            if (tid < 64) sb[tid] = br;
             __syncthreads();
             float off = 0.0f;
             for (int j = 0; j < qd; ++j) off += part[j * K + c];
@@ -635,30 +662,63 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
                 f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
                 M::nt(acc, sK + 16 * w * LDK, LDK, sK + 16 * w * LDK, LDK, K);
                 float* sN = sLd + w * 16 * 17;
+                const f32x4_t gr = *reinterpret_cast<const f32x4_t*>(sg + 16 * w + 4 * g4);
+                const f32x4_t br = *reinterpret_cast<const f32x4_t*>(sb + 16 * w + 4 * g4);
+                const float gj = sg[16 * w + lr];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int rr = 4 * g4 + e, r = 16 * w + rr, j = 16 * w + lr;
-                    sN[rr * 17 + lr] = (rr > lr) ? sb[r] * exp_f32(sg[r] - sg[j]) * acc[e] : 0.0f;
+                    const int rr = 4 * g4 + e;
+                    const float x = br[e] * exp_f32(gr[e] - gj) * acc[e];
+                    sN[rr * 17 + lr] = (rr > lr) ? x : 0.0f;
                 }
                 // the tile's LDS writes complete before this wave's lanes read other lanes' entries
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
                 invert_unit_lower_16<MT>(sN, sD + 16 * w * LDD, LDD);
             }
-            const int w0 = NW > 4 ? 4 : 0, nw = NW > 4 ? NW - 4 : NW;
-            for (int t = w - w0; t >= 0 && t < 16; t += nw) {
-                int I, J;
+            // the 6 strictly lower tiles of L and the 10 lower tiles of P: tile t = (w - w0) + NWT k,
+            // two at a time so that both tiles' operand reads are in flight together
+            constexpr int W0 = NW > 4 ? 4 : 0, NWT = NW - W0, TPW = (16 + NWT - 1) / NWT;
+            auto tile = [&](int t, int& I, int& J, const S*& pa, const S*& pb) {
                 const bool isL = t < 6;
                 if (isL) strict_tile(t, I, J);
                 else lower_tile(t - 6, I, J);
-                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-                M::nt(acc, (isL ? sK : sQ) + 16 * I * LDK, LDK, sK + 16 * J * LDK, LDK, K);
+                pa = (isL ? sK : sQ) + 16 * I * LDK;
+                pb = sK + 16 * J * LDK;
+            };
+            auto epilogue = [&](int t, int I, int J, const f32x4_t& acc) {
+                const f32x4_t gr = *reinterpret_cast<const f32x4_t*>(sg + 16 * I + 4 * g4);
+                const float gj = sg[16 * J + lr];
+                if (t < 6) {
+                    const f32x4_t br = *reinterpret_cast<const f32x4_t*>(sb + 16 * I + 4 * g4);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 16 * I + 4 * g4 + e, j = 16 * J + lr;
-                    const float d = exp_f32(sg[r] - sg[j]);
-                    if (isL) sLo[r * LDO + j] = M::cvt(-sb[r] * d * acc[e]);
-                    else sP[r * LDT + perm<MT>(j)] = M::cvt((r >= j) ? d * acc[e] : 0.0f);
+                    for (int e = 0; e < 4; ++e)
+                        sLo[(16 * I + 4 * g4 + e) * LDO + 16 * J + lr] = M::cvt(-br[e] * exp_f32(gr[e] - gj) * acc[e]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 16 * I + 4 * g4 + e, j = 16 * J + lr;
+                        const float x = exp_f32(gr[e] - gj) * acc[e];  // inf above the diagonal is discarded
+                        sP[r * LDT + perm<MT>(j)] = M::cvt((r >= j) ? x : 0.0f);
+                    }
                 }
+            };
+            if (w >= W0) {
+#pragma unroll
+                for (int k = 0; k < TPW; k += 2) {
+                    const int t0 = w - W0 + NWT * k, t1 = t0 + NWT;
+                    if (t0 < 16) {
+                        const bool has1 = k + 1 < TPW && t1 < 16;
+                        int I0, J0, I1, J1;
+                        const S *a0, *b0, *a1, *b1;
+                        tile(t0, I0, J0, a0, b0);
+                        tile(has1 ? t1 : t0, I1, J1, a1, b1);
+                        f32x4_t c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+                        M::template nt2<K>(c0, a0, b0, c1, a1, b1, LDK);
+                        epilogue(t0, I0, J0, c0);
+                        if (has1) epilogue(t1, I1, J1, c1);
+                    }
+                }
+                if (NW > 4 && ci + 1 < nc) load_chunk(ci + 1);
             }
         } else {
             S* sLK = SP(Lay::k_lk);
@@ -722,21 +782,21 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
 #pragma unroll
             for (int i = 0; i < PK::NPASS; ++i) {
                 if (PK::valid(tid, i)) {
-                    const int c8 = PK::col(tid, i);
-                    st_pair_t_scaled<MT, IO>(sKgT, LDT, c8, pr0, kr[2 * i], pr0 < len, kr[2 * i + 1], pr0 + 1 < len, f_g);
-                    st_pair_t_scaled<MT, IO>(sKdT, LDT, c8, pr0, kr[2 * i], pr0 < len, kr[2 * i + 1], pr0 + 1 < len, f_d);
+                    const int c8 = PK::col(tid, i), pr0 = 2 * PK::pair(tid, i);
+                    st_pair_t_scaled<MT, IO>(sKgT, LDT, c8, pr0, kr[2 * i], kr[2 * i + 1], f_g);
+                    st_pair_t_scaled<MT, IO>(sKdT, LDT, c8, pr0, kr[2 * i], kr[2 * i + 1], f_d);
                 }
             }
 #pragma unroll
             for (int i = 0; i < PV::NPASS; ++i) {
                 if (PV::valid(tid, i))
-                    st_pair_t<MT, IO>(sVT, LDT, PV::col(tid, i), pr0, vr[2 * i], pr0 < len, vr[2 * i + 1], pr0 + 1 < len);
+                    st_pair_t<MT, IO>(sVT, LDT, PV::col(tid, i), 2 * PV::pair(tid, i), vr[2 * i], vr[2 * i + 1]);
             }
 #pragma unroll
             for (int i = 0; i < TQ::NV; ++i) {
                 const int r = TQ::row(tid, i), c8 = TQ::col(tid);
                 float y[8];
-                qr[i].get(y, r < len);
+                qr[i].get(y);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) y[e] *= exp_f32(sg[r * K + c8 + e]);
                 if constexpr (Lay::BF) {
@@ -751,6 +811,7 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
         __syncthreads();
 
         // ===== D: [W | U] = (I + L)^-1 [beta e^gamma K | beta V] by blocked substitution =====
+        if ((PER_K || NW == 4 || w < 4) && ci + 1 < nc) load_chunk(ci + 1);
         f32x4_t nu[4];
         {
             const S* sKb = SP(PER_K ? Lay::k_kgt : Lay::g_kt);

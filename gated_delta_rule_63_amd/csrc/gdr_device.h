@@ -126,6 +126,24 @@ __device__ __forceinline__ float row16_sum(float x) {
     return x;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave.  row_shr steps (lanes shifted in from
+// outside the 16-lane row read 0) scan each DPP row; row_bcast:15 then adds row 0's total to
+// row 1 and row 2's to row 3, and row_bcast:31 adds the total of rows 0-1 to rows 2-3 (rows
+// outside the row mask keep the 0 passed as the old value).
+template <int CTRL, int ROW_MASK, bool BOUND_ZERO>
+__device__ __forceinline__ float dpp_or_zero(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xF, BOUND_ZERO));
+}
+__device__ __forceinline__ float wave_inclusive_sum(float x) {
+    x += dpp_or_zero<0x111, 0xF, true>(x);   // row_shr:1
+    x += dpp_or_zero<0x112, 0xF, true>(x);   // row_shr:2
+    x += dpp_or_zero<0x114, 0xF, true>(x);   // row_shr:4
+    x += dpp_or_zero<0x118, 0xF, true>(x);   // row_shr:8
+    x += dpp_or_zero<0x142, 0xA, false>(x);  // row_bcast:15
+    x += dpp_or_zero<0x143, 0xC, false>(x);  // row_bcast:31
+    return x;
+}
+
 __device__ __forceinline__ float exp_f32(float x) {
     // e^x = 2^(x * log2(e)); v_exp_f32 evaluates 2^y.
     return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
