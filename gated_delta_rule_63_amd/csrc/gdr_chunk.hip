@@ -303,24 +303,69 @@ __device__ __forceinline__ void st_pair_t_scaled(typename MM<MT>::S* dst, int ld
     }
 }
 
-// D = (I + N)^-1 for a strictly lower 16x16 N (fp32, stride 17), by forward substitution:
-// lane j < 16 of the calling wave computes column j.  D is written row-major (stride ldd) in
-// the MFMA operand dtype.
+// Row stride (floats) of the fp32 16x16 diagonal blocks of L in LDS: rows stay 16-byte aligned.
+constexpr int LDN = 20;
+
+// Value of register x held by the lanes of row group S (lanes 16S .. 16S+15), broadcast to the
+// same lane position of every row group.  v_permlane16_swap with both operands x yields
+// [x.r0, x.r0, x.r2, x.r2] and [x.r1, x.r1, x.r3, x.r3]; v_permlane32_swap of such a value
+// with itself yields its lower half [a.r0, a.r1, a.r0, a.r1] and upper half [a.r2, a.r3, a.r2, a.r3].
+template <int S>
+__device__ __forceinline__ float row_group_bcast(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const uint32_t a = (S & 1) ? p[1] : p[0];
+    const auto q = __builtin_amdgcn_permlane32_swap(a, a, false, false);
+    return __uint_as_float((S & 2) ? q[1] : q[0]);
+}
+
+// D = (I + N)^-1 for a strictly lower 16x16 N (fp32 in LDS, row stride LDN, zero on and above
+// the diagonal), with all 64 lanes of the calling wave: lane (g, j) = (l / 16, l % 16) holds
+// rows 4g .. 4g+3 of column j (the MFMA accumulator layout).  Blockwise forward substitution
+// over the four 4-row groups: at step s the lanes of group s finish their rows by a local 4x4
+// substitution, the four finished values of each column are broadcast across row groups, and
+// the groups below subtract their N(4g.., 4s..) block times them.  D is written row-major
+// (stride ldd) in the MFMA operand dtype.
 template <typename MT>
 __device__ __forceinline__ void invert_unit_lower_16(const float* sN, typename MM<MT>::S* sD, int ldd) {
-    const int j = threadIdx.x & 63;
-    if (j < 16) {
-        float x[16];
+    const int l = threadIdx.x & 63, g = l >> 4, j = l & 15;
+    f32x4_t nb[4][4];  // nb[s][a] = N[4g + a][4s .. 4s+3]
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            float acc = (i == j) ? 1.0f : 0.0f;
+    for (int s = 0; s < 4; ++s)
 #pragma unroll
-            for (int m = 0; m < i; ++m) acc = fmaf(-sN[i * 17 + m], x[m], acc);
-            x[i] = acc;
+        for (int a = 0; a < 4; ++a) nb[s][a] = *reinterpret_cast<const f32x4_t*>(sN + (4 * g + a) * LDN + 4 * s);
+    float x[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = (4 * g + e == j) ? 1.0f : 0.0f;
+    auto step = [&](auto sc) {
+        constexpr int s = decltype(sc)::value;
+        // rows of group s: local substitution with the diagonal 4x4 block of N
+        float y[4] = {x[0], x[1], x[2], x[3]};
+#pragma unroll
+        for (int e = 1; e < 4; ++e)
+#pragma unroll
+            for (int f = 0; f < e; ++f) y[e] = fmaf(-nb[s][e][f], y[f], y[e]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = (g == s) ? y[e] : x[e];
+        if constexpr (s < 3) {
+            float b[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) b[e] = row_group_bcast<s>(x[e]);
+            float z[4] = {x[0], x[1], x[2], x[3]};
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int f = 0; f < 4; ++f) z[a] = fmaf(-nb[s][a][f], b[f], z[a]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = (g > s) ? z[e] : x[e];
         }
+    };
+    step(std::integral_constant<int, 0>{});
+    step(std::integral_constant<int, 1>{});
+    step(std::integral_constant<int, 2>{});
+    step(std::integral_constant<int, 3>{});
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sD[i * ldd + j] = MM<MT>::cvt(x[i]);
-    }
+    for (int e = 0; e < 4; ++e) sD[(4 * g + e) * ldd + j] = MM<MT>::cvt(x[e]);
 }
 
 // X = (I + L)^-1 B for one 16-column tile of B (64 rows), by blocked forward substitution:
@@ -412,7 +457,7 @@ struct Layout {
     static constexpr size_t KT_ = sizeof(S) * K * LDT;     // [K][LDT]
     static constexpr size_t VT_ = sizeof(S) * BV * LDT;    // [BV][LDT]
     static constexpr size_t LO_ = sizeof(S) * CH * LDO;    // [64][LDO]
-    static constexpr size_t LD_ = sizeof(float) * 4 * 16 * 17;  // diagonal L blocks, fp32
+    static constexpr size_t LD_ = sizeof(float) * 4 * 16 * LDN;  // diagonal L blocks, fp32
     static constexpr size_t D_ = sizeof(S) * CH * LDD;     // [4*16][LDD]
 
     // ---- scalar gate ----
@@ -528,41 +573,67 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
     constexpr int GQ = NTHR / K;                   // per-K gate: row groups per channel
     constexpr int RPQ = PER_K ? CH / GQ : 1;       // gate values per thread
     Raw8<IO> qn[TQ::NV], kn[2 * PK::NPASS], vn[2 * PV::NPASS];
-    float gn[RPQ];
+    float gn[RPQ] = {};
     uint32_t bn = 0;  // beta kept as loaded (bf16 bits or fp32 bits): converting here would wait on the load
     // byte strides of one token row and this thread's byte offsets inside a chunk (fixed)
     constexpr int ESZ = sizeof(IO) == 4 ? 4 : 2;
     const int qk_row = a.HK * K * ESZ, v_row = a.HV * a.V * ESZ;
     const int g_row = (PER_K ? a.HV * K : a.HV) * 4, b_row = a.HV * ESZ;
     const int gq_c = PER_K ? tid % K : 0, gq_r = PER_K ? (tid / K) * RPQ : (tid & 63);
-    auto load_chunk = [&](int ci) {
+    // the next chunk's rows are loaded in three parts at three points of the current chunk, so
+    // that the cache-line misses a workgroup has in flight stay bounded and no wave stalls long
+    // on issue: q (end of B/C), k (start of D), v with g and beta (in E, after v_new)
+    auto chunk_len = [&](int ci) {
         const int64_t bos = s0 + (int64_t)CH * ci;
-        const int len = (s1 - bos) < CH ? (int)(s1 - bos) : CH;
-        const char* q0 = static_cast<const char*>(a.q) + ((bos * a.HK + hk) * K) * ESZ;
-        const char* k0 = static_cast<const char*>(a.k) + ((bos * a.HK + hk) * K) * ESZ;
-        const char* v0p = static_cast<const char*>(a.v) + ((bos * a.HV + h) * a.V + v0) * ESZ;
-        const __amdgpu_buffer_rsrc_t rq = chunk_rsrc(q0, len, qk_row), rk = chunk_rsrc(k0, len, qk_row);
-        const __amdgpu_buffer_rsrc_t rv = chunk_rsrc(v0p, len, v_row);
+        return (s1 - bos) < CH ? (int)(s1 - bos) : CH;
+    };
+    auto load_q = [&](int ci) {
+        const int64_t bos = s0 + (int64_t)CH * ci;
+        const __amdgpu_buffer_rsrc_t rq =
+            chunk_rsrc(static_cast<const char*>(a.q) + ((bos * a.HK + hk) * K) * ESZ, chunk_len(ci), qk_row);
 #pragma unroll
         for (int i = 0; i < TQ::NV; ++i) qn[i].load(rq, TQ::row(tid, i) * qk_row + TQ::col(tid) * ESZ);
+    };
+    auto load_k = [&](int ci) {
+        const int64_t bos = s0 + (int64_t)CH * ci;
+        const __amdgpu_buffer_rsrc_t rk =
+            chunk_rsrc(static_cast<const char*>(a.k) + ((bos * a.HK + hk) * K) * ESZ, chunk_len(ci), qk_row);
 #pragma unroll
         for (int i = 0; i < PK::NPASS; ++i)
 #pragma unroll
             for (int u = 0; u < 2; ++u) kn[2 * i + u].load(rk, (2 * PK::pair(tid, i) + u) * qk_row + PK::col(tid, i) * ESZ);
+    };
+    auto load_vgb = [&](int ci) {
+        const int64_t bos = s0 + (int64_t)CH * ci;
+        const int len = chunk_len(ci);
+        const __amdgpu_buffer_rsrc_t rv =
+            chunk_rsrc(static_cast<const char*>(a.v) + ((bos * a.HV + h) * a.V + v0) * ESZ, len, v_row);
 #pragma unroll
         for (int i = 0; i < PV::NPASS; ++i)
 #pragma unroll
             for (int u = 0; u < 2; ++u) vn[2 * i + u].load(rv, (2 * PV::pair(tid, i) + u) * v_row + PV::col(tid, i) * ESZ);
-        const float* g0 = a.g + (PER_K ? (bos * a.HV + h) * K : bos * a.HV + h);
-        const __amdgpu_buffer_rsrc_t rg = chunk_rsrc(g0, len, g_row);
+        // the scalar gate and beta are read by wave 0 only (one value per row, one cache line each)
+        if (PER_K || w == 0) {
+            const float* g0 = a.g + (PER_K ? (bos * a.HV + h) * K : bos * a.HV + h);
+            const __amdgpu_buffer_rsrc_t rg = chunk_rsrc(g0, len, g_row);
 #pragma unroll
-        for (int i = 0; i < RPQ; ++i)
-            gn[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, (gq_r + i) * g_row + gq_c * 4, 0, 0));
-        const __amdgpu_buffer_rsrc_t rb = chunk_rsrc(static_cast<const char*>(a.beta) + (bos * a.HV + h) * ESZ, len, b_row);
-        if constexpr (std::is_same<IO, float>::value)
-            bn = __builtin_amdgcn_raw_buffer_load_b32(rb, (tid & 63) * b_row, 0, 0);
-        else
-            bn = __builtin_amdgcn_raw_buffer_load_b16(rb, (tid & 63) * b_row, 0, 0);
+            for (int i = 0; i < RPQ; ++i)
+                gn[i] = __builtin_bit_cast(float,
+                                           __builtin_amdgcn_raw_buffer_load_b32(rg, (gq_r + i) * g_row + gq_c * 4, 0, 0));
+        }
+        if (w == 0) {
+            const __amdgpu_buffer_rsrc_t rb =
+                chunk_rsrc(static_cast<const char*>(a.beta) + (bos * a.HV + h) * ESZ, len, b_row);
+            if constexpr (std::is_same<IO, float>::value)
+                bn = __builtin_amdgcn_raw_buffer_load_b32(rb, (tid & 63) * b_row, 0, 0);
+            else
+                bn = __builtin_amdgcn_raw_buffer_load_b16(rb, (tid & 63) * b_row, 0, 0);
+        }
+    };
+    auto load_chunk = [&](int ci) {
+        load_q(ci);
+        load_k(ci);
+        load_vgb(ci);
     };
     if (nc > 0) load_chunk(0);
 
@@ -583,10 +654,7 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
         const int64_t bos = s0 + (int64_t)CH * ci;
         const int len = (s1 - bos) < CH ? (int)(s1 - bos) : CH;
 
-        // current chunk <- prefetched registers.  The next chunk's loads are issued later, at a
-        // point that differs by wave (after the L/P tiles for the waves that compute them, at the
-        // start of D for the waves that invert the diagonal blocks), so that the workgroup's load
-        // instructions do not all queue for the vector memory pipe at once.
+        // current chunk <- prefetched registers (the next chunk's loads are issued in B/C, D and E)
         Raw8<IO> qr[TQ::NV], kr[2 * PK::NPASS], vr[2 * PV::NPASS];
         float gr[RPQ];
         const float br = std::is_same<IO, float>::value ? __uint_as_float(bn) : __uint_as_float(bn << 16);
@@ -661,7 +729,7 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
             if (w < 4) {  // diagonal tile (w, w) of L, then D_w = (I + L_ww)^-1
                 f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
                 M::nt(acc, sK + 16 * w * LDK, LDK, sK + 16 * w * LDK, LDK, K);
-                float* sN = sLd + w * 16 * 17;
+                float* sN = sLd + w * 16 * LDN;
                 const f32x4_t gr = *reinterpret_cast<const f32x4_t*>(sg + 16 * w + 4 * g4);
                 const f32x4_t br = *reinterpret_cast<const f32x4_t*>(sb + 16 * w + 4 * g4);
                 const float gj = sg[16 * w + lr];
@@ -669,15 +737,14 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
                 for (int e = 0; e < 4; ++e) {
                     const int rr = 4 * g4 + e;
                     const float x = br[e] * exp_f32(gr[e] - gj) * acc[e];
-                    sN[rr * 17 + lr] = (rr > lr) ? x : 0.0f;
+                    sN[rr * LDN + lr] = (rr > lr) ? x : 0.0f;
                 }
                 // the tile's LDS writes complete before this wave's lanes read other lanes' entries
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
                 invert_unit_lower_16<MT>(sN, sD + 16 * w * LDD, LDD);
             }
-            // the 6 strictly lower tiles of L and the 10 lower tiles of P: tile t = (w - w0) + NWT k,
-            // two at a time so that both tiles' operand reads are in flight together
-            constexpr int W0 = NW > 4 ? 4 : 0, NWT = NW - W0, TPW = (16 + NWT - 1) / NWT;
+            // the 6 strictly lower tiles of L and the 10 lower tiles of P (t = 0..15), two at a time
+            // so that both tiles' operand reads are in flight together
             auto tile = [&](int t, int& I, int& J, const S*& pa, const S*& pb) {
                 const bool isL = t < 6;
                 if (isL) strict_tile(t, I, J);
@@ -702,24 +769,38 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
                     }
                 }
             };
-            if (w >= W0) {
+            auto tiles = [&](int first, int stride, auto count_c) {
+                constexpr int CNT = decltype(count_c)::value;
 #pragma unroll
-                for (int k = 0; k < TPW; k += 2) {
-                    const int t0 = w - W0 + NWT * k, t1 = t0 + NWT;
-                    if (t0 < 16) {
-                        const bool has1 = k + 1 < TPW && t1 < 16;
-                        int I0, J0, I1, J1;
-                        const S *a0, *b0, *a1, *b1;
-                        tile(t0, I0, J0, a0, b0);
-                        tile(has1 ? t1 : t0, I1, J1, a1, b1);
-                        f32x4_t c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
-                        M::template nt2<K>(c0, a0, b0, c1, a1, b1, LDK);
-                        epilogue(t0, I0, J0, c0);
-                        if (has1) epilogue(t1, I1, J1, c1);
-                    }
+                for (int k = 0; k + 1 < CNT; k += 2) {
+                    const int t0 = first + stride * k, t1 = t0 + stride;
+                    int I0, J0, I1, J1;
+                    const S *a0, *b0, *a1, *b1;
+                    tile(t0, I0, J0, a0, b0);
+                    tile(t1, I1, J1, a1, b1);
+                    f32x4_t c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+                    M::template nt2<K>(c0, a0, b0, c1, a1, b1, LDK);
+                    epilogue(t0, I0, J0, c0);
+                    epilogue(t1, I1, J1, c1);
                 }
-                if (NW > 4 && ci + 1 < nc) load_chunk(ci + 1);
+                if constexpr (CNT % 2 == 1) {
+                    const int t0 = first + stride * (CNT - 1);
+                    int I0, J0;
+                    const S *a0, *b0;
+                    tile(t0, I0, J0, a0, b0);
+                    f32x4_t c0 = {0.f, 0.f, 0.f, 0.f};
+                    M::nt(c0, a0, LDK, b0, LDK, K);
+                    epilogue(t0, I0, J0, c0);
+                }
+            };
+            if constexpr (NW > 4) {
+                // waves 4-7: tiles 0..11; waves 0-3 (after their inversion): tiles 12..15
+                if (w >= 4) tiles(w - 4, 4, std::integral_constant<int, 3>{});
+                else tiles(12 + w, 4, std::integral_constant<int, 1>{});
+            } else {
+                tiles(w, 4, std::integral_constant<int, 4>{});
             }
+            if (ci + 1 < nc) load_q(ci + 1);
         } else {
             S* sLK = SP(Lay::k_lk);
             S* sLQ = SP(Lay::k_lq);
@@ -739,7 +820,7 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
                     }
                 }
                 sP[r * LDT + perm<MT>(j)] = M::cvt(accp);  // zero above the diagonal
-                sLd[b * 16 * 17 + rr * 17 + jj] = (jj < rr) ? sb[r] * accl : 0.0f;
+                sLd[b * 16 * LDN + rr * LDN + jj] = (jj < rr) ? sb[r] * accl : 0.0f;
             }
             // off-diagonal blocks (I > J) through MFMA, reference point rho = gamma[16I - 1]
             for (int I = 1; I < 4; ++I) {
@@ -770,7 +851,7 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
                 }
                 __syncthreads();
             }
-            if (w < 4) invert_unit_lower_16<MT>(sLd + w * 16 * 17, sD + 16 * w * LDD, LDD);
+            if (w < 4) invert_unit_lower_16<MT>(sLd + w * 16 * LDN, sD + 16 * w * LDD, LDD);
             // the transposed / scaled operands of D and E, from this chunk's registers
             S* sKgT = SP(Lay::k_kgt);
             S* sVT = SP(Lay::k_vt);
@@ -811,7 +892,10 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
         __syncthreads();
 
         // ===== D: [W | U] = (I + L)^-1 [beta e^gamma K | beta V] by blocked substitution =====
-        if ((PER_K || NW == 4 || w < 4) && ci + 1 < nc) load_chunk(ci + 1);
+        if constexpr (PER_K) {
+            if (ci + 1 < nc) load_q(ci + 1);
+        }
+        if (ci + 1 < nc) load_k(ci + 1);
         f32x4_t nu[4];
         {
             const S* sKb = SP(PER_K ? Lay::k_kgt : Lay::g_kt);
@@ -833,6 +917,7 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
         // ===== E: v_new, output, state update (wave w: columns 16w .. 16w+15) =====
         // v_new = U - W S^T  (LDS holds -W)
         gemm_regs<MT, K, 4>(nu, sW, LDK, hs);
+        if (ci + 1 < nc) load_vgb(ci + 1);
         // O = scale (diag(e^gamma) Q S^T + P v_new)
         f32x4_t oa[4];
 #pragma unroll
