@@ -368,52 +368,111 @@ __device__ __forceinline__ void invert_unit_lower_16(const float* sN, typename M
     for (int e = 0; e < 4; ++e) sD[(4 * g + e) * ldd + j] = MM<MT>::cvt(x[e]);
 }
 
-// X = (I + L)^-1 B for one 16-column tile of B (64 rows), by blocked forward substitution:
-// X_I = D_I (B_I - sum_{J<I} L_IJ X_J), D_I = (I + L_II)^-1.  L's off-diagonal blocks are read
-// negated from sLo (row-major, stride ldo), the D_I from sD (block I at sD + 16*I*ldd).  Row t
-// of the B tile is sBt[perm(t)] * sc[t] (sBt: the transposed-B row of this lane's column).
-// X stays in registers in C layout; with v_mfma_f32_16x16x16_bf16 the C layout of one block
-// is the B operand layout of the next product, so each wave solves its own columns without
-// synchronising with the others.
-template <typename MT>
-__device__ __forceinline__ void block_solve(f32x4_t* X, const typename MM<MT>::S* sLo, int ldo,
-                                            const typename MM<MT>::S* sD, int ldd,
-                                            const typename MM<MT>::S* sBt, const float* sc) {
-    const int l = threadIdx.x & 63, g4 = l >> 4, lr = l & 15;
-#pragma unroll
-    for (int I = 0; I < 4; ++I) {
-        const int t0 = 16 * I + 4 * g4;
+// Transposing LDS read (ds_read_b64_tr_b16): for the 16 lanes of each row group g, lane i receives
+// [M[r0][c0+i], M[r0+1][c0+i], M[r0+2][c0+i], M[r0+3][c0+i]] of a row-major bf16 matrix M
+// (row stride ld elements), where r0 and c0 may differ between row groups.  Lanes 4r .. 4r+3 of
+// the group hand the hardware row r0+r, columns c0 .. c0+15 in four 8-byte pieces.  With PERM
+// the columns are stored in perm() order (4-element runs stay contiguous).
+template <bool PERM>
+__device__ __forceinline__ uint2 ld_tr4(const uint16_t* m, int ld, int r0, int c0) {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+    const int l = threadIdx.x & 63, r = (l >> 2) & 3, q = l & 3;
+    const int c = c0 + 4 * q;
+    const uint16_t* p = m + (r0 + r) * ld + (PERM ? perm<bf16_t>(c) : c);
+    const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
+    return __builtin_bit_cast(uint2, v);
+}
+
+// RHS block loaders for block_solve: rows 16I + 4*(l/16) + e (e = 0..3) of column l%16 of a
+// 16-column tile, scaled per row by sc[t].
+template <typename MT> struct RhsFromTransposed {   // the tile's transposed row (this lane's column)
+    const typename MM<MT>::S* bt;
+    const float* sc;
+    __device__ __forceinline__ f32x4_t operator()(int I) const {
+        const int t0 = 16 * I + 4 * ((threadIdx.x & 63) >> 4);
+        const f32x4_t f = *reinterpret_cast<const f32x4_t*>(sc + t0);
         f32x4_t R;
         if constexpr (sizeof(typename MM<MT>::S) == 2) {
-            const uint2 raw = *reinterpret_cast<const uint2*>(sBt + perm<MT>(t0));
-            R[0] = __uint_as_float(raw.x << 16) * sc[t0];
-            R[1] = __uint_as_float(raw.x & 0xFFFF0000u) * sc[t0 + 1];
-            R[2] = __uint_as_float(raw.y << 16) * sc[t0 + 2];
-            R[3] = __uint_as_float(raw.y & 0xFFFF0000u) * sc[t0 + 3];
+            const uint2 raw = *reinterpret_cast<const uint2*>(bt + perm<MT>(t0));
+            R[0] = __uint_as_float(raw.x << 16) * f[0];
+            R[1] = __uint_as_float(raw.x & 0xFFFF0000u) * f[1];
+            R[2] = __uint_as_float(raw.y << 16) * f[2];
+            R[3] = __uint_as_float(raw.y & 0xFFFF0000u) * f[3];
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) R[e] = bt[t0 + e] * f[e];
+        }
+        return R;
+    }
+};
+struct RhsFromRows {                               // row-major bf16 rows (perm() columns), columns c0 .. c0+15
+    const uint16_t* m;
+    int ld, c0;
+    const float* sc;
+    __device__ __forceinline__ f32x4_t operator()(int I) const {
+        const int t0 = 16 * I + 4 * ((threadIdx.x & 63) >> 4);
+        const f32x4_t f = *reinterpret_cast<const f32x4_t*>(sc + t0);
+        const uint2 raw = ld_tr4<true>(m, ld, t0, c0);
+        return f32x4_t{__uint_as_float(raw.x << 16) * f[0], __uint_as_float(raw.x & 0xFFFF0000u) * f[1],
+                       __uint_as_float(raw.y << 16) * f[2], __uint_as_float(raw.y & 0xFFFF0000u) * f[3]};
+    }
+};
+
+// X = (I + L)^-1 B for NR 16-column tiles of B (64 rows each), by blocked forward substitution:
+// X_I = D_I (B_I - sum_{J<I} L_IJ X_J), D_I = (I + L_II)^-1.  L's off-diagonal blocks are read
+// negated from sLo (row-major, stride ldo), the D_I from sD (block I at sD + 16*I*ldd); rhs[n](I)
+// returns block I of tile n.  X stays in registers in C layout; with v_mfma_f32_16x16x16_bf16 the
+// C layout of one block is the B operand layout of the next product, so each wave solves its own
+// columns without synchronising with the others.  The NR tiles share every read of L and D, and
+// their dependency chains interleave.
+template <typename MT, int NR, typename Rhs>
+__device__ __forceinline__ void block_solve(f32x4_t (*X)[4], const typename MM<MT>::S* sLo, int ldo,
+                                            const typename MM<MT>::S* sD, int ldd, const Rhs* rhs) {
+    const int l = threadIdx.x & 63, g4 = l >> 4, lr = l & 15;
+    f32x4_t R[NR][4];
+#pragma unroll
+    for (int I = 0; I < 4; ++I)
+#pragma unroll
+        for (int n = 0; n < NR; ++n) R[n][I] = rhs[n](I);
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+        if constexpr (sizeof(typename MM<MT>::S) == 2) {
 #pragma unroll
             for (int J = 0; J < I; ++J) {
                 const s16x4_t av = *reinterpret_cast<const s16x4_t*>(sLo + (16 * I + lr) * ldo + 16 * J + 4 * g4);
-                const s16x4_t bv = __builtin_bit_cast(s16x4_t, uint2{pack_tile_lo(X[J]), pack_tile_hi(X[J])});
-                R = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, R, 0, 0, 0);
+#pragma unroll
+                for (int n = 0; n < NR; ++n) {
+                    const s16x4_t bv = __builtin_bit_cast(s16x4_t, uint2{pack_tile_lo(X[n][J]), pack_tile_hi(X[n][J])});
+                    R[n][I] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, R[n][I], 0, 0, 0);
+                }
             }
             const s16x4_t dv = *reinterpret_cast<const s16x4_t*>(sD + (16 * I + lr) * ldd + 4 * g4);
-            const s16x4_t rv = __builtin_bit_cast(s16x4_t, uint2{pack_tile_lo(R), pack_tile_hi(R)});
-            X[I] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(dv, rv, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-        } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) R[e] = sBt[t0 + e] * sc[t0 + e];
+            for (int n = 0; n < NR; ++n) {
+                const s16x4_t rv = __builtin_bit_cast(s16x4_t, uint2{pack_tile_lo(R[n][I]), pack_tile_hi(R[n][I])});
+                X[n][I] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(dv, rv, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            }
+        } else {
 #pragma unroll
             for (int J = 0; J < I; ++J) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    R = __builtin_amdgcn_mfma_f32_16x16x4f32(sLo[(16 * I + lr) * ldo + 16 * J + 4 * g4 + e], X[J][e],
-                                                             R, 0, 0, 0);
-            }
-            f32x4_t x = {0.f, 0.f, 0.f, 0.f};
+                for (int e = 0; e < 4; ++e) {
+                    const float av = sLo[(16 * I + lr) * ldo + 16 * J + 4 * g4 + e];
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                x = __builtin_amdgcn_mfma_f32_16x16x4f32(sD[(16 * I + lr) * ldd + 4 * g4 + e], R[e], x, 0, 0, 0);
-            X[I] = x;
+                    for (int n = 0; n < NR; ++n)
+                        R[n][I] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, X[n][J][e], R[n][I], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int n = 0; n < NR; ++n) X[n][I] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float dv = sD[(16 * I + lr) * ldd + 4 * g4 + e];
+#pragma unroll
+                for (int n = 0; n < NR; ++n)
+                    X[n][I] = __builtin_amdgcn_mfma_f32_16x16x4f32(dv, R[n][I][e], X[n][I], 0, 0, 0);
+            }
         }
     }
 }
@@ -459,6 +518,11 @@ struct Layout {
     static constexpr size_t LO_ = sizeof(S) * CH * LDO;    // [64][LDO]
     static constexpr size_t LD_ = sizeof(float) * 4 * 16 * LDN;  // diagonal L blocks, fp32
     static constexpr size_t D_ = sizeof(S) * CH * LDD;     // [4*16][LDD]
+    // bf16 scalar gate with one K tile per wave: V is kept row-major ([64][LDV], perm() columns)
+    // in the V^T area and read through transposing LDS reads, and K^T is not built
+    static constexpr int LDV = BV + MM<MT>::PAD;
+    static constexpr bool TRK = !PER_K && BF && K / 16 == BV / 16;
+    static_assert(!TRK || sizeof(S) * CH * LDV <= VT_, "row-major V fits the V^T area");
 
     // ---- scalar gate ----
     static constexpr size_t g_q = 0;              // Q rows
@@ -532,6 +596,7 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
     constexpr int LDK = Lay::LDK, LDT = Lay::LDT, LDO = Lay::LDO, LDD = Lay::LDD;
     static_assert(NW >= 4, "four waves invert the diagonal blocks");
     typedef OStage<BV, IO> OS;
+    constexpr bool TRK = Lay::TRK;
     static_assert(Lay::total <= 160 * 1024, "LDS budget");
     static_assert(OS::bytes <= Lay::LO_ + Lay::LD_ + Lay::D_, "output staging overlays -L and the inverses");
     __shared__ __align__(16) char smem[Lay::total];
@@ -687,14 +752,21 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
                 const int c8 = PK::col(tid, i), pr0 = 2 * PK::pair(tid, i);
                 st8_perm<MT, IO>(sK + pr0 * LDK, c8, kr[2 * i]);
                 st8_perm<MT, IO>(sK + (pr0 + 1) * LDK, c8, kr[2 * i + 1]);
-                if constexpr (!PER_K) st_pair_t<MT, IO>(SP(Lay::g_kt), LDT, c8, pr0, kr[2 * i], kr[2 * i + 1]);
+                if constexpr (!PER_K && !TRK) st_pair_t<MT, IO>(SP(Lay::g_kt), LDT, c8, pr0, kr[2 * i], kr[2 * i + 1]);
             }
         }
         if constexpr (!PER_K) {
 #pragma unroll
             for (int i = 0; i < PV::NPASS; ++i) {
-                if (PV::valid(tid, i))
-                    st_pair_t<MT, IO>(SP(Lay::g_vt), LDT, PV::col(tid, i), 2 * PV::pair(tid, i), vr[2 * i], vr[2 * i + 1]);
+                if (PV::valid(tid, i)) {
+                    const int c8 = PV::col(tid, i), pr0 = 2 * PV::pair(tid, i);
+                    if constexpr (TRK) {
+                        st8_perm<MT, IO>(SP(Lay::g_vt) + pr0 * Lay::LDV, c8, vr[2 * i]);
+                        st8_perm<MT, IO>(SP(Lay::g_vt) + (pr0 + 1) * Lay::LDV, c8, vr[2 * i + 1]);
+                    } else {
+                        st_pair_t<MT, IO>(SP(Lay::g_vt), LDT, c8, pr0, vr[2 * i], vr[2 * i + 1]);
+                    }
+                }
             }
             if (tid < 64) {  // wave 0: inclusive prefix sum of the 64 gates (rows past the end are 0)
                 const int r = tid;
@@ -901,16 +973,45 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
             const S* sKb = SP(PER_K ? Lay::k_kgt : Lay::g_kt);
             const S* sVb = SP(PER_K ? Lay::k_vt : Lay::g_vt);
             const float* wsc = PER_K ? sb : FP(Lay::g_be);
-            for (int jt = w; jt < KT; jt += NW) {
-                f32x4_t X[4];
-                block_solve<MT>(X, sLo, LDO, sD, LDD, sKb + (16 * jt + lr) * LDT, wsc);
+            auto store_w = [&](int jt, const f32x4_t* X) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         sW[(16 * i + 4 * g4 + e) * LDK + perm<MT>(16 * jt + lr)] = M::cvt(-X[i][e]);
+            };
+            if constexpr (TRK) {
+                // one W tile and the U tile per wave, solved together, both read straight from the
+                // row-major K and V copies through transposing LDS reads
+                static_assert(KT == NW, "one W tile per wave");
+                const uint16_t* sVr = SP(Lay::g_vt);
+                f32x4_t X[2][4];
+                const RhsFromRows rhs[2] = {{sK, LDK, 16 * w, wsc}, {sVr, Lay::LDV, 16 * w, sb}};
+                block_solve<MT, 2>(X, sLo, LDO, sD, LDD, rhs);
+                store_w(w, X[0]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) nu[i] = X[1][i];
+            } else if constexpr (KT == NW) {
+                // one W tile and the U tile per wave, solved together
+                f32x4_t X[2][4];
+                const RhsFromTransposed<MT> rhs[2] = {{sKb + (16 * w + lr) * LDT, wsc}, {sVb + (16 * w + lr) * LDT, sb}};
+                block_solve<MT, 2>(X, sLo, LDO, sD, LDD, rhs);
+                store_w(w, X[0]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) nu[i] = X[1][i];
+            } else {
+                for (int jt = w; jt < KT; jt += NW) {
+                    f32x4_t X[1][4];
+                    const RhsFromTransposed<MT> rhs[1] = {{sKb + (16 * jt + lr) * LDT, wsc}};
+                    block_solve<MT, 1>(X, sLo, LDO, sD, LDD, rhs);
+                    store_w(jt, X[0]);
+                }
+                f32x4_t X[1][4];
+                const RhsFromTransposed<MT> rhs[1] = {{sVb + (16 * w + lr) * LDT, sb}};
+                block_solve<MT, 1>(X, sLo, LDO, sD, LDD, rhs);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) nu[i] = X[0][i];
             }
-            block_solve<MT>(nu, sLo, LDO, sD, LDD, sVb + (16 * w + lr) * LDT, sb);
         }
         __syncthreads();
 
@@ -953,7 +1054,25 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) nu[i][e] *= exp_f32(gl - sg[16 * i + 4 * g4 + e]);
-            gemm_regs<MT, CH, KT>(hs, SP(Lay::g_kt), LDT, nu);
+            if constexpr (TRK) {
+                // hs[kt] += K[:, 16 kt ..]^T v_new~ with the A operand read from the row-major K rows:
+                // MFMA position 8 (l/16) + e is chunk row 32m + 4 (l/16) + e or 32m + 16 + 4 (l/16) + e - 4
+#pragma unroll
+                for (int m = 0; m < CH / 32; ++m) {
+                    const uint4 bw = {pack_tile_lo(nu[2 * m]), pack_tile_hi(nu[2 * m]), pack_tile_lo(nu[2 * m + 1]),
+                                      pack_tile_hi(nu[2 * m + 1])};
+                    const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, bw);
+#pragma unroll
+                    for (int kt = 0; kt < KT; ++kt) {
+                        const uint2 lo = ld_tr4<true>(sK, LDK, 32 * m + 4 * g4, 16 * kt);
+                        const uint2 hi = ld_tr4<true>(sK, LDK, 32 * m + 16 + 4 * g4, 16 * kt);
+                        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, uint4{lo.x, lo.y, hi.x, hi.y});
+                        hs[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, hs[kt], 0, 0, 0);
+                    }
+                }
+            } else {
+                gemm_regs<MT, CH, KT>(hs, SP(Lay::g_kt), LDT, nu);
+            }
         } else {
             const float* sgl = FP(Lay::k_gl);
 #pragma unroll
