@@ -85,6 +85,7 @@ gdr_status gdr_recurrent_fwd(const gdr_problem* p, const void* q, const void* k,
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.o = o;
     a.cu_seqlens = cu_seqlens;
     a.one_token_per_seq = 0;
+    a.prefetch = 1;
     a.T = p->total_tokens;
     a.src = initial_state;
     a.dst = final_state;
@@ -122,6 +123,7 @@ gdr_status gdr_decode_paged(const gdr_problem* p, int32_t max_q_len, const void*
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.o = o;
     a.cu_seqlens = cu_seqlens;
     a.one_token_per_seq = cu_seqlens ? 0 : 1;
+    a.prefetch = max_q_len > 1;
     a.T = p->total_tokens;
     a.src = pool;
     a.dst = commit ? pool : nullptr;

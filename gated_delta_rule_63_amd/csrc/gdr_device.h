@@ -109,6 +109,56 @@ template <int N> struct Vec<bf16_t, N> {
     }
 };
 
+// ---- raw (unconverted) vectors, so loads can be issued well before their use ----
+template <typename T, int N> struct RawVec;
+template <int N> struct RawVec<float, N> {
+    static_assert(N % 4 == 0, "fp32 raw vectors are whole float4s");
+    f32x4_t v[N / 4];
+    __device__ __forceinline__ void load(const void* p, int64_t i) {
+        const f32x4_t* src = reinterpret_cast<const f32x4_t*>(static_cast<const float*>(p) + i);
+#pragma unroll
+        for (int j = 0; j < N / 4; ++j) v[j] = src[j];
+    }
+    __device__ __forceinline__ void get(float* out) const {
+#pragma unroll
+        for (int j = 0; j < N; ++j) out[j] = v[j / 4][j % 4];
+    }
+};
+template <int N> struct RawVec<bf16_t, N> {
+    static_assert(N == 4 || N == 8, "bf16 raw vectors are 8 or 16 bytes");
+    uint32_t w[N / 2];
+    __device__ __forceinline__ void load(const void* p, int64_t i) {
+        const uint16_t* base = static_cast<const uint16_t*>(p) + i;
+        if constexpr (N == 8) {
+            const uint4 x = *reinterpret_cast<const uint4*>(base);
+            w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
+        } else {
+            const uint2 x = *reinterpret_cast<const uint2*>(base);
+            w[0] = x.x; w[1] = x.y;
+        }
+    }
+    __device__ __forceinline__ void get(float* out) const {
+#pragma unroll
+        for (int j = 0; j < N / 2; ++j) {
+            out[2 * j] = __uint_as_float(w[j] << 16);
+            out[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+        }
+    }
+};
+
+// One element held as its bits.
+template <typename T> struct RawElem;
+template <> struct RawElem<float> {
+    float x;
+    __device__ __forceinline__ void load(const void* p, int64_t i) { x = static_cast<const float*>(p)[i]; }
+    __device__ __forceinline__ float get() const { return x; }
+};
+template <> struct RawElem<bf16_t> {
+    uint32_t x;
+    __device__ __forceinline__ void load(const void* p, int64_t i) { x = static_cast<const uint16_t*>(p)[i]; }
+    __device__ __forceinline__ float get() const { return __uint_as_float(x << 16); }
+};
+
 // ---- 16-lane reductions through DPP ----------------------------------------
 // Lanes are grouped in DPP rows of 16.  After the four steps every lane of the row
 // holds the same, bitwise-identical sum (each step adds the same two operands in

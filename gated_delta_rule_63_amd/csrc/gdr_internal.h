@@ -19,6 +19,7 @@ struct RecurrentArgs {
     void* o;
     const int32_t* cu_seqlens;   // NULL: see one_token_per_seq
     int32_t one_token_per_seq;   // with cu_seqlens NULL: 1 -> sequence n is token n; 0 -> one sequence of T tokens
+    int32_t prefetch;            // 1: load token t+1's inputs while token t computes (multi-token sequences)
     int64_t T;
     const void* src;             // state source [*, HV, V, K] (pool or initial state), NULL = zeros
     void* dst;                   // state destination (pool on commit, final state), NULL = none

@@ -16,13 +16,15 @@
 //    in-register FMAs followed by a 4-step DPP reduction over the 16 lanes;
 //  * the state is read once, kept in registers for all tokens of the sequence and
 //    written once (commit / final state), V-major, no transpose; the verify mode
-//    streams each post-update state out as it is produced.
+//    streams each post-update state out as it is produced;
+//  * with several tokens per sequence, token t+1's inputs are loaded while token t
+//    computes (PF); single-token decode skips that to keep the register count low.
 #include "gdr_device.h"
 #include "gdr_internal.h"
 
 namespace gdr {
 
-template <int K, typename IO, typename ST, typename DT, typename IB, bool PER_K, int SLOTS>
+template <int K, typename IO, typename ST, typename DT, typename IB, bool PER_K, int SLOTS, bool PF>
 __global__ __launch_bounds__(256) void recurrent_kernel(const RecurrentArgs a) {
     constexpr int EPL = K / 16;                                  // key channels per lane
     constexpr int VW = (16 / Elem<ST>::bytes) < EPL ? (16 / Elem<ST>::bytes) : EPL;
@@ -72,29 +74,62 @@ __global__ __launch_bounds__(256) void recurrent_kernel(const RecurrentArgs a) {
 
     const int64_t ib_row = a.ibuf ? (int64_t)a.ibuf_idx[n] * a.cache_steps : 0;
 
-    for (int64_t t = bos; t < eos; ++t) {
-        float kk[EPL], qq[EPL], al[EPL];
+    // one token's inputs, raw; the next token's are loaded while the current one computes
+    struct TokIn {
+        RawVec<IO, VW> k[UNITS], q[UNITS];
+        RawVec<float, VW> gk[PER_K ? UNITS : 1];
+        float g;
+        RawElem<IO> b;
+        RawVec<IO, SLOTS> v;
+    };
+    auto load_tok = [&](int64_t t, TokIn& x) {
         const int64_t qk_off = (t * a.HK + hk) * K;
+        const int64_t th = t * a.HV + h;
 #pragma unroll
         for (int u = 0; u < UNITS; ++u) {
-            Vec<IO, VW>::load(a.k, qk_off + cols[u], &kk[u * VW]);
-            Vec<IO, VW>::load(a.q, qk_off + cols[u], &qq[u * VW]);
+            x.k[u].load(a.k, qk_off + cols[u]);
+            x.q[u].load(a.q, qk_off + cols[u]);
         }
-        const int64_t th = t * a.HV + h;
         if constexpr (PER_K) {
 #pragma unroll
-            for (int u = 0; u < UNITS; ++u) Vec<float, VW>::load(a.g, th * K + cols[u], &al[u * VW]);
+            for (int u = 0; u < UNITS; ++u) x.gk[u].load(a.g, th * K + cols[u]);
+        } else {
+            x.g = a.g[th];
+        }
+        x.b.load(a.beta, th);
+        x.v.load(a.v, th * a.V + row0);
+    };
+    TokIn nxt;
+    if (PF && bos < eos) load_tok(bos, nxt);
+
+    for (int64_t t = bos; t < eos; ++t) {
+        TokIn cur;
+        if constexpr (PF) {
+            cur = nxt;
+            if (t + 1 < eos) load_tok(t + 1, nxt);
+        } else {
+            load_tok(t, cur);
+        }
+        const int64_t th = t * a.HV + h;
+        float kk[EPL], qq[EPL], al[EPL];
+#pragma unroll
+        for (int u = 0; u < UNITS; ++u) {
+            cur.k[u].get(&kk[u * VW]);
+            cur.q[u].get(&qq[u * VW]);
+        }
+        if constexpr (PER_K) {
+#pragma unroll
+            for (int u = 0; u < UNITS; ++u) cur.gk[u].get(&al[u * VW]);
 #pragma unroll
             for (int e = 0; e < EPL; ++e) al[e] = exp_f32(al[e]);
         } else {
-            const float alpha = exp_f32(a.g[th]);
+            const float alpha = exp_f32(cur.g);
 #pragma unroll
             for (int e = 0; e < EPL; ++e) al[e] = alpha;
         }
-        const float bt = Elem<IO>::load(a.beta, th);
+        const float bt = cur.b.get();
         float vv[SLOTS];
-#pragma unroll
-        for (int s = 0; s < SLOTS; ++s) vv[s] = Elem<IO>::load(a.v, th * a.V + row0 + s);
+        cur.v.get(vv);
 
         float ka[EPL];
 #pragma unroll
@@ -148,7 +183,10 @@ constexpr int kSlots = 4;  // BV = 64 rows per workgroup
 template <int K, typename IO, typename ST, typename DT, typename IB, bool PER_K>
 hipError_t launch_t(const RecurrentArgs& a, hipStream_t stream) {
     dim3 grid(a.V / (16 * kSlots), a.HV, a.N);
-    hipLaunchKernelGGL((recurrent_kernel<K, IO, ST, DT, IB, PER_K, kSlots>), grid, dim3(256), 0, stream, a);
+    if (a.prefetch)
+        hipLaunchKernelGGL((recurrent_kernel<K, IO, ST, DT, IB, PER_K, kSlots, true>), grid, dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((recurrent_kernel<K, IO, ST, DT, IB, PER_K, kSlots, false>), grid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
