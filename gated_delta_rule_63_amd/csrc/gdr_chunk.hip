@@ -154,7 +154,9 @@ __device__ __forceinline__ uint32_t pack_tile_hi(const f32x4_t& t) { return pack
 // the tiles provide it: for a 32-wide bf16 step m, MFMA position 8*(l/16) + e is index
 // 32m + 4*(l/16) + e (e < 4) or 32m + 16 + 4*(l/16) + e - 4 (e >= 4) -- one 16-byte read of a
 // perm()-ordered A row; for an fp32 step (t, e) position l/16 is index 16t + 4*(l/16) + e.
-template <typename MT, int NP, int NI>
+// With LOWER, A is lower triangular (A[r][j] = 0 for j > r): reduction steps entirely above the
+// diagonal of a 16-row tile are skipped.
+template <typename MT, int NP, int NI, bool LOWER = false>
 __device__ __forceinline__ void gemm_regs(f32x4_t* acc, const typename MM<MT>::S* sA, int lda, const f32x4_t* Bt) {
     const int l = threadIdx.x & 63, g4 = l >> 4, lr = l & 15;
     if constexpr (sizeof(typename MM<MT>::S) == 2) {
@@ -165,6 +167,7 @@ __device__ __forceinline__ void gemm_regs(f32x4_t* acc, const typename MM<MT>::S
             const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, bw);
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
+                if (LOWER && 32 * m > 16 * i + 15) continue;
                 const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(sA + (16 * i + lr) * lda + 32 * m + 8 * g4);
                 acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[i], 0, 0, 0);
             }
@@ -176,6 +179,7 @@ __device__ __forceinline__ void gemm_regs(f32x4_t* acc, const typename MM<MT>::S
             for (int e = 0; e < 4; ++e) {
 #pragma unroll
                 for (int i = 0; i < NI; ++i) {
+                    if (LOWER && t > i) continue;
                     const float av = sA[(16 * i + lr) * lda + 16 * t + 4 * g4 + e];
                     acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, Bt[t][e], acc[i], 0, 0, 0);
                 }
@@ -798,9 +802,42 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
         // ===== B/C: L = beta (K K^T) decay (strictly lower), P = (Q K^T) decay (lower incl. diag);
         //       waves 0-3 also invert the diagonal block of L they computed =====
         if constexpr (!PER_K) {
-            if (w < 4) {  // diagonal tile (w, w) of L, then D_w = (I + L_ww)^-1
-                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-                M::nt(acc, sK + 16 * w * LDK, LDK, sK + 16 * w * LDK, LDK, K);
+            // L(I, J) and P(I, J) share their right operand K_J: they are computed as pairs,
+            // with every operand read issued before the first product
+            auto pair = [&](int I, int J, f32x4_t& cl, f32x4_t& cp) {
+                cl = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                cp = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                M::template nt2<K>(cl, sK + 16 * I * LDK, sK + 16 * J * LDK, cp, sQ + 16 * I * LDK, sK + 16 * J * LDK, LDK);
+            };
+            auto store_p = [&](int I, int J, const f32x4_t& acc) {
+                const f32x4_t gr = *reinterpret_cast<const f32x4_t*>(sg + 16 * I + 4 * g4);
+                const float gj = sg[16 * J + lr];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * I + 4 * g4 + e, j = 16 * J + lr;
+                    const float x = exp_f32(gr[e] - gj) * acc[e];  // inf above the diagonal is discarded
+                    sP[r * LDT + perm<MT>(j)] = M::cvt((r >= j) ? x : 0.0f);
+                }
+            };
+            auto store_l = [&](int I, int J, const f32x4_t& acc) {  // off-diagonal block, negated
+                const f32x4_t gr = *reinterpret_cast<const f32x4_t*>(sg + 16 * I + 4 * g4);
+                const f32x4_t br = *reinterpret_cast<const f32x4_t*>(sb + 16 * I + 4 * g4);
+                const float gj = sg[16 * J + lr];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    sLo[(16 * I + 4 * g4 + e) * LDO + 16 * J + lr] = M::cvt(-br[e] * exp_f32(gr[e] - gj) * acc[e]);
+            };
+            auto off_pair = [&](int q) {  // q-th of the pairs (1,0),(2,0),(2,1),(3,0),(3,1),(3,2)
+                int I, J;
+                strict_tile(q, I, J);
+                f32x4_t cl, cp;
+                pair(I, J, cl, cp);
+                store_l(I, J, cl);
+                store_p(I, J, cp);
+            };
+            if (w < 4) {  // diagonal pair (w, w), then D_w = (I + L_ww)^-1
+                f32x4_t cl, cp;
+                pair(w, w, cl, cp);
                 float* sN = sLd + w * 16 * LDN;
                 const f32x4_t gr = *reinterpret_cast<const f32x4_t*>(sg + 16 * w + 4 * g4);
                 const f32x4_t br = *reinterpret_cast<const f32x4_t*>(sb + 16 * w + 4 * g4);
@@ -808,69 +845,23 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int rr = 4 * g4 + e;
-                    const float x = br[e] * exp_f32(gr[e] - gj) * acc[e];
+                    const float x = br[e] * exp_f32(gr[e] - gj) * cl[e];
                     sN[rr * LDN + lr] = (rr > lr) ? x : 0.0f;
                 }
+                store_p(w, w, cp);
                 // the tile's LDS writes complete before this wave's lanes read other lanes' entries
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
                 invert_unit_lower_16<MT>(sN, sD + 16 * w * LDD, LDD);
             }
-            // the 6 strictly lower tiles of L and the 10 lower tiles of P (t = 0..15), two at a time
-            // so that both tiles' operand reads are in flight together
-            auto tile = [&](int t, int& I, int& J, const S*& pa, const S*& pb) {
-                const bool isL = t < 6;
-                if (isL) strict_tile(t, I, J);
-                else lower_tile(t - 6, I, J);
-                pa = (isL ? sK : sQ) + 16 * I * LDK;
-                pb = sK + 16 * J * LDK;
-            };
-            auto epilogue = [&](int t, int I, int J, const f32x4_t& acc) {
-                const f32x4_t gr = *reinterpret_cast<const f32x4_t*>(sg + 16 * I + 4 * g4);
-                const float gj = sg[16 * J + lr];
-                if (t < 6) {
-                    const f32x4_t br = *reinterpret_cast<const f32x4_t*>(sb + 16 * I + 4 * g4);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        sLo[(16 * I + 4 * g4 + e) * LDO + 16 * J + lr] = M::cvt(-br[e] * exp_f32(gr[e] - gj) * acc[e]);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = 16 * I + 4 * g4 + e, j = 16 * J + lr;
-                        const float x = exp_f32(gr[e] - gj) * acc[e];  // inf above the diagonal is discarded
-                        sP[r * LDT + perm<MT>(j)] = M::cvt((r >= j) ? x : 0.0f);
-                    }
-                }
-            };
-            auto tiles = [&](int first, int stride, auto count_c) {
-                constexpr int CNT = decltype(count_c)::value;
-#pragma unroll
-                for (int k = 0; k + 1 < CNT; k += 2) {
-                    const int t0 = first + stride * k, t1 = t0 + stride;
-                    int I0, J0, I1, J1;
-                    const S *a0, *b0, *a1, *b1;
-                    tile(t0, I0, J0, a0, b0);
-                    tile(t1, I1, J1, a1, b1);
-                    f32x4_t c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
-                    M::template nt2<K>(c0, a0, b0, c1, a1, b1, LDK);
-                    epilogue(t0, I0, J0, c0);
-                    epilogue(t1, I1, J1, c1);
-                }
-                if constexpr (CNT % 2 == 1) {
-                    const int t0 = first + stride * (CNT - 1);
-                    int I0, J0;
-                    const S *a0, *b0;
-                    tile(t0, I0, J0, a0, b0);
-                    f32x4_t c0 = {0.f, 0.f, 0.f, 0.f};
-                    M::nt(c0, a0, LDK, b0, LDK, K);
-                    epilogue(t0, I0, J0, c0);
-                }
-            };
             if constexpr (NW > 4) {
-                // waves 4-7: tiles 0..11; waves 0-3 (after their inversion): tiles 12..15
-                if (w >= 4) tiles(w - 4, 4, std::integral_constant<int, 3>{});
-                else tiles(12 + w, 4, std::integral_constant<int, 1>{});
+                // waves 4-7: the six off-diagonal pairs (two each for waves 4 and 5)
+                if (w >= 4) {
+                    off_pair(w - 4);
+                    if (w < 6) off_pair(w - 4 + 4);
+                }
             } else {
-                tiles(w, 4, std::integral_constant<int, 4>{});
+                off_pair(w);
+                if (w < 2) off_pair(w + 4);
             }
             if (ci + 1 < nc) load_q(ci + 1);
         } else {
@@ -1030,7 +1021,7 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
 #pragma unroll
                 for (int e = 0; e < 4; ++e) oa[i][e] *= exp_f32(sg[16 * i + 4 * g4 + e]);
         }
-        gemm_regs<MT, CH, 4>(oa, sP, LDT, nu);
+        gemm_regs<MT, CH, 4, true>(oa, sP, LDT, nu);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
 #pragma unroll
