@@ -541,7 +541,9 @@ struct Layout {
     static constexpr size_t g_g = g_p + ROWT;     // gamma [64]
     static constexpr size_t g_b = g_g + sizeof(float) * CH;    // beta [64]
     static constexpr size_t g_be = g_b + sizeof(float) * CH;   // beta e^gamma [64]
-    static constexpr size_t g_total = g_be + sizeof(float) * CH;
+    static constexpr size_t g_eg = g_be + sizeof(float) * CH;  // e^gamma [64]
+    static constexpr size_t g_ed = g_eg + sizeof(float) * CH;  // e^(gamma_last - gamma) [64]
+    static constexpr size_t g_total = g_ed + sizeof(float) * CH;
 
     // ---- per-K gate: fixed part, then X (phases A-B, then C-E) and Y (B-D), W (D-E) ----
     static constexpr size_t k_g = 0;                                  // gamma [64][K]
@@ -775,9 +777,13 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
             if (tid < 64) {  // wave 0: inclusive prefix sum of the 64 gates (rows past the end are 0)
                 const int r = tid;
                 const float x = wave_inclusive_sum(gr[0]);
+                const float xl = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), CH - 1));
+                const float ex = exp_f32(x);
                 sg[r] = x;
                 sb[r] = br;
-                FP(Lay::g_be)[r] = br * exp_f32(x);
+                FP(Lay::g_be)[r] = br * ex;
+                FP(Lay::g_eg)[r] = ex;                   // row factors of E, both <= 1
+                FP(Lay::g_ed)[r] = exp_f32(xl - x);
             }
         } else {
             // thread (c, qd): prefix over its RPQ rows of channel c, then group offsets
@@ -1017,9 +1023,11 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
         gemm_regs<MT, K, 4>(oa, SP(PER_K ? Lay::k_qt : Lay::g_q), LDK, hs);
         if constexpr (!PER_K) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 4; ++i) {
+                const f32x4_t f = *reinterpret_cast<const f32x4_t*>(FP(Lay::g_eg) + 16 * i + 4 * g4);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) oa[i][e] *= exp_f32(sg[16 * i + 4 * g4 + e]);
+                for (int e = 0; e < 4; ++e) oa[i][e] *= f[e];
+            }
         }
         gemm_regs<MT, CH, 4, true>(oa, sP, LDT, nu);
 #pragma unroll
@@ -1035,16 +1043,17 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
         }
         // S <- e^{gamma_last} S + sum_r v_new_r (k_r e^{gamma_last - gamma_r})^T
         if constexpr (!PER_K) {
-            const float gl = sg[CH - 1];
-            const float dec = exp_f32(gl);
+            const float dec = FP(Lay::g_eg)[CH - 1];
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) hs[kt][e] *= dec;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 4; ++i) {
+                const f32x4_t f = *reinterpret_cast<const f32x4_t*>(FP(Lay::g_ed) + 16 * i + 4 * g4);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) nu[i][e] *= exp_f32(gl - sg[16 * i + 4 * g4 + e]);
+                for (int e = 0; e < 4; ++e) nu[i][e] *= f[e];
+            }
             if constexpr (TRK) {
                 // hs[kt] += K[:, 16 kt ..]^T v_new~ with the A operand read from the row-major K rows:
                 // MFMA position 8 (l/16) + e is chunk row 32m + 4 (l/16) + e or 32m + 16 + 4 (l/16) + e - 4
