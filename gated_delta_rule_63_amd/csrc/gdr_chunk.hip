@@ -543,7 +543,12 @@ struct Layout {
     static constexpr size_t g_be = g_b + sizeof(float) * CH;   // beta e^gamma [64]
     static constexpr size_t g_eg = g_be + sizeof(float) * CH;  // e^gamma [64]
     static constexpr size_t g_ed = g_eg + sizeof(float) * CH;  // e^(gamma_last - gamma) [64]
-    static constexpr size_t g_total = g_ed + sizeof(float) * CH;
+    // off-diagonal decay factors with reference point rho_J = gamma[16J + 15]:
+    // e^(gamma_r - gamma_j) = e^(gamma_r - rho_J) e^(rho_J - gamma_j), both <= 1 for r in a
+    // later 16-row block than j (block J)
+    static constexpr size_t g_fa = g_ed + sizeof(float) * CH;  // [3][64] e^(gamma_r - rho_J)
+    static constexpr size_t g_fb = g_fa + sizeof(float) * 3 * CH;  // [64] e^(rho_(j/16) - gamma_j)
+    static constexpr size_t g_total = g_fb + sizeof(float) * CH;
 
     // ---- per-K gate: fixed part, then X (phases A-B, then C-E) and Y (B-D), W (D-E) ----
     static constexpr size_t k_g = 0;                                  // gamma [64][K]
@@ -784,6 +789,14 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
                 FP(Lay::g_be)[r] = br * ex;
                 FP(Lay::g_eg)[r] = ex;                   // row factors of E, both <= 1
                 FP(Lay::g_ed)[r] = exp_f32(xl - x);
+                float rho[4];
+#pragma unroll
+                for (int J = 0; J < 4; ++J) rho[J] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16 * J + 15));
+#pragma unroll
+                for (int J = 0; J < 3; ++J) FP(Lay::g_fa)[J * CH + r] = exp_f32(fminf(x - rho[J], 0.0f));
+                const int jb = r >> 4;
+                const float rj = jb == 0 ? rho[0] : jb == 1 ? rho[1] : jb == 2 ? rho[2] : rho[3];
+                FP(Lay::g_fb)[r] = exp_f32(rj - x);
             }
         } else {
             // thread (c, qd): prefix over its RPQ rows of channel c, then group offsets
@@ -815,35 +828,46 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
                 cp = f32x4_t{0.f, 0.f, 0.f, 0.f};
                 M::template nt2<K>(cl, sK + 16 * I * LDK, sK + 16 * J * LDK, cp, sQ + 16 * I * LDK, sK + 16 * J * LDK, LDK);
             };
-            auto store_p = [&](int I, int J, const f32x4_t& acc) {
+            auto store_p_diag = [&](int I, const f32x4_t& acc) {  // element-wise decay, masked
                 const f32x4_t gr = *reinterpret_cast<const f32x4_t*>(sg + 16 * I + 4 * g4);
-                const float gj = sg[16 * J + lr];
+                const float gj = sg[16 * I + lr];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int r = 16 * I + 4 * g4 + e, j = 16 * J + lr;
+                    const int r = 16 * I + 4 * g4 + e, j = 16 * I + lr;
                     const float x = exp_f32(gr[e] - gj) * acc[e];  // inf above the diagonal is discarded
                     sP[r * LDT + perm<MT>(j)] = M::cvt((r >= j) ? x : 0.0f);
                 }
             };
-            auto store_l = [&](int I, int J, const f32x4_t& acc) {  // off-diagonal block, negated
-                const f32x4_t gr = *reinterpret_cast<const f32x4_t*>(sg + 16 * I + 4 * g4);
+            // off-diagonal blocks (I > J): decay from the per-row factor tables
+            auto store_off = [&](int I, int J, const f32x4_t& cl, const f32x4_t& cp) {
+                const f32x4_t fa = *reinterpret_cast<const f32x4_t*>(FP(Lay::g_fa) + J * CH + 16 * I + 4 * g4);
                 const f32x4_t br = *reinterpret_cast<const f32x4_t*>(sb + 16 * I + 4 * g4);
-                const float gj = sg[16 * J + lr];
+                const float fb = FP(Lay::g_fb)[16 * J + lr];
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    sLo[(16 * I + 4 * g4 + e) * LDO + 16 * J + lr] = M::cvt(-br[e] * exp_f32(gr[e] - gj) * acc[e]);
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * I + 4 * g4 + e, j = 16 * J + lr;
+                    const float d = fa[e] * fb;
+                    sLo[r * LDO + j] = M::cvt(-br[e] * d * cl[e]);
+                    sP[r * LDT + perm<MT>(j)] = M::cvt(d * cp[e]);
+                }
             };
             auto off_pair = [&](int q) {  // q-th of the pairs (1,0),(2,0),(2,1),(3,0),(3,1),(3,2)
                 int I, J;
                 strict_tile(q, I, J);
                 f32x4_t cl, cp;
                 pair(I, J, cl, cp);
-                store_l(I, J, cl);
-                store_p(I, J, cp);
+                store_off(I, J, cl, cp);
             };
-            if (w < 4) {  // diagonal pair (w, w), then D_w = (I + L_ww)^-1
+            // diagonal blocks: with eight waves, waves 0-3 compute L(w, w) and invert it while waves
+            // 6 and 7 (which have one off-diagonal pair each) compute the diagonal P tiles
+            if (w < 4) {  // diagonal L(w, w) (and P(w, w) with four waves), then D_w = (I + L_ww)^-1
                 f32x4_t cl, cp;
-                pair(w, w, cl, cp);
+                if constexpr (NW > 4) {
+                    cl = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                    M::nt(cl, sK + 16 * w * LDK, LDK, sK + 16 * w * LDK, LDK, K);
+                } else {
+                    pair(w, w, cl, cp);
+                }
                 float* sN = sLd + w * 16 * LDN;
                 const f32x4_t gr = *reinterpret_cast<const f32x4_t*>(sg + 16 * w + 4 * g4);
                 const f32x4_t br = *reinterpret_cast<const f32x4_t*>(sb + 16 * w + 4 * g4);
@@ -854,7 +878,7 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
                     const float x = br[e] * exp_f32(gr[e] - gj) * cl[e];
                     sN[rr * LDN + lr] = (rr > lr) ? x : 0.0f;
                 }
-                store_p(w, w, cp);
+                if constexpr (NW == 4) store_p_diag(w, cp);
                 // the tile's LDS writes complete before this wave's lanes read other lanes' entries
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
                 invert_unit_lower_16<MT>(sN, sD + 16 * w * LDD, LDD);
@@ -863,7 +887,16 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
                 // waves 4-7: the six off-diagonal pairs (two each for waves 4 and 5)
                 if (w >= 4) {
                     off_pair(w - 4);
-                    if (w < 6) off_pair(w - 4 + 4);
+                    if (w < 6) {
+                        off_pair(w - 4 + 4);
+                    } else {  // waves 6 and 7: diagonal P tiles (I, I), I = 2 (w - 6), 2 (w - 6) + 1
+                        const int I0 = 2 * (w - 6);
+                        f32x4_t c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+                        M::template nt2<K>(c0, sQ + 16 * I0 * LDK, sK + 16 * I0 * LDK, c1, sQ + 16 * (I0 + 1) * LDK,
+                                           sK + 16 * (I0 + 1) * LDK, LDK);
+                        store_p_diag(I0, c0);
+                        store_p_diag(I0 + 1, c1);
+                    }
                 }
             } else {
                 off_pair(w);
