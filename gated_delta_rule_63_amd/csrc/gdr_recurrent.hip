@@ -101,6 +101,10 @@ __global__ __launch_bounds__(256) void recurrent_kernel(const RecurrentArgs a) {
     };
     TokIn nxt;
     if (PF && bos < eos) load_tok(bos, nxt);
+    // Drain the state and first-token loads here, where they are needed anyway.  Otherwise the
+    // wait-count pass merges their pending state into the loop head and every token would wait
+    // for the previous token's stores before it touches its prefetched inputs.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt left at their maximum
 
     for (int64_t t = bos; t < eos; ++t) {
         TokIn cur;
@@ -131,17 +135,22 @@ __global__ __launch_bounds__(256) void recurrent_kernel(const RecurrentArgs a) {
         float vv[SLOTS];
         cur.v.get(vv);
 
-        float ka[EPL];
+        // (decayed S) . k: with the per-channel gate the decay multiplies k element-wise; a scalar
+        // gate multiplies the reduced dot product once (fewer registers and instructions)
+        float ka[PER_K ? EPL : 1];
+        if constexpr (PER_K) {
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) ka[e] = al[e] * kk[e];
+            for (int e = 0; e < EPL; ++e) ka[e] = al[e] * kk[e];
+        }
 
         float ov[SLOTS];
 #pragma unroll
         for (int s = 0; s < SLOTS; ++s) {
             float p = 0.0f;
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) p = fmaf(S[s][e], ka[e], p);   // (decayed S) . k
+            for (int e = 0; e < EPL; ++e) p = fmaf(S[s][e], PER_K ? ka[e] : kk[e], p);
             p = row16_sum(p);
+            if constexpr (!PER_K) p *= al[0];
             const float nu = bt * (vv[s] - p);
             float po = 0.0f;
 #pragma unroll
@@ -151,20 +160,21 @@ __global__ __launch_bounds__(256) void recurrent_kernel(const RecurrentArgs a) {
             }
             ov[s] = a.scale * row16_sum(po);                              // post-update read
         }
-        // lane j < SLOTS of each row group writes row (row0 + j)
+        // Lane j of each row group writes row (row0 + j % SLOTS): lanes past SLOTS repeat the same
+        // value to the same address.  No store in the token loop is conditional, so the vector
+        // memory counter stays exact and waiting for the next token's prefetched loads does not
+        // also wait for this token's stores.
         float mine = ov[0];
 #pragma unroll
-        for (int s = 1; s < SLOTS; ++s) mine = (j == s) ? ov[s] : mine;
-        if (j < SLOTS) Elem<IO>::store(a.o, th * a.V + row0 + j, mine);
+        for (int s = 1; s < SLOTS; ++s) mine = ((j % SLOTS) == s) ? ov[s] : mine;
+        Elem<IO>::store(a.o, th * a.V + row0 + (j % SLOTS), mine);
 
-        if constexpr (!std::is_same<IB, void>::value) {
-            if (a.ibuf) {
-                const int64_t ib = (((ib_row + (t - bos)) * a.HV + h) * a.V + row0) * K;
+        if constexpr (!std::is_same<IB, void>::value) {  // instantiated only with an intermediate buffer
+            const int64_t ib = (((ib_row + (t - bos)) * a.HV + h) * a.V + row0) * K;
 #pragma unroll
-                for (int s = 0; s < SLOTS; ++s)
+            for (int s = 0; s < SLOTS; ++s)
 #pragma unroll
-                    for (int u = 0; u < UNITS; ++u) Vec<IB, VW>::store(a.ibuf, ib + (int64_t)s * K + cols[u], &S[s][u * VW]);
-            }
+                for (int u = 0; u < UNITS; ++u) Vec<IB, VW>::store(a.ibuf, ib + (int64_t)s * K + cols[u], &S[s][u * VW]);
         }
     }
 
