@@ -279,3 +279,44 @@ def verify(seed: int = 3, B: int = 64, num_slots: int = 1024, pad: bool = False)
     return paged_problem(seed, B=B, q_len=12, HK=16, HV=32, K=128, V=128, num_slots=num_slots,
                          pool_dtype=BF16, pad_count=int(round(0.1 * B)) if pad else 0, commit=False,
                          inter_dtype=BF16, cache_steps=12, name="verify")
+
+
+@dataclasses.dataclass
+class RawGating:
+    """Raw inputs of the gating front (for the gated entry points), drawn only:
+
+    q, k     [T, HK, K] io dtype, NOT normalised (N(0,1) rows times a per-row length
+             in U[0.25, 4], so the normalisation changes them)
+    a, b     [T, HV] io dtype: the decay and beta inputs before softplus / sigmoid
+    A_log    [HV] fp32 (log of U[1, 16]);  dt_bias [HV] fp32 (U[-7, -2])
+    eps      added to the sum of squares under the square root of the normalisation
+    allow_neg_eigval  beta doubled
+    A fraction ``over_threshold`` of the a values is set to 25 so a + dt_bias exceeds the
+    softplus threshold 20 and the pass-through branch is exercised.
+    """
+    q: np.ndarray
+    k: np.ndarray
+    a: np.ndarray
+    b: np.ndarray
+    A_log: np.ndarray
+    dt_bias: np.ndarray
+    eps: float
+    qk_l2norm: bool
+    allow_neg_eigval: bool
+
+
+def raw_gating(seed: int, T: int, HK: int, HV: int, K: int, io_dtype: str = BF16,
+               allow_neg_eigval: bool = False, qk_l2norm: bool = True, eps: float = 1e-6,
+               over_threshold: float = 0.02) -> RawGating:
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((T, HK, K), dtype=np.float32) * rng.uniform(0.25, 4.0, (T, HK, 1)).astype(np.float32)
+    k = rng.standard_normal((T, HK, K), dtype=np.float32) * rng.uniform(0.25, 4.0, (T, HK, 1)).astype(np.float32)
+    a = rng.standard_normal((T, HV), dtype=np.float32)
+    if over_threshold > 0:
+        a[rng.uniform(0.0, 1.0, (T, HV)) < over_threshold] = np.float32(25.0)
+    b = (rng.standard_normal((T, HV), dtype=np.float32) * np.float32(1.5)).astype(np.float32)
+    A_log = np.log(rng.uniform(1.0, 16.0, HV)).astype(np.float32)
+    dt_bias = rng.uniform(-7.0, -2.0, HV).astype(np.float32)
+    return RawGating(q=cast_io(q, io_dtype), k=cast_io(k, io_dtype), a=cast_io(a, io_dtype),
+                     b=cast_io(b, io_dtype), A_log=A_log, dt_bias=dt_bias, eps=float(eps),
+                     qk_l2norm=bool(qk_l2norm), allow_neg_eigval=bool(allow_neg_eigval))

@@ -11,6 +11,8 @@ Contents
                       on top of ``recurrent`` (slot gather, -1 skip, commit,
                       per-token intermediate states).
 * ``chunk_form``      the chunk-64 WY/UT algebra in numpy fp64 (module of its own).
+* ``gating``          the gating front: decay from (a, A_log, dt_bias) through softplus,
+                      beta through the sigmoid, q/k l2 normalisation (numpy fp64).
 
 Every function takes float64 numpy arrays (widen bf16 inputs exactly before
 calling) and returns float64.  Pins: see ``tests/test_oracle_pins.py``
