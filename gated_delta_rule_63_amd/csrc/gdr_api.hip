@@ -53,6 +53,65 @@ bool token_inputs_ok(const gdr_problem* p, const void* q, const void* k, const v
 
 gdr_status status_of(hipError_t e) { return e == hipSuccess ? GDR_SUCCESS : GDR_ERROR_LAUNCH_FAILED; }
 
+// Gating-front metadata: scalar decay only, flags 0/1, eps finite and >= 0, pointers present.
+gdr_status check_gating(const gdr_problem* p, const gdr_gating* gt) {
+    if (!gt) return GDR_ERROR_INVALID_VALUE;
+    if (p->gate != GDR_GATE_SCALAR) return GDR_ERROR_NOT_SUPPORTED;
+    if (gt->qk_l2norm != 0 && gt->qk_l2norm != 1) return GDR_ERROR_INVALID_VALUE;
+    if (gt->allow_neg_eigval != 0 && gt->allow_neg_eigval != 1) return GDR_ERROR_INVALID_VALUE;
+    if (!(gt->l2norm_eps >= 0.0f) || gt->l2norm_eps > 3.0e38f) return GDR_ERROR_INVALID_VALUE;  // NaN fails too
+    if (p->total_tokens > 0 && !(gt->a && gt->b && gt->A_log && gt->dt_bias)) return GDR_ERROR_INVALID_VALUE;
+    return GDR_SUCCESS;
+}
+
+// Shared body of the paged entry points; either (g, beta) or gating is set, and the token
+// inputs have been checked by the caller.
+gdr_status decode_paged_impl(const gdr_problem* p, int32_t max_q_len, const void* q, const void* k, const void* v,
+                             const float* g, const void* beta, const gdr_gating* gating,
+                             const int32_t* cu_seqlens, void* pool, gdr_dtype pool_dtype, int32_t num_slots,
+                             const int32_t* state_indices, int32_t commit, void* inter_states,
+                             gdr_dtype inter_dtype, int32_t num_cache_slots, int32_t cache_steps,
+                             const int32_t* inter_state_indices, void* o, void* hip_stream) {
+    if (max_q_len < 1 || max_q_len > 12) return GDR_ERROR_INVALID_VALUE;
+    if (!pool || num_slots <= 0 || !state_indices) return GDR_ERROR_INVALID_VALUE;
+    if (!dtype_ok(pool_dtype)) return GDR_ERROR_INVALID_VALUE;
+    if (commit != 0 && commit != 1) return GDR_ERROR_INVALID_VALUE;
+    if (p->total_tokens > 0 && !o) return GDR_ERROR_INVALID_VALUE;
+    if (!cu_seqlens && p->total_tokens != p->num_seqs) return GDR_ERROR_INVALID_VALUE;
+    if (p->total_tokens > (int64_t)p->num_seqs * max_q_len) return GDR_ERROR_INVALID_VALUE;
+    if (inter_states) {
+        if (!inter_state_indices || num_cache_slots <= 0 || cache_steps < max_q_len) return GDR_ERROR_INVALID_VALUE;
+        if (!dtype_ok(inter_dtype)) return GDR_ERROR_INVALID_VALUE;
+    }
+    if (p->num_seqs == 0 || p->total_tokens == 0) return GDR_SUCCESS;
+    gdr_status st = check_device();
+    if (st != GDR_SUCCESS) return st;
+
+    RecurrentArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.o = o;
+    a.cu_seqlens = cu_seqlens;
+    a.one_token_per_seq = cu_seqlens ? 0 : 1;
+    a.prefetch = max_q_len > 1;
+    a.T = p->total_tokens;
+    a.src = pool;
+    a.dst = commit ? pool : nullptr;
+    a.slots = state_indices;
+    a.ibuf = inter_states;
+    a.ibuf_idx = inter_state_indices;
+    a.cache_steps = cache_steps;
+    a.N = p->num_seqs; a.HK = p->num_k_heads; a.HV = p->num_v_heads; a.V = p->head_dim_v;
+    a.scale = p->scale;
+    if (gating) {
+        a.ga = gating->a; a.gb = gating->b; a.A_log = gating->A_log; a.dt_bias = gating->dt_bias;
+        a.l2_eps = gating->l2norm_eps;
+        a.qk_l2norm = gating->qk_l2norm;
+        a.beta_mul = gating->allow_neg_eigval ? 2.0f : 1.0f;
+    }
+    return status_of(gdr::launch_recurrent(a, p->head_dim_k, p->io_dtype, pool_dtype,
+                                           inter_states ? (int)inter_dtype : -1, p->gate == GDR_GATE_PER_K,
+                                           gating != nullptr, static_cast<hipStream_t>(hip_stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -94,7 +153,7 @@ gdr_status gdr_recurrent_fwd(const gdr_problem* p, const void* q, const void* k,
     a.N = p->num_seqs; a.HK = p->num_k_heads; a.HV = p->num_v_heads; a.V = p->head_dim_v;
     a.scale = p->scale;
     return status_of(gdr::launch_recurrent(a, p->head_dim_k, p->io_dtype, GDR_F32, -1,
-                                           p->gate == GDR_GATE_PER_K, static_cast<hipStream_t>(hip_stream)));
+                                           p->gate == GDR_GATE_PER_K, false, static_cast<hipStream_t>(hip_stream)));
 }
 
 gdr_status gdr_decode_paged(const gdr_problem* p, int32_t max_q_len, const void* q, const void* k, const void* v,
@@ -104,38 +163,47 @@ gdr_status gdr_decode_paged(const gdr_problem* p, int32_t max_q_len, const void*
                             int32_t cache_steps, const int32_t* inter_state_indices, void* o, void* hip_stream) {
     gdr_status st = check_problem(p);
     if (st != GDR_SUCCESS) return st;
-    if (max_q_len < 1 || max_q_len > 12) return GDR_ERROR_INVALID_VALUE;
-    if (!pool || num_slots <= 0 || !state_indices) return GDR_ERROR_INVALID_VALUE;
-    if (!dtype_ok(pool_dtype)) return GDR_ERROR_INVALID_VALUE;
-    if (commit != 0 && commit != 1) return GDR_ERROR_INVALID_VALUE;
     if (!token_inputs_ok(p, q, k, v, g, beta)) return GDR_ERROR_INVALID_VALUE;
-    if (p->total_tokens > 0 && !o) return GDR_ERROR_INVALID_VALUE;
-    if (!cu_seqlens && p->total_tokens != p->num_seqs) return GDR_ERROR_INVALID_VALUE;
-    if (p->total_tokens > (int64_t)p->num_seqs * max_q_len) return GDR_ERROR_INVALID_VALUE;
-    if (inter_states) {
-        if (!inter_state_indices || num_cache_slots <= 0 || cache_steps < max_q_len) return GDR_ERROR_INVALID_VALUE;
-        if (!dtype_ok(inter_dtype)) return GDR_ERROR_INVALID_VALUE;
-    }
-    if (p->num_seqs == 0 || p->total_tokens == 0) return GDR_SUCCESS;
-    if ((st = check_device()) != GDR_SUCCESS) return st;
+    return decode_paged_impl(p, max_q_len, q, k, v, g, beta, nullptr, cu_seqlens, pool, pool_dtype, num_slots,
+                             state_indices, commit, inter_states, inter_dtype, num_cache_slots, cache_steps,
+                             inter_state_indices, o, hip_stream);
+}
 
-    RecurrentArgs a{};
-    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.o = o;
-    a.cu_seqlens = cu_seqlens;
-    a.one_token_per_seq = cu_seqlens ? 0 : 1;
-    a.prefetch = max_q_len > 1;
-    a.T = p->total_tokens;
-    a.src = pool;
-    a.dst = commit ? pool : nullptr;
-    a.slots = state_indices;
-    a.ibuf = inter_states;
-    a.ibuf_idx = inter_state_indices;
-    a.cache_steps = cache_steps;
-    a.N = p->num_seqs; a.HK = p->num_k_heads; a.HV = p->num_v_heads; a.V = p->head_dim_v;
-    a.scale = p->scale;
-    return status_of(gdr::launch_recurrent(a, p->head_dim_k, p->io_dtype, pool_dtype,
-                                           inter_states ? (int)inter_dtype : -1, p->gate == GDR_GATE_PER_K,
-                                           static_cast<hipStream_t>(hip_stream)));
+gdr_status gdr_decode_paged_gated(const gdr_problem* p, int32_t max_q_len, const void* q, const void* k,
+                                  const void* v, const gdr_gating* gating, const int32_t* cu_seqlens, void* pool,
+                                  gdr_dtype pool_dtype, int32_t num_slots, const int32_t* state_indices,
+                                  int32_t commit, void* inter_states, gdr_dtype inter_dtype,
+                                  int32_t num_cache_slots, int32_t cache_steps,
+                                  const int32_t* inter_state_indices, void* o, void* hip_stream) {
+    gdr_status st = check_problem(p);
+    if (st != GDR_SUCCESS) return st;
+    if ((st = check_gating(p, gating)) != GDR_SUCCESS) return st;
+    if (p->total_tokens > 0 && !(q && k && v)) return GDR_ERROR_INVALID_VALUE;
+    return decode_paged_impl(p, max_q_len, q, k, v, nullptr, nullptr, gating, cu_seqlens, pool, pool_dtype,
+                             num_slots, state_indices, commit, inter_states, inter_dtype, num_cache_slots,
+                             cache_steps, inter_state_indices, o, hip_stream);
+}
+
+gdr_status gdr_gating_prepass(const gdr_problem* p, const void* q, const void* k, const gdr_gating* gating,
+                              void* q_out, void* k_out, float* g_out, void* beta_out, void* hip_stream) {
+    gdr_status st = check_problem(p);
+    if (st != GDR_SUCCESS) return st;
+    if ((st = check_gating(p, gating)) != GDR_SUCCESS) return st;
+    if (p->total_tokens > 0) {
+        if (!g_out || !beta_out) return GDR_ERROR_INVALID_VALUE;
+        if (gating->qk_l2norm && !(q && k && q_out && k_out)) return GDR_ERROR_INVALID_VALUE;
+    }
+    if (p->total_tokens == 0) return GDR_SUCCESS;
+    if ((st = check_device()) != GDR_SUCCESS) return st;
+    gdr::GatingArgs a{};
+    a.q = q; a.k = k; a.q_out = q_out; a.k_out = k_out;
+    a.a = gating->a; a.b = gating->b; a.A_log = gating->A_log; a.dt_bias = gating->dt_bias;
+    a.g_out = g_out; a.beta_out = beta_out;
+    a.T = p->total_tokens; a.HK = p->num_k_heads; a.HV = p->num_v_heads;
+    a.l2_eps = gating->l2norm_eps;
+    a.qk_l2norm = gating->qk_l2norm;
+    a.beta_mul = gating->allow_neg_eigval ? 2.0f : 1.0f;
+    return status_of(gdr::launch_gating(a, p->head_dim_k, p->io_dtype, static_cast<hipStream_t>(hip_stream)));
 }
 
 size_t gdr_chunk_workspace_size(const gdr_problem* p, int32_t chunk_size) {

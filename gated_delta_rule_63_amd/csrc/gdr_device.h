@@ -199,4 +199,15 @@ __device__ __forceinline__ float exp_f32(float x) {
     return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
 }
 
+// ---- gating front (FlashQLA PR #1: host-gating and in-kernel gated verify commits) ----
+// softplus with beta 1 and threshold 20: inputs above 20 pass through unchanged.
+__device__ __forceinline__ float softplus_f32(float x) { return x > 20.0f ? x : log1pf(exp_f32(x)); }
+
+__device__ __forceinline__ float sigmoid_f32(float x) { return 1.0f / (1.0f + exp_f32(-x)); }
+
+// decay g = -exp(A_log) softplus(a + dt_bias), with neg_exp_a_log = -exp(A_log) of the head
+__device__ __forceinline__ float gate_decay(float a, float neg_exp_a_log, float dt_bias) {
+    return neg_exp_a_log * softplus_f32(a + dt_bias);
+}
+
 }  // namespace gdr

@@ -29,11 +29,41 @@ struct RecurrentArgs {
     int32_t cache_steps;
     int32_t N, HK, HV, V;
     float scale;
+    // gating front, read only by the gated instantiation: g and beta are formed per token from
+    // the raw inputs a, b and the per-head A_log, dt_bias; q and k are l2-normalised when asked
+    const void* ga;              // a [T, HV] io dtype
+    const void* gb;              // b [T, HV] io dtype
+    const float* A_log;          // [HV]
+    const float* dt_bias;        // [HV]
+    float l2_eps;
+    int32_t qk_l2norm;
+    float beta_mul;              // 1, or 2 when negative eigenvalues are allowed
 };
 
-// dtype codes: 0 = fp32, 1 = bf16; ib_dtype -1 = no intermediate buffer
+// dtype codes: 0 = fp32, 1 = bf16; ib_dtype -1 = no intermediate buffer.  gated needs !per_k.
 hipError_t launch_recurrent(const RecurrentArgs& a, int K, int io_dtype, int st_dtype, int ib_dtype,
-                            bool per_k, hipStream_t stream);
+                            bool per_k, bool gated, hipStream_t stream);
+
+// Gating front as a pass of its own: normalised q, k and activated g, beta for every token.
+struct GatingArgs {
+    const void* q;
+    const void* k;
+    void* q_out;                 // may equal q (each row is read whole before it is written)
+    void* k_out;
+    const void* a;
+    const void* b;
+    const float* A_log;
+    const float* dt_bias;
+    float* g_out;                // [T, HV] fp32
+    void* beta_out;              // [T, HV] io dtype
+    int64_t T;
+    int32_t HK, HV;
+    float l2_eps;
+    int32_t qk_l2norm;
+    float beta_mul;
+};
+
+hipError_t launch_gating(const GatingArgs& a, int K, int io_dtype, hipStream_t stream);
 
 // Chunked path (64-token chunks).
 struct ChunkArgs {

@@ -18,14 +18,20 @@
 //    written once (commit / final state), V-major, no transpose; the verify mode
 //    streams each post-update state out as it is produced;
 //  * with several tokens per sequence, token t+1's inputs are loaded while token t
-//    computes (PF); single-token decode skips that to keep the register count low.
+//    computes (PF); single-token decode skips that to keep the register count low;
+//  * GATED instantiations take the raw gating inputs instead of g and beta (FlashQLA
+//    PR #1, in-kernel gated verify commit): per token g = -exp(A_log) softplus(a + dt_bias),
+//    beta = sigmoid(b) (doubled when negative eigenvalues are allowed), and q, k are
+//    l2-normalised with one more 16-lane reduction each.  Every row group repeats this
+//    small per-token work; it hides under the state traffic.
 #include "gdr_device.h"
 #include "gdr_internal.h"
 
 namespace gdr {
 
-template <int K, typename IO, typename ST, typename DT, typename IB, bool PER_K, int SLOTS, bool PF>
+template <int K, typename IO, typename ST, typename DT, typename IB, bool PER_K, int SLOTS, bool PF, bool GATED>
 __global__ __launch_bounds__(256) void recurrent_kernel(const RecurrentArgs a) {
+    static_assert(!(GATED && PER_K), "the gating front defines a scalar decay only");
     constexpr int EPL = K / 16;                                  // key channels per lane
     constexpr int VW = (16 / Elem<ST>::bytes) < EPL ? (16 / Elem<ST>::bytes) : EPL;
     constexpr int UNITS = EPL / VW;                              // vectors per lane per row
@@ -73,13 +79,16 @@ __global__ __launch_bounds__(256) void recurrent_kernel(const RecurrentArgs a) {
     }
 
     const int64_t ib_row = a.ibuf ? (int64_t)a.ibuf_idx[n] * a.cache_steps : 0;
+    const float neg_exp_a_log = GATED ? -exp_f32(a.A_log[h]) : 0.0f;
+    const float dt_bias = GATED ? a.dt_bias[h] : 0.0f;
 
     // one token's inputs, raw; the next token's are loaded while the current one computes
     struct TokIn {
         RawVec<IO, VW> k[UNITS], q[UNITS];
         RawVec<float, VW> gk[PER_K ? UNITS : 1];
         float g;
-        RawElem<IO> b;
+        RawElem<IO> ga;                                          // GATED: raw decay input a
+        RawElem<IO> b;                                           // beta, or GATED: raw input b
         RawVec<IO, SLOTS> v;
     };
     auto load_tok = [&](int64_t t, TokIn& x) {
@@ -93,10 +102,12 @@ __global__ __launch_bounds__(256) void recurrent_kernel(const RecurrentArgs a) {
         if constexpr (PER_K) {
 #pragma unroll
             for (int u = 0; u < UNITS; ++u) x.gk[u].load(a.g, th * K + cols[u]);
+        } else if constexpr (GATED) {
+            x.ga.load(a.ga, th);
         } else {
             x.g = a.g[th];
         }
-        x.b.load(a.beta, th);
+        x.b.load(GATED ? a.gb : a.beta, th);
         x.v.load(a.v, th * a.V + row0);
     };
     TokIn nxt;
@@ -127,11 +138,30 @@ __global__ __launch_bounds__(256) void recurrent_kernel(const RecurrentArgs a) {
 #pragma unroll
             for (int e = 0; e < EPL; ++e) al[e] = exp_f32(al[e]);
         } else {
-            const float alpha = exp_f32(cur.g);
+            const float gt = GATED ? gate_decay(cur.ga.get(), neg_exp_a_log, dt_bias) : cur.g;
+            const float alpha = exp_f32(gt);
 #pragma unroll
             for (int e = 0; e < EPL; ++e) al[e] = alpha;
         }
-        const float bt = cur.b.get();
+        float bt = cur.b.get();
+        if constexpr (GATED) {
+            bt = a.beta_mul * sigmoid_f32(bt);
+            if (a.qk_l2norm) {  // uniform over the launch
+                float sk = 0.0f, sq = 0.0f;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) {
+                    sk = fmaf(kk[e], kk[e], sk);
+                    sq = fmaf(qq[e], qq[e], sq);
+                }
+                const float rk = rsqrtf(row16_sum(sk) + a.l2_eps);
+                const float rq = rsqrtf(row16_sum(sq) + a.l2_eps);
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) {
+                    kk[e] *= rk;
+                    qq[e] *= rq;
+                }
+            }
+        }
         float vv[SLOTS];
         cur.v.get(vv);
 
@@ -190,47 +220,54 @@ namespace {
 
 constexpr int kSlots = 4;  // BV = 64 rows per workgroup
 
-template <int K, typename IO, typename ST, typename DT, typename IB, bool PER_K>
+template <int K, typename IO, typename ST, typename DT, typename IB, bool PER_K, bool GATED>
 hipError_t launch_t(const RecurrentArgs& a, hipStream_t stream) {
     dim3 grid(a.V / (16 * kSlots), a.HV, a.N);
     if (a.prefetch)
-        hipLaunchKernelGGL((recurrent_kernel<K, IO, ST, DT, IB, PER_K, kSlots, true>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((recurrent_kernel<K, IO, ST, DT, IB, PER_K, kSlots, true, GATED>), grid, dim3(256), 0,
+                           stream, a);
     else
-        hipLaunchKernelGGL((recurrent_kernel<K, IO, ST, DT, IB, PER_K, kSlots, false>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((recurrent_kernel<K, IO, ST, DT, IB, PER_K, kSlots, false, GATED>), grid, dim3(256), 0,
+                           stream, a);
     return hipGetLastError();
 }
 
-template <int K, typename IO, typename ST, typename DT, bool PER_K>
+template <int K, typename IO, typename ST, typename DT, bool PER_K, bool GATED>
 hipError_t launch_ib(const RecurrentArgs& a, int ib_dtype, hipStream_t stream) {
-    if (ib_dtype < 0) return launch_t<K, IO, ST, DT, void, PER_K>(a, stream);
-    if (ib_dtype == 0) return launch_t<K, IO, ST, DT, float, PER_K>(a, stream);
-    return launch_t<K, IO, ST, DT, bf16_t, PER_K>(a, stream);
+    if (ib_dtype < 0) return launch_t<K, IO, ST, DT, void, PER_K, GATED>(a, stream);
+    if (ib_dtype == 0) return launch_t<K, IO, ST, DT, float, PER_K, GATED>(a, stream);
+    return launch_t<K, IO, ST, DT, bf16_t, PER_K, GATED>(a, stream);
 }
 
-template <int K, typename IO, bool PER_K>
+template <int K, typename IO, bool PER_K, bool GATED>
 hipError_t launch_st(const RecurrentArgs& a, int st_dtype, int ib_dtype, hipStream_t stream) {
     // state source and destination share a dtype (pool) except in the dense mode,
     // where both are fp32
-    if (st_dtype == 0) return launch_ib<K, IO, float, float, PER_K>(a, ib_dtype, stream);
-    return launch_ib<K, IO, bf16_t, bf16_t, PER_K>(a, ib_dtype, stream);
+    if (st_dtype == 0) return launch_ib<K, IO, float, float, PER_K, GATED>(a, ib_dtype, stream);
+    return launch_ib<K, IO, bf16_t, bf16_t, PER_K, GATED>(a, ib_dtype, stream);
 }
 
-template <int K, bool PER_K>
+template <int K, bool PER_K, bool GATED>
 hipError_t launch_io(const RecurrentArgs& a, int io_dtype, int st_dtype, int ib_dtype, hipStream_t stream) {
-    if (io_dtype == 0) return launch_st<K, float, PER_K>(a, st_dtype, ib_dtype, stream);
-    return launch_st<K, bf16_t, PER_K>(a, st_dtype, ib_dtype, stream);
+    if (io_dtype == 0) return launch_st<K, float, PER_K, GATED>(a, st_dtype, ib_dtype, stream);
+    return launch_st<K, bf16_t, PER_K, GATED>(a, st_dtype, ib_dtype, stream);
+}
+
+template <int K>
+hipError_t launch_k(const RecurrentArgs& a, int io_dtype, int st_dtype, int ib_dtype, bool per_k, bool gated,
+                    hipStream_t stream) {
+    if (per_k) return launch_io<K, true, false>(a, io_dtype, st_dtype, ib_dtype, stream);
+    if (gated) return launch_io<K, false, true>(a, io_dtype, st_dtype, ib_dtype, stream);
+    return launch_io<K, false, false>(a, io_dtype, st_dtype, ib_dtype, stream);
 }
 
 }  // namespace
 
 hipError_t launch_recurrent(const RecurrentArgs& a, int K, int io_dtype, int st_dtype, int ib_dtype,
-                            bool per_k, hipStream_t stream) {
-    if (K == 64) {
-        return per_k ? launch_io<64, true>(a, io_dtype, st_dtype, ib_dtype, stream)
-                     : launch_io<64, false>(a, io_dtype, st_dtype, ib_dtype, stream);
-    }
-    return per_k ? launch_io<128, true>(a, io_dtype, st_dtype, ib_dtype, stream)
-                 : launch_io<128, false>(a, io_dtype, st_dtype, ib_dtype, stream);
+                            bool per_k, bool gated, hipStream_t stream) {
+    if (per_k && gated) return hipErrorInvalidValue;
+    if (K == 64) return launch_k<64>(a, io_dtype, st_dtype, ib_dtype, per_k, gated, stream);
+    return launch_k<128>(a, io_dtype, st_dtype, ib_dtype, per_k, gated, stream);
 }
 
 }  // namespace gdr

@@ -7,7 +7,8 @@ given are contiguous device tensors of the documented shape and dtype, builds th
 HIP kernels.  If the library has not been built, loading it raises immediately.
 
 Names follow the C entry points: ``gdr_recurrent_fwd``, ``gdr_chunk_fwd``,
-``gdr_chunk_workspace_size``, ``gdr_decode_paged``, ``gdr_status_string``.
+``gdr_chunk_workspace_size``, ``gdr_decode_paged``, ``gdr_gating_prepass``,
+``gdr_decode_paged_gated``, ``gdr_status_string``.
 """
 from __future__ import annotations
 
@@ -30,6 +31,18 @@ class GdrError(RuntimeError):
     def __init__(self, status: int, where: str):
         super().__init__(f"{where}: {gdr_status_string(status)} ({status})")
         self.status = status
+
+
+class Gating(ctypes.Structure):
+    _fields_ = [
+        ("a", ctypes.c_void_p),
+        ("b", ctypes.c_void_p),
+        ("A_log", ctypes.c_void_p),
+        ("dt_bias", ctypes.c_void_p),
+        ("l2norm_eps", ctypes.c_float),
+        ("qk_l2norm", ctypes.c_int32),
+        ("allow_neg_eigval", ctypes.c_int32),
+    ]
 
 
 class Problem(ctypes.Structure):
@@ -70,6 +83,12 @@ def lib():
         L.gdr_decode_paged.restype = ctypes.c_int
         L.gdr_decode_paged.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, i32, vp, i32,
                                        vp, ctypes.c_int, i32, i32, vp, vp, vp]
+        G = ctypes.POINTER(Gating)
+        L.gdr_gating_prepass.restype = ctypes.c_int
+        L.gdr_gating_prepass.argtypes = [P, vp, vp, G, vp, vp, vp, vp, vp]
+        L.gdr_decode_paged_gated.restype = ctypes.c_int
+        L.gdr_decode_paged_gated.argtypes = [P, i32, vp, vp, vp, G, vp, vp, ctypes.c_int, i32, vp, i32,
+                                             vp, ctypes.c_int, i32, i32, vp, vp, vp]
         _lib = L
     return _lib
 
@@ -234,4 +253,92 @@ def gdr_decode_paged(q, k, v, g, beta, pool, state_indices, cu_seqlens=None, max
                                 1 if commit else 0, _ptr(inter_states), inter_dt, ncs, steps,
                                 _ptr(inter_state_indices), _ptr(o), _stream(stream))
     _raise(st, "gdr_decode_paged")
+    return o
+
+
+# ---------------------------------------------------------------------------
+def _gating(q, v, a, b, A_log, dt_bias, eps: float, qk_l2norm: bool, allow_neg_eigval: bool) -> Gating:
+    T, HV = q.shape[0], v.shape[1] if v is not None else a.shape[1]
+    _check(a, "a", (T, HV), q.dtype)
+    _check(b, "b", (T, HV), q.dtype)
+    _check(A_log, "A_log", (HV,), torch.float32)
+    _check(dt_bias, "dt_bias", (HV,), torch.float32)
+    return Gating(a.data_ptr(), b.data_ptr(), A_log.data_ptr(), dt_bias.data_ptr(), float(eps),
+                  1 if qk_l2norm else 0, 1 if allow_neg_eigval else 0)
+
+
+def gdr_gating_prepass(q, k, a, b, A_log, dt_bias, l2norm_eps: float = 1e-6, qk_l2norm: bool = True,
+                       allow_neg_eigval: bool = False, q_out=None, k_out=None, g_out=None, beta_out=None,
+                       stream=None):
+    """Gating front as one pass.  q, k [T, HK, K] raw; a, b [T, HV] (q's dtype); A_log, dt_bias
+    [HV] fp32.  Returns (q_out, k_out, g [T, HV] fp32, beta [T, HV]); q_out/k_out may be q/k
+    (in place) and are None when qk_l2norm is False."""
+    if q.dim() != 3 or a.dim() != 2:
+        raise ValueError("q, k are [T, HK, K]; a, b are [T, HV]")
+    T, HK, K = q.shape
+    HV = a.shape[1]
+    _check(q, "q")
+    _check(k, "k", (T, HK, K), q.dtype)
+    gt = _gating(q, None, a, b, A_log, dt_bias, l2norm_eps, qk_l2norm, allow_neg_eigval)
+    if qk_l2norm:
+        q_out = torch.empty_like(q) if q_out is None else q_out
+        k_out = torch.empty_like(k) if k_out is None else k_out
+        _check(q_out, "q_out", (T, HK, K), q.dtype)
+        _check(k_out, "k_out", (T, HK, K), q.dtype)
+    else:
+        q_out = k_out = None
+    g_out = torch.empty((T, HV), dtype=torch.float32, device=q.device) if g_out is None else g_out
+    beta_out = torch.empty((T, HV), dtype=q.dtype, device=q.device) if beta_out is None else beta_out
+    _check(g_out, "g_out", (T, HV), torch.float32)
+    _check(beta_out, "beta_out", (T, HV), q.dtype)
+    # gdr_problem: V is not read by this pass; K is given as the value width to pass validation
+    p = Problem(T, 1, HK, HV, K, K, 1.0, GDR_GATE_SCALAR, _dtype_code(q.dtype))
+    st = lib().gdr_gating_prepass(ctypes.byref(p), _ptr(q), _ptr(k), ctypes.byref(gt), _ptr(q_out), _ptr(k_out),
+                                  _ptr(g_out), _ptr(beta_out), _stream(stream))
+    _raise(st, "gdr_gating_prepass")
+    return q_out, k_out, g_out, beta_out
+
+
+def gdr_decode_paged_gated(q, k, v, a, b, A_log, dt_bias, pool, state_indices, cu_seqlens=None,
+                           max_q_len: int = 1, commit: bool = True, inter_states=None, inter_state_indices=None,
+                           scale=None, l2norm_eps: float = 1e-6, qk_l2norm: bool = True,
+                           allow_neg_eigval: bool = False, o=None, stream=None):
+    """gdr_decode_paged with the gating front in the token loop: q, k raw; a, b [T, HV] (q's
+    dtype); A_log, dt_bias [HV] fp32.  Returns o."""
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k are [T, HK, K] and v is [T, HV, V]")
+    T, HK, K = q.shape
+    HV, V = v.shape[1], v.shape[2]
+    _check(q, "q")
+    _check(k, "k", (T, HK, K), q.dtype)
+    _check(v, "v", (T, HV, V), q.dtype)
+    gt = _gating(q, v, a, b, A_log, dt_bias, l2norm_eps, qk_l2norm, allow_neg_eigval)
+    _check(state_indices, "state_indices", dtype=torch.int32)
+    N = state_indices.shape[0]
+    if cu_seqlens is not None:
+        _check(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32)
+    if pool.dim() != 4:
+        raise ValueError("pool is [num_slots, HV, V, K]")
+    _check(pool, "pool", (pool.shape[0], HV, V, K))
+    pool_dt = _dtype_code(pool.dtype)
+    ncs = steps = 0
+    inter_dt = GDR_F32
+    if inter_states is not None:
+        if inter_states.dim() != 5:
+            raise ValueError("inter_states is [num_cache_slots, cache_steps, HV, V, K]")
+        ncs, steps = inter_states.shape[0], inter_states.shape[1]
+        _check(inter_states, "inter_states", (ncs, steps, HV, V, K))
+        inter_dt = _dtype_code(inter_states.dtype)
+        _check(inter_state_indices, "inter_state_indices", (N,), torch.int32)
+    if o is None:
+        o = torch.empty((T, HV, V), dtype=q.dtype, device=q.device)
+    _check(o, "o", (T, HV, V), q.dtype)
+    if scale is None:
+        scale = 1.0 / math.sqrt(K)
+    p = Problem(T, N, HK, HV, K, V, float(scale), GDR_GATE_SCALAR, _dtype_code(q.dtype))
+    st = lib().gdr_decode_paged_gated(ctypes.byref(p), int(max_q_len), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(gt),
+                                      _ptr(cu_seqlens), _ptr(pool), pool_dt, pool.shape[0], _ptr(state_indices),
+                                      1 if commit else 0, _ptr(inter_states), inter_dt, ncs, steps,
+                                      _ptr(inter_state_indices), _ptr(o), _stream(stream))
+    _raise(st, "gdr_decode_paged_gated")
     return o

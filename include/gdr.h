@@ -13,9 +13,11 @@
  *     output   o[t,h,v] = scale * sum_c S[v][c] * q[t,hk,c]    (post-update state)
  *
  * with key/query head hk = h / (HV / HK) (grouped-query mapping, same page, review
- * commit).  q and k arrive l2-normalised per (token, head) and g, beta arrive
- * already activated (same page, verify-kernel commit); the library never
- * re-normalises.  g is the natural-log decay and must be finite and <= 0.
+ * commit).  For gdr_recurrent_fwd, gdr_chunk_fwd and gdr_decode_paged, q and k arrive
+ * l2-normalised per (token, head) and g, beta arrive already activated (same page,
+ * verify-kernel commit); those entry points never re-normalise.  g is the natural-log
+ * decay and must be finite and <= 0.  The gated entry points (gdr_gating_prepass,
+ * gdr_decode_paged_gated) take the raw inputs instead; see gdr_gating below.
  *
  * Layouts (all tensors contiguous, row-major, packed variable-length batch):
  *   q, k           [T, HK, K]          io_dtype
@@ -172,6 +174,68 @@ GDR_API gdr_status gdr_decode_paged(const gdr_problem* p, int32_t max_q_len,
                             int32_t num_cache_slots, int32_t cache_steps,
                             const int32_t* inter_state_indices,
                             void* o, void* hip_stream);
+
+/*
+ * Gating front (FlashQLA PR #1: host-gating wrapper commit, in-kernel gated verify commit,
+ * verify pre-pass commit, and the pull-request description for softplus 1.0 / 20.0).  The
+ * entry points below take the raw inputs of the usual GDN layer instead of activated ones:
+ *
+ *     g[t,h]    = -exp(A_log[h]) * softplus(a[t,h] + dt_bias[h])
+ *                 softplus(x) = x for x > 20, log(1 + exp(x)) otherwise
+ *     beta[t,h] = sigmoid(b[t,h]), times 2 when allow_neg_eigval
+ *     q, k      <- x / sqrt(sum_c x_c^2 + l2norm_eps) per (token, key head), when qk_l2norm
+ *
+ * The pages give no epsilon for the normalisation; it is the caller's (0 allowed, 1e-6 is
+ * the binding's default).  Only the scalar gate (GDR_GATE_SCALAR) has a gating front;
+ * a per-K-channel problem returns GDR_ERROR_NOT_SUPPORTED.
+ */
+typedef struct gdr_gating {
+    const void*  a;                 /* [T, HV] io_dtype: decay input before softplus        */
+    const void*  b;                 /* [T, HV] io_dtype: beta input before the sigmoid       */
+    const float* A_log;             /* [HV] fp32                                            */
+    const float* dt_bias;           /* [HV] fp32                                            */
+    float        l2norm_eps;        /* finite, >= 0                                         */
+    int32_t      qk_l2norm;         /* 1: normalise q and k; 0: take them as given          */
+    int32_t      allow_neg_eigval;  /* 1: beta = 2 sigmoid(b)                               */
+} gdr_gating;
+
+/*
+ * gdr_gating_prepass -- the gating front as one pass over the batch (the pre-pass design of
+ * the verify pre-pass commit): writes normalised q, k and activated g, beta for every token,
+ * ready for gdr_recurrent_fwd, gdr_chunk_fwd or gdr_decode_paged.
+ *
+ *   q, k           [T, HK, K] io_dtype, raw (read only when gating->qk_l2norm)
+ *   q_out, k_out   [T, HK, K] io_dtype (written when qk_l2norm; may be NULL otherwise);
+ *                  q_out may equal q and k_out may equal k (in place)
+ *   g_out          [T, HV] fp32;  beta_out [T, HV] io_dtype
+ * T == 0 returns GDR_SUCCESS without a launch.  p->num_seqs and p->head_dim_v are not used
+ * beyond validation.
+ */
+GDR_API gdr_status gdr_gating_prepass(const gdr_problem* p,
+                              const void* q, const void* k,
+                              const gdr_gating* gating,
+                              void* q_out, void* k_out,
+                              float* g_out, void* beta_out,
+                              void* hip_stream);
+
+/*
+ * gdr_decode_paged_gated -- gdr_decode_paged with the gating front inside the token loop
+ * (the fused design of the in-kernel gated verify commit): q and k are the raw inputs, and
+ * g and beta are formed from gating->a, gating->b per token.  Every other argument, the
+ * padded-slot rule, commit and the intermediate states behave exactly as in
+ * gdr_decode_paged.  Equivalent, up to rounding, to gdr_gating_prepass followed by
+ * gdr_decode_paged.
+ */
+GDR_API gdr_status gdr_decode_paged_gated(const gdr_problem* p, int32_t max_q_len,
+                                  const void* q, const void* k, const void* v,
+                                  const gdr_gating* gating,
+                                  const int32_t* cu_seqlens,
+                                  void* pool, gdr_dtype pool_dtype, int32_t num_slots,
+                                  const int32_t* state_indices, int32_t commit,
+                                  void* inter_states, gdr_dtype inter_dtype,
+                                  int32_t num_cache_slots, int32_t cache_steps,
+                                  const int32_t* inter_state_indices,
+                                  void* o, void* hip_stream);
 
 /* Human-readable name of a status code (static string). */
 GDR_API const char* gdr_status_string(gdr_status s);

@@ -20,7 +20,7 @@ def _declared_symbols():
 def test_header_declares_the_three_entry_points():
     syms = _declared_symbols()
     for name in ("gdr_recurrent_fwd", "gdr_chunk_fwd", "gdr_decode_paged", "gdr_chunk_workspace_size",
-                 "gdr_status_string"):
+                 "gdr_status_string", "gdr_gating_prepass", "gdr_decode_paged_gated"):
         assert name in syms
 
 
@@ -122,3 +122,55 @@ def test_chunk_workspace_and_rejections():
     assert call(p, cu=None) == 1                        # N > 1 needs cu_seqlens
     assert call(_p(K=96)) == 2
     assert call(_p(K=128, io=0)) == 2                   # fp32 operands need K = 64
+
+
+def _gating(**kw):
+    f = dict(a=0x1000, b=0x1000, A_log=0x1000, dt_bias=0x1000, l2norm_eps=1e-6, qk_l2norm=1, allow_neg_eigval=0)
+    f.update(kw)
+    return gdr.Gating(f["a"], f["b"], f["A_log"], f["dt_bias"], f["l2norm_eps"], f["qk_l2norm"],
+                      f["allow_neg_eigval"])
+
+
+def _pre(p, gt, q=DUMMY, k=DUMMY, qo=DUMMY, ko=DUMMY, g=DUMMY, b=DUMMY):
+    return gdr.lib().gdr_gating_prepass(ctypes.byref(p), q, k, ctypes.byref(gt) if gt is not None else None,
+                                        qo, ko, g, b, None)
+
+
+def _decg(p, gt, max_q_len=1, **kw):
+    a = dict(cu=None, pool=DUMMY, pool_dt=0, slots=4, idx=DUMMY, commit=1, ib=None, ib_dt=1, ncs=0, steps=0,
+             ibidx=None, q=DUMMY)
+    a.update(kw)
+    return gdr.lib().gdr_decode_paged_gated(ctypes.byref(p), max_q_len, a["q"], DUMMY, DUMMY,
+                                            ctypes.byref(gt) if gt is not None else None, a["cu"], a["pool"],
+                                            a["pool_dt"], a["slots"], a["idx"], a["commit"], a["ib"], a["ib_dt"],
+                                            a["ncs"], a["steps"], a["ibidx"], DUMMY, None)
+
+
+def test_gated_entry_points_reject_bad_metadata():
+    p = _p(T=4, N=4)
+    for call in (lambda gt, **kw: _pre(p, gt, **kw), lambda gt, **kw: _decg(p, gt, **kw)):
+        assert call(None) == 1
+        assert call(_gating(qk_l2norm=2)) == 1
+        assert call(_gating(allow_neg_eigval=-1)) == 1
+        assert call(_gating(l2norm_eps=-1e-6)) == 1
+        assert call(_gating(l2norm_eps=float("nan"))) == 1
+        assert call(_gating(l2norm_eps=float("inf"))) == 1
+        assert call(_gating(a=None)) == 1
+        assert call(_gating(dt_bias=None)) == 1
+    # the gating front defines a scalar decay only
+    assert _pre(_p(T=4, N=4, gate=1), _gating()) == 2
+    assert _decg(_p(T=4, N=4, gate=1), _gating()) == 2
+    # pre-pass outputs; q/k outputs only matter when normalising
+    assert _pre(p, _gating(), g=None) == 1
+    assert _pre(p, _gating(), b=None) == 1
+    assert _pre(p, _gating(), qo=None) == 1
+    # decode checks apply to the gated variant as well
+    assert _decg(p, _gating(), max_q_len=13) == 1
+    assert _decg(p, _gating(), q=None) == 1
+    assert _decg(_p(T=5, N=4), _gating()) == 1
+
+
+def test_gated_entry_points_accept_empty_batches_without_the_device():
+    assert _pre(_p(T=0, N=1), _gating(a=None, b=None, A_log=None, dt_bias=None), q=None, k=None, qo=None, ko=None,
+                g=None, b=None) == 0
+    assert _decg(_p(T=0, N=4), _gating(), cu=DUMMY) == 0

@@ -1,0 +1,222 @@
+"""Gating front on the GPU: gdr_gating_prepass and gdr_decode_paged_gated against the fp64
+oracle of oracle/gating.py composed with the recurrence oracle, with the same bit-exact slot
+and sentinel rules as the plain paged entry point."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import gating
+from _cmp import TOL, max_rel_l2_tokens, rel_l2
+from _dev import f64, to_dev, to_host
+from gated_delta_rule_63_amd import gdr, inputs
+from test_paged_gpu import SENT_IB, SENT_O, _check_ibuf, _check_o, _check_pool, _fill_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def _raw_dev(r):
+    return {"q": to_dev(r.q), "k": to_dev(r.k), "a": to_dev(r.a), "b": to_dev(r.b), "A_log": to_dev(r.A_log),
+            "dt_bias": to_dev(r.dt_bias)}
+
+
+def _oracle_gated(r):
+    return gating.gated_inputs(inputs.widen(r.q), inputs.widen(r.k), inputs.widen(r.a), inputs.widen(r.b),
+                               r.A_log, r.dt_bias, r.eps, r.qk_l2norm, r.allow_neg_eigval)
+
+
+def _prepass(r, d, **kw):
+    out = gdr.gdr_gating_prepass(d["q"], d["k"], d["a"], d["b"], d["A_log"], d["dt_bias"], l2norm_eps=r.eps,
+                                 qk_l2norm=r.qk_l2norm, allow_neg_eigval=r.allow_neg_eigval, **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("io,K,neg,norm", [("bf16", 128, False, True), ("bf16", 64, True, True),
+                                           ("f32", 128, True, True), ("f32", 64, False, True),
+                                           ("bf16", 128, False, False)])
+def test_prepass_matches_oracle(io, K, neg, norm):
+    T, HK, HV = 301, 4, 8
+    r = inputs.raw_gating(31, T, HK, HV, K, io_dtype=io, allow_neg_eigval=neg, qk_l2norm=norm)
+    d = _raw_dev(r)
+    qo, ko, g, beta = _prepass(r, d)
+    qn, kn, g_ref, b_ref = _oracle_gated(r)
+    # each output is one rounding of a correctly computed fp32 value: half an ulp of the output
+    # type plus a few fp32 ulps of the arithmetic before it
+    out_rel = 2.0 ** -8 + 1e-5 if io == "bf16" else 1e-6
+    np.testing.assert_allclose(f64(g), g_ref, rtol=1e-5, atol=0)
+    np.testing.assert_allclose(f64(beta), b_ref, rtol=out_rel, atol=0)
+    assert np.all(f64(g) <= 0)
+    if norm:
+        for got, ref in ((qo, qn), (ko, kn)):
+            np.testing.assert_allclose(f64(got), ref, rtol=out_rel, atol=1e-7)
+            assert np.allclose(np.linalg.norm(f64(got), axis=-1), 1.0, rtol=4 * out_rel)
+    else:
+        assert qo is None and ko is None
+
+
+def test_prepass_in_place_equals_out_of_place_and_zero_rows():
+    r = inputs.raw_gating(32, 64, 2, 4, 128, io_dtype="bf16")
+    r.q[5] = 0  # a zero row: eps keeps it finite and zero
+    d = _raw_dev(r)
+    qo, ko, g, beta = _prepass(r, d)
+    assert torch.all(qo[5] == 0)
+    qi, ki = d["q"].clone(), d["k"].clone()
+    _prepass(r, {**d, "q": qi, "k": ki}, q_out=qi, k_out=ki)
+    assert torch.equal(qi, qo) and torch.equal(ki, ko)
+
+
+def _run_gated(p, r, with_ibuf=None, commit=None, pool_dev=None):
+    d = _raw_dev(r)
+    v = to_dev(p.v)
+    cu = to_dev(p.cu_seqlens.astype(np.int32)) if getattr(p, "_use_cu", True) else None
+    pool = to_dev(p.pool) if pool_dev is None else pool_dev
+    idx = to_dev(p.state_indices)
+    o = torch.empty((p.T, p.HV, p.V), dtype=d["q"].dtype, device="cuda")
+    _fill_bits(o, SENT_O)
+    ib = ibi = None
+    if with_ibuf is not None:
+        ib = torch.empty((p.num_cache_slots, p.cache_steps, p.HV, p.V, p.K), dtype=with_ibuf, device="cuda")
+        _fill_bits(ib, SENT_IB)
+        ibi = to_dev(p.inter_state_indices)
+    gdr.gdr_decode_paged_gated(d["q"], d["k"], v, d["a"], d["b"], d["A_log"], d["dt_bias"], pool, idx,
+                               cu_seqlens=cu, max_q_len=p.max_q_len, commit=p.commit if commit is None else commit,
+                               inter_states=ib, inter_state_indices=ibi, scale=p.scale, l2norm_eps=r.eps,
+                               qk_l2norm=r.qk_l2norm, allow_neg_eigval=r.allow_neg_eigval, o=o)
+    torch.cuda.synchronize()
+    return o, pool, ib
+
+
+def _ref(p, r, want_states=False):
+    qn, kn, g, beta = _oracle_gated(r)
+    return oracle.decode_paged(qn, kn, inputs.widen(p.v), g, beta, p.cu_seqlens, p.scale, inputs.widen(p.pool),
+                               p.state_indices, want_states=want_states)
+
+
+def test_decode_gated_fp32_pool_commit_with_padding():
+    p = inputs.paged_problem(33, B=40, q_len=1, HK=16, HV=32, K=128, V=128, num_slots=64, pool_dtype="f32",
+                             pad_count=4, commit=True)
+    r = inputs.raw_gating(34, p.T, p.HK, p.HV, p.K, io_dtype=p.io_dtype)
+    before = p.pool.copy()
+    o, pool, _ = _run_gated(p, r)
+    ref = _ref(p, r)
+    _check_o(p, o, ref)
+    _check_pool(p, before, pool, ref, committed=True)
+
+
+@pytest.mark.parametrize("neg,K", [(False, 128), (True, 128), (False, 64)])
+def test_verify_gated_ragged_no_commit(neg, K):
+    p = inputs.paged_problem(35, B=10, q_len=12, HK=4, HV=8, K=K, V=K, num_slots=20, pool_dtype="bf16",
+                             pad_count=2, commit=False, inter_dtype="bf16", ragged=True, cache_steps=12)
+    r = inputs.raw_gating(36, p.T, p.HK, p.HV, p.K, io_dtype=p.io_dtype, allow_neg_eigval=neg)
+    before = p.pool.copy()
+    o, pool, ib = _run_gated(p, r, with_ibuf=torch.bfloat16)
+    ref = _ref(p, r, want_states=True)
+    _check_o(p, o, ref)
+    _check_pool(p, before, pool, ref, committed=False)
+    _check_ibuf(p, ib, ref)
+
+
+def test_gated_fp32_equals_prepass_then_plain_decode_bitwise():
+    """fp32 I/O: the pre-pass stores its fp32 results unrounded, so the fused kernel, which forms
+    the same values in registers with the same instructions and lane layout, must agree bit for bit."""
+    p = inputs.paged_problem(37, B=12, q_len=4, HK=2, HV=4, K=128, V=128, num_slots=16, pool_dtype="f32",
+                             io_dtype="f32", pad_count=2, commit=True, ragged=True)
+    r = inputs.raw_gating(38, p.T, p.HK, p.HV, p.K, io_dtype="f32", allow_neg_eigval=True)
+    o1, pool1, _ = _run_gated(p, r)
+    d = _raw_dev(r)
+    qn, kn, g, beta = _prepass(r, d)
+    cu = to_dev(p.cu_seqlens.astype(np.int32))
+    pool2 = to_dev(p.pool)
+    o2 = torch.empty_like(o1)
+    _fill_bits(o2, SENT_O)
+    gdr.gdr_decode_paged(qn, kn, to_dev(p.v), g, beta, pool2, to_dev(p.state_indices), cu_seqlens=cu,
+                         max_q_len=p.max_q_len, commit=True, scale=p.scale, o=o2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int32), o2.view(torch.int32))
+    assert torch.equal(pool1.view(torch.int32), pool2.view(torch.int32))
+
+
+def test_gated_bf16_close_to_prepass_then_plain_decode():
+    p = inputs.paged_problem(39, B=12, q_len=6, HK=2, HV=4, K=128, V=128, num_slots=16, pool_dtype="bf16",
+                             pad_count=1, commit=True, ragged=True)
+    r = inputs.raw_gating(40, p.T, p.HK, p.HV, p.K, io_dtype="bf16")
+    o1, _, _ = _run_gated(p, r)
+    d = _raw_dev(r)
+    qn, kn, g, beta = _prepass(r, d)
+    o2 = gdr.gdr_decode_paged(qn, kn, to_dev(p.v), g, beta, to_dev(p.pool), to_dev(p.state_indices),
+                              cu_seqlens=to_dev(p.cu_seqlens.astype(np.int32)), max_q_len=p.max_q_len,
+                              commit=True, scale=p.scale)
+    torch.cuda.synchronize()
+    act = [b for b in range(p.N) if p.state_indices[b] >= 0]
+    rows = np.concatenate([np.arange(p.cu_seqlens[b], p.cu_seqlens[b + 1]) for b in act])
+    assert rel_l2(f64(o1)[rows], f64(o2)[rows]) <= TOL["bf16"]
+
+
+def test_gated_graph_capture_replay_equals_eager():
+    p = inputs.paged_problem(41, B=8, q_len=4, HK=2, HV=4, K=128, V=128, num_slots=16, pool_dtype="bf16",
+                             pad_count=1, commit=False, inter_dtype="bf16")
+    r = inputs.raw_gating(42, p.T, p.HK, p.HV, p.K)
+    d = _raw_dev(r)
+    v = to_dev(p.v)
+    cu = to_dev(p.cu_seqlens.astype(np.int32))
+    pool = to_dev(p.pool)
+    idx = to_dev(p.state_indices)
+    ibi = to_dev(p.inter_state_indices)
+    ib = torch.zeros((p.num_cache_slots, p.cache_steps, p.HV, p.V, p.K), dtype=torch.bfloat16, device="cuda")
+    o = torch.zeros((p.T, p.HV, p.V), dtype=torch.bfloat16, device="cuda")
+
+    def call():
+        gdr.gdr_decode_paged_gated(d["q"], d["k"], v, d["a"], d["b"], d["A_log"], d["dt_bias"], pool, idx,
+                                   cu_seqlens=cu, max_q_len=4, commit=False, inter_states=ib, inter_state_indices=ibi,
+                                   scale=p.scale, o=o)
+
+    call()
+    torch.cuda.synchronize()
+    o_ref, ib_ref = o.clone(), ib.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for _ in range(3):
+        o.zero_()
+        ib.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(ib, ib_ref)
+
+
+def test_verify_gated_full_size_sampled():
+    """64 sequences x 12 tokens, 32 value / 16 key heads, bf16 pool and intermediate buffer:
+    slot and sentinel handling checked everywhere, values on a sample of sequences."""
+    p = inputs.verify(num_slots=128)
+    r = inputs.raw_gating(43, p.T, p.HK, p.HV, p.K)
+    before = p.pool.copy()
+    o, pool, ib = _run_gated(p, r, with_ibuf=torch.bfloat16)
+    assert np.array_equal(to_host(pool), before)  # no commit
+    rng = np.random.default_rng(1)
+    sample = sorted(rng.choice(p.N, size=6, replace=False).tolist())
+    sub = np.full(p.N, -1, dtype=np.int32)
+    sub[sample] = p.state_indices[sample]
+    qn, kn, g, beta = _oracle_gated(r)
+    pool_s = {int(p.state_indices[b]): inputs.widen(p.pool[int(p.state_indices[b])]) for b in sample}
+    ref = oracle.decode_paged(qn, kn, inputs.widen(p.v), g, beta, p.cu_seqlens, p.scale, pool_s, sub,
+                              want_states=True)
+    oh = f64(o)
+    ibh = to_host(ib)
+    worst = 0.0
+    for b in sample:
+        s, e = p.cu_seqlens[b], p.cu_seqlens[b + 1]
+        row = int(p.inter_state_indices[b])
+        for h in range(p.HV):
+            worst = max(worst, rel_l2(oh[s:e, h], ref["o"][s:e, h]))
+            for t in range(e - s):
+                worst = max(worst, rel_l2(inputs.widen(ibh[row, t, h]), ref["states"][b][t, h]))
+    assert worst <= TOL["bf16"], worst
+    # every intermediate row past the batch keeps its sentinel
+    assert np.all(ibh[p.N:] == SENT_IB)
