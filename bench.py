@@ -12,9 +12,14 @@ already resident in HBM:
   verify   gdr_decode_paged  64 sequences x 12 tokens, bf16 pool, bf16 per-token states
                              [1025, 12, 32, 128, 128], no commit  (speculative verify)
 
+After the step, three legs outside it are timed the same way: the decode and verify launches
+with the gating front fused into the token loop (raw q, k, a, b in; gdr_decode_paged_gated),
+and the gating pass followed by the plain verify launch (gdr_gating_prepass + gdr_decode_paged).
+
 The JSON line reports prefill tokens/s as ``value`` and the decode state GB/s beside it,
 each leg's time from HIP events recorded on the stream the library launches on (torch's
-current stream, passed explicitly to every call), the roofline of the step's dominant kernel
+current stream, passed explicitly to every call), every launch starting from a clean cache (a
+512 MiB read outside the event window evicts L2 and the MALL and leaves no dirty lines), the roofline of the step's dominant kernel
 (the longest leg; each leg's own roofline beside it), HBM traffic per launch where the
 rocprofv3 counter passes recorded under profiles/ match the current kernel sources, and the
 CPU oracle timed on a bounded sample of the prefill workload.
@@ -60,26 +65,34 @@ def _alg_flops_prefill(p, full_tile=False):
     return per_chunk * p.T * p.HV // C
 
 
-def _alg_bytes_paged(p, with_ibuf: bool):
-    """Per active sequence: state read (+ write on commit) per value head, q/k/v/o/g/beta per token,
+def _alg_bytes_paged(p, with_ibuf: bool, gated: bool = False):
+    """Per active sequence: state read (+ write on commit) per value head, q/k/v/o/g/beta per token
+    (gated: the raw a, b in the io dtype instead of g, beta, plus A_log and dt_bias once),
     per-token intermediate states; 4 bytes (the index) per padded sequence."""
     io = 2 if p.io_dtype == "bf16" else 4
     st = 4 if p.pool_dtype == "f32" else 2
     lens = p.lengths
-    total = 0
+    gate_bytes = p.HV * io * 2 if gated else p.HV * 4 + p.HV * io
+    total = p.HV * 8 if gated else 0
     for b in range(p.N):
         if p.state_indices[b] < 0:
             total += 4
             continue
         L = int(lens[b])
         total += 4 + p.HV * p.V * p.K * st * (2 if p.commit else 1)
-        total += L * (2 * p.HK * p.K * io + 2 * p.HV * p.V * io + p.HV * 4 + p.HV * io)
+        total += L * (2 * p.HK * p.K * io + 2 * p.HV * p.V * io + gate_bytes)
         if with_ibuf:
             ib = 2 if p.inter_dtype == "bf16" else 4
             total += L * p.HV * p.V * p.K * ib + 4
     if getattr(p, "_use_cu", True):
         total += 4 * (p.N + 1)
     return total
+
+
+def _alg_bytes_prepass(p):
+    """Gating pass: q, k read and written, a and b read, g (fp32) and beta written, A_log and dt_bias."""
+    io = 2 if p.io_dtype == "bf16" else 4
+    return p.T * (4 * p.HK * p.K * io + 3 * p.HV * io + p.HV * 4) + p.HV * 8
 
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -146,6 +159,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--legs", default="prefill,decode,verify",
                     help="comma-separated subset of legs to run (profiling passes); the JSON line needs all three")
+    ap.add_argument("--extra-legs", default="decode_gated,verify_gated,verify_prepass",
+                    help="legs outside the step, timed after it: the gating front fused into the decode and verify "
+                         "launches, and the gating pass followed by the plain verify launch ('' for none)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before the legs, run one device-to-device copy of this many MiB (a plain copy kernel of "
                          "known size, used to scale the HBM byte counters of a profiling pass) and stop after the legs")
@@ -195,6 +211,15 @@ def main():
     V_["ib"] = torch.zeros((pv.num_cache_slots, pv.cache_steps, pv.HV, pv.V, pv.K), dtype=torch.bfloat16, device=dev)
     V_["o"] = torch.empty((pv.T, pv.HV, pv.V), dtype=torch.bfloat16, device=dev)
 
+    # gating front: raw q, k, a, b (same shapes as the step's decode / verify inputs)
+    rd = inputs.raw_gating(12, pd.T, pd.HK, pd.HV, pd.K)
+    rv = inputs.raw_gating(13, pv.T, pv.HK, pv.HV, pv.K)
+    DG = {k: to_dev(getattr(rd, k)) for k in ("q", "k", "a", "b", "A_log", "dt_bias")}
+    VG = {k: to_dev(getattr(rv, k)) for k in ("q", "k", "a", "b", "A_log", "dt_bias")}
+    VP = {"q": torch.empty_like(VG["q"]), "k": torch.empty_like(VG["k"]),
+          "g": torch.empty((pv.T, pv.HV), dtype=torch.float32, device=dev),
+          "beta": torch.empty((pv.T, pv.HV), dtype=torch.bfloat16, device=dev)}
+
     def prefill():
         gdr.gdr_chunk_fwd(P["q"], P["k"], P["v"], P["g"], P["beta"], P["cu"], pp.scale, P["h0"], o=P["o"],
                           final_state=P["ht"], workspace=P["ws"])
@@ -208,8 +233,28 @@ def main():
                              cu_seqlens=V_["cu"], max_q_len=12, commit=False, inter_states=V_["ib"],
                              inter_state_indices=V_["ibi"], scale=pv.scale, o=V_["o"])
 
+    def decode_gated():
+        gdr.gdr_decode_paged_gated(DG["q"], DG["k"], D["v"], DG["a"], DG["b"], DG["A_log"], DG["dt_bias"], D["pool"],
+                                   D["idx"], cu_seqlens=None, max_q_len=1, commit=True, scale=pd.scale,
+                                   l2norm_eps=rd.eps, o=D["o"])
+
+    def verify_gated():
+        gdr.gdr_decode_paged_gated(VG["q"], VG["k"], V_["v"], VG["a"], VG["b"], VG["A_log"], VG["dt_bias"],
+                                   V_["pool"], V_["idx"], cu_seqlens=V_["cu"], max_q_len=12, commit=False,
+                                   inter_states=V_["ib"], inter_state_indices=V_["ibi"], scale=pv.scale,
+                                   l2norm_eps=rv.eps, o=V_["o"])
+
+    def verify_prepass():
+        gdr.gdr_gating_prepass(VG["q"], VG["k"], VG["a"], VG["b"], VG["A_log"], VG["dt_bias"], l2norm_eps=rv.eps,
+                               q_out=VP["q"], k_out=VP["k"], g_out=VP["g"], beta_out=VP["beta"])
+        gdr.gdr_decode_paged(VP["q"], VP["k"], V_["v"], VP["g"], VP["beta"], V_["pool"], V_["idx"],
+                             cu_seqlens=V_["cu"], max_q_len=12, commit=False, inter_states=V_["ib"],
+                             inter_state_indices=V_["ibi"], scale=pv.scale, o=V_["o"])
+
     legs = [(n, f) for n, f in (("prefill", prefill), ("decode", decode), ("verify", verify))
             if n in args.legs.split(",")]
+    extra = [(n, f) for n, f in (("decode_gated", decode_gated), ("verify_gated", verify_gated),
+                                 ("verify_prepass", verify_prepass)) if n in args.extra_legs.split(",")]
     if args.calib_copy_mib:
         n = args.calib_copy_mib << 20
         src = torch.ones(n // 4, dtype=torch.float32, device=dev)
@@ -218,6 +263,14 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    # Each timed launch starts from a clean cache: a 512 MiB read outside the event window evicts
+    # L2 and the 256 MB MALL, and, being a read, leaves no dirty lines behind (a leg that follows a
+    # write-heavy leg would otherwise pay for writing back the previous leg's output).
+    flush_buf = torch.ones((512 << 20) // 4, dtype=torch.float32, device=dev)
+
+    def clean_cache():
+        flush_buf.sum()
+
     print("bench: warmup", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         for _, fn in legs:
@@ -232,11 +285,29 @@ def main():
     t0 = time.perf_counter()
     for i in range(K):
         for name, fn in legs:
+            clean_cache()
             ev[name][i][0].record()
             fn()
             ev[name][i][1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # legs outside the step, timed the same way after it
+    extra_ms = {}
+    if extra and len(legs) == 3 and not args.calib_copy_mib:
+        print("bench: timing the gated legs", file=sys.stderr, flush=True)
+        for _ in range(args.warmup):
+            for _, fn in extra:
+                fn()
+        xev = {name: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                      for _ in range(K)] for name, _ in extra}
+        for i in range(K):
+            for name, fn in extra:
+                clean_cache()
+                xev[name][i][0].record()
+                fn()
+                xev[name][i][1].record()
+        torch.cuda.synchronize()
+        extra_ms = {name: float(np.mean([a.elapsed_time(b) for a, b in xev[name]])) for name, _ in extra}
     if len(legs) < 3 or args.calib_copy_mib:
         print(json.dumps({"profiling_pass": [n for n, _ in legs], "steps": K}))
         return
@@ -260,6 +331,20 @@ def main():
         "verify": {"kernel": "recurrent_kernel (64 x 12 tokens, bf16 pool, bf16 per-token states)", "bytes": b_ver,
                    "flops": None, "secs": s_ver, "sources": ["gdr_recurrent.hip", "gdr_device.h"]},
     }
+    gated_sources = ["gdr_recurrent.hip", "gdr_device.h"]
+    if "decode_gated" in extra_ms:
+        leg_info["decode_gated"] = {"kernel": "recurrent_kernel, gating front in the token loop (decode shape)",
+                                    "bytes": _alg_bytes_paged(pd, with_ibuf=False, gated=True), "flops": None,
+                                    "secs": extra_ms["decode_gated"] / 1e3, "sources": gated_sources}
+    if "verify_gated" in extra_ms:
+        leg_info["verify_gated"] = {"kernel": "recurrent_kernel, gating front in the token loop (verify shape)",
+                                    "bytes": _alg_bytes_paged(pv, with_ibuf=True, gated=True), "flops": None,
+                                    "secs": extra_ms["verify_gated"] / 1e3, "sources": gated_sources}
+    if "verify_prepass" in extra_ms:
+        leg_info["verify_prepass"] = {"kernel": "gating_prepass_kernel then recurrent_kernel (verify shape)",
+                                      "bytes": _alg_bytes_prepass(pv) + b_ver, "flops": None,
+                                      "secs": extra_ms["verify_prepass"] / 1e3,
+                                      "sources": ["gdr_gating.hip"] + gated_sources}
     traffic = _measured_traffic()
 
     def roofline(leg):
@@ -284,9 +369,11 @@ def main():
             r["frac_hbm"] = li["bytes"] / li["secs"] / HBM_PEAK
         return r
 
-    dominant = max(leg_info, key=lambda n: leg_info[n]["secs"])
+    step_legs = ("prefill", "decode", "verify")
+    dominant = max(step_legs, key=lambda n: leg_info[n]["secs"])
     roof = roofline(dominant)
-    roof_legs = {n: roofline(n) for n in leg_info}
+    roof_legs = {n: roofline(n) for n in step_legs}
+    extra_legs = {n: {"ms": extra_ms[n], "roofline": roofline(n)} for n in extra_ms}
     roof_legs["prefill"]["frac_bf16_mfma_full_tile"] = f_pre_full / s_pre / BF16_MFMA_PEAK
     roof_legs["prefill"]["alg_flops_full_tile"] = f_pre_full
     roof_legs["decode"]["state_GBps"] = state_bytes_dec / s_dec / 1e9
@@ -313,6 +400,7 @@ def main():
         "leg_ms_min": leg_ms_min,
         "roofline": roof,
         "roofline_legs": roof_legs,
+        "extra_legs": extra_legs,
     }
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)

@@ -139,6 +139,10 @@ gdr_status gdr_recurrent_fwd(const gdr_problem* p, const void* q, const void* k,
     // all sequences empty and no final state requested: nothing to compute
     if (p->total_tokens == 0 && !final_state) return GDR_SUCCESS;
     if ((st = check_device()) != GDR_SUCCESS) return st;
+    if (p->total_tokens == 0) {  // every sequence empty: final state = initial state (or zeros)
+        const int64_t n = (int64_t)p->num_seqs * p->num_v_heads * p->head_dim_v * p->head_dim_k;
+        return status_of(gdr::launch_state_copy(initial_state, final_state, n, static_cast<hipStream_t>(hip_stream)));
+    }
 
     RecurrentArgs a{};
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.o = o;

@@ -109,6 +109,44 @@ template <int N> struct Vec<bf16_t, N> {
     }
 };
 
+// ---- loads through a buffer resource: bytes past the resource's range read as zero ----
+template <typename T, int N> struct BufVec;
+
+template <int N> struct BufVec<float, N> {
+    static_assert(N % 4 == 0, "fp32 vectors are whole float4s");
+    __device__ __forceinline__ static void load(__amdgpu_buffer_rsrc_t r, uint32_t off, float* out) {
+#pragma unroll
+        for (int j = 0; j < N / 4; ++j) {
+            const f32x4_t x = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * j, 0, 0));
+            out[4 * j + 0] = x[0];
+            out[4 * j + 1] = x[1];
+            out[4 * j + 2] = x[2];
+            out[4 * j + 3] = x[3];
+        }
+    }
+};
+
+template <int N> struct BufVec<bf16_t, N> {
+    static_assert(N == 4 || N == 8, "bf16 vectors are 8 or 16 bytes");
+    __device__ __forceinline__ static void load(__amdgpu_buffer_rsrc_t r, uint32_t off, float* out) {
+        if constexpr (N == 8) {
+            const uint4 w = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                out[2 * j] = __uint_as_float(ws[j] << 16);
+                out[2 * j + 1] = __uint_as_float(ws[j] & 0xFFFF0000u);
+            }
+        } else {
+            const uint2 w = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+            out[0] = __uint_as_float(w.x << 16);
+            out[1] = __uint_as_float(w.x & 0xFFFF0000u);
+            out[2] = __uint_as_float(w.y << 16);
+            out[3] = __uint_as_float(w.y & 0xFFFF0000u);
+        }
+    }
+};
+
 // ---- raw (unconverted) vectors, so loads can be issued well before their use ----
 template <typename T, int N> struct RawVec;
 template <int N> struct RawVec<float, N> {
@@ -200,10 +238,25 @@ __device__ __forceinline__ float exp_f32(float x) {
 }
 
 // ---- gating front (FlashQLA PR #1: host-gating and in-kernel gated verify commits) ----
-// softplus with beta 1 and threshold 20: inputs above 20 pass through unchanged.
-__device__ __forceinline__ float softplus_f32(float x) { return x > 20.0f ? x : log1pf(exp_f32(x)); }
+// log(1 + e) for e >= 0 from the hardware log2: log(u) e / (u - 1) with u = fl(1 + e) cancels
+// the rounding of 1 + e (the classic correction for small e), and u == 1 means log(1 + e) = e to
+// fp32 precision.  A few ulps; no table constants, so it costs few registers.
+__device__ __forceinline__ float log1p_nonneg_f32(float e) {
+    const float u = 1.0f + e;
+    const float d = u - 1.0f;
+    const float r = __builtin_amdgcn_logf(u) * 0.69314718055994531f * (e * __builtin_amdgcn_rcpf(d));
+    return d == 0.0f ? e : r;
+}
 
-__device__ __forceinline__ float sigmoid_f32(float x) { return 1.0f / (1.0f + exp_f32(-x)); }
+// softplus with beta 1 and threshold 20: inputs above 20 pass through unchanged.  Both sides
+// are evaluated and selected (no branch), so the token loop stays one basic block.
+__device__ __forceinline__ float softplus_f32(float x) {
+    const float smooth = log1p_nonneg_f32(exp_f32(fminf(x, 20.0f)));
+    return x > 20.0f ? x : smooth;
+}
+
+// 1 / (1 + e^-x) with the hardware reciprocal (about 1 ulp); 0 once e^-x overflows
+__device__ __forceinline__ float sigmoid_f32(float x) { return __builtin_amdgcn_rcpf(1.0f + exp_f32(-x)); }
 
 // decay g = -exp(A_log) softplus(a + dt_bias), with neg_exp_a_log = -exp(A_log) of the head
 __device__ __forceinline__ float gate_decay(float a, float neg_exp_a_log, float dt_bias) {

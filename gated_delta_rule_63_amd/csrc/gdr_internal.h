@@ -40,7 +40,11 @@ struct RecurrentArgs {
     float beta_mul;              // 1, or 2 when negative eigenvalues are allowed
 };
 
+// Copy n fp32 values src -> dst (zeros when src is NULL); nothing when src == dst.
+hipError_t launch_state_copy(const float* src, float* dst, int64_t n, hipStream_t stream);
+
 // dtype codes: 0 = fp32, 1 = bf16; ib_dtype -1 = no intermediate buffer.  gated needs !per_k.
+// Requires a.T >= 1.
 hipError_t launch_recurrent(const RecurrentArgs& a, int K, int io_dtype, int st_dtype, int ib_dtype,
                             bool per_k, bool gated, hipStream_t stream);
 

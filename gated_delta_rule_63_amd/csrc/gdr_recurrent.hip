@@ -29,8 +29,12 @@
 
 namespace gdr {
 
-template <int K, typename IO, typename ST, typename DT, typename IB, bool PER_K, int SLOTS, bool PF, bool GATED>
+// GATE: 0 = g and beta given; 1 = gating front (g, beta from a, b); 2 = gating front and q/k
+// l2 normalisation.  The normalisation is a template choice, not a runtime branch, so the
+// token loop stays one basic block and its loads issue together.
+template <int K, typename IO, typename ST, typename DT, typename IB, bool PER_K, int SLOTS, bool PF, int GATE>
 __global__ __launch_bounds__(256) void recurrent_kernel(const RecurrentArgs a) {
+    constexpr bool GATED = GATE > 0;
     static_assert(!(GATED && PER_K), "the gating front defines a scalar decay only");
     constexpr int EPL = K / 16;                                  // key channels per lane
     constexpr int VW = (16 / Elem<ST>::bytes) < EPL ? (16 / Elem<ST>::bytes) : EPL;
@@ -64,24 +68,6 @@ __global__ __launch_bounds__(256) void recurrent_kernel(const RecurrentArgs a) {
 #pragma unroll
     for (int u = 0; u < UNITS; ++u) cols[u] = (u * 16 + j) * VW;
 
-    float S[SLOTS][EPL];
-    const int64_t sbase = (((int64_t)slot * a.HV + h) * a.V + row0) * K;
-    if (a.src) {
-#pragma unroll
-        for (int s = 0; s < SLOTS; ++s)
-#pragma unroll
-            for (int u = 0; u < UNITS; ++u) Vec<ST, VW>::load(a.src, sbase + (int64_t)s * K + cols[u], &S[s][u * VW]);
-    } else {
-#pragma unroll
-        for (int s = 0; s < SLOTS; ++s)
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) S[s][e] = 0.0f;
-    }
-
-    const int64_t ib_row = a.ibuf ? (int64_t)a.ibuf_idx[n] * a.cache_steps : 0;
-    const float neg_exp_a_log = GATED ? -exp_f32(a.A_log[h]) : 0.0f;
-    const float dt_bias = GATED ? a.dt_bias[h] : 0.0f;
-
     // one token's inputs, raw; the next token's are loaded while the current one computes
     struct TokIn {
         RawVec<IO, VW> k[UNITS], q[UNITS];
@@ -110,20 +96,48 @@ __global__ __launch_bounds__(256) void recurrent_kernel(const RecurrentArgs a) {
         x.b.load(GATED ? a.gb : a.beta, th);
         x.v.load(a.v, th * a.V + row0);
     };
+    // The first token's inputs are requested before the state and without a branch, so a
+    // sequence's first token waits for one round trip to memory, not two.  An empty sequence
+    // reads a valid token it never uses (the launch guarantees T >= 1).
     TokIn nxt;
-    if (PF && bos < eos) load_tok(bos, nxt);
-    // Drain the state and first-token loads here, where they are needed anyway.  Otherwise the
-    // wait-count pass merges their pending state into the loop head and every token would wait
-    // for the previous token's stores before it touches its prefetched inputs.
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt left at their maximum
+    load_tok(bos < eos ? bos : a.T - 1, nxt);
+
+    // per-head gate constants, read before the state so their latency overlaps its loads
+    const float neg_exp_a_log = GATED ? -exp_f32(a.A_log[h]) : 0.0f;
+    const float dt_bias = GATED ? a.dt_bias[h] : 0.0f;
+
+    // The workgroup's state tile (BV rows of K) is read through a buffer resource that spans the
+    // tile, or nothing when there is no source state: reads then return zeros, so the start state
+    // needs no branch and its loads schedule together with the first token's.
+    float S[SLOTS][EPL];
+    const int64_t sbase = (((int64_t)slot * a.HV + h) * a.V + row0) * K;
+    {
+        const int64_t tile = (((int64_t)slot * a.HV + h) * a.V + vt * BV) * K;
+        const char* tile_ptr = a.src ? static_cast<const char*>(a.src) + tile * Elem<ST>::bytes : nullptr;
+        const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<char*>(tile_ptr), 0, a.src ? BV * K * Elem<ST>::bytes : 0, 0x00020000);
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s)
+#pragma unroll
+            for (int u = 0; u < UNITS; ++u)
+                BufVec<ST, VW>::load(srs, (uint32_t)(((rg * SLOTS + s) * K + cols[u]) * Elem<ST>::bytes), &S[s][u * VW]);
+    }
+
+    const int64_t ib_row = a.ibuf ? (int64_t)a.ibuf_idx[n] * a.cache_steps : 0;
+
+    if constexpr (PF) {
+        // Drain the state and first-token loads here, where they are needed anyway.  Otherwise
+        // the wait-count pass merges their pending state into the loop head and every token
+        // would wait for the previous token's stores before it touches its prefetched inputs.
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt left at their maximum
+    }
 
     for (int64_t t = bos; t < eos; ++t) {
-        TokIn cur;
+        // PF: token t+1's loads are issued now and overlap token t's work.  Otherwise (one token
+        // per sequence, decode) they are issued after it, so two tokens' inputs are never live.
+        TokIn cur = nxt;
         if constexpr (PF) {
-            cur = nxt;
             if (t + 1 < eos) load_tok(t + 1, nxt);
-        } else {
-            load_tok(t, cur);
         }
         const int64_t th = t * a.HV + h;
         float kk[EPL], qq[EPL], al[EPL];
@@ -146,20 +160,20 @@ __global__ __launch_bounds__(256) void recurrent_kernel(const RecurrentArgs a) {
         float bt = cur.b.get();
         if constexpr (GATED) {
             bt = a.beta_mul * sigmoid_f32(bt);
-            if (a.qk_l2norm) {  // uniform over the launch
-                float sk = 0.0f, sq = 0.0f;
+        }
+        if constexpr (GATE == 2) {
+            float sk = 0.0f, sq = 0.0f;
 #pragma unroll
-                for (int e = 0; e < EPL; ++e) {
-                    sk = fmaf(kk[e], kk[e], sk);
-                    sq = fmaf(qq[e], qq[e], sq);
-                }
-                const float rk = rsqrtf(row16_sum(sk) + a.l2_eps);
-                const float rq = rsqrtf(row16_sum(sq) + a.l2_eps);
+            for (int e = 0; e < EPL; ++e) {
+                sk = fmaf(kk[e], kk[e], sk);
+                sq = fmaf(qq[e], qq[e], sq);
+            }
+            const float rk = rsqrtf(row16_sum(sk) + a.l2_eps);
+            const float rq = rsqrtf(row16_sum(sq) + a.l2_eps);
 #pragma unroll
-                for (int e = 0; e < EPL; ++e) {
-                    kk[e] *= rk;
-                    qq[e] *= rq;
-                }
+            for (int e = 0; e < EPL; ++e) {
+                kk[e] *= rk;
+                qq[e] *= rq;
             }
         }
         float vv[SLOTS];
@@ -206,6 +220,9 @@ __global__ __launch_bounds__(256) void recurrent_kernel(const RecurrentArgs a) {
 #pragma unroll
                 for (int u = 0; u < UNITS; ++u) Vec<IB, VW>::store(a.ibuf, ib + (int64_t)s * K + cols[u], &S[s][u * VW]);
         }
+        if constexpr (!PF) {
+            if (t + 1 < eos) load_tok(t + 1, nxt);
+        }
     }
 
     if (a.dst) {
@@ -216,49 +233,64 @@ __global__ __launch_bounds__(256) void recurrent_kernel(const RecurrentArgs a) {
     }
 }
 
+// Empty batch with a final state requested: final = initial (or zeros), fp32.
+__global__ __launch_bounds__(256) void state_copy_kernel(const float* __restrict__ src, float* __restrict__ dst,
+                                                         int64_t n) {
+    for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+        dst[i] = src ? src[i] : 0.0f;
+}
+
+hipError_t launch_state_copy(const float* src, float* dst, int64_t n, hipStream_t stream) {
+    if (n <= 0 || src == dst) return hipSuccess;
+    const int64_t blocks = (n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536;
+    hipLaunchKernelGGL(state_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, src, dst, n);
+    return hipGetLastError();
+}
+
 namespace {
 
 constexpr int kSlots = 4;  // BV = 64 rows per workgroup
 
-template <int K, typename IO, typename ST, typename DT, typename IB, bool PER_K, bool GATED>
+template <int K, typename IO, typename ST, typename DT, typename IB, bool PER_K, int GATE>
 hipError_t launch_t(const RecurrentArgs& a, hipStream_t stream) {
     dim3 grid(a.V / (16 * kSlots), a.HV, a.N);
     if (a.prefetch)
-        hipLaunchKernelGGL((recurrent_kernel<K, IO, ST, DT, IB, PER_K, kSlots, true, GATED>), grid, dim3(256), 0,
+        hipLaunchKernelGGL((recurrent_kernel<K, IO, ST, DT, IB, PER_K, kSlots, true, GATE>), grid, dim3(256), 0,
                            stream, a);
     else
-        hipLaunchKernelGGL((recurrent_kernel<K, IO, ST, DT, IB, PER_K, kSlots, false, GATED>), grid, dim3(256), 0,
+        hipLaunchKernelGGL((recurrent_kernel<K, IO, ST, DT, IB, PER_K, kSlots, false, GATE>), grid, dim3(256), 0,
                            stream, a);
     return hipGetLastError();
 }
 
-template <int K, typename IO, typename ST, typename DT, bool PER_K, bool GATED>
+template <int K, typename IO, typename ST, typename DT, bool PER_K, int GATE>
 hipError_t launch_ib(const RecurrentArgs& a, int ib_dtype, hipStream_t stream) {
-    if (ib_dtype < 0) return launch_t<K, IO, ST, DT, void, PER_K, GATED>(a, stream);
-    if (ib_dtype == 0) return launch_t<K, IO, ST, DT, float, PER_K, GATED>(a, stream);
-    return launch_t<K, IO, ST, DT, bf16_t, PER_K, GATED>(a, stream);
+    if (ib_dtype < 0) return launch_t<K, IO, ST, DT, void, PER_K, GATE>(a, stream);
+    if (ib_dtype == 0) return launch_t<K, IO, ST, DT, float, PER_K, GATE>(a, stream);
+    return launch_t<K, IO, ST, DT, bf16_t, PER_K, GATE>(a, stream);
 }
 
-template <int K, typename IO, bool PER_K, bool GATED>
+template <int K, typename IO, bool PER_K, int GATE>
 hipError_t launch_st(const RecurrentArgs& a, int st_dtype, int ib_dtype, hipStream_t stream) {
     // state source and destination share a dtype (pool) except in the dense mode,
     // where both are fp32
-    if (st_dtype == 0) return launch_ib<K, IO, float, float, PER_K, GATED>(a, ib_dtype, stream);
-    return launch_ib<K, IO, bf16_t, bf16_t, PER_K, GATED>(a, ib_dtype, stream);
+    if (st_dtype == 0) return launch_ib<K, IO, float, float, PER_K, GATE>(a, ib_dtype, stream);
+    return launch_ib<K, IO, bf16_t, bf16_t, PER_K, GATE>(a, ib_dtype, stream);
 }
 
-template <int K, bool PER_K, bool GATED>
+template <int K, bool PER_K, int GATE>
 hipError_t launch_io(const RecurrentArgs& a, int io_dtype, int st_dtype, int ib_dtype, hipStream_t stream) {
-    if (io_dtype == 0) return launch_st<K, float, PER_K, GATED>(a, st_dtype, ib_dtype, stream);
-    return launch_st<K, bf16_t, PER_K, GATED>(a, st_dtype, ib_dtype, stream);
+    if (io_dtype == 0) return launch_st<K, float, PER_K, GATE>(a, st_dtype, ib_dtype, stream);
+    return launch_st<K, bf16_t, PER_K, GATE>(a, st_dtype, ib_dtype, stream);
 }
 
 template <int K>
 hipError_t launch_k(const RecurrentArgs& a, int io_dtype, int st_dtype, int ib_dtype, bool per_k, bool gated,
                     hipStream_t stream) {
-    if (per_k) return launch_io<K, true, false>(a, io_dtype, st_dtype, ib_dtype, stream);
-    if (gated) return launch_io<K, false, true>(a, io_dtype, st_dtype, ib_dtype, stream);
-    return launch_io<K, false, false>(a, io_dtype, st_dtype, ib_dtype, stream);
+    if (per_k) return launch_io<K, true, 0>(a, io_dtype, st_dtype, ib_dtype, stream);
+    if (gated && a.qk_l2norm) return launch_io<K, false, 2>(a, io_dtype, st_dtype, ib_dtype, stream);
+    if (gated) return launch_io<K, false, 1>(a, io_dtype, st_dtype, ib_dtype, stream);
+    return launch_io<K, false, 0>(a, io_dtype, st_dtype, ib_dtype, stream);
 }
 
 }  // namespace
@@ -266,6 +298,7 @@ hipError_t launch_k(const RecurrentArgs& a, int io_dtype, int st_dtype, int ib_d
 hipError_t launch_recurrent(const RecurrentArgs& a, int K, int io_dtype, int st_dtype, int ib_dtype,
                             bool per_k, bool gated, hipStream_t stream) {
     if (per_k && gated) return hipErrorInvalidValue;
+    if (a.T < 1) return hipErrorInvalidValue;  // the kernel reads one token per sequence up front
     if (K == 64) return launch_k<64>(a, io_dtype, st_dtype, ib_dtype, per_k, gated, stream);
     return launch_k<128>(a, io_dtype, st_dtype, ib_dtype, per_k, gated, stream);
 }
