@@ -12,9 +12,10 @@ already resident in HBM:
   verify   gdr_decode_paged  64 sequences x 12 tokens, bf16 pool, bf16 per-token states
                              [1025, 12, 32, 128, 128], no commit  (speculative verify)
 
-After the step, three legs outside it are timed the same way: the decode and verify launches
+After the step, four legs outside it are timed the same way: the decode and verify launches
 with the gating front fused into the token loop (raw q, k, a, b in; gdr_decode_paged_gated),
-and the gating pass followed by the plain verify launch (gdr_gating_prepass + gdr_decode_paged).
+the gating pass followed by the plain verify launch (gdr_gating_prepass + gdr_decode_paged),
+and the per-channel-gate (KDA) chunked forward over one sequence of 65573 tokens, 16 heads.
 
 The JSON line reports prefill tokens/s as ``value`` and the decode state GB/s beside it,
 each leg's time from HIP events recorded on the stream the library launches on (torch's
@@ -43,10 +44,13 @@ BF16_MFMA_PEAK = 2.5e15    # dense flop/s
 
 
 def _alg_bytes_prefill(p):
-    """q, k, v, o (io dtype) + g fp32 + beta (io dtype) per token-head, initial + final state, cu_seqlens."""
+    """q, k, v, o (io dtype) + g fp32 (per key channel for the per-K gate) + beta (io dtype) per
+    token-head, initial (if given) + final state, cu_seqlens."""
     io = 2 if p.io_dtype == "bf16" else 4
-    per_tok = p.HK * p.K * io * 2 + p.HV * p.V * io * 2 + p.HV * 4 + p.HV * io
-    return p.T * per_tok + 2 * p.N * p.HV * p.V * p.K * 4 + 4 * (p.N + 1)
+    gate = p.HV * p.K * 4 if p.per_k_gate else p.HV * 4
+    per_tok = p.HK * p.K * io * 2 + p.HV * p.V * io * 2 + gate + p.HV * io
+    states = (2 if p.initial_state is not None else 1) * p.N * p.HV * p.V * p.K * 4
+    return p.T * per_tok + states + 4 * (p.N + 1)
 
 
 def _alg_flops_prefill(p, full_tile=False):
@@ -159,9 +163,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--legs", default="prefill,decode,verify",
                     help="comma-separated subset of legs to run (profiling passes); the JSON line needs all three")
-    ap.add_argument("--extra-legs", default="decode_gated,verify_gated,verify_prepass",
+    ap.add_argument("--extra-legs", default="decode_gated,verify_gated,verify_prepass,kda",
                     help="legs outside the step, timed after it: the gating front fused into the decode and verify "
-                         "launches, and the gating pass followed by the plain verify launch ('' for none)")
+                         "launches, the gating pass followed by the plain verify launch, and the per-channel-gate "
+                         "(KDA) chunked forward over one 65573-token sequence ('' for none)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before the legs, run one device-to-device copy of this many MiB (a plain copy kernel of "
                          "known size, used to scale the HBM byte counters of a profiling pass) and stop after the legs")
@@ -220,6 +225,19 @@ def main():
           "g": torch.empty((pv.T, pv.HV), dtype=torch.float32, device=dev),
           "beta": torch.empty((pv.T, pv.HV), dtype=torch.bfloat16, device=dev)}
 
+    K_ = None
+    if "kda" in args.extra_legs.split(","):
+        pk = inputs.kda()
+        K_ = {k: to_dev(getattr(pk, k)) for k in ("q", "k", "v", "g", "beta")}
+        K_["o"] = torch.empty((pk.T, pk.HV, pk.V), dtype=torch.bfloat16, device=dev)
+        K_["ht"] = torch.empty((pk.N, pk.HV, pk.V, pk.K), dtype=torch.float32, device=dev)
+        K_["ws"] = torch.empty(max(256, gdr.gdr_chunk_workspace_size(K_["q"], K_["v"], K_["g"], pk.N)),
+                               dtype=torch.uint8, device=dev)
+
+    def kda():
+        gdr.gdr_chunk_fwd(K_["q"], K_["k"], K_["v"], K_["g"], K_["beta"], None, pk.scale, None, o=K_["o"],
+                          final_state=K_["ht"], workspace=K_["ws"])
+
     def prefill():
         gdr.gdr_chunk_fwd(P["q"], P["k"], P["v"], P["g"], P["beta"], P["cu"], pp.scale, P["h0"], o=P["o"],
                           final_state=P["ht"], workspace=P["ws"])
@@ -254,7 +272,7 @@ def main():
     legs = [(n, f) for n, f in (("prefill", prefill), ("decode", decode), ("verify", verify))
             if n in args.legs.split(",")]
     extra = [(n, f) for n, f in (("decode_gated", decode_gated), ("verify_gated", verify_gated),
-                                 ("verify_prepass", verify_prepass)) if n in args.extra_legs.split(",")]
+                                 ("verify_prepass", verify_prepass), ("kda", kda)) if n in args.extra_legs.split(",")]
     if args.calib_copy_mib:
         n = args.calib_copy_mib << 20
         src = torch.ones(n // 4, dtype=torch.float32, device=dev)
@@ -345,6 +363,10 @@ def main():
                                       "bytes": _alg_bytes_prepass(pv) + b_ver, "flops": None,
                                       "secs": extra_ms["verify_prepass"] / 1e3,
                                       "sources": ["gdr_gating.hip"] + gated_sources}
+    if "kda" in extra_ms:
+        leg_info["kda"] = {"kernel": "chunk_fused_kernel<128,128,bf16,per-K gate> (1 x 65573 tokens, 16 heads)",
+                           "bytes": _alg_bytes_prefill(pk), "flops": None, "secs": extra_ms["kda"] / 1e3,
+                           "sources": ["gdr_chunk.hip", "gdr_device.h"]}
     traffic = _measured_traffic()
 
     def roofline(leg):
@@ -374,6 +396,8 @@ def main():
     roof = roofline(dominant)
     roof_legs = {n: roofline(n) for n in step_legs}
     extra_legs = {n: {"ms": extra_ms[n], "roofline": roofline(n)} for n in extra_ms}
+    if "kda" in extra_legs:
+        extra_legs["kda"]["tokens_per_s"] = pk.T / (extra_ms["kda"] / 1e3)
     roof_legs["prefill"]["frac_bf16_mfma_full_tile"] = f_pre_full / s_pre / BF16_MFMA_PEAK
     roof_legs["prefill"]["alg_flops_full_tile"] = f_pre_full
     roof_legs["decode"]["state_GBps"] = state_bytes_dec / s_dec / 1e9

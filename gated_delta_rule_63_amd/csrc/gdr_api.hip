@@ -212,10 +212,9 @@ gdr_status gdr_gating_prepass(const gdr_problem* p, const void* q, const void* k
 
 size_t gdr_chunk_workspace_size(const gdr_problem* p, int32_t chunk_size) {
     if (check_problem(p) != GDR_SUCCESS || chunk_size != 64) return 0;
-    return gdr::chunk_workspace_layout(p->total_tokens, p->num_seqs, p->num_v_heads, p->head_dim_k,
-                                       p->head_dim_v, p->io_dtype == GDR_BF16 ? 2 : 4,
-                                       p->gate == GDR_GATE_PER_K)
-        .total;
+    const gdr::CpPlan pl = gdr::cp_plan(p->total_tokens, p->num_seqs, p->num_v_heads, p->head_dim_k,
+                                        p->head_dim_v, p->io_dtype == GDR_BF16 ? 2 : 4);
+    return pl.P > 1 ? pl.total : 0;
 }
 
 gdr_status gdr_chunk_fwd(const gdr_problem* p, int32_t chunk_size, const void* q, const void* k, const void* v,
@@ -240,10 +239,7 @@ gdr_status gdr_chunk_fwd(const gdr_problem* p, int32_t chunk_size, const void* q
     if ((st = check_device()) != GDR_SUCCESS) return st;
 
     const bool per_k = p->gate == GDR_GATE_PER_K;
-    const int io_bytes = p->io_dtype == GDR_BF16 ? 2 : 4;
-    const gdr::ChunkWorkspaceLayout L = gdr::chunk_workspace_layout(p->total_tokens, p->num_seqs, p->num_v_heads,
-                                                                   p->head_dim_k, p->head_dim_v, io_bytes, per_k);
-    char* ws = static_cast<char*>(workspace);
+    const hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     gdr::ChunkArgs a{};
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
     a.cu_seqlens = cu_seqlens;
@@ -253,15 +249,43 @@ gdr_status gdr_chunk_fwd(const gdr_problem* p, int32_t chunk_size, const void* q
     a.T = p->total_tokens;
     a.N = p->num_seqs; a.HK = p->num_k_heads; a.HV = p->num_v_heads; a.K = p->head_dim_k; a.V = p->head_dim_v;
     a.scale = p->scale;
-    a.max_chunks = (int32_t)(p->total_tokens / 64 + p->num_seqs);
-    a.chunk_seq = reinterpret_cast<int32_t*>(ws + L.chunk_seq);
-    a.chunk_first = reinterpret_cast<int32_t*>(ws + L.chunk_first);
-    a.gcum = reinterpret_cast<float*>(ws + L.gcum);
-    a.w = ws + L.w;
-    a.u = ws + L.u;
-    a.vnew = ws + L.vnew;
-    a.hc = ws + L.hc;
-    return status_of(gdr::launch_chunk(a, p->io_dtype, per_k, static_cast<hipStream_t>(hip_stream)));
+
+    const gdr::CpPlan pl = gdr::cp_plan(p->total_tokens, p->num_seqs, p->num_v_heads, p->head_dim_k,
+                                        p->head_dim_v, p->io_dtype == GDR_BF16 ? 2 : 4);
+    if (pl.P <= 1) return status_of(gdr::launch_chunk(a, p->io_dtype, per_k, stream));
+
+    // One long sequence, few heads: cut it into P segments and run them in parallel.
+    //   1. B_s = end state of segment s from zero; M_s = end state of segment s from the identity
+    //      with v = 0 (the K x K linear part of its map), for s < P - 1; outputs discarded
+    //   2. scan: S_0 = initial state, S_{s+1} = S_s M_s + B_s
+    //   3. every segment from its true start state: outputs, and the end state in place
+    char* ws = static_cast<char*>(workspace);
+    const int32_t* cu_seg = reinterpret_cast<const int32_t*>(ws + pl.cu_seg);
+    float* Bs = reinterpret_cast<float*>(ws + pl.B);
+    float* Ms = reinterpret_cast<float*>(ws + pl.M);
+    float* Ss = reinterpret_cast<float*>(ws + pl.S);
+    hipError_t e = gdr::launch_cp_setup(pl, ws, p->total_tokens, p->num_v_heads, p->head_dim_k, stream);
+    if (e != hipSuccess) return status_of(e);
+
+    gdr::ChunkArgs b = a;  // 1a: offsets B_s
+    b.cu_seqlens = cu_seg; b.N = pl.P - 1; b.h0 = nullptr; b.o = nullptr; b.ht = Bs;
+    if ((e = gdr::launch_chunk(b, p->io_dtype, per_k, stream)) != hipSuccess) return status_of(e);
+
+    gdr::ChunkArgs m = a;  // 1b: linear parts M_s (a K-row state, v = 0), in place from the identity
+    m.cu_seqlens = cu_seg; m.N = pl.P - 1; m.v = nullptr; m.V = p->head_dim_k; m.h0 = Ms; m.o = nullptr; m.ht = Ms;
+    if ((e = gdr::launch_chunk(m, p->io_dtype, per_k, stream)) != hipSuccess) return status_of(e);
+
+    e = gdr::launch_cp_scan(pl, ws, initial_state, p->num_v_heads, p->head_dim_k, p->head_dim_v, stream);
+    if (e != hipSuccess) return status_of(e);
+
+    gdr::ChunkArgs f = a;  // 3: outputs from the true start states; end states in place
+    f.cu_seqlens = cu_seg; f.N = pl.P; f.h0 = Ss; f.ht = Ss;
+    if ((e = gdr::launch_chunk(f, p->io_dtype, per_k, stream)) != hipSuccess) return status_of(e);
+    if (final_state) {
+        const int64_t hvk = (int64_t)p->num_v_heads * p->head_dim_v * p->head_dim_k;
+        e = gdr::launch_state_copy(Ss + (int64_t)(pl.P - 1) * hvk, final_state, hvk, stream);
+    }
+    return status_of(e);
 }
 
 }  // extern "C"

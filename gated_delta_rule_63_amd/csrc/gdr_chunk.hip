@@ -782,8 +782,9 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
     auto load_vgb = [&](int ci) {
         const int64_t bos = s0 + (int64_t)CH * ci;
         const int len = chunk_len(ci);
-        const __amdgpu_buffer_rsrc_t rv =
-            chunk_rsrc(static_cast<const char*>(a.v) + ((bos * a.HV + h) * a.V + v0) * ESZ, len, v_row);
+        // v == NULL reads as zeros (a zero-byte range): the run that forms a segment's linear map
+        const __amdgpu_buffer_rsrc_t rv = chunk_rsrc(
+            a.v ? static_cast<const char*>(a.v) + ((bos * a.HV + h) * a.V + v0) * ESZ : nullptr, a.v ? len : 0, v_row);
 #pragma unroll
         for (int i = 0; i < PV::NPASS; ++i)
 #pragma unroll
@@ -816,6 +817,7 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
     // staged output rows of a chunk -> o, one 16-byte granule per thread and pass
     char* const so = smem + Lay::o_stage;
     auto flush_o = [&](int64_t bos, int len) {
+        if (!a.o) return;  // outputs not wanted (the segment-map runs)
         for (int idx = tid; idx < CH * OS::NG; idx += NTHR) {
             const int r = idx / OS::NG, gi = idx % OS::NG;
             if (r < len) {
@@ -1277,12 +1279,6 @@ hipError_t launch_kv(const ChunkArgs& a, int io, bool per_k, hipStream_t s) {
 }
 
 }  // namespace
-
-ChunkWorkspaceLayout chunk_workspace_layout(int64_t, int32_t, int32_t, int32_t, int32_t, int, bool) {
-    ChunkWorkspaceLayout L{};
-    L.total = 0;  // the fused path keeps every intermediate on chip
-    return L;
-}
 
 hipError_t launch_chunk(const ChunkArgs& a, int io_dtype, bool per_k, hipStream_t stream) {
     if (a.K == 64) {

@@ -73,34 +73,35 @@ hipError_t launch_gating(const GatingArgs& a, int K, int io_dtype, hipStream_t s
 struct ChunkArgs {
     const void* q;
     const void* k;
-    const void* v;
+    const void* v;               // NULL reads as zeros
     const float* g;
     const void* beta;
     const int32_t* cu_seqlens;   // NULL only when N == 1
-    const float* h0;             // [N, HV, V, K] or NULL
-    void* o;
-    float* ht;                   // [N, HV, V, K] or NULL
+    const float* h0;             // [N, HV, V, K] or NULL (zeros)
+    void* o;                     // NULL: outputs not written
+    float* ht;                   // [N, HV, V, K] or NULL; may equal h0 (each thread reads its part first)
     int64_t T;
     int32_t N, HK, HV, K, V;
     float scale;
-    int32_t max_chunks;          // upper bound on the number of chunks: T/64 + N
-    // workspace views
-    int32_t* chunk_seq;          // [max_chunks] sequence of each chunk, -1 unused
-    int32_t* chunk_first;        // [N + 1] index of each sequence's first chunk
-    float* gcum;                 // [T, HV] or [T, HV, K] chunk-local cumulative gate
-    void* w;                     // [T, HV, K] io dtype
-    void* u;                     // [T, HV, V] io dtype
-    void* vnew;                  // [T, HV, V] io dtype
-    void* hc;                    // [max_chunks, HV, V, K] io dtype: state at each chunk start
 };
-
-struct ChunkWorkspaceLayout {
-    size_t chunk_seq, chunk_first, gcum, w, u, vnew, hc, total;
-};
-
-ChunkWorkspaceLayout chunk_workspace_layout(int64_t T, int32_t N, int32_t HV, int32_t K, int32_t V,
-                                            int io_bytes, bool per_k);
 
 hipError_t launch_chunk(const ChunkArgs& a, int io_dtype, bool per_k, hipStream_t stream);
+
+// Context parallelism for one long sequence (gdr_cp.hip): the sequence is cut into P segments of
+// seg_tokens tokens (a multiple of 64; the last may be shorter) and run as P sequences.
+constexpr int kCpWorkgroups = 256;   // target chunk-kernel workgroups per run: one per CU of the part
+constexpr int kCpMinChunks = 8;      // at least this many chunks per segment
+constexpr int kCpMinSegments = 6;    // below this the three runs cost more than they save
+
+struct CpPlan {
+    int P;                           // segments; 1 = no context parallelism
+    int64_t seg_tokens;
+    size_t cu_seg, B, M, S, total;   // workspace offsets (256-byte aligned) and size
+};
+
+CpPlan cp_plan(int64_t T, int32_t N, int32_t HV, int32_t K, int32_t V, int io_bytes);
+hipError_t launch_cp_setup(const CpPlan& pl, char* ws, int64_t T, int32_t HV, int32_t K, hipStream_t stream);
+hipError_t launch_cp_scan(const CpPlan& pl, char* ws, const float* h0, int32_t HV, int32_t K, int32_t V,
+                          hipStream_t stream);
 
 }  // namespace gdr
