@@ -145,6 +145,76 @@ __device__ __forceinline__ int perm(int c) {
         return c;
 }
 
+// Logical column of physical column p (the inverse of perm).
+template <typename MT>
+__device__ __forceinline__ int iperm(int p) {
+    if constexpr (sizeof(typename MM<MT>::S) == 2)
+        return (p & ~31) | (((p >> 2) & 1) << 4) | (((p >> 3) & 3) << 2) | (p & 3);
+    else
+        return p;
+}
+
+// c0 += A0 B'^T and c1 += A1 B'^T over KD columns (16-row tiles from LDS, as MM::nt), where B'
+// is B with every column multiplied by f[column] (fp32, physical column order; NULL: none).  The
+// two products share the scaled B operand, and every operand read is issued before the first
+// product.
+template <typename MT, int KD>
+__device__ __forceinline__ void nt2_bscaled(f32x4_t& c0, const typename MM<MT>::S* a0, f32x4_t& c1,
+                                            const typename MM<MT>::S* a1, int lda, const typename MM<MT>::S* b,
+                                            int ldb, const float* f) {
+    const int l = threadIdx.x & 63;
+    if constexpr (sizeof(typename MM<MT>::S) == 2) {
+        // in halves of at most 64 columns: the operands of one half are in flight at a time, which
+        // bounds the registers this needs inside a kernel that holds its state in registers
+        constexpr int NS = KD > 64 ? 2 : KD / 32;
+        const int oa = (l & 15) * lda + 8 * (l >> 4), ob = (l & 15) * ldb + 8 * (l >> 4), of = 8 * (l >> 4);
+#pragma unroll
+        for (int h0 = 0; h0 < KD; h0 += 32 * NS) {
+        bf16x8_t va0[NS], va1[NS];
+        uint4 vb[NS];
+        f32x4_t f0[NS], f1[NS];
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            va0[s] = *reinterpret_cast<const bf16x8_t*>(a0 + oa + h0 + 32 * s);
+            va1[s] = *reinterpret_cast<const bf16x8_t*>(a1 + oa + h0 + 32 * s);
+            vb[s] = *reinterpret_cast<const uint4*>(b + ob + h0 + 32 * s);
+            if (f) {
+                f0[s] = *reinterpret_cast<const f32x4_t*>(f + of + h0 + 32 * s);
+                f1[s] = *reinterpret_cast<const f32x4_t*>(f + of + h0 + 32 * s + 4);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            uint4 w = vb[s];
+            if (f) {
+                w.x = pack_bf16x2(__uint_as_float(w.x << 16) * f0[s][0], __uint_as_float(w.x & 0xFFFF0000u) * f0[s][1]);
+                w.y = pack_bf16x2(__uint_as_float(w.y << 16) * f0[s][2], __uint_as_float(w.y & 0xFFFF0000u) * f0[s][3]);
+                w.z = pack_bf16x2(__uint_as_float(w.z << 16) * f1[s][0], __uint_as_float(w.z & 0xFFFF0000u) * f1[s][1]);
+                w.w = pack_bf16x2(__uint_as_float(w.w << 16) * f1[s][2], __uint_as_float(w.w & 0xFFFF0000u) * f1[s][3]);
+            }
+            const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, w);
+            c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va0[s], bv, c0, 0, 0, 0);
+            c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va1[s], bv, c1, 0, 0, 0);
+        }
+        }
+    } else {
+        constexpr int NS = KD / 4;
+        const int oa = (l & 15) * lda + (l >> 4), ob = (l & 15) * ldb + (l >> 4);
+        float va0[NS], va1[NS], vb[NS];
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            va0[s] = a0[oa + 4 * s];
+            va1[s] = a1[oa + 4 * s];
+            vb[s] = f ? b[ob + 4 * s] * f[4 * s + (l >> 4)] : b[ob + 4 * s];
+        }
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            c0 = __builtin_amdgcn_mfma_f32_16x16x4f32(va0[s], vb[s], c0, 0, 0, 0);
+            c1 = __builtin_amdgcn_mfma_f32_16x16x4f32(va1[s], vb[s], c1, 0, 0, 0);
+        }
+    }
+}
+
 __device__ __forceinline__ uint32_t pack_tile_lo(const f32x4_t& t) { return pack_bf16x2(t[0], t[1]); }
 __device__ __forceinline__ uint32_t pack_tile_hi(const f32x4_t& t) { return pack_bf16x2(t[2], t[3]); }
 
@@ -284,25 +354,6 @@ __device__ __forceinline__ void st_pair_t(typename MM<MT>::S* dst, int ldt, int 
         for (int e = 0; e < 8; ++e) {
             dst[(c8 + e) * ldt + perm<MT>(r0)] = MM<MT>::cvt(a[e]);
             dst[(c8 + e) * ldt + perm<MT>(r0 + 1)] = MM<MT>::cvt(b[e]);
-        }
-    }
-}
-
-// Scaled transposed store of a row pair: dst[(c8 + e) * ldt + perm(r)] = x_r[e] * f(r, c8 + e).
-template <typename MT, typename IO, typename F>
-__device__ __forceinline__ void st_pair_t_scaled(typename MM<MT>::S* dst, int ldt, int c8, int r0,
-                                                 const Raw8<IO>& x0, const Raw8<IO>& x1, F f) {
-    float a[8], b[8];
-    x0.get(a);
-    x1.get(b);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const float ya = a[e] * f(r0, c8 + e), yb = b[e] * f(r0 + 1, c8 + e);
-        if constexpr (sizeof(typename MM<MT>::S) == 2) {
-            *reinterpret_cast<uint32_t*>(dst + (c8 + e) * ldt + perm<MT>(r0)) = pack_bf16x2(ya, yb);
-        } else {
-            dst[(c8 + e) * ldt + r0] = ya;
-            dst[(c8 + e) * ldt + r0 + 1] = yb;
         }
     }
 }
@@ -652,14 +703,14 @@ struct Layout {
     static constexpr size_t k_b = k_gl + sizeof(float) * K;           // beta [64]
     static constexpr size_t k_p = k_b + sizeof(float) * CH;           // P rows
     static constexpr size_t X = k_p + ROWT;
-    static constexpr size_t AB = 2 * ROWK + sizeof(S) * 80 * LDK;     // Q, K rows; 16 + 16 + 48 operand rows
+    static constexpr size_t AB = 2 * ROWK + sizeof(S) * 96 * LDK;     // Q, K rows; 16 + 16 + 64 operand rows
     static constexpr size_t CE = KT_ + VT_ + ROWK + KT_;              // (K e^g)^T, V^T, Q e^g, (K e^{gl-g})^T
     static constexpr size_t SX = AB > CE ? AB : CE;
     static constexpr size_t k_q = X;
     static constexpr size_t k_k = k_q + ROWK;
     static constexpr size_t k_lk = k_k + ROWK;                        // K_I e^{gamma - rho}   [16][LDK]
     static constexpr size_t k_lq = k_lk + sizeof(S) * 16 * LDK;       // Q_I e^{gamma - rho}   [16][LDK]
-    static constexpr size_t k_rg = k_lq + sizeof(S) * 16 * LDK;       // K_<I e^{rho - gamma}  [48][LDK]
+    static constexpr size_t k_rg = k_lq + sizeof(S) * 16 * LDK;       // K_<=I e^{rho - gamma} [64][LDK]
     static constexpr size_t k_kgt = X;
     static constexpr size_t k_vt = k_kgt + KT_;
     static constexpr size_t k_qt = k_vt + VT_;
@@ -691,6 +742,11 @@ struct OStage {
         return r * ROWB + gr * 16 + (c % EPG) * SZ;
     }
 };
+
+// Per-channel gate: largest decay range (in natural-log units) across one 16-row diagonal block
+// that the MFMA form of that block accepts; e^64 ~ 6e27 keeps both scaled operands and their
+// products well inside the fp32 / bf16 exponent range.
+constexpr float kKdaDiagRange = 64.0f;
 
 template <int K, int BV, typename IO, typename MT, bool PER_K>
 __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) {
@@ -1031,6 +1087,113 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
             S* sLK = SP(Lay::k_lk);
             S* sLQ = SP(Lay::k_lq);
             S* sRG = SP(Lay::k_rg);
+            // Row block I against blocks J <= I on MFMA, reference point rho = gamma[16I - 1]
+            // (0 for I = 0): e^(gamma_r - gamma_j) = e^(gamma_r - rho) e^(rho - gamma_j).  The left
+            // factor is <= 1; the right one is <= 1 for J < I and exceeds 1 only on block I's own
+            // rows, by at most e^(rho - gamma[16I + 15]).  While that range stays below
+            // kKdaDiagRange on every channel (checked here) both operands stay far inside the bf16 /
+            // fp32 range; otherwise the diagonal blocks are evaluated element-wise and only the
+            // blocks J < I use MFMA.
+            bool wide = false;
+            if (tid < K) {
+#pragma unroll
+                for (int I = 0; I < 4; ++I) {
+                    const float rho = I ? sg[(16 * I - 1) * K + tid] : 0.0f;
+                    wide = wide || (rho - sg[(16 * I + 15) * K + tid] > kKdaDiagRange);
+                }
+            }
+            if (!__syncthreads_or(wide)) {
+                // One pass scales the operands for every block pair, in physical column order:
+                //   left  (in place)  K_r, Q_r times e^(gamma_r - rho_I),  rho_I = gamma[16I - 1] (0 for I = 0)
+                //   right (into sRG)  K_j times e^(rho'_J - gamma_j),      rho'_J = gamma[16J + 15]
+                // and the pair (I, J) multiplies the right operand's columns by
+                //   f_IJ = e^(rho_I - rho'_J): 1 for J = I - 1, <= 1 for J < I - 1, and bounded by
+                //   e^kKdaDiagRange for J = I,
+                // so every product is k_r k_j e^(gamma_r - gamma_j) and every operand stays in range.
+                float* fperm = FP(Lay::k_lk);  // [7][K]: pairs (0,0) (1,1) (2,2) (3,3) (2,0) (3,0) (3,1)
+                static_assert(7 * K * sizeof(float) <= 2 * 16 * LDK * sizeof(S), "pair factors fit the left-operand rows");
+                constexpr int GP = 8;  // physical columns per work unit (16 bytes of bf16, 32 of fp32)
+                for (int u = tid; u < CH * (K / GP); u += NTHR) {
+                    const int r = u / (K / GP), p0 = (u % (K / GP)) * GP, I = r >> 4;
+                    float kv[GP], qv[GP];
+                    if constexpr (Lay::BF) {
+                        const uint4 kw = *reinterpret_cast<const uint4*>(sK + r * LDK + p0);
+                        const uint4 qw = *reinterpret_cast<const uint4*>(sQ + r * LDK + p0);
+                        const uint32_t ka[4] = {kw.x, kw.y, kw.z, kw.w}, qa[4] = {qw.x, qw.y, qw.z, qw.w};
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            kv[2 * i] = __uint_as_float(ka[i] << 16);
+                            kv[2 * i + 1] = __uint_as_float(ka[i] & 0xFFFF0000u);
+                            qv[2 * i] = __uint_as_float(qa[i] << 16);
+                            qv[2 * i + 1] = __uint_as_float(qa[i] & 0xFFFF0000u);
+                        }
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < GP; ++i) {
+                            kv[i] = M::back(sK[r * LDK + p0 + i]);
+                            qv[i] = M::back(sQ[r * LDK + p0 + i]);
+                        }
+                    }
+                    // the 8 physical columns are two runs of 4 logical channels: gamma of row r, of
+                    // row 16I - 1 and of row 16I + 15 come in as 16-byte reads
+                    float gv[GP], rv0[GP], rv1[GP];
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const int c0 = iperm<MT>(p0 + 4 * hh);
+                        const f32x4_t a = *reinterpret_cast<const f32x4_t*>(sg + r * K + c0);
+                        const f32x4_t b = I ? *reinterpret_cast<const f32x4_t*>(sg + (16 * I - 1) * K + c0)
+                                            : f32x4_t{0.f, 0.f, 0.f, 0.f};
+                        const f32x4_t d = *reinterpret_cast<const f32x4_t*>(sg + (16 * I + 15) * K + c0);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            gv[4 * hh + e] = a[e];
+                            rv0[4 * hh + e] = b[e];
+                            rv1[4 * hh + e] = d[e];
+                        }
+                    }
+                    float lk[GP], lq[GP], rk[GP];
+#pragma unroll
+                    for (int i = 0; i < GP; ++i) {
+                        const float el = exp_f32(gv[i] - rv0[i]);
+                        const float er = exp_f32(rv1[i] - gv[i]);
+                        lk[i] = kv[i] * el;
+                        lq[i] = qv[i] * el;
+                        rk[i] = kv[i] * er;
+                    }
+                    M::st8(sK + r * LDK + p0, lk);
+                    M::st8(sQ + r * LDK + p0, lq);
+                    M::st8(sRG + r * LDK + p0, rk);
+                }
+                for (int u = tid; u < 7 * K; u += NTHR) {
+                    const int pi = u / K, pcol = u % K, c = iperm<MT>(pcol);
+                    const int I = pi < 4 ? pi : (pi == 4 ? 2 : 3), J = pi < 4 ? pi : (pi == 6 ? 1 : 0);
+                    const float rho = I ? sg[(16 * I - 1) * K + c] : 0.0f;
+                    fperm[pi * K + pcol] = exp_f32(rho - sg[(16 * J + 15) * K + c]);
+                }
+                __syncthreads();
+                // the pairs (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3); each pair's L and P
+                // tiles share the scaled right operand; wave w takes pairs w and w + NW
+                for (int tp = w; tp < 10; tp += NW) {
+                    const int I = tp < 1 ? 0 : tp < 3 ? 1 : tp < 6 ? 2 : 3;
+                    const int J = tp - I * (I + 1) / 2;
+                    const int fi = J == I ? I : J == I - 1 ? -1 : (I == 2 ? 4 : (J == 0 ? 5 : 6));
+                    f32x4_t cl = {0.f, 0.f, 0.f, 0.f}, cp = {0.f, 0.f, 0.f, 0.f};
+                    nt2_bscaled<MT, K>(cl, sK + 16 * I * LDK, cp, sQ + 16 * I * LDK, LDK, sRG + 16 * J * LDK, LDK,
+                                       fi >= 0 ? fperm + fi * K : nullptr);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int rr = 4 * g4 + e, r = 16 * I + rr, j = 16 * J + lr;
+                        if (J < I) {
+                            sLo[r * LDO + j] = M::cvt(-sb[r] * cl[e]);
+                            sP[r * LDT + perm<MT>(j)] = M::cvt(cp[e]);
+                        } else {  // diagonal blocks: L in fp32, strictly lower, for the inversion; P lower
+                            sLd[I * 16 * LDN + rr * LDN + lr] = (lr < rr) ? sb[r] * cl[e] : 0.0f;
+                            sP[r * LDT + perm<MT>(j)] = M::cvt((lr <= rr) ? cp[e] : 0.0f);
+                        }
+                    }
+                }
+                __syncthreads();
+            } else {
             // diagonal 16x16 blocks, element-wise: (r, j) in the same block, j <= r
             for (int p = tid; p < 4 * 256; p += NTHR) {
                 const int b = p >> 8, rr = (p >> 4) & 15, jj = p & 15;
@@ -1077,21 +1240,48 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
                 }
                 __syncthreads();
             }
+            }
             if (w < 4) invert_unit_lower_16<MT>(sLd + w * 16 * LDN, sD + 16 * w * LDD, LDD);
             // the transposed / scaled operands of D and E, from this chunk's registers
             S* sKgT = SP(Lay::k_kgt);
             S* sVT = SP(Lay::k_vt);
             S* sQt = SP(Lay::k_qt);
             S* sKdT = SP(Lay::k_kdt);
-            const float* sgc = sg;
-            auto f_g = [sgc](int r, int c) { return exp_f32(sgc[r * K + c]); };
-            auto f_d = [sgc](int r, int c) { return exp_f32(sgc[(CH - 1) * K + c] - sgc[r * K + c]); };
+            // 8 consecutive channels of gamma in two 16-byte reads
+            auto g8 = [&](int r, int c8, float* x) {
+                const f32x4_t a = *reinterpret_cast<const f32x4_t*>(sg + r * K + c8);
+                const f32x4_t b = *reinterpret_cast<const f32x4_t*>(sg + r * K + c8 + 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    x[e] = a[e];
+                    x[4 + e] = b[e];
+                }
+            };
+            // (K e^gamma)^T and (K e^(gamma_last - gamma))^T, a row pair per thread and pass
 #pragma unroll
             for (int i = 0; i < PK::NPASS; ++i) {
                 if (PK::valid(tid, i)) {
                     const int c8 = PK::col(tid, i), pr0 = 2 * PK::pair(tid, i);
-                    st_pair_t_scaled<MT, IO>(sKgT, LDT, c8, pr0, kr[2 * i], kr[2 * i + 1], f_g);
-                    st_pair_t_scaled<MT, IO>(sKdT, LDT, c8, pr0, kr[2 * i], kr[2 * i + 1], f_d);
+                    float ka[8], kb[8], ga[8], gb[8], gl[8];
+                    kr[2 * i].get(ka);
+                    kr[2 * i + 1].get(kb);
+                    g8(pr0, c8, ga);
+                    g8(pr0 + 1, c8, gb);
+                    g8(CH - 1, c8, gl);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float ya = ka[e] * exp_f32(ga[e]), yb = kb[e] * exp_f32(gb[e]);
+                        const float da = ka[e] * exp_f32(gl[e] - ga[e]), db = kb[e] * exp_f32(gl[e] - gb[e]);
+                        if constexpr (Lay::BF) {
+                            *reinterpret_cast<uint32_t*>(sKgT + (c8 + e) * LDT + perm<MT>(pr0)) = pack_bf16x2(ya, yb);
+                            *reinterpret_cast<uint32_t*>(sKdT + (c8 + e) * LDT + perm<MT>(pr0)) = pack_bf16x2(da, db);
+                        } else {
+                            sKgT[(c8 + e) * LDT + pr0] = ya;
+                            sKgT[(c8 + e) * LDT + pr0 + 1] = yb;
+                            sKdT[(c8 + e) * LDT + pr0] = da;
+                            sKdT[(c8 + e) * LDT + pr0 + 1] = db;
+                        }
+                    }
                 }
             }
 #pragma unroll
@@ -1102,10 +1292,11 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
 #pragma unroll
             for (int i = 0; i < TQ::NV; ++i) {
                 const int r = TQ::row(tid, i), c8 = TQ::col(tid);
-                float y[8];
+                float y[8], gq[8];
                 qr[i].get(y);
+                g8(r, c8, gq);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) y[e] *= exp_f32(sg[r * K + c8 + e]);
+                for (int e = 0; e < 8; ++e) y[e] *= exp_f32(gq[e]);
                 if constexpr (Lay::BF) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) sQt[r * LDK + perm<MT>(c8 + e)] = M::cvt(y[e]);

@@ -90,6 +90,17 @@ def test_kda_exp_minus_prefix_overflow_case():
     _check(p, o, ht, h0=False)
 
 
+@pytest.mark.parametrize("lo,io,K", [(-20.0, "bf16", 128), (-6.0, "bf16", 128), (-20.0, "f32", 64)])
+def test_kda_wide_decay_range(lo, io, K):
+    """Per-channel decays whose range over a 16-row block exceeds e^64 on some channels (gk down to
+    -20: up to 320 per block; -6: around the limit): those chunks evaluate their diagonal blocks
+    element-wise, the others on MFMA; every chunk must match the oracle."""
+    p = inputs.dense_problem(73 + int(-lo), [200, 65, 7], HK=2, HV=2, K=K, V=K, io_dtype=io, g_range=(lo, 0.0),
+                             g_endpoints=0.1, per_k_gate=True, beta_mode="mixed")
+    o, ht = _chunk(p)
+    _check(p, o, ht)
+
+
 def test_kda_fp32_k64():
     p = inputs.dense_problem(72, [90, 3], HK=1, HV=2, K=64, V=64, io_dtype="f32", g_range=(-1.0, 0.0),
                              per_k_gate=True)
