@@ -109,6 +109,48 @@ template <int N> struct Vec<bf16_t, N> {
     }
 };
 
+// ---- LDS staging: raw element type, and N consecutive elements read back as fp32 ----
+template <typename T> struct RawT;
+template <> struct RawT<float> { typedef float T; };
+template <> struct RawT<bf16_t> { typedef uint16_t T; };
+
+template <typename T, int N> struct LdsVec;
+
+template <int N> struct LdsVec<float, N> {
+    static_assert(N % 4 == 0, "fp32 vectors are whole float4s");
+    __device__ __forceinline__ static void get(const float* p, float* out) {
+#pragma unroll
+        for (int j = 0; j < N / 4; ++j) {
+            const f32x4_t x = reinterpret_cast<const f32x4_t*>(p)[j];
+            out[4 * j + 0] = x[0];
+            out[4 * j + 1] = x[1];
+            out[4 * j + 2] = x[2];
+            out[4 * j + 3] = x[3];
+        }
+    }
+};
+
+template <int N> struct LdsVec<bf16_t, N> {
+    static_assert(N == 4 || N == 8, "bf16 vectors are 8 or 16 bytes");
+    __device__ __forceinline__ static void get(const uint16_t* p, float* out) {
+        if constexpr (N == 8) {
+            const uint4 w = *reinterpret_cast<const uint4*>(p);
+            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                out[2 * j] = __uint_as_float(ws[j] << 16);
+                out[2 * j + 1] = __uint_as_float(ws[j] & 0xFFFF0000u);
+            }
+        } else {
+            const uint2 w = *reinterpret_cast<const uint2*>(p);
+            out[0] = __uint_as_float(w.x << 16);
+            out[1] = __uint_as_float(w.x & 0xFFFF0000u);
+            out[2] = __uint_as_float(w.y << 16);
+            out[3] = __uint_as_float(w.y & 0xFFFF0000u);
+        }
+    }
+};
+
 // ---- loads through a buffer resource: bytes past the resource's range read as zero ----
 template <typename T, int N> struct BufVec;
 

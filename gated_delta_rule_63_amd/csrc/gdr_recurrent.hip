@@ -68,50 +68,17 @@ __global__ __launch_bounds__(256) void recurrent_kernel(const RecurrentArgs a) {
 #pragma unroll
     for (int u = 0; u < UNITS; ++u) cols[u] = (u * 16 + j) * VW;
 
-    // one token's inputs, raw; the next token's are loaded while the current one computes
-    struct TokIn {
-        RawVec<IO, VW> k[UNITS], q[UNITS];
-        RawVec<float, VW> gk[PER_K ? UNITS : 1];
-        float g;
-        RawElem<IO> ga;                                          // GATED: raw decay input a
-        RawElem<IO> b;                                           // beta, or GATED: raw input b
-        RawVec<IO, SLOTS> v;
-    };
-    auto load_tok = [&](int64_t t, TokIn& x) {
-        const int64_t qk_off = (t * a.HK + hk) * K;
-        const int64_t th = t * a.HV + h;
-#pragma unroll
-        for (int u = 0; u < UNITS; ++u) {
-            x.k[u].load(a.k, qk_off + cols[u]);
-            x.q[u].load(a.q, qk_off + cols[u]);
-        }
-        if constexpr (PER_K) {
-#pragma unroll
-            for (int u = 0; u < UNITS; ++u) x.gk[u].load(a.g, th * K + cols[u]);
-        } else if constexpr (GATED) {
-            x.ga.load(a.ga, th);
-        } else {
-            x.g = a.g[th];
-        }
-        x.b.load(GATED ? a.gb : a.beta, th);
-        x.v.load(a.v, th * a.V + row0);
-    };
-    // The first token's inputs are requested before the state and without a branch, so a
-    // sequence's first token waits for one round trip to memory, not two.  An empty sequence
-    // reads a valid token it never uses (the launch guarantees T >= 1).
-    TokIn nxt;
-    load_tok(bos < eos ? bos : a.T - 1, nxt);
-
-    // per-head gate constants, read before the state so their latency overlaps its loads
+    // per-head gate constants
     const float neg_exp_a_log = GATED ? -exp_f32(a.A_log[h]) : 0.0f;
     const float dt_bias = GATED ? a.dt_bias[h] : 0.0f;
+    const int64_t ib_row = a.ibuf ? (int64_t)a.ibuf_idx[n] * a.cache_steps : 0;
 
+    float S[SLOTS][EPL];
+    const int64_t sbase = (((int64_t)slot * a.HV + h) * a.V + row0) * K;
     // The workgroup's state tile (BV rows of K) is read through a buffer resource that spans the
     // tile, or nothing when there is no source state: reads then return zeros, so the start state
     // needs no branch and its loads schedule together with the first token's.
-    float S[SLOTS][EPL];
-    const int64_t sbase = (((int64_t)slot * a.HV + h) * a.V + row0) * K;
-    {
+    auto load_state = [&]() {
         const int64_t tile = (((int64_t)slot * a.HV + h) * a.V + vt * BV) * K;
         const char* tile_ptr = a.src ? static_cast<const char*>(a.src) + tile * Elem<ST>::bytes : nullptr;
         const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
@@ -121,46 +88,12 @@ __global__ __launch_bounds__(256) void recurrent_kernel(const RecurrentArgs a) {
 #pragma unroll
             for (int u = 0; u < UNITS; ++u)
                 BufVec<ST, VW>::load(srs, (uint32_t)(((rg * SLOTS + s) * K + cols[u]) * Elem<ST>::bytes), &S[s][u * VW]);
-    }
+    };
 
-    const int64_t ib_row = a.ibuf ? (int64_t)a.ibuf_idx[n] * a.cache_steps : 0;
-
-    if constexpr (PF) {
-        // Drain the state and first-token loads here, where they are needed anyway.  Otherwise
-        // the wait-count pass merges their pending state into the loop head and every token
-        // would wait for the previous token's stores before it touches its prefetched inputs.
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt left at their maximum
-    }
-
-    for (int64_t t = bos; t < eos; ++t) {
-        // PF: token t+1's loads are issued now and overlap token t's work.  Otherwise (one token
-        // per sequence, decode) they are issued after it, so two tokens' inputs are never live.
-        TokIn cur = nxt;
-        if constexpr (PF) {
-            if (t + 1 < eos) load_tok(t + 1, nxt);
-        }
+    // One token on this thread's SLOTS rows, from its unpacked inputs: k and q (this lane's
+    // channels), the decay factors, beta and v (this thread's rows).
+    auto step = [&](int64_t t, float* kk, float* qq, const float* al, float bt, const float* vv) {
         const int64_t th = t * a.HV + h;
-        float kk[EPL], qq[EPL], al[EPL];
-#pragma unroll
-        for (int u = 0; u < UNITS; ++u) {
-            cur.k[u].get(&kk[u * VW]);
-            cur.q[u].get(&qq[u * VW]);
-        }
-        if constexpr (PER_K) {
-#pragma unroll
-            for (int u = 0; u < UNITS; ++u) cur.gk[u].get(&al[u * VW]);
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) al[e] = exp_f32(al[e]);
-        } else {
-            const float gt = GATED ? gate_decay(cur.ga.get(), neg_exp_a_log, dt_bias) : cur.g;
-            const float alpha = exp_f32(gt);
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) al[e] = alpha;
-        }
-        float bt = cur.b.get();
-        if constexpr (GATED) {
-            bt = a.beta_mul * sigmoid_f32(bt);
-        }
         if constexpr (GATE == 2) {
             float sk = 0.0f, sq = 0.0f;
 #pragma unroll
@@ -176,9 +109,6 @@ __global__ __launch_bounds__(256) void recurrent_kernel(const RecurrentArgs a) {
                 qq[e] *= rq;
             }
         }
-        float vv[SLOTS];
-        cur.v.get(vv);
-
         // (decayed S) . k: with the per-channel gate the decay multiplies k element-wise; a scalar
         // gate multiplies the reduced dot product once (fewer registers and instructions)
         float ka[PER_K ? EPL : 1];
@@ -186,7 +116,6 @@ __global__ __launch_bounds__(256) void recurrent_kernel(const RecurrentArgs a) {
 #pragma unroll
             for (int e = 0; e < EPL; ++e) ka[e] = al[e] * kk[e];
         }
-
         float ov[SLOTS];
 #pragma unroll
         for (int s = 0; s < SLOTS; ++s) {
@@ -199,15 +128,13 @@ __global__ __launch_bounds__(256) void recurrent_kernel(const RecurrentArgs a) {
             float po = 0.0f;
 #pragma unroll
             for (int e = 0; e < EPL; ++e) {
-                S[s][e] = fmaf(nu, kk[e], al[e] * S[s][e]);               // decay + rank-1
+                S[s][e] = fmaf(nu, kk[e], al[PER_K ? e : 0] * S[s][e]);  // decay + rank-1
                 po = fmaf(S[s][e], qq[e], po);
             }
             ov[s] = a.scale * row16_sum(po);                              // post-update read
         }
         // Lane j of each row group writes row (row0 + j % SLOTS): lanes past SLOTS repeat the same
-        // value to the same address.  No store in the token loop is conditional, so the vector
-        // memory counter stays exact and waiting for the next token's prefetched loads does not
-        // also wait for this token's stores.
+        // value to the same address, so no store in the token loop is conditional.
         float mine = ov[0];
 #pragma unroll
         for (int s = 1; s < SLOTS; ++s) mine = ((j % SLOTS) == s) ? ov[s] : mine;
@@ -220,7 +147,173 @@ __global__ __launch_bounds__(256) void recurrent_kernel(const RecurrentArgs a) {
 #pragma unroll
                 for (int u = 0; u < UNITS; ++u) Vec<IB, VW>::store(a.ibuf, ib + (int64_t)s * K + cols[u], &S[s][u * VW]);
         }
-        if constexpr (!PF) {
+    };
+    // scalar decay factor and beta from the raw per-token values (gating front when GATED)
+    auto gate_scalar = [&](float graw) { return exp_f32(GATED ? gate_decay(graw, neg_exp_a_log, dt_bias) : graw); };
+    auto beta_of = [&](float braw) { return GATED ? a.beta_mul * sigmoid_f32(braw) : braw; };
+
+    if constexpr (PF) {
+        // Several tokens per sequence: the workgroup stages TB tokens' inputs in LDS at a time, so
+        // the token loop itself waits on no global load, and every row group reads the shared k,
+        // q, gate and beta from LDS (one copy per workgroup instead of one per row group).
+        typedef typename RawT<IO>::T R;
+        constexpr int ESZ = Elem<IO>::bytes;
+        constexpr int TB = ESZ == 2 ? 16 : 8;                      // tokens per block
+        constexpr int KROW = K * ESZ / 16, VROW = BV * ESZ / 16, GROW = K * 4 / 16;  // 16-byte chunks per row
+        constexpr int NK = (TB * KROW + 255) / 256, NV = (TB * VROW + 255) / 256;
+        constexpr int NG = PER_K ? (TB * GROW + 255) / 256 : 0;
+        __shared__ __align__(16) R sk[TB][K], sq[TB][K], sv[TB][BV];
+        __shared__ __align__(16) float sgk[PER_K ? TB : 1][PER_K ? K : 4];
+        __shared__ float sg[TB], sb[TB];
+        uint4 rk[NK], rq[NK], rv[NV], rgk[NG > 0 ? NG : 1];
+        uint32_t rgs = 0, rbs = 0;                                 // raw bits, widened in put()
+        auto raw_bits = [](const void* p, int64_t i) -> uint32_t {
+            if constexpr (ESZ == 2) return static_cast<const uint16_t*>(p)[i];
+            else return __float_as_uint(static_cast<const float*>(p)[i]);
+        };
+        auto widen = [](uint32_t u) { return ESZ == 2 ? __uint_as_float(u << 16) : __uint_as_float(u); };
+        auto fetch = [&](int64_t tb, int nt) {
+#pragma unroll
+            for (int i = 0; i < NK; ++i) {
+                const int c = tid + 256 * i, r = c / KROW, c16 = c % KROW;
+                if (c < TB * KROW && r < nt) {
+                    const int64_t off = ((tb + r) * a.HK + hk) * K * ESZ + c16 * 16;
+                    rk[i] = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.k) + off);
+                    rq[i] = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) + off);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                const int c = tid + 256 * i, r = c / VROW, c16 = c % VROW;
+                if (c < TB * VROW && r < nt)
+                    rv[i] = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.v) +
+                                                             (((tb + r) * a.HV + h) * a.V + vt * BV) * ESZ + c16 * 16);
+            }
+            if constexpr (PER_K) {
+#pragma unroll
+                for (int i = 0; i < NG; ++i) {
+                    const int c = tid + 256 * i, r = c / GROW, c16 = c % GROW;
+                    if (c < TB * GROW && r < nt)
+                        rgk[i] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(a.g) +
+                                                                  ((tb + r) * a.HV + h) * K * 4 + c16 * 16);
+                }
+            }
+            if (tid < nt) {
+                const int64_t th = (tb + tid) * a.HV + h;
+                if constexpr (!PER_K) rgs = GATED ? raw_bits(a.ga, th) : __float_as_uint(a.g[th]);
+                rbs = raw_bits(GATED ? a.gb : a.beta, th);
+            }
+        };
+        auto put = [&](int nt) {
+#pragma unroll
+            for (int i = 0; i < NK; ++i) {
+                const int c = tid + 256 * i, r = c / KROW, c16 = c % KROW;
+                if (c < TB * KROW && r < nt) {
+                    *reinterpret_cast<uint4*>(reinterpret_cast<char*>(&sk[r][0]) + c16 * 16) = rk[i];
+                    *reinterpret_cast<uint4*>(reinterpret_cast<char*>(&sq[r][0]) + c16 * 16) = rq[i];
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                const int c = tid + 256 * i, r = c / VROW, c16 = c % VROW;
+                if (c < TB * VROW && r < nt) *reinterpret_cast<uint4*>(reinterpret_cast<char*>(&sv[r][0]) + c16 * 16) = rv[i];
+            }
+            if constexpr (PER_K) {
+#pragma unroll
+                for (int i = 0; i < NG; ++i) {
+                    const int c = tid + 256 * i, r = c / GROW, c16 = c % GROW;
+                    if (c < TB * GROW && r < nt)
+                        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(&sgk[r][0]) + c16 * 16) = rgk[i];
+                }
+            }
+            if (tid < nt) {
+                sg[tid] = GATED ? widen(rgs) : __uint_as_float(rgs);
+                sb[tid] = widen(rbs);
+            }
+        };
+
+        fetch(bos, (int)(eos - bos < TB ? eos - bos : TB));   // the first block's loads, then the state's
+        load_state();
+        for (int64_t tb = bos; tb < eos; tb += TB) {
+            const int nt = (int)(eos - tb < TB ? eos - tb : TB);
+            if (tb > bos) __syncthreads();                      // the previous block has been read
+            put(nt);
+            __syncthreads();
+            for (int i = 0; i < nt; ++i) {
+                float kk[EPL], qq[EPL], al[PER_K ? EPL : 1], vv[SLOTS];
+#pragma unroll
+                for (int u = 0; u < UNITS; ++u) {
+                    LdsVec<IO, VW>::get(&sk[i][cols[u]], &kk[u * VW]);
+                    LdsVec<IO, VW>::get(&sq[i][cols[u]], &qq[u * VW]);
+                }
+                if constexpr (PER_K) {
+#pragma unroll
+                    for (int u = 0; u < UNITS; ++u) LdsVec<float, VW>::get(&sgk[i][cols[u]], &al[u * VW]);
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) al[e] = exp_f32(al[e]);
+                } else {
+                    al[0] = gate_scalar(sg[i]);
+                }
+                LdsVec<IO, SLOTS>::get(&sv[i][rg * SLOTS], vv);
+                step(tb + i, kk, qq, al, beta_of(sb[i]), vv);
+            }
+            // the next block's loads are issued after this block's tokens, so the staging
+            // registers are dead while the tokens run (a longer sequence pays one memory round
+            // trip per block of TB tokens)
+            if (tb + TB < eos) fetch(tb + TB, (int)(eos - tb - TB < TB ? eos - tb - TB : TB));
+        }
+    } else {
+        // One token per sequence in practice (decode): the token's inputs come straight into
+        // registers, requested before the state so the first token waits one round trip; a longer
+        // sequence loads each further token after the previous one.
+        struct TokIn {
+            RawVec<IO, VW> k[UNITS], q[UNITS];
+            RawVec<float, VW> gk[PER_K ? UNITS : 1];
+            float g;
+            RawElem<IO> ga;                                      // GATED: raw decay input a
+            RawElem<IO> b;                                       // beta, or GATED: raw input b
+            RawVec<IO, SLOTS> v;
+        };
+        auto load_tok = [&](int64_t t, TokIn& x) {
+            const int64_t qk_off = (t * a.HK + hk) * K;
+            const int64_t th = t * a.HV + h;
+#pragma unroll
+            for (int u = 0; u < UNITS; ++u) {
+                x.k[u].load(a.k, qk_off + cols[u]);
+                x.q[u].load(a.q, qk_off + cols[u]);
+            }
+            if constexpr (PER_K) {
+#pragma unroll
+                for (int u = 0; u < UNITS; ++u) x.gk[u].load(a.g, th * K + cols[u]);
+            } else if constexpr (GATED) {
+                x.ga.load(a.ga, th);
+            } else {
+                x.g = a.g[th];
+            }
+            x.b.load(GATED ? a.gb : a.beta, th);
+            x.v.load(a.v, th * a.V + row0);
+        };
+        TokIn nxt;
+        load_tok(bos < eos ? bos : a.T - 1, nxt);  // an empty sequence reads a valid token it never uses
+        load_state();
+        for (int64_t t = bos; t < eos; ++t) {
+            TokIn cur = nxt;
+            float kk[EPL], qq[EPL], al[PER_K ? EPL : 1], vv[SLOTS];
+#pragma unroll
+            for (int u = 0; u < UNITS; ++u) {
+                cur.k[u].get(&kk[u * VW]);
+                cur.q[u].get(&qq[u * VW]);
+            }
+            if constexpr (PER_K) {
+#pragma unroll
+                for (int u = 0; u < UNITS; ++u) cur.gk[u].get(&al[u * VW]);
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) al[e] = exp_f32(al[e]);
+            } else {
+                al[0] = gate_scalar(GATED ? cur.ga.get() : cur.g);
+            }
+            cur.v.get(vv);
+            step(t, kk, qq, al, beta_of(cur.b.get()), vv);
             if (t + 1 < eos) load_tok(t + 1, nxt);
         }
     }
