@@ -32,19 +32,19 @@ __global__ __launch_bounds__(256) void cp_setup_kernel(int32_t* __restrict__ cu_
 }
 
 // S[0] = h0 (or zeros); S[s+1] = S[s] M_s + B_s for s = 0..P-2, per value head.  One workgroup
-// owns 16 state rows of one head (grid: V/16 x HV); the 16 x K rows live in LDS between steps,
-// thread t forms row t/16, columns 8 (t%16) .. 8 (t%16) + 7, reading M_s from L2.
+// owns 16 state rows of one head (grid: V/16 x HV) and keeps them in LDS between steps; wave w
+// forms output columns 32w .. 32w + 31 (two 16-column tiles; one tile when K = 64) with fp32
+// MFMA (16x16x4): A = the 16 rows from LDS, B = M_s from L2, C starting from B_s.
 template <int K>
 __global__ __launch_bounds__(256) void cp_scan_kernel(const float* __restrict__ h0, const float* __restrict__ B,
                                                       const float* __restrict__ M, float* __restrict__ S, int P,
                                                       int HV, int V) {
-    __shared__ float rows[16][K];
-    const int tid = threadIdx.x;
+    constexpr int LDR = K + 4;                  // padded LDS row: the A reads of a k-step hit 16 banks
+    constexpr int TPW = K / 64;                 // 16-column tiles per wave (K / 16 tiles over 4 waves)
+    __shared__ __align__(16) float rows[16][LDR];
+    const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
     const int h = blockIdx.y, r0 = blockIdx.x * 16;
-    const int r = tid / 16, c0 = (tid % 16) * (K / 16);
-    constexpr int CPT = K / 16;  // columns per thread
     const int64_t vk = (int64_t)V * K;
-    // start state
     for (int e = tid; e < 16 * K; e += 256) {
         const int rr = e / K, cc = e % K;
         const int64_t idx = ((int64_t)h * V + r0 + rr) * K + cc;  // segment 0 of S / h0
@@ -55,21 +55,33 @@ __global__ __launch_bounds__(256) void cp_scan_kernel(const float* __restrict__ 
     __syncthreads();
     for (int s = 0; s + 1 < P; ++s) {
         const float* Ms = M + ((int64_t)s * HV + h) * K * K;
-        const float* Bs = B + ((int64_t)s * HV + h) * vk + (int64_t)(r0 + r) * K;
-        float acc[CPT];
+        const float* Bs = B + ((int64_t)s * HV + h) * vk + (int64_t)r0 * K;
+        f32x4_t acc[TPW];
 #pragma unroll
-        for (int e = 0; e < CPT; ++e) acc[e] = Bs[c0 + e];
-        for (int j = 0; j < K; ++j) {
-            const float x = rows[r][j];
+        for (int t = 0; t < TPW; ++t) {
+            const int col = (w * TPW + t) * 16 + (l & 15);
 #pragma unroll
-            for (int e = 0; e < CPT; ++e) acc[e] = fmaf(x, Ms[(int64_t)j * K + c0 + e], acc[e]);
+            for (int e = 0; e < 4; ++e) acc[t][e] = Bs[(int64_t)(4 * (l >> 4) + e) * K + col];
         }
-        __syncthreads();  // every thread has read the previous rows
-        float* Sn = S + ((int64_t)(s + 1) * HV + h) * vk + (int64_t)(r0 + r) * K;
+#pragma unroll 8
+        for (int k0 = 0; k0 < K; k0 += 4) {
+            const float av = rows[l & 15][k0 + (l >> 4)];
 #pragma unroll
-        for (int e = 0; e < CPT; ++e) {
-            rows[r][c0 + e] = acc[e];
-            Sn[c0 + e] = acc[e];
+            for (int t = 0; t < TPW; ++t) {
+                const float bv = Ms[(int64_t)(k0 + (l >> 4)) * K + (w * TPW + t) * 16 + (l & 15)];
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[t], 0, 0, 0);
+            }
+        }
+        __syncthreads();  // every wave has read the previous rows
+        float* Sn = S + ((int64_t)(s + 1) * HV + h) * vk + (int64_t)r0 * K;
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            const int col = (w * TPW + t) * 16 + (l & 15);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                rows[4 * (l >> 4) + e][col] = acc[t][e];
+                Sn[(int64_t)(4 * (l >> 4) + e) * K + col] = acc[t][e];
+            }
         }
         __syncthreads();
     }
