@@ -174,3 +174,40 @@ def test_gated_entry_points_accept_empty_batches_without_the_device():
     assert _pre(_p(T=0, N=1), _gating(a=None, b=None, A_log=None, dt_bias=None), q=None, k=None, qo=None, ko=None,
                 g=None, b=None) == 0
     assert _decg(_p(T=0, N=4), _gating(), cu=DUMMY) == 0
+
+
+def _cp_size(T, N, HV, K=128, V=128, io=1):
+    p = gdr.Problem(T, N, 1, HV, K, V, 0.1, 1, io)
+    return gdr.lib().gdr_chunk_workspace_size(ctypes.byref(p), 64)
+
+
+def _cp_expected(T, HV, K, V, io_bytes):
+    """Workspace of the segmented path, written out from its definition: segments target one
+    workgroup per (segment, head) on 256 CUs with at least 8 chunks each, at least 6 of them; the
+    workspace holds the segment table, P-1 offsets [HV, V, K], P-1 maps [HV, K, K] and P start
+    states [HV, V, K], each rounded up to 256 bytes."""
+    nchunks = (T + 63) // 64
+    vt = V // 64 if io_bytes == 4 else 1
+    P = min(256 // (HV * vt), nchunks // 8)
+    if P < 6:
+        return 0
+    seg = -(-nchunks // P)
+    P = -(-nchunks // seg)
+    if P < 6:
+        return 0
+    up = lambda x: -(-x // 256) * 256
+    return up(4 * (P + 1)) + up(4 * (P - 1) * HV * V * K) + up(4 * (P - 1) * HV * K * K) + up(4 * P * HV * V * K)
+
+
+@pytest.mark.parametrize("T,N,HV,K,V,io", [(65573, 1, 16, 128, 128, 1), (6417, 1, 2, 128, 128, 1),
+                                          (3845, 1, 2, 64, 64, 0), (65573, 2, 16, 128, 128, 1),
+                                          (2000, 1, 16, 128, 128, 1), (64, 1, 2, 64, 64, 0),
+                                          (32768, 1, 32, 128, 128, 1), (65573, 1, 64, 128, 128, 1)])
+def test_segmented_workspace_size(T, N, HV, K, V, io):
+    """Host-side planning of the context-parallel route: only one sequence, enough chunks and few
+    enough heads take it; everything else needs no workspace."""
+    got = _cp_size(T, N, HV, K, V, io)
+    want = _cp_expected(T, HV, K, V, 4 if io == 0 else 2) if N == 1 else 0
+    assert got == want
+    if (T, N, HV) == (65573, 1, 16):
+        assert got > 0  # the KDA stress shape is segmented (16 segments)

@@ -8,7 +8,7 @@ import torch
 
 import oracle
 from _cmp import TOL, max_rel_l2_states, max_rel_l2_tokens
-from _dev import f64, oracle_inputs, problem_to_dev
+from _dev import f64, oracle_inputs, problem_to_dev, to_dev
 from gated_delta_rule_63_amd import gdr, inputs
 
 pytestmark = pytest.mark.gpu
@@ -62,3 +62,69 @@ def test_segmented_path_is_deterministic():
     o1, h1 = _run_and_check(p)
     o2, h2 = _run_and_check(p)
     assert torch.equal(o1, o2) and torch.equal(h1, h2)
+
+
+def test_segmented_path_graph_capture_replay_equals_eager():
+    """The segmented route (setup, three chunk runs, scan, copy) is capturable: it allocates
+    nothing and records no memset; every replay equals the eager result bit for bit."""
+    p = inputs.dense_problem(86, [64 * 50 + 3], HK=1, HV=2, K=128, V=128, io_dtype="bf16")
+    d = problem_to_dev(p)
+    need = gdr.gdr_chunk_workspace_size(d["q"], d["v"], d["g"], 1)
+    assert need > 0
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    o = torch.zeros((p.T, p.HV, p.V), dtype=torch.bfloat16, device="cuda")
+    ht = torch.zeros((1, p.HV, p.V, p.K), dtype=torch.float32, device="cuda")
+
+    def call():
+        gdr.gdr_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], p.scale, d["h0"], o=o,
+                          final_state=ht, workspace=ws)
+
+    call()
+    torch.cuda.synchronize()
+    o_ref, ht_ref = o.clone(), ht.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for _ in range(3):
+        o.zero_()
+        ht.zero_()
+        ws.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(ht, ht_ref)
+
+
+def test_gating_prepass_graph_capture_replay_equals_eager():
+    r = inputs.raw_gating(87, 300, 2, 8, 128)
+    dq, dk, da, db, A_log, dt = (to_dev(x) for x in (r.q, r.k, r.a, r.b, r.A_log, r.dt_bias))
+    qo, ko = torch.zeros_like(dq), torch.zeros_like(dk)
+    g = torch.zeros((300, 8), dtype=torch.float32, device="cuda")
+    beta = torch.zeros((300, 8), dtype=torch.bfloat16, device="cuda")
+
+    def call():
+        gdr.gdr_gating_prepass(dq, dk, da, db, A_log, dt, q_out=qo, k_out=ko, g_out=g, beta_out=beta)
+
+    call()
+    torch.cuda.synchronize()
+    refs = [t.clone() for t in (qo, ko, g, beta)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for _ in range(3):
+        for t in (qo, ko, g, beta):
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert all(torch.equal(t, r_) for t, r_ in zip((qo, ko, g, beta), refs))
