@@ -239,6 +239,8 @@ __global__ __launch_bounds__(256) void recurrent_kernel(const RecurrentArgs a) {
             if (tb > bos) __syncthreads();                      // the previous block has been read
             put(nt);
             __syncthreads();
+            // the next block's loads are in flight while this block's tokens run
+            if (tb + TB < eos) fetch(tb + TB, (int)(eos - tb - TB < TB ? eos - tb - TB : TB));
             for (int i = 0; i < nt; ++i) {
                 float kk[EPL], qq[EPL], al[PER_K ? EPL : 1], vv[SLOTS];
 #pragma unroll
@@ -257,10 +259,6 @@ __global__ __launch_bounds__(256) void recurrent_kernel(const RecurrentArgs a) {
                 LdsVec<IO, SLOTS>::get(&sv[i][rg * SLOTS], vv);
                 step(tb + i, kk, qq, al, beta_of(sb[i]), vv);
             }
-            // the next block's loads are issued after this block's tokens, so the staging
-            // registers are dead while the tokens run (a longer sequence pays one memory round
-            // trip per block of TB tokens)
-            if (tb + TB < eos) fetch(tb + TB, (int)(eos - tb - TB < TB ? eos - tb - TB : TB));
         }
     } else {
         // One token per sequence in practice (decode): the token's inputs come straight into
