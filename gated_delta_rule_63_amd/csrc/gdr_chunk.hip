@@ -54,7 +54,9 @@ template <typename MT> struct MM;
 
 template <> struct MM<bf16_t> {
     typedef uint16_t S;  // LDS element
-    static constexpr int PAD = 8;
+    // rows padded to a stride of 8 dwords modulo 32 banks: the 16-row MFMA operand reads (16-byte
+    // lanes, rows l % 16, column granules l / 16) are then free of bank conflicts
+    static constexpr int PAD = 16;
     __device__ __forceinline__ static S cvt(float x) { return f32_to_bf16(x); }
     __device__ __forceinline__ static float back(S x) { return bf16_to_f32(x); }
     __device__ __forceinline__ static void nt(f32x4_t& acc, const S* sA, int lda, const S* sB, int ldb, int kdim) {
@@ -439,80 +441,6 @@ __device__ __forceinline__ uint2 ld_tr4(const uint16_t* m, int ld, int r0, int c
     return __builtin_bit_cast(uint2, v);
 }
 
-// ---- swizzled bf16 operand rows (128 channels, no padding) ----------------------------------
-// The 16-byte granule g of row r is stored at granule g ^ swz(r).  This keeps two read patterns
-// free of LDS bank conflicts: 16-byte MFMA operand reads (8 consecutive rows, same granule, per
-// LDS pass) and the transposing reads (4 consecutive rows x 4 consecutive granules per 16-lane
-// group).  swz was found by an exhaustive search over XOR maps of the row's low four bits.
-// Lane offsets are computed once: `b128[s]` for operand reads of 32-wide step s in a 16-row tile,
-// `tr[mb]` for transposing reads of 32-channel block mb in a 4-row group.
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 1); }
-struct SwzLanes {
-    int b128[4], tr[4];
-    __device__ __forceinline__ void init() {
-        const int l = threadIdx.x & 63, g4 = l >> 4, lr = l & 15;
-        const int rr = 4 * g4 + ((l >> 2) & 3), q = l & 3;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) b128[s] = lr * 128 + (((4 * s + g4) ^ swz(lr)) << 3);
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) tr[mb] = rr * 128 + (((4 * mb + q) ^ swz(rr)) << 3);
-    }
-};
-// this lane's transposing-read offset for channel tile kt (runtime kt), rows 4 (l/16) + r of a
-// 16-row block
-__device__ __forceinline__ int swz_tr_off(int kt) {
-    const int l = threadIdx.x & 63, rr = 4 * (l >> 4) + ((l >> 2) & 3), q = l & 3;
-    return rr * 128 + (((4 * (kt >> 1) + q) ^ swz(rr)) << 3) + 4 * (kt & 1);
-}
-// element offset of (row, perm()-ordered element pc) in swizzled rows of 128
-__device__ __forceinline__ int swz_off(int row, int pc) { return row * 128 + ((((pc >> 3) ^ swz(row))) << 3) + (pc & 7); }
-
-// two 16x16 tiles over 128 channels from swizzled rows (tile pointers at a row multiple of 16)
-__device__ __forceinline__ void nt2_swz(f32x4_t& c0, const uint16_t* a0, const uint16_t* b0, f32x4_t& c1,
-                                        const uint16_t* a1, const uint16_t* b1, const SwzLanes& z) {
-    bf16x8_t va0[4], vb0[4], va1[4], vb1[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        va0[s] = *reinterpret_cast<const bf16x8_t*>(a0 + z.b128[s]);
-        vb0[s] = *reinterpret_cast<const bf16x8_t*>(b0 + z.b128[s]);
-        va1[s] = *reinterpret_cast<const bf16x8_t*>(a1 + z.b128[s]);
-        vb1[s] = *reinterpret_cast<const bf16x8_t*>(b1 + z.b128[s]);
-    }
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va0[s], vb0[s], c0, 0, 0, 0);
-        c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va1[s], vb1[s], c1, 0, 0, 0);
-    }
-}
-__device__ __forceinline__ void nt_swz(f32x4_t& c, const uint16_t* a, const uint16_t* b, const SwzLanes& z) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8_t*>(a + z.b128[s]),
-                                                    *reinterpret_cast<const bf16x8_t*>(b + z.b128[s]), c, 0, 0, 0);
-}
-// gemm_regs with A in swizzled rows of 128 channels (NP = 128)
-template <int NI>
-__device__ __forceinline__ void gemm_regs_swz(f32x4_t* acc, const uint16_t* sA, const SwzLanes& z, const f32x4_t* Bt) {
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const uint4 bw = {pack_tile_lo(Bt[2 * m]), pack_tile_hi(Bt[2 * m]), pack_tile_lo(Bt[2 * m + 1]),
-                          pack_tile_hi(Bt[2 * m + 1])};
-        const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, bw);
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(sA + 16 * i * 128 + z.b128[m]);
-            acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[i], 0, 0, 0);
-        }
-    }
-}
-// ld_tr4 on swizzled rows: rows rb + 4 (l/16) + r (rb a multiple of 16), logical channels 16 kt ..
-__device__ __forceinline__ uint2 ld_tr4_swz(const uint16_t* m, int rb, int kt, const SwzLanes& z) {
-    typedef short v4i16 __attribute__((ext_vector_type(4)));
-    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-    const uint16_t* p = m + rb * 128 + z.tr[kt >> 1] + 4 * (kt & 1);
-    return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p)));
-}
-
 // RHS block loaders for block_solve: rows 16I + 4*(l/16) + e (e = 0..3) of column l%16 of a
 // 16-column tile, scaled per row by sc[t].
 template <typename MT> struct RhsFromTransposed {   // the tile's transposed row (this lane's column)
@@ -543,22 +471,6 @@ struct RhsFromRows {                               // row-major bf16 rows (perm(
         const int t0 = 16 * I + 4 * ((threadIdx.x & 63) >> 4);
         const f32x4_t f = *reinterpret_cast<const f32x4_t*>(sc + t0);
         const uint2 raw = ld_tr4<true>(m, ld, t0, c0);
-        return f32x4_t{__uint_as_float(raw.x << 16) * f[0], __uint_as_float(raw.x & 0xFFFF0000u) * f[1],
-                       __uint_as_float(raw.y << 16) * f[2], __uint_as_float(raw.y & 0xFFFF0000u) * f[3]};
-    }
-};
-
-struct RhsFromSwzRows {                             // swizzled rows of 128, channels 16 kt .. 16 kt + 15
-    const uint16_t* m;
-    int off;                                       // this lane's offset for the channel tile (swz_tr_off)
-    const float* sc;
-    __device__ __forceinline__ f32x4_t operator()(int I) const {
-        typedef short v4i16 __attribute__((ext_vector_type(4)));
-        typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-        const int t0 = 16 * I + 4 * ((threadIdx.x & 63) >> 4);
-        const f32x4_t f = *reinterpret_cast<const f32x4_t*>(sc + t0);
-        const uint2 raw =
-            __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(m + 16 * I * 128 + off)));
         return f32x4_t{__uint_as_float(raw.x << 16) * f[0], __uint_as_float(raw.x & 0xFFFF0000u) * f[1],
                        __uint_as_float(raw.y << 16) * f[2], __uint_as_float(raw.y & 0xFFFF0000u) * f[3]};
     }
@@ -644,12 +556,6 @@ __device__ __forceinline__ void st8_perm(typename MM<MT>::S* row, int c8, const 
         x.get(f);
         MM<MT>::st8(row + c8, f);
     }
-}
-
-// Store the 8 consecutive logical columns c8 .. c8+7 of row r of swizzled bf16 rows of 128.
-__device__ __forceinline__ void st8_swz(uint16_t* base, int r, int c8, const Raw8<bf16_t>& x) {
-    *reinterpret_cast<uint2*>(base + swz_off(r, perm<bf16_t>(c8))) = uint2{x.w.x, x.w.y};
-    *reinterpret_cast<uint2*>(base + swz_off(r, perm<bf16_t>(c8 + 4))) = uint2{x.w.z, x.w.w};
 }
 
 // ---------------------------------------------------------------------------
@@ -760,10 +666,6 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
     static_assert(NW >= 4, "four waves invert the diagonal blocks");
     typedef OStage<BV, IO> OS;
     constexpr bool TRK = Lay::TRK;
-    // with 128 channels, the q, k and v operand rows of the TRK path are XOR-swizzled (no padding)
-    constexpr bool SWZ = TRK && K == 128;
-    SwzLanes zl;
-    if constexpr (SWZ) zl.init();
     static_assert(Lay::total <= 160 * 1024, "LDS budget");
     static_assert(OS::bytes <= Lay::LO_ + Lay::LD_ + Lay::D_, "output staging overlays -L and the inverses");
     __shared__ __align__(16) char smem[Lay::total];
@@ -915,20 +817,14 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
         // ===== A: raw rows into LDS, gate prefix =====
 #pragma unroll
         for (int i = 0; i < TQ::NV; ++i) {
-            if constexpr (SWZ) st8_swz(sQ, TQ::row(tid, i), TQ::col(tid), qr[i]);
-            else st8_perm<MT, IO>(sQ + TQ::row(tid, i) * LDK, TQ::col(tid), qr[i]);
+            st8_perm<MT, IO>(sQ + TQ::row(tid, i) * LDK, TQ::col(tid), qr[i]);
         }
 #pragma unroll
         for (int i = 0; i < PK::NPASS; ++i) {
             if (PK::valid(tid, i)) {
                 const int c8 = PK::col(tid, i), pr0 = 2 * PK::pair(tid, i);
-                if constexpr (SWZ) {
-                    st8_swz(sK, pr0, c8, kr[2 * i]);
-                    st8_swz(sK, pr0 + 1, c8, kr[2 * i + 1]);
-                } else {
-                    st8_perm<MT, IO>(sK + pr0 * LDK, c8, kr[2 * i]);
-                    st8_perm<MT, IO>(sK + (pr0 + 1) * LDK, c8, kr[2 * i + 1]);
-                }
+                st8_perm<MT, IO>(sK + pr0 * LDK, c8, kr[2 * i]);
+                st8_perm<MT, IO>(sK + (pr0 + 1) * LDK, c8, kr[2 * i + 1]);
                 if constexpr (!PER_K && !TRK) st_pair_t<MT, IO>(SP(Lay::g_kt), LDT, c8, pr0, kr[2 * i], kr[2 * i + 1]);
             }
         }
@@ -938,13 +834,8 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
                 if (PV::valid(tid, i)) {
                     const int c8 = PV::col(tid, i), pr0 = 2 * PV::pair(tid, i);
                     if constexpr (TRK) {
-                        if constexpr (SWZ) {
-                            st8_swz(SP(Lay::g_vt), pr0, c8, vr[2 * i]);
-                            st8_swz(SP(Lay::g_vt), pr0 + 1, c8, vr[2 * i + 1]);
-                        } else {
-                            st8_perm<MT, IO>(SP(Lay::g_vt) + pr0 * Lay::LDV, c8, vr[2 * i]);
-                            st8_perm<MT, IO>(SP(Lay::g_vt) + (pr0 + 1) * Lay::LDV, c8, vr[2 * i + 1]);
-                        }
+                        st8_perm<MT, IO>(SP(Lay::g_vt) + pr0 * Lay::LDV, c8, vr[2 * i]);
+                        st8_perm<MT, IO>(SP(Lay::g_vt) + (pr0 + 1) * Lay::LDV, c8, vr[2 * i + 1]);
                     } else {
                         st_pair_t<MT, IO>(SP(Lay::g_vt), LDT, c8, pr0, vr[2 * i], vr[2 * i + 1]);
                     }
@@ -997,11 +888,8 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
             auto pair = [&](int I, int J, f32x4_t& cl, f32x4_t& cp) {
                 cl = f32x4_t{0.f, 0.f, 0.f, 0.f};
                 cp = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                if constexpr (SWZ)
-                    nt2_swz(cl, sK + 16 * I * K, sK + 16 * J * K, cp, sQ + 16 * I * K, sK + 16 * J * K, zl);
-                else
-                    M::template nt2<K>(cl, sK + 16 * I * LDK, sK + 16 * J * LDK, cp, sQ + 16 * I * LDK, sK + 16 * J * LDK,
-                                       LDK);
+                M::template nt2<K>(cl, sK + 16 * I * LDK, sK + 16 * J * LDK, cp, sQ + 16 * I * LDK, sK + 16 * J * LDK,
+                                   LDK);
             };
             auto store_p_diag = [&](int I, const f32x4_t& acc) {  // element-wise decay, masked
                 const f32x4_t gr = *reinterpret_cast<const f32x4_t*>(sg + 16 * I + 4 * g4);
@@ -1039,8 +927,7 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
                 f32x4_t cl, cp;
                 if constexpr (NW > 4) {
                     cl = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                    if constexpr (SWZ) nt_swz(cl, sK + 16 * w * K, sK + 16 * w * K, zl);
-                    else M::nt(cl, sK + 16 * w * LDK, LDK, sK + 16 * w * LDK, LDK, K);
+                    M::nt(cl, sK + 16 * w * LDK, LDK, sK + 16 * w * LDK, LDK, K);
                 } else {
                     pair(w, w, cl, cp);
                 }
@@ -1068,12 +955,8 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
                     } else {  // waves 6 and 7: diagonal P tiles (I, I), I = 2 (w - 6), 2 (w - 6) + 1
                         const int I0 = 2 * (w - 6);
                         f32x4_t c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
-                        if constexpr (SWZ)
-                            nt2_swz(c0, sQ + 16 * I0 * K, sK + 16 * I0 * K, c1, sQ + 16 * (I0 + 1) * K, sK + 16 * (I0 + 1) * K,
-                                    zl);
-                        else
-                            M::template nt2<K>(c0, sQ + 16 * I0 * LDK, sK + 16 * I0 * LDK, c1, sQ + 16 * (I0 + 1) * LDK,
-                                               sK + 16 * (I0 + 1) * LDK, LDK);
+                        M::template nt2<K>(c0, sQ + 16 * I0 * LDK, sK + 16 * I0 * LDK, c1, sQ + 16 * (I0 + 1) * LDK,
+                                           sK + 16 * (I0 + 1) * LDK, LDK);
                         store_p_diag(I0, c0);
                         store_p_diag(I0 + 1, c1);
                     }
@@ -1174,8 +1057,8 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
                 // the pairs (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3); each pair's L and P
                 // tiles share the scaled right operand; wave w takes pairs w and w + NW
                 for (int tp = w; tp < 10; tp += NW) {
-                    const int I = tp < 1 ? 0 : tp < 3 ? 1 : tp < 6 ? 2 : 3;
-                    const int J = tp - I * (I + 1) / 2;
+                    int I, J;
+                    lower_tile(tp, I, J);
                     const int fi = J == I ? I : J == I - 1 ? -1 : (I == 2 ? 4 : (J == 0 ? 5 : 6));
                     f32x4_t cl = {0.f, 0.f, 0.f, 0.f}, cp = {0.f, 0.f, 0.f, 0.f};
                     nt2_bscaled<MT, K>(cl, sK + 16 * I * LDK, cp, sQ + 16 * I * LDK, LDK, sRG + 16 * J * LDK, LDK,
@@ -1331,14 +1214,8 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
                 static_assert(KT == NW, "one W tile per wave");
                 const uint16_t* sVr = SP(Lay::g_vt);
                 f32x4_t X[2][4];
-                if constexpr (SWZ) {
-                    const int off = swz_tr_off(w);
-                    const RhsFromSwzRows rhs[2] = {{sK, off, wsc}, {sVr, off, sb}};
-                    block_solve<MT, 2>(X, sLo, LDO, sD, LDD, rhs);
-                } else {
-                    const RhsFromRows rhs[2] = {{sK, LDK, 16 * w, wsc}, {sVr, Lay::LDV, 16 * w, sb}};
-                    block_solve<MT, 2>(X, sLo, LDO, sD, LDD, rhs);
-                }
+                const RhsFromRows rhs[2] = {{sK, LDK, 16 * w, wsc}, {sVr, Lay::LDV, 16 * w, sb}};
+                block_solve<MT, 2>(X, sLo, LDO, sD, LDD, rhs);
                 store_w(w, X[0]);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) nu[i] = X[1][i];
@@ -1374,8 +1251,7 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
         f32x4_t oa[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) oa[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        if constexpr (SWZ) gemm_regs_swz<4>(oa, sQ, zl, hs);
-        else gemm_regs<MT, K, 4>(oa, SP(PER_K ? Lay::k_qt : Lay::g_q), LDK, hs);
+        gemm_regs<MT, K, 4>(oa, SP(PER_K ? Lay::k_qt : Lay::g_q), LDK, hs);
         if constexpr (!PER_K) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -1419,9 +1295,8 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
                     const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, bw);
 #pragma unroll
                     for (int kt = 0; kt < KT; ++kt) {
-                        const uint2 lo = SWZ ? ld_tr4_swz(sK, 32 * m, kt, zl) : ld_tr4<true>(sK, LDK, 32 * m + 4 * g4, 16 * kt);
-                        const uint2 hi =
-                            SWZ ? ld_tr4_swz(sK, 32 * m + 16, kt, zl) : ld_tr4<true>(sK, LDK, 32 * m + 16 + 4 * g4, 16 * kt);
+                        const uint2 lo = ld_tr4<true>(sK, LDK, 32 * m + 4 * g4, 16 * kt);
+                        const uint2 hi = ld_tr4<true>(sK, LDK, 32 * m + 16 + 4 * g4, 16 * kt);
                         const bf16x8_t av = __builtin_bit_cast(bf16x8_t, uint4{lo.x, lo.y, hi.x, hi.y});
                         hs[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, hs[kt], 0, 0, 0);
                     }
