@@ -443,42 +443,53 @@ __device__ __forceinline__ uint2 ld_tr4(const uint16_t* m, int ld, int r0, int c
 
 // RHS block loaders for block_solve: rows 16I + 4*(l/16) + e (e = 0..3) of column l%16 of a
 // 16-column tile, scaled per row by sc[t].
+// A loader's raw() issues the block's LDS reads; value() forms the scaled block from them.
 template <typename MT> struct RhsFromTransposed {   // the tile's transposed row (this lane's column)
     const typename MM<MT>::S* bt;
     const float* sc;
-    __device__ __forceinline__ f32x4_t operator()(int I) const {
+    struct Raw {
+        f32x4_t f;
+        typename std::conditional<sizeof(typename MM<MT>::S) == 2, uint2, f32x4_t>::type x;
+    };
+    __device__ __forceinline__ Raw raw(int I) const {
         const int t0 = 16 * I + 4 * ((threadIdx.x & 63) >> 4);
-        const f32x4_t f = *reinterpret_cast<const f32x4_t*>(sc + t0);
-        f32x4_t R;
-        if constexpr (sizeof(typename MM<MT>::S) == 2) {
-            const uint2 raw = *reinterpret_cast<const uint2*>(bt + perm<MT>(t0));
-            R[0] = __uint_as_float(raw.x << 16) * f[0];
-            R[1] = __uint_as_float(raw.x & 0xFFFF0000u) * f[1];
-            R[2] = __uint_as_float(raw.y << 16) * f[2];
-            R[3] = __uint_as_float(raw.y & 0xFFFF0000u) * f[3];
-        } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) R[e] = bt[t0 + e] * f[e];
-        }
-        return R;
+        Raw r;
+        r.f = *reinterpret_cast<const f32x4_t*>(sc + t0);
+        if constexpr (sizeof(typename MM<MT>::S) == 2)
+            r.x = *reinterpret_cast<const uint2*>(bt + perm<MT>(t0));
+        else
+            r.x = *reinterpret_cast<const f32x4_t*>(bt + t0);
+        return r;
+    }
+    __device__ __forceinline__ static f32x4_t value(const Raw& r) {
+        if constexpr (sizeof(typename MM<MT>::S) == 2)
+            return f32x4_t{__uint_as_float(r.x.x << 16) * r.f[0], __uint_as_float(r.x.x & 0xFFFF0000u) * r.f[1],
+                           __uint_as_float(r.x.y << 16) * r.f[2], __uint_as_float(r.x.y & 0xFFFF0000u) * r.f[3]};
+        else
+            return r.x * r.f;
     }
 };
 struct RhsFromRows {                               // row-major bf16 rows (perm() columns), columns c0 .. c0+15
     const uint16_t* m;
     int ld, c0;
     const float* sc;
-    __device__ __forceinline__ f32x4_t operator()(int I) const {
+    struct Raw {
+        f32x4_t f;
+        uint2 x;
+    };
+    __device__ __forceinline__ Raw raw(int I) const {
         const int t0 = 16 * I + 4 * ((threadIdx.x & 63) >> 4);
-        const f32x4_t f = *reinterpret_cast<const f32x4_t*>(sc + t0);
-        const uint2 raw = ld_tr4<true>(m, ld, t0, c0);
-        return f32x4_t{__uint_as_float(raw.x << 16) * f[0], __uint_as_float(raw.x & 0xFFFF0000u) * f[1],
-                       __uint_as_float(raw.y << 16) * f[2], __uint_as_float(raw.y & 0xFFFF0000u) * f[3]};
+        return Raw{*reinterpret_cast<const f32x4_t*>(sc + t0), ld_tr4<true>(m, ld, t0, c0)};
+    }
+    __device__ __forceinline__ static f32x4_t value(const Raw& r) {
+        return f32x4_t{__uint_as_float(r.x.x << 16) * r.f[0], __uint_as_float(r.x.x & 0xFFFF0000u) * r.f[1],
+                       __uint_as_float(r.x.y << 16) * r.f[2], __uint_as_float(r.x.y & 0xFFFF0000u) * r.f[3]};
     }
 };
 
 // X = (I + L)^-1 B for NR 16-column tiles of B (64 rows each), by blocked forward substitution:
 // X_I = D_I (B_I - sum_{J<I} L_IJ X_J), D_I = (I + L_II)^-1.  L's off-diagonal blocks are read
-// negated from sLo (row-major, stride ldo), the D_I from sD (block I at sD + 16*I*ldd); rhs[n](I)
+// negated from sLo (row-major, stride ldo), the D_I from sD (block I at sD + 16*I*ldd); rhs[n].raw(I)
 // returns block I of tile n.  X stays in registers in C layout; with v_mfma_f32_16x16x16_bf16 the
 // C layout of one block is the B operand layout of the next product, so each wave solves its own
 // columns without synchronising with the others.  The NR tiles share every read of L and D, and
@@ -487,30 +498,54 @@ template <typename MT, int NR, typename Rhs>
 __device__ __forceinline__ void block_solve(f32x4_t (*X)[4], const typename MM<MT>::S* sLo, int ldo,
                                             const typename MM<MT>::S* sD, int ldd, const Rhs* rhs) {
     const int l = threadIdx.x & 63, g4 = l >> 4, lr = l & 15;
-    f32x4_t R[NR][4];
+    typedef typename MM<MT>::S S;
+    // every LDS read of the solve (the right-hand sides and, for bf16, the blocks of L and D) is
+    // issued before the first is used, so the dependency chain below waits on no LDS access
+    typename Rhs::Raw raw[NR][4];
 #pragma unroll
     for (int I = 0; I < 4; ++I)
 #pragma unroll
-        for (int n = 0; n < NR; ++n) R[n][I] = rhs[n](I);
+        for (int n = 0; n < NR; ++n) raw[n][I] = rhs[n].raw(I);
+    if constexpr (sizeof(S) == 2) {
+        s16x4_t lv[6], dv[4];  // L_IJ at I (I - 1) / 2 + J, J < I
 #pragma unroll
-    for (int I = 0; I < 4; ++I) {
-        if constexpr (sizeof(typename MM<MT>::S) == 2) {
+        for (int I = 0; I < 4; ++I) {
+            dv[I] = *reinterpret_cast<const s16x4_t*>(sD + (16 * I + lr) * ldd + 4 * g4);
+#pragma unroll
+            for (int J = 0; J < I; ++J)
+                lv[I * (I - 1) / 2 + J] = *reinterpret_cast<const s16x4_t*>(sLo + (16 * I + lr) * ldo + 16 * J + 4 * g4);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4_t R[NR][4];
+#pragma unroll
+        for (int I = 0; I < 4; ++I)
+#pragma unroll
+            for (int n = 0; n < NR; ++n) R[n][I] = Rhs::value(raw[n][I]);
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
 #pragma unroll
             for (int J = 0; J < I; ++J) {
-                const s16x4_t av = *reinterpret_cast<const s16x4_t*>(sLo + (16 * I + lr) * ldo + 16 * J + 4 * g4);
 #pragma unroll
                 for (int n = 0; n < NR; ++n) {
                     const s16x4_t bv = __builtin_bit_cast(s16x4_t, uint2{pack_tile_lo(X[n][J]), pack_tile_hi(X[n][J])});
-                    R[n][I] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, R[n][I], 0, 0, 0);
+                    R[n][I] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lv[I * (I - 1) / 2 + J], bv, R[n][I], 0, 0, 0);
                 }
             }
-            const s16x4_t dv = *reinterpret_cast<const s16x4_t*>(sD + (16 * I + lr) * ldd + 4 * g4);
 #pragma unroll
             for (int n = 0; n < NR; ++n) {
                 const s16x4_t rv = __builtin_bit_cast(s16x4_t, uint2{pack_tile_lo(R[n][I]), pack_tile_hi(R[n][I])});
-                X[n][I] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(dv, rv, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                X[n][I] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(dv[I], rv, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
             }
-        } else {
+        }
+    } else {
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4_t R[NR][4];
+#pragma unroll
+        for (int I = 0; I < 4; ++I)
+#pragma unroll
+            for (int n = 0; n < NR; ++n) R[n][I] = Rhs::value(raw[n][I]);
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
 #pragma unroll
             for (int J = 0; J < I; ++J) {
 #pragma unroll
