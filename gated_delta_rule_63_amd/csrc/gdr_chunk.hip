@@ -232,16 +232,28 @@ template <typename MT, int NP, int NI, bool LOWER = false>
 __device__ __forceinline__ void gemm_regs(f32x4_t* acc, const typename MM<MT>::S* sA, int lda, const f32x4_t* Bt) {
     const int l = threadIdx.x & 63, g4 = l >> 4, lr = l & 15;
     if constexpr (sizeof(typename MM<MT>::S) == 2) {
+        // the A reads of two k-steps are issued together, before their products
+        constexpr int MS = NP / 32, G = MS < 2 ? MS : 2;
 #pragma unroll
-        for (int m = 0; m < NP / 32; ++m) {
-            const uint4 bw = {pack_tile_lo(Bt[2 * m]), pack_tile_hi(Bt[2 * m]), pack_tile_lo(Bt[2 * m + 1]),
-                              pack_tile_hi(Bt[2 * m + 1])};
-            const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, bw);
+        for (int m0 = 0; m0 < MS; m0 += G) {
+            bf16x8_t av[G][NI];
 #pragma unroll
-            for (int i = 0; i < NI; ++i) {
-                if (LOWER && 32 * m > 16 * i + 15) continue;
-                const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(sA + (16 * i + lr) * lda + 32 * m + 8 * g4);
-                acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[i], 0, 0, 0);
+            for (int m = 0; m < G; ++m)
+#pragma unroll
+                for (int i = 0; i < NI; ++i)
+                    if (!(LOWER && 32 * (m0 + m) > 16 * i + 15))
+                        av[m][i] = *reinterpret_cast<const bf16x8_t*>(sA + (16 * i + lr) * lda + 32 * (m0 + m) + 8 * g4);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int m = 0; m < G; ++m) {
+                const uint4 bw = {pack_tile_lo(Bt[2 * (m0 + m)]), pack_tile_hi(Bt[2 * (m0 + m)]),
+                                  pack_tile_lo(Bt[2 * (m0 + m) + 1]), pack_tile_hi(Bt[2 * (m0 + m) + 1])};
+                const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, bw);
+#pragma unroll
+                for (int i = 0; i < NI; ++i) {
+                    if (LOWER && 32 * (m0 + m) > 16 * i + 15) continue;
+                    acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[m][i], bv, acc[i], 0, 0, 0);
+                }
             }
         }
     } else {
