@@ -1372,10 +1372,470 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
     }
 }
 
+// ---------------------------------------------------------------------------
+// Pipelined form for the common case (scalar gate, bf16 operands, K = V = 128).
+//
+// B, C and D of a chunk depend only on that chunk's inputs, and E is the only step that needs
+// the state.  Each iteration therefore overlaps E of chunk c with B/C of chunk c + 1:
+//
+//   phase 1  all waves:   A(c+1)  raw rows of chunk c + 1 into LDS, gate prefix and factor tables
+//   phase 2  waves 0-3:   E(c)    v_new, output, state update; wave w owns the 32 state columns
+//                                 32w .. 32w+31 (two 16-column groups)
+//            waves 4-7:   B/C(c+1) L, P and the diagonal inverses of chunk c + 1
+//   phase 3  all waves:   D(c+1)  waves 0-3 solve U for their own columns (kept in registers until
+//                                 E(c+1)); waves 4-7 solve the eight W tiles, two each, into LDS
+//
+// with one workgroup barrier after each phase.  Q, K, P and the gate tables are double-buffered
+// (chunk c is read by E while chunk c + 1 is written by A and B/C).  With four state waves
+// instead of eight, every wave of E reads the shared operands W, Q, K and P for 32 columns at once,
+// which halves E's LDS operand traffic.  The output is formed transposed (O^T = S Q^T + v_new^T P^T,
+// the state and v_new tiles as the A operand) so that each lane holds four consecutive value
+// columns of one token and writes them to o with one 8-byte store: no staging area.
+struct PipeLayout {
+    static constexpr int K = 128, V = 128;
+    static constexpr int LDK = K + 16, LDT = CH + 16, LDO = CH + 16, LDD = 16 + 16, LDV = V + 16;
+    static constexpr size_t ROWK = 2 * CH * LDK;          // [64][LDK] bf16
+    static constexpr size_t ROWT = 2 * CH * LDT;          // [64][LDT] bf16
+    static constexpr int TABF = 10 * CH;                  // floats per gate-table set
+    // gate tables (floats, offsets inside one set)
+    static constexpr int t_g = 0, t_b = CH, t_be = 2 * CH, t_eg = 3 * CH, t_ed = 4 * CH, t_fa = 5 * CH,
+                         t_fb = 8 * CH;
+    static constexpr size_t q0 = 0;                        // Q rows, two buffers
+    static constexpr size_t k0 = q0 + 2 * ROWK;            // K rows, two buffers
+    static constexpr size_t vr = k0 + 2 * ROWK;            // V rows
+    static constexpr size_t w = vr + 2 * CH * LDV;         // -W rows
+    static constexpr size_t lo = w + ROWK;                 // -L off-diagonal blocks
+    static constexpr size_t ld = lo + 2 * CH * LDO;        // diagonal L blocks, fp32
+    static constexpr size_t dd = ld + sizeof(float) * 4 * 16 * LDN;  // diagonal-block inverses
+    static constexpr size_t p0 = dd + 2 * CH * LDD;        // P rows, two buffers
+    static constexpr size_t tab = p0 + 2 * ROWT;           // gate tables, two sets
+    static constexpr size_t total = tab + 2 * sizeof(float) * TABF;
+};
+
+template <typename IO>
+__global__ __launch_bounds__(512) void chunk_pipe_kernel(const ChunkArgs a) {
+    typedef PipeLayout L;
+    typedef MM<bf16_t> M;
+    typedef uint16_t S;
+    constexpr int K = L::K, KT = K / 16;
+    constexpr int LDK = L::LDK, LDT = L::LDT, LDO = L::LDO, LDD = L::LDD, LDV = L::LDV;
+    static_assert(L::total <= 160 * 1024, "LDS budget");
+    static_assert(std::is_same<IO, bf16_t>::value, "bf16 I/O");
+    __shared__ __align__(16) char smem[L::total];
+    auto SP = [&](size_t off) { return reinterpret_cast<S*>(smem + off); };
+    auto FP = [&](size_t off) { return reinterpret_cast<float*>(smem + off); };
+
+    const int h = blockIdx.y, n = blockIdx.z;
+    const int tid = threadIdx.x, l = tid & 63, g4 = l >> 4, lr = l & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t s0 = a.cu_seqlens ? a.cu_seqlens[n] : 0;
+    const int64_t s1 = a.cu_seqlens ? a.cu_seqlens[n + 1] : a.T;
+    const int nc = (int)((s1 - s0 + CH - 1) / CH);
+    auto chunk_len = [&](int ci) {
+        const int64_t bos = s0 + (int64_t)CH * ci;
+        return (s1 - bos) < CH ? (int)(s1 - bos) : CH;
+    };
+    S* const sV = SP(L::vr);
+    S* const sW = SP(L::w);
+    S* const sLo = SP(L::lo);
+    float* const sLd = FP(L::ld);
+    S* const sD = SP(L::dd);
+
+    // The two roles run loops of their own (so that neither holds the other's registers); both take
+    // the same three workgroup barriers per iteration, nc + 1 iterations.
+    if (w < 4) {
+        // ---------------- state waves 0-3: E(it - 1) in phase 2, U of chunk it in phase 3 ----------------
+        // hs[j][kt][e] = S[32w + 16j + lane%16][16kt + 4(l/16) + e]
+        f32x4_t hs[2][KT];
+        const int64_t sbase = ((int64_t)n * a.HV + h) * a.V * K;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt)
+                hs[j][kt] = a.h0 ? *reinterpret_cast<const f32x4_t*>(a.h0 + sbase + (int64_t)(32 * w + 16 * j + lr) * K +
+                                                                    16 * kt + 4 * g4)
+                                 : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        f32x4_t nu[2][4];  // U of the chunk solved in the last phase 3, then v_new
+        // wave 0 reads the gate and beta of a chunk (one value per row) one chunk ahead and forms the
+        // chunk's factor tables in phase 1
+        float gn = 0.0f;
+        uint32_t bn = 0;
+        auto load_gb = [&](int ci) {
+            if (w != 0) return;
+            const int64_t bos = s0 + (int64_t)CH * ci;
+            const int len = chunk_len(ci);
+            const __amdgpu_buffer_rsrc_t rg = chunk_rsrc(a.g + bos * a.HV + h, len, a.HV * 4);
+            gn = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, l * a.HV * 4, 0, 0));
+            const __amdgpu_buffer_rsrc_t rb =
+                chunk_rsrc(static_cast<const char*>(a.beta) + (bos * a.HV + h) * 2, len, a.HV * 2);
+            bn = __builtin_amdgcn_raw_buffer_load_b16(rb, l * a.HV * 2, 0, 0);
+        };
+        if (nc > 0) load_gb(0);
+        for (int it = 0; it <= nc; ++it) {
+            const int b1 = it & 1, b0 = b1 ^ 1;  // buffers of chunk it and of chunk it - 1
+            float* const tb1 = FP(L::tab) + b1 * L::TABF;
+            if (w == 0 && it < nc) {  // inclusive prefix of the 64 gates (rows past the end are 0), factor tables
+                const float br = __uint_as_float(bn << 16);
+                const float x = wave_inclusive_sum(gn);
+                const float xl = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), CH - 1));
+                const float ex = exp_f32(x);
+                tb1[L::t_g + l] = x;
+                tb1[L::t_b + l] = br;
+                tb1[L::t_be + l] = br * ex;
+                tb1[L::t_eg + l] = ex;
+                tb1[L::t_ed + l] = exp_f32(xl - x);
+                float rho[4];
+#pragma unroll
+                for (int J = 0; J < 4; ++J) rho[J] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16 * J + 15));
+#pragma unroll
+                for (int J = 0; J < 3; ++J) tb1[L::t_fa + J * CH + l] = exp_f32(fminf(x - rho[J], 0.0f));
+                const int jb = l >> 4;
+                const float rj = jb == 0 ? rho[0] : jb == 1 ? rho[1] : jb == 2 ? rho[2] : rho[3];
+                tb1[L::t_fb + l] = exp_f32(rj - x);
+            }
+            __syncthreads();  // end of phase 1
+            if (it >= 1) {
+                const int ce = it - 1;
+                const int64_t bos = s0 + (int64_t)CH * ce;
+                const int len = chunk_len(ce);
+                const S* sQ0 = SP(L::q0 + b0 * L::ROWK);
+                const S* sK0 = SP(L::k0 + b0 * L::ROWK);
+                const S* sP0 = SP(L::p0 + b0 * L::ROWT);
+                const float* tb0 = FP(L::tab) + b0 * L::TABF;
+                // v_new_j = U_j - W S_j^T  (LDS holds -W); the A reads of two k-steps are issued together
+#pragma unroll
+                for (int m0 = 0; m0 < K / 32; m0 += 2) {
+                    bf16x8_t av[2][4];
+#pragma unroll
+                    for (int m = 0; m < 2; ++m)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            av[m][i] = *reinterpret_cast<const bf16x8_t*>(sW + (16 * i + lr) * LDK + 32 * (m0 + m) + 8 * g4);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int m = 0; m < 2; ++m)
+#pragma unroll
+                        for (int j = 0; j < 2; ++j) {
+                            const int t = 2 * (m0 + m);
+                            const bf16x8_t bv = __builtin_bit_cast(
+                                bf16x8_t, uint4{pack_tile_lo(hs[j][t]), pack_tile_hi(hs[j][t]), pack_tile_lo(hs[j][t + 1]),
+                                                pack_tile_hi(hs[j][t + 1])});
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                nu[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[m][i], bv, nu[j][i], 0, 0, 0);
+                        }
+                }
+                if (a.o) {
+                    // O^T_j[v][r] = e^{gamma_r} sum_k S[v][k] q_r[k] + sum_t v_new[t][v] P[r][t]; lane (g, i) holds
+                    // value columns 32w + 16j + 4g .. +3 of token 16i + lane%16
+                    f32x4_t ot[2][4];
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) ot[j][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int m0 = 0; m0 < K / 32; m0 += 2) {
+                        bf16x8_t bq[2][4];
+#pragma unroll
+                        for (int m = 0; m < 2; ++m)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                bq[m][i] = *reinterpret_cast<const bf16x8_t*>(sQ0 + (16 * i + lr) * LDK + 32 * (m0 + m) + 8 * g4);
+                        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                        for (int m = 0; m < 2; ++m)
+#pragma unroll
+                            for (int j = 0; j < 2; ++j) {
+                                const int t = 2 * (m0 + m);
+                                const bf16x8_t sa = __builtin_bit_cast(
+                                    bf16x8_t, uint4{pack_tile_lo(hs[j][t]), pack_tile_hi(hs[j][t]),
+                                                    pack_tile_lo(hs[j][t + 1]), pack_tile_hi(hs[j][t + 1])});
+#pragma unroll
+                                for (int i = 0; i < 4; ++i)
+                                    ot[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sa, bq[m][i], ot[j][i], 0, 0, 0);
+                            }
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float f = tb0[L::t_eg + 16 * i + lr];
+#pragma unroll
+                        for (int j = 0; j < 2; ++j) ot[j][i] *= f;
+                    }
+                    {
+                        // P is lower triangular: token tile i needs the steps m with 32m <= 16i + 15
+                        bf16x8_t bp[2][4];
+#pragma unroll
+                        for (int m = 0; m < 2; ++m)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                if (32 * m <= 16 * i + 15)
+                                    bp[m][i] = *reinterpret_cast<const bf16x8_t*>(sP0 + (16 * i + lr) * LDT + 32 * m + 8 * g4);
+                        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                        for (int m = 0; m < 2; ++m)
+#pragma unroll
+                            for (int j = 0; j < 2; ++j) {
+                                const bf16x8_t na = __builtin_bit_cast(
+                                    bf16x8_t, uint4{pack_tile_lo(nu[j][2 * m]), pack_tile_hi(nu[j][2 * m]),
+                                                    pack_tile_lo(nu[j][2 * m + 1]), pack_tile_hi(nu[j][2 * m + 1])});
+#pragma unroll
+                                for (int i = 0; i < 4; ++i)
+                                    if (32 * m <= 16 * i + 15)
+                                        ot[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(na, bp[m][i], ot[j][i], 0, 0, 0);
+                            }
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = 16 * i + lr;
+                        if (r < len) {
+                            uint16_t* dst = static_cast<uint16_t*>(a.o) + ((bos + r) * a.HV + h) * a.V + 32 * w + 4 * g4;
+#pragma unroll
+                            for (int j = 0; j < 2; ++j) {
+                                const f32x4_t x = ot[j][i] * a.scale;
+                                *reinterpret_cast<uint2*>(dst + 16 * j) = uint2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+                            }
+                        }
+                    }
+                }
+                // S <- e^{gamma_last} S + sum_r v_new_r (k_r e^{gamma_last - gamma_r})^T, the K^T operand read
+                // from the row-major K rows with transposing reads
+                const float dec = tb0[L::t_eg + CH - 1];
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int kt = 0; kt < KT; ++kt) hs[j][kt] *= dec;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const f32x4_t f = *reinterpret_cast<const f32x4_t*>(tb0 + L::t_ed + 16 * i + 4 * g4);
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) nu[j][i] *= f;
+                }
+#pragma unroll
+                for (int m = 0; m < CH / 32; ++m) {
+                    bf16x8_t bw[2];
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        bw[j] = __builtin_bit_cast(bf16x8_t, uint4{pack_tile_lo(nu[j][2 * m]), pack_tile_hi(nu[j][2 * m]),
+                                                                   pack_tile_lo(nu[j][2 * m + 1]),
+                                                                   pack_tile_hi(nu[j][2 * m + 1])});
+#pragma unroll
+                    for (int kt = 0; kt < KT; ++kt) {
+                        const uint2 lo = ld_tr4<true>(sK0, LDK, 32 * m + 4 * g4, 16 * kt);
+                        const uint2 hi = ld_tr4<true>(sK0, LDK, 32 * m + 16 + 4 * g4, 16 * kt);
+                        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, uint4{lo.x, lo.y, hi.x, hi.y});
+#pragma unroll
+                        for (int j = 0; j < 2; ++j) hs[j][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bw[j], hs[j][kt], 0, 0, 0);
+                    }
+                }
+            }
+            __syncthreads();  // end of phase 2
+            if (it + 1 < nc) load_gb(it + 1);
+            if (it < nc) {
+                // U for the wave's own 32 value columns
+                f32x4_t X[2][4];
+                const RhsFromRows rhs[2] = {{sV, LDV, 32 * w, tb1 + L::t_b}, {sV, LDV, 32 * w + 16, tb1 + L::t_b}};
+                block_solve<bf16_t, 2>(X, sLo, LDO, sD, LDD, rhs);
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) nu[j][i] = X[j][i];
+                // P of chunk it (read by E in the next iteration): the diagonal tile (w, w) with element-wise
+                // decay, masked above the diagonal, and the off-diagonal tiles q = w (and w + 4 for w < 2) of
+                // (1,0),(2,0),(2,1),(3,0),(3,1),(3,2) with the factor tables
+                const S* sQ1 = SP(L::q0 + b1 * L::ROWK);
+                const S* sK1 = SP(L::k0 + b1 * L::ROWK);
+                S* const sP1 = SP(L::p0 + b1 * L::ROWT);
+                auto store_off = [&](int q, const f32x4_t& cp) {
+                    int I, J;
+                    strict_tile(q, I, J);
+                    const f32x4_t fa = *reinterpret_cast<const f32x4_t*>(tb1 + L::t_fa + J * CH + 16 * I + 4 * g4);
+                    const float fb = tb1[L::t_fb + 16 * J + lr];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        sP1[(16 * I + 4 * g4 + e) * LDT + perm<bf16_t>(16 * J + lr)] = M::cvt((fa[e] * fb) * cp[e]);
+                };
+                int I0, J0;
+                strict_tile(w, I0, J0);
+                f32x4_t cd = {0.f, 0.f, 0.f, 0.f}, c0 = {0.f, 0.f, 0.f, 0.f};
+                M::template nt2<K>(cd, sQ1 + 16 * w * LDK, sK1 + 16 * w * LDK, c0, sQ1 + 16 * I0 * LDK, sK1 + 16 * J0 * LDK,
+                                   LDK);
+                {
+                    const f32x4_t gr = *reinterpret_cast<const f32x4_t*>(tb1 + L::t_g + 16 * w + 4 * g4);
+                    const float gj = tb1[L::t_g + 16 * w + lr];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 16 * w + 4 * g4 + e, jj = 16 * w + lr;
+                        const float x = exp_f32(gr[e] - gj) * cd[e];  // inf above the diagonal is discarded
+                        sP1[r * LDT + perm<bf16_t>(jj)] = M::cvt((r >= jj) ? x : 0.0f);
+                    }
+                }
+                store_off(w, c0);
+                if (w < 2) {
+                    int I1, J1;
+                    strict_tile(w + 4, I1, J1);
+                    f32x4_t c1 = {0.f, 0.f, 0.f, 0.f};
+                    M::nt(c1, sQ1 + 16 * I1 * LDK, LDK, sK1 + 16 * J1 * LDK, LDK, K);
+                    store_off(w + 4, c1);
+                }
+            }
+            __syncthreads();  // end of phase 3
+        }
+        if (a.ht) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int kt = 0; kt < KT; ++kt)
+                    *reinterpret_cast<f32x4_t*>(a.ht + sbase + (int64_t)(32 * w + 16 * j + lr) * K + 16 * kt + 4 * g4) =
+                        hs[j][kt];
+        }
+    } else {
+        // ---------------- waves 4-7: loads, A(it), B/C(it), W of chunk it ----------------
+        constexpr int NLD = 256;
+        const int lt = tid - 256;  // thread index among waves 4-7
+        const int u = w - 4;
+        const int hk = h / (a.HV / a.HK);
+        // strictly upper tiles of both P buffers are never written: zero them once
+        for (int idx = lt; idx < 2 * CH * CH; idx += NLD) {
+            const int b = idx / (CH * CH), r = (idx / CH) % CH, j = idx % CH;
+            if ((j >> 4) > (r >> 4)) SP(L::p0 + b * L::ROWT)[r * LDT + perm<bf16_t>(j)] = M::cvt(0.0f);
+        }
+        typedef Tile<CH, K, NLD> TQ;
+        typedef PairTile<K, NLD> PK;
+        typedef PairTile<128, NLD> PV;
+        Raw8<IO> qn[TQ::NV], kn[2 * PK::NPASS], vn[2 * PV::NPASS];
+        constexpr int ESZ = 2;
+        const int qk_row = a.HK * K * ESZ, v_row = a.HV * a.V * ESZ;
+        auto load_qk = [&](int ci) {
+            const int64_t bos = s0 + (int64_t)CH * ci;
+            const int len = chunk_len(ci);
+            const __amdgpu_buffer_rsrc_t rq =
+                chunk_rsrc(static_cast<const char*>(a.q) + ((bos * a.HK + hk) * K) * ESZ, len, qk_row);
+#pragma unroll
+            for (int i = 0; i < TQ::NV; ++i) qn[i].load(rq, TQ::row(lt, i) * qk_row + TQ::col(lt) * ESZ);
+            const __amdgpu_buffer_rsrc_t rk =
+                chunk_rsrc(static_cast<const char*>(a.k) + ((bos * a.HK + hk) * K) * ESZ, len, qk_row);
+#pragma unroll
+            for (int i = 0; i < PK::NPASS; ++i)
+#pragma unroll
+                for (int q = 0; q < 2; ++q)
+                    kn[2 * i + q].load(rk, (2 * PK::pair(lt, i) + q) * qk_row + PK::col(lt, i) * ESZ);
+        };
+        auto load_vgb = [&](int ci) {
+            const int64_t bos = s0 + (int64_t)CH * ci;
+            const int len = chunk_len(ci);
+            // v == NULL reads as zeros (a zero-byte range): the run that forms a segment's linear map
+            const __amdgpu_buffer_rsrc_t rv = chunk_rsrc(
+                a.v ? static_cast<const char*>(a.v) + ((bos * a.HV + h) * a.V) * ESZ : nullptr, a.v ? len : 0, v_row);
+#pragma unroll
+            for (int i = 0; i < PV::NPASS; ++i)
+#pragma unroll
+                for (int q = 0; q < 2; ++q)
+                    vn[2 * i + q].load(rv, (2 * PV::pair(lt, i) + q) * v_row + PV::col(lt, i) * ESZ);
+        };
+        if (nc > 0) {
+            load_qk(0);
+            load_vgb(0);
+        }
+        for (int it = 0; it <= nc; ++it) {
+            const int b1 = it & 1;
+            S* const sQ1 = SP(L::q0 + b1 * L::ROWK);
+            S* const sK1 = SP(L::k0 + b1 * L::ROWK);
+            float* const tb1 = FP(L::tab) + b1 * L::TABF;
+            // ===== phase 1: A(it) =====
+            if (it < nc) {
+#pragma unroll
+                for (int i = 0; i < TQ::NV; ++i) st8_perm<bf16_t, IO>(sQ1 + TQ::row(lt, i) * LDK, TQ::col(lt), qn[i]);
+#pragma unroll
+                for (int i = 0; i < PK::NPASS; ++i) {
+                    if (PK::valid(lt, i)) {
+                        const int c8 = PK::col(lt, i), pr0 = 2 * PK::pair(lt, i);
+                        st8_perm<bf16_t, IO>(sK1 + pr0 * LDK, c8, kn[2 * i]);
+                        st8_perm<bf16_t, IO>(sK1 + (pr0 + 1) * LDK, c8, kn[2 * i + 1]);
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < PV::NPASS; ++i) {
+                    if (PV::valid(lt, i)) {
+                        const int c8 = PV::col(lt, i), pr0 = 2 * PV::pair(lt, i);
+                        st8_perm<bf16_t, IO>(sV + pr0 * LDV, c8, vn[2 * i]);
+                        st8_perm<bf16_t, IO>(sV + (pr0 + 1) * LDV, c8, vn[2 * i + 1]);
+                    }
+                }
+            }
+            __syncthreads();  // end of phase 1
+            // ===== phase 2: L of chunk it: wave u forms L(u, u) and inverts I + L(u, u), and one or two of the
+            // six off-diagonal blocks (1,0),(2,0),(2,1),(3,0),(3,1),(3,2) =====
+            if (it + 1 < nc) load_qk(it + 1);
+            if (it < nc) {
+                const float* sg = tb1 + L::t_g;
+                const float* sb = tb1 + L::t_b;
+                auto store_off = [&](int q, const f32x4_t& cl) {
+                    int I, J;
+                    strict_tile(q, I, J);
+                    const f32x4_t fa = *reinterpret_cast<const f32x4_t*>(tb1 + L::t_fa + J * CH + 16 * I + 4 * g4);
+                    const f32x4_t br = *reinterpret_cast<const f32x4_t*>(sb + 16 * I + 4 * g4);
+                    const float fb = tb1[L::t_fb + 16 * J + lr];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float d = fa[e] * fb;
+                        sLo[(16 * I + 4 * g4 + e) * LDO + 16 * J + lr] = M::cvt(-br[e] * d * cl[e]);
+                    }
+                };
+                int I0, J0;
+                strict_tile(u, I0, J0);
+                f32x4_t cd = {0.f, 0.f, 0.f, 0.f}, c0 = {0.f, 0.f, 0.f, 0.f};
+                M::template nt2<K>(cd, sK1 + 16 * u * LDK, sK1 + 16 * u * LDK, c0, sK1 + 16 * I0 * LDK, sK1 + 16 * J0 * LDK,
+                                   LDK);
+                float* sN = sLd + u * 16 * LDN;
+                const f32x4_t gr = *reinterpret_cast<const f32x4_t*>(sg + 16 * u + 4 * g4);
+                const f32x4_t br = *reinterpret_cast<const f32x4_t*>(sb + 16 * u + 4 * g4);
+                const float gj = sg[16 * u + lr];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int rr = 4 * g4 + e;
+                    const float x = br[e] * exp_f32(gr[e] - gj) * cd[e];  // inf above the diagonal is discarded
+                    sN[rr * LDN + lr] = (rr > lr) ? x : 0.0f;
+                }
+                // the tile's LDS writes complete before this wave's lanes read other lanes' entries
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                invert_unit_lower_16<bf16_t>(sN, sD + 16 * u * LDD, LDD);
+                store_off(u, c0);
+                if (u < 2) {
+                    int I1, J1;
+                    strict_tile(u + 4, I1, J1);
+                    f32x4_t c1 = {0.f, 0.f, 0.f, 0.f};
+                    M::nt(c1, sK1 + 16 * I1 * LDK, LDK, sK1 + 16 * J1 * LDK, LDK, K);
+                    store_off(u + 4, c1);
+                }
+            }
+            __syncthreads();  // end of phase 2
+            // ===== phase 3: W tiles 2u and 2u + 1 of chunk it =====
+            if (it + 1 < nc) load_vgb(it + 1);
+            if (it < nc) {
+                f32x4_t X[2][4];
+                const RhsFromRows rhs[2] = {{sK1, LDK, 32 * u, tb1 + L::t_be}, {sK1, LDK, 32 * u + 16, tb1 + L::t_be}};
+                block_solve<bf16_t, 2>(X, sLo, LDO, sD, LDD, rhs);
+#pragma unroll
+                for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            sW[(16 * i + 4 * g4 + e) * LDK + perm<bf16_t>(32 * u + 16 * jt + lr)] = M::cvt(-X[jt][i][e]);
+            }
+            __syncthreads();  // end of phase 3
+        }
+    }
+}
+
 template <int K, int V, typename IO, bool PER_K>
 hipError_t launch_fused(const ChunkArgs& a, hipStream_t stream) {
     // bf16: the workgroup owns all V columns; fp32 operands (K = 64 only) use 64-column tiles
     constexpr int BV = std::is_same<IO, float>::value ? 64 : V;
+    if constexpr (K == 128 && V == 128 && std::is_same<IO, bf16_t>::value && !PER_K) {
+        hipLaunchKernelGGL(chunk_pipe_kernel<IO>, dim3(1, a.HV, a.N), dim3(512), 0, stream, a);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL((chunk_fused_kernel<K, BV, IO, IO, PER_K>), dim3(V / BV, a.HV, a.N), dim3(4 * BV), 0, stream,
                        a);
     return hipGetLastError();
