@@ -342,7 +342,7 @@ def main():
 
     prefill_tps = pp.T / s_pre
     leg_info = {
-        "prefill": {"kernel": "chunk_fused_kernel<128,128,bf16> (one launch per call)", "bytes": b_pre,
+        "prefill": {"kernel": "chunk_pipe_kernel<bf16> (one launch per call)", "bytes": b_pre,
                     "flops": f_pre, "secs": s_pre, "sources": ["gdr_chunk.hip", "gdr_device.h"]},
         "decode": {"kernel": "recurrent_kernel (256 x 1 token, fp32 pool, commit)", "bytes": b_dec, "flops": None,
                    "secs": s_dec, "sources": ["gdr_recurrent.hip", "gdr_device.h"]},

@@ -1,5 +1,9 @@
 // Chunked gated delta rule for gfx950: one fused kernel over 64-token chunks (WY/UT form).
 //
+// Two kernels: chunk_pipe_kernel (below, near the end) for bf16 I/O with the scalar gate at K = V = 128,
+// which overlaps the state-dependent step of one chunk with the state-independent steps of the next,
+// and chunk_fused_kernel for every other configuration, described here.
+//
 // One workgroup owns the whole state S[V][K] of one (sequence, value head) -- or a 64-wide
 // V tile of it -- and walks the sequence's chunks in order.  Wave w keeps the 16 state
 // columns v = 16*w + lane%16 of its tile in MFMA accumulators for the whole sequence.
