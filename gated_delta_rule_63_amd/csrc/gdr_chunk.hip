@@ -509,8 +509,10 @@ struct RhsFromRows {                               // row-major bf16 rows (perm(
 // returns block I of tile n.  X stays in registers in C layout; with v_mfma_f32_16x16x16_bf16 the
 // C layout of one block is the B operand layout of the next product, so each wave solves its own
 // columns without synchronising with the others.  The NR tiles share every read of L and D, and
-// their dependency chains interleave.
-template <typename MT, int NR, typename Rhs>
+// their dependency chains interleave.  With FENCE the chain is kept behind the reads (a scheduling
+// barrier); without it the compiler interleaves the two, which the pipelined kernel prefers (its
+// solve shares the SIMD with a wave of the other role).
+template <typename MT, int NR, typename Rhs, bool FENCE = true>
 __device__ __forceinline__ void block_solve(f32x4_t (*X)[4], const typename MM<MT>::S* sLo, int ldo,
                                             const typename MM<MT>::S* sD, int ldd, const Rhs* rhs) {
     const int l = threadIdx.x & 63, g4 = l >> 4, lr = l & 15;
@@ -531,7 +533,7 @@ __device__ __forceinline__ void block_solve(f32x4_t (*X)[4], const typename MM<M
             for (int J = 0; J < I; ++J)
                 lv[I * (I - 1) / 2 + J] = *reinterpret_cast<const s16x4_t*>(sLo + (16 * I + lr) * ldo + 16 * J + 4 * g4);
         }
-        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (FENCE) __builtin_amdgcn_sched_barrier(0);
         f32x4_t R[NR][4];
 #pragma unroll
         for (int I = 0; I < 4; ++I)
@@ -554,7 +556,7 @@ __device__ __forceinline__ void block_solve(f32x4_t (*X)[4], const typename MM<M
             }
         }
     } else {
-        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (FENCE) __builtin_amdgcn_sched_barrier(0);
         f32x4_t R[NR][4];
 #pragma unroll
         for (int I = 0; I < 4; ++I)
@@ -1638,7 +1640,7 @@ __global__ __launch_bounds__(512) void chunk_pipe_kernel(const ChunkArgs a) {
                 // U for the wave's own 32 value columns
                 f32x4_t X[2][4];
                 const RhsFromRows rhs[2] = {{sV, LDV, 32 * w, tb1 + L::t_b}, {sV, LDV, 32 * w + 16, tb1 + L::t_b}};
-                block_solve<bf16_t, 2>(X, sLo, LDO, sD, LDD, rhs);
+                block_solve<bf16_t, 2, RhsFromRows, false>(X, sLo, LDO, sD, LDD, rhs);
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -1818,7 +1820,7 @@ __global__ __launch_bounds__(512) void chunk_pipe_kernel(const ChunkArgs a) {
             if (it < nc) {
                 f32x4_t X[2][4];
                 const RhsFromRows rhs[2] = {{sK1, LDK, 32 * u, tb1 + L::t_be}, {sK1, LDK, 32 * u + 16, tb1 + L::t_be}};
-                block_solve<bf16_t, 2>(X, sLo, LDO, sD, LDD, rhs);
+                block_solve<bf16_t, 2, RhsFromRows, false>(X, sLo, LDO, sD, LDD, rhs);
 #pragma unroll
                 for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
