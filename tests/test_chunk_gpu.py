@@ -139,6 +139,24 @@ def test_chunk_runs_without_workspace():
     _check(p, o1, h1)
 
 
+def test_outputs_stay_in_their_rows_and_final_state_in_place():
+    """Every token row of o is written, nothing past the last row is, and the final state can overwrite
+    the initial state in place (lengths cover both buffer parities of the chunk loop and short tails)."""
+    lengths = [1, 63, 64, 65, 128, 129, 200]
+    p = inputs.dense_problem(77, lengths, HK=2, HV=4, K=128, V=128, io_dtype="bf16")
+    d = problem_to_dev(p)
+    guard = 64
+    sentinel = 0x7FC1  # a bf16 NaN pattern
+    o_big = torch.full((p.T + guard, p.HV, p.V), sentinel, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    o = o_big[: p.T]
+    state = d["h0"].clone()  # initial state in, final state out, same memory
+    gdr.gdr_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], p.scale, state, o=o, final_state=state)
+    torch.cuda.synchronize()
+    tail = o_big[p.T:].view(torch.int16)
+    assert bool((tail == sentinel).all()), "rows past the end were written"
+    _check(p, o, state)
+
+
 def _sampled_heads_oracle(p, heads):
     """Oracle on a subset of heads (HK == HV here, so key head = value head)."""
     assert p.HK == p.HV
