@@ -841,7 +841,6 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
 
     for (int ci = 0; ci < nc; ++ci) {
         const int64_t bos = s0 + (int64_t)CH * ci;
-        const int len = (s1 - bos) < CH ? (int)(s1 - bos) : CH;
 
         // current chunk <- prefetched registers (the next chunk's loads are issued in B/C, D and E)
         Raw8<IO> qr[TQ::NV], kr[2 * PK::NPASS], vr[2 * PV::NPASS];
