@@ -157,6 +157,41 @@ def test_outputs_stay_in_their_rows_and_final_state_in_place():
     _check(p, o, state)
 
 
+def test_varlen_prefill_graph_capture_replay_equals_eager():
+    """A varlen prefill call (several sequences, the pipelined kernel) is capturable: it allocates
+    nothing and records no memset; every replay, with eager work between replays, equals the eager
+    result bit for bit."""
+    p = inputs.dense_problem(78, [65, 130, 1, 64], HK=2, HV=4, K=128, V=128, io_dtype="bf16")
+    d = problem_to_dev(p)
+    o = torch.zeros((p.T, p.HV, p.V), dtype=torch.bfloat16, device="cuda")
+    ht = torch.zeros((p.N, p.HV, p.V, p.K), dtype=torch.float32, device="cuda")
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+
+    def call():
+        gdr.gdr_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], p.scale, d["h0"], o=o,
+                          final_state=ht, workspace=ws)
+
+    call()
+    torch.cuda.synchronize()
+    o_ref, ht_ref = o.clone(), ht.clone()
+    _check(p, o_ref, ht_ref)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for _ in range(3):
+        o.zero_()
+        ht.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(ht, ht_ref)
+
+
 def _sampled_heads_oracle(p, heads):
     """Oracle on a subset of heads (HK == HV here, so key head = value head)."""
     assert p.HK == p.HV
