@@ -1381,21 +1381,25 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
 // Pipelined form for the common case (scalar gate, bf16 operands, K = V = 128).
 //
 // B, C and D of a chunk depend only on that chunk's inputs, and E is the only step that needs
-// the state.  Each iteration therefore overlaps E of chunk c with B/C of chunk c + 1:
+// the state.  Each iteration therefore overlaps E of chunk c with the L products and inverses of
+// chunk c + 1:
 //
-//   phase 1  all waves:   A(c+1)  raw rows of chunk c + 1 into LDS, gate prefix and factor tables
+//   phase 1  waves 4-7:   A(c+1)  raw q, k, v rows of chunk c + 1 into LDS (loaded one chunk ahead)
+//            wave 0:              gate prefix and factor tables of chunk c + 1
 //   phase 2  waves 0-3:   E(c)    v_new, output, state update; wave w owns the 32 state columns
 //                                 32w .. 32w+31 (two 16-column groups)
-//            waves 4-7:   B/C(c+1) L, P and the diagonal inverses of chunk c + 1
-//   phase 3  all waves:   D(c+1)  waves 0-3 solve U for their own columns (kept in registers until
-//                                 E(c+1)); waves 4-7 solve the eight W tiles, two each, into LDS
+//            waves 4-7:   B/C(c+1) L and the diagonal inverses of chunk c + 1
+//   phase 3  waves 0-3:   D(c+1)  U for the wave's own columns (kept in registers until E(c+1)),
+//                                 then the ten P tiles of chunk c + 1
+//            waves 4-7:   D(c+1)  the eight W tiles, two per wave, into LDS
 //
-// with one workgroup barrier after each phase.  Q, K, P and the gate tables are double-buffered
-// (chunk c is read by E while chunk c + 1 is written by A and B/C).  With four state waves
-// instead of eight, every wave of E reads the shared operands W, Q, K and P for 32 columns at once,
-// which halves E's LDS operand traffic.  The output is formed transposed (O^T = S Q^T + v_new^T P^T,
-// the state and v_new tiles as the A operand) so that each lane holds four consecutive value
-// columns of one token and writes them to o with one 8-byte store: no staging area.
+// The two roles run loops of their own, with one workgroup barrier after each phase.  Q, K, P and
+// the gate tables are double-buffered (chunk c is read by E while chunk c + 1 is written).  With
+// four state waves instead of eight, every wave of E reads the shared operands W, Q, K and P for
+// 32 columns at once, which halves E's LDS operand traffic.  The output is formed transposed
+// (O^T = S Q^T + v_new^T P^T, the state and v_new tiles as the A operand) so that each lane holds
+// four consecutive value columns of one token and writes them to o with one 8-byte store: no
+// staging area.
 struct PipeLayout {
     static constexpr int K = 128, V = 128;
     static constexpr int LDK = K + 16, LDT = CH + 16, LDO = CH + 16, LDD = 16 + 16, LDV = V + 16;
@@ -1449,7 +1453,7 @@ __global__ __launch_bounds__(512) void chunk_pipe_kernel(const ChunkArgs a) {
     // The two roles run loops of their own (so that neither holds the other's registers); both take
     // the same three workgroup barriers per iteration, nc + 1 iterations.
     if (w < 4) {
-        // ---------------- state waves 0-3: E(it - 1) in phase 2, U of chunk it in phase 3 ----------------
+        // ------- state waves 0-3: tables of chunk it (wave 0) in phase 1, E(it - 1) in phase 2, U and P of chunk it in phase 3 -------
         // hs[j][kt][e] = S[32w + 16j + lane%16][16kt + 4(l/16) + e]
         f32x4_t hs[2][KT];
         const int64_t sbase = ((int64_t)n * a.HV + h) * a.V * K;
