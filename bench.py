@@ -364,9 +364,10 @@ def main():
                                       "secs": extra_ms["verify_prepass"] / 1e3,
                                       "sources": ["gdr_gating.hip"] + gated_sources}
     if "kda" in extra_ms:
-        leg_info["kda"] = {"kernel": "chunk_fused_kernel<128,128,bf16,per-K gate> (1 x 65573 tokens, 16 heads)",
+        leg_info["kda"] = {"kernel": "segmented route: chunk_fused_kernel<128,128,bf16,per-K gate> x3, scan, setup, "
+                                     "copy (1 x 65573 tokens, 16 heads; bytes, time and traffic per call)",
                            "bytes": _alg_bytes_prefill(pk), "flops": None, "secs": extra_ms["kda"] / 1e3,
-                           "sources": ["gdr_chunk.hip", "gdr_device.h"]}
+                           "sources": ["gdr_chunk.hip", "gdr_device.h", "gdr_cp.hip", "gdr_api.hip"]}
     traffic = _measured_traffic()
 
     def roofline(leg):
