@@ -1224,8 +1224,10 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
                 if (PV::valid(tid, i))
                     st_pair_t<MT, IO>(sVT, LDT, PV::col(tid, i), 2 * PV::pair(tid, i), vr[2 * i], vr[2 * i + 1]);
             }
+            // Q e^gamma only feeds the output: skipped when no outputs are wanted (segment-map runs)
 #pragma unroll
             for (int i = 0; i < TQ::NV; ++i) {
+                if (!a.o) break;
                 const int r = TQ::row(tid, i), c8 = TQ::col(tid);
                 float y[8], gq[8];
                 qr[i].get(y);
@@ -1299,7 +1301,8 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
         // v_new = U - W S^T  (LDS holds -W)
         gemm_regs<MT, K, 4>(nu, sW, LDK, hs);
         if (ci + 1 < nc) load_vgb(ci + 1);
-        // O = scale (diag(e^gamma) Q S^T + P v_new)
+        // O = scale (diag(e^gamma) Q S^T + P v_new), when outputs are wanted
+        if (a.o) {
         f32x4_t oa[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) oa[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -1323,6 +1326,7 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
                 else
                     *reinterpret_cast<uint16_t*>(so + OS::off(r, c)) = f32_to_bf16(a.scale * oa[i][e]);
             }
+        }
         }
         // S <- e^{gamma_last} S + sum_r v_new_r (k_r e^{gamma_last - gamma_r})^T
         if constexpr (!PER_K) {
