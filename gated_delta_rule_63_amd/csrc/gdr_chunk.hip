@@ -163,8 +163,8 @@ __device__ __forceinline__ int iperm(int p) {
 // c0 += A0 B'^T and c1 += A1 B'^T over KD columns (16-row tiles from LDS, as MM::nt), where B'
 // is B with every column multiplied by f[column] (fp32, physical column order; NULL: none).  The
 // two products share the scaled B operand, and every operand read is issued before the first
-// product.
-template <typename MT, int KD>
+// product.  With TWO = false only c0 is formed (a1 is not read).
+template <typename MT, int KD, bool TWO = true>
 __device__ __forceinline__ void nt2_bscaled(f32x4_t& c0, const typename MM<MT>::S* a0, f32x4_t& c1,
                                             const typename MM<MT>::S* a1, int lda, const typename MM<MT>::S* b,
                                             int ldb, const float* f) {
@@ -182,7 +182,7 @@ __device__ __forceinline__ void nt2_bscaled(f32x4_t& c0, const typename MM<MT>::
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             va0[s] = *reinterpret_cast<const bf16x8_t*>(a0 + oa + h0 + 32 * s);
-            va1[s] = *reinterpret_cast<const bf16x8_t*>(a1 + oa + h0 + 32 * s);
+            if constexpr (TWO) va1[s] = *reinterpret_cast<const bf16x8_t*>(a1 + oa + h0 + 32 * s);
             vb[s] = *reinterpret_cast<const uint4*>(b + ob + h0 + 32 * s);
             if (f) {
                 f0[s] = *reinterpret_cast<const f32x4_t*>(f + of + h0 + 32 * s);
@@ -200,7 +200,7 @@ __device__ __forceinline__ void nt2_bscaled(f32x4_t& c0, const typename MM<MT>::
             }
             const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, w);
             c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va0[s], bv, c0, 0, 0, 0);
-            c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va1[s], bv, c1, 0, 0, 0);
+            if constexpr (TWO) c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va1[s], bv, c1, 0, 0, 0);
         }
         }
     } else {
@@ -210,13 +210,13 @@ __device__ __forceinline__ void nt2_bscaled(f32x4_t& c0, const typename MM<MT>::
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             va0[s] = a0[oa + 4 * s];
-            va1[s] = a1[oa + 4 * s];
+            if constexpr (TWO) va1[s] = a1[oa + 4 * s];
             vb[s] = f ? b[ob + 4 * s] * f[4 * s + (l >> 4)] : b[ob + 4 * s];
         }
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             c0 = __builtin_amdgcn_mfma_f32_16x16x4f32(va0[s], vb[s], c0, 0, 0, 0);
-            c1 = __builtin_amdgcn_mfma_f32_16x16x4f32(va1[s], vb[s], c1, 0, 0, 0);
+            if constexpr (TWO) c1 = __builtin_amdgcn_mfma_f32_16x16x4f32(va1[s], vb[s], c1, 0, 0, 0);
         }
     }
 }
@@ -1096,7 +1096,7 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
                         rk[i] = kv[i] * er;
                     }
                     M::st8(sK + r * LDK + p0, lk);
-                    M::st8(sQ + r * LDK + p0, lq);
+                    if (a.o) M::st8(sQ + r * LDK + p0, lq);  // P only feeds the output
                     M::st8(sRG + r * LDK + p0, rk);
                 }
                 for (int u = tid; u < 7 * K; u += NTHR) {
@@ -1113,17 +1113,21 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
                     lower_tile(tp, I, J);
                     const int fi = J == I ? I : J == I - 1 ? -1 : (I == 2 ? 4 : (J == 0 ? 5 : 6));
                     f32x4_t cl = {0.f, 0.f, 0.f, 0.f}, cp = {0.f, 0.f, 0.f, 0.f};
-                    nt2_bscaled<MT, K>(cl, sK + 16 * I * LDK, cp, sQ + 16 * I * LDK, LDK, sRG + 16 * J * LDK, LDK,
-                                       fi >= 0 ? fperm + fi * K : nullptr);
+                    if (a.o)
+                        nt2_bscaled<MT, K>(cl, sK + 16 * I * LDK, cp, sQ + 16 * I * LDK, LDK, sRG + 16 * J * LDK, LDK,
+                                           fi >= 0 ? fperm + fi * K : nullptr);
+                    else  // no outputs: P is not needed
+                        nt2_bscaled<MT, K, false>(cl, sK + 16 * I * LDK, cp, sQ + 16 * I * LDK, LDK, sRG + 16 * J * LDK,
+                                                  LDK, fi >= 0 ? fperm + fi * K : nullptr);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int rr = 4 * g4 + e, r = 16 * I + rr, j = 16 * J + lr;
                         if (J < I) {
                             sLo[r * LDO + j] = M::cvt(-sb[r] * cl[e]);
-                            sP[r * LDT + perm<MT>(j)] = M::cvt(cp[e]);
+                            if (a.o) sP[r * LDT + perm<MT>(j)] = M::cvt(cp[e]);
                         } else {  // diagonal blocks: L in fp32, strictly lower, for the inversion; P lower
                             sLd[I * 16 * LDN + rr * LDN + lr] = (lr < rr) ? sb[r] * cl[e] : 0.0f;
-                            sP[r * LDT + perm<MT>(j)] = M::cvt((lr <= rr) ? cp[e] : 0.0f);
+                            if (a.o) sP[r * LDT + perm<MT>(j)] = M::cvt((lr <= rr) ? cp[e] : 0.0f);
                         }
                     }
                 }
