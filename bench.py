@@ -158,8 +158,10 @@ def _cpu_baseline(p, target_s: float = 12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    # the first steps after process start run several percent slower (clocks and caches settle):
+    # the default warm-up lets the timed steps see the steady state
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--legs", default="prefill,decode,verify",
                     help="comma-separated subset of legs to run (profiling passes); the JSON line needs all three")
