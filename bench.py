@@ -41,6 +41,7 @@ import numpy as np
 
 HBM_PEAK = 8.0e12          # B/s
 BF16_MFMA_PEAK = 2.5e15    # dense flop/s
+FP32_VALU_PEAK = 157.3e12  # flop/s, fp32 vector
 
 
 def _alg_bytes_prefill(p):
@@ -404,6 +405,13 @@ def main():
     roof_legs["prefill"]["frac_bf16_mfma_full_tile"] = f_pre_full / s_pre / BF16_MFMA_PEAK
     roof_legs["prefill"]["alg_flops_full_tile"] = f_pre_full
     roof_legs["decode"]["state_GBps"] = state_bytes_dec / s_dec / 1e9
+    # the token loop is fp32 vector arithmetic (7 V K flops per token and value head): its share of the
+    # fp32 VALU peak shows how far the decode and verify launches are from an ALU bound
+    for leg, pr, secs in (("decode", pd, s_dec), ("verify", pv, s_ver)):
+        active = int(sum(n for n, slot in zip(pr.lengths, pr.state_indices) if slot >= 0))  # padded: no work
+        fl = 7.0 * pr.V * pr.K * pr.HV * active
+        roof_legs[leg]["alg_valu_flops_per_launch"] = fl
+        roof_legs[leg]["frac_fp32_valu"] = fl / secs / FP32_VALU_PEAK
     out = {
         "metric": "GDN prefill tokens/s + decode state GB/s (fraction of HBM/MFMA peak), 1 GPU",
         "value": prefill_tps,
