@@ -44,14 +44,14 @@ BF16_MFMA_PEAK = 2.5e15    # dense flop/s
 FP32_VALU_PEAK = 157.3e12  # flop/s, fp32 vector
 
 
-def _alg_bytes_prefill(p):
+def _alg_bytes_prefill(p, with_cu: bool = True):
     """q, k, v, o (io dtype) + g fp32 (per key channel for the per-K gate) + beta (io dtype) per
-    token-head, initial (if given) + final state, cu_seqlens."""
+    token-head, initial (if given) + final state, cu_seqlens (when the call passes them)."""
     io = 2 if p.io_dtype == "bf16" else 4
     gate = p.HV * p.K * 4 if p.per_k_gate else p.HV * 4
     per_tok = p.HK * p.K * io * 2 + p.HV * p.V * io * 2 + gate + p.HV * io
     states = (2 if p.initial_state is not None else 1) * p.N * p.HV * p.V * p.K * 4
-    return p.T * per_tok + states + 4 * (p.N + 1)
+    return p.T * per_tok + states + (4 * (p.N + 1) if with_cu else 0)
 
 
 def _alg_flops_prefill(p, full_tile=False):
@@ -369,7 +369,7 @@ def main():
     if "kda" in extra_ms:
         leg_info["kda"] = {"kernel": "segmented route: chunk_fused_kernel<128,128,bf16,per-K gate> x3, scan, setup, "
                                      "copy (1 x 65573 tokens, 16 heads; bytes, time and traffic per call)",
-                           "bytes": _alg_bytes_prefill(pk), "flops": None, "secs": extra_ms["kda"] / 1e3,
+                           "bytes": _alg_bytes_prefill(pk, with_cu=False), "flops": None, "secs": extra_ms["kda"] / 1e3,
                            "sources": ["gdr_chunk.hip", "gdr_device.h", "gdr_cp.hip", "gdr_api.hip"]}
     traffic = _measured_traffic()
 

@@ -1,0 +1,48 @@
+"""The benchmark's algorithmic counts (the numerators of every roofline fraction it reports), pinned
+to hand-derived values for the workloads: bytes a single pass must move and flops of the chunk
+algorithm.  CPU only; the benchmark module imports torch and the oracle only inside its GPU and
+CPU-baseline paths."""
+import bench
+from gated_delta_rule_63_amd import inputs
+
+
+def test_prefill_bytes_and_flops():
+    p = inputs.prefill()
+    # per token-head: q, k, v, o in bf16 (1024 B), g fp32 (4 B), beta bf16 (2 B); HK = HV = 32
+    per_tok = 32 * (4 * 128 * 2 + 4 + 2)
+    states = 2 * 8 * 32 * 128 * 128 * 4  # initial and final fp32 states
+    assert bench._alg_bytes_prefill(p) == 32768 * per_tok + states + 4 * 9 == 1_113_587_748
+    # per 64-token chunk-head, triangle-exact: 8,992,085 flops; whole MFMA tiles: 11,534,336
+    assert bench._alg_flops_prefill(p) == 8_992_085 * 32768 * 32 // 64 == 147_326_320_640
+    assert bench._alg_flops_prefill(p, full_tile=True) == 11_534_336 * 32768 * 32 // 64 == 188_978_561_024
+
+
+def test_chunk_flops_per_chunk_head_by_term():
+    # K K^T strictly lower, (I+L)^-1, A.(beta V), A.(beta e^g K), W.h, (K*)^T v_new, Q.h,
+    # Q K^T and P v_new over the lower triangle including the diagonal (K = V = 128, C = 64)
+    terms = [516_096, 87_381, 516_096, 516_096, 2_097_152, 2_097_152, 2_097_152, 532_480, 532_480]
+    p = inputs.dense_problem(1, [64], HK=1, HV=1, K=128, V=128, io_dtype="bf16")
+    assert bench._alg_flops_prefill(p) == sum(terms) == 8_992_085
+
+
+def test_kda_bytes_without_cu_seqlens():
+    p = inputs.kda()
+    # gk is fp32 per key channel (512 B per token-head); no initial state; the call passes no cu_seqlens
+    per_tok = 16 * (4 * 128 * 2 + 128 * 4 + 2)
+    assert bench._alg_bytes_prefill(p, with_cu=False) == 65573 * per_tok + 16 * 128 * 128 * 4 == 1_614_668_960
+
+
+def test_decode_and_verify_bytes():
+    d = inputs.decode()
+    active = int(sum(1 for s in d.state_indices if s >= 0))
+    assert active == 230 and d.N - active == 26
+    # per active sequence: the fp32 state read and written for 32 heads, the index, and one token's
+    # q, k (16 key heads), v, o (32 value heads) in bf16 with g fp32 and beta bf16; 4 B per padded one
+    per_seq = 4 + 32 * 128 * 128 * 4 * 2 + (2 * 16 * 128 * 2 + 2 * 32 * 128 * 2 + 32 * 4 + 32 * 2)
+    assert per_seq == 4_219_076
+    assert bench._alg_bytes_paged(d, with_ibuf=False) == active * per_seq + 26 * 4 == 970_387_584
+    v = inputs.verify()
+    # 64 sequences x 12 tokens: bf16 state read once, per-token bf16 states written, cu_seqlens
+    per_seq = 4 + 32 * 128 * 128 * 2 + 12 * (2 * 16 * 128 * 2 + 2 * 32 * 128 * 2 + 32 * 4 + 32 * 2) \
+        + 12 * 32 * 128 * 128 * 2 + 4
+    assert bench._alg_bytes_paged(v, with_ibuf=True) == 64 * per_seq + 4 * 65 == 891_437_828
