@@ -192,6 +192,25 @@ def test_varlen_prefill_graph_capture_replay_equals_eager():
         assert torch.equal(o, o_ref) and torch.equal(ht, ht_ref)
 
 
+@pytest.mark.parametrize("seed", range(200, 210))
+def test_random_shapes_bf16_k128(seed):
+    """Seeded random shapes through the bf16, scalar-gate, K = V = 128 path (the pipelined kernel):
+    1-12 sequences of 0-300 tokens, GQA ratios 1, 2 and 4, decay ranges up to [-2, 0], with and
+    without an initial state."""
+    rng = np.random.default_rng(seed)
+    N = int(rng.integers(1, 13))
+    lengths = [int(x) for x in rng.integers(0, 301, size=N)]
+    if sum(lengths) == 0:
+        lengths[0] = 1  # empty batches are covered on their own
+    HK = int(rng.choice([1, 2, 4]))
+    HV = HK * int(rng.choice([1, 2, 4]))
+    lo = float(rng.choice([-0.1, -0.5, -2.0]))
+    p = inputs.dense_problem(seed, lengths, HK=HK, HV=HV, K=128, V=128, io_dtype="bf16", g_range=(lo, 0.0))
+    with_h0 = bool(rng.integers(0, 2))
+    o, ht = _chunk(p, h0=with_h0)
+    _check(p, o, ht, h0=with_h0)
+
+
 def _sampled_heads_oracle(p, heads):
     """Oracle on a subset of heads (HK == HV here, so key head = value head)."""
     assert p.HK == p.HV
