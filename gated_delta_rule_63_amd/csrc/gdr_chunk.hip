@@ -1461,7 +1461,8 @@ __global__ __launch_bounds__(512) void chunk_pipe_kernel(const ChunkArgs a) {
     // The two roles run loops of their own (so that neither holds the other's registers); both take
     // the same three workgroup barriers per iteration, nc + 1 iterations.
     if (w < 4) {
-        // ------- state waves 0-3: tables of chunk it (wave 0) in phase 1, E(it - 1) in phase 2, U and P of chunk it in phase 3 -------
+        // ---- state waves 0-3: phase 1 the tables of chunk it (wave 0), phase 2 E(it - 1),
+        //      phase 3 U and P of chunk it ----
         // hs[j][kt][e] = S[32w + 16j + lane%16][16kt + 4(l/16) + e]
         f32x4_t hs[2][KT];
         const int64_t sbase = ((int64_t)n * a.HV + h) * a.V * K;
@@ -1706,7 +1707,7 @@ __global__ __launch_bounds__(512) void chunk_pipe_kernel(const ChunkArgs a) {
                         hs[j][kt];
         }
     } else {
-        // ---------------- waves 4-7: loads, A(it), B/C(it), W of chunk it ----------------
+        // ---- waves 4-7: loads, phase 1 A(it), phase 2 L and the inverses of chunk it, phase 3 W of chunk it ----
         constexpr int NLD = 256;
         const int lt = tid - 256;  // thread index among waves 4-7
         const int u = w - 4;
