@@ -105,13 +105,24 @@ _CSRC = os.path.join(_HERE, "gated_delta_rule_63_amd", "csrc")
 _TRAFFIC = os.path.join(_HERE, "profiles", "hbm_traffic.md")
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source with comments and all whitespace removed: edits to comments or layout leave it
+    unchanged, any change to the code changes it."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return "".join(text.split())
+
+
 def _source_digest(names):
-    """sha256 over the kernel sources a leg runs, so measured traffic is dropped once they change."""
+    """sha256 over the code (comments and whitespace stripped) of the kernel sources a leg runs, so
+    measured traffic is dropped once the code changes.  Never edited by hand: a changed digest means
+    the counters are taken again."""
     import hashlib
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(_CSRC, n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(_CSRC, n), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()
 
 
@@ -130,16 +141,28 @@ def _measured_traffic():
     return out
 
 
-def _cpu_baseline(p, target_s: float = 12.0):
-    """The fp64 oracle on the host cores, on the first heads of the prefill workload."""
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _cpu_baseline(p, pass_s: float = 4.0):
+    """The fp64 oracle on the host cores, on the first heads of the prefill workload: the first pass
+    picks as many whole heads as fit about ``pass_s`` seconds, then the same heads run twice more;
+    the median of the three passes is reported."""
     import oracle  # test infrastructure: only this leg of the benchmark loads it
     from gated_delta_rule_63_amd import inputs
 
     threads = oracle.default_threads()
     w = [inputs.widen(x) for x in (p.q, p.k, p.v, p.g, p.beta)]
-    heads_done, secs = 0, 0.0
-    h = 0
-    while secs < target_s and h < p.HV:
+
+    def run_head(h):
         sel = lambda x: np.ascontiguousarray(x[:, h:h + 1])
         hk = h // (p.HV // p.HK)
         t0 = time.perf_counter()
@@ -147,19 +170,92 @@ def _cpu_baseline(p, target_s: float = 12.0):
                          sel(w[2]), sel(w[3]), sel(w[4]), p.cu_seqlens, p.scale,
                          None if p.initial_state is None else np.ascontiguousarray(p.initial_state[:, h:h + 1]),
                          threads=threads)
-        secs += time.perf_counter() - t0
-        heads_done += 1
-        h += 1
-    tok_per_s = p.T * heads_done / p.HV / secs
+        return time.perf_counter() - t0
+
+    first, heads = 0.0, 0
+    while first < pass_s and heads < p.HV:
+        first += run_head(heads)
+        heads += 1
+    passes = [first] + [sum(run_head(h) for h in range(heads)) for _ in range(2)]
+    secs = float(np.median(passes))
+    tok_per_s = p.T * heads / p.HV / secs
     return {"value": tok_per_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"prefill workload, all {p.T} tokens of {heads_done} of {p.HV} value heads "
-                      f"({secs:.1f} s), scaled to whole-problem tokens/s"}
+            "cpu_model": _cpu_model(), "passes_s": passes,
+            "sample": f"prefill workload, all {p.T} tokens of {heads} of {p.HV} value heads per pass, "
+                      f"median of 3 passes ({secs:.2f} s), scaled to whole-problem tokens/s"}
+
+
+def _provenance():
+    """git commit (where the tree carries .git), a digest of the library sources (always), ROCm and
+    torch versions."""
+    import hashlib
+    import subprocess
+    sha = None
+    try:
+        sha = subprocess.run(["git", "-C", _HERE, "rev-parse", "HEAD"], capture_output=True, text=True,
+                             timeout=10).stdout.strip() or None
+    except (OSError, subprocess.SubprocessError):
+        sha = None
+    h = hashlib.sha256()
+    for root in (_CSRC, os.path.join(_HERE, "include")):
+        for dp, _, fs in sorted(os.walk(root)):
+            for fn in sorted(fs):
+                if fn.endswith((".hip", ".h")):
+                    with open(os.path.join(dp, fn), "rb") as f:
+                        h.update(f.read())
+    rocm = None
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            rocm = f.read().strip()
+    except OSError:
+        pass
+    import torch
+    return {"git_sha": sha, "source_sha256": h.hexdigest(), "rocm": rocm, "torch": torch.__version__,
+            "torch_hip": getattr(torch.version, "hip", None)}
+
+
+def _measured_mfma_peak(dev):
+    """Dense bf16 MFMA rate measured on this GPU by the probe kernel (back-to-back 16x16x32 products
+    on every SIMD), median of 5 launches; None when the probe library is missing."""
+    import ctypes
+    import torch
+    path = os.path.join(_HERE, "gated_delta_rule_63_amd", "libgdr_probe.so")
+    if not os.path.exists(path):
+        return None
+    L = ctypes.CDLL(path)
+    L.gdr_probe_mfma_bf16.restype = ctypes.c_int
+    L.gdr_probe_mfma_bf16.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    L.gdr_probe_mfma_bf16_flops.restype = ctypes.c_double
+    L.gdr_probe_mfma_bf16_flops.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    blocks, iters = 4096, 2048
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    ts = []
+    for i in range(7):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        rc = L.gdr_probe_mfma_bf16(blocks, iters, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stream))
+        e1.record()
+        torch.cuda.synchronize()
+        if rc != 0:
+            return None
+        if i >= 2:
+            ts.append(e0.elapsed_time(e1) / 1e3)
+    fl = L.gdr_probe_mfma_bf16_flops(blocks, iters)
+    return {"tflops": fl / float(np.median(ts)) / 1e12, "kernel": "v_mfma_f32_16x16x32_bf16, 8 chains per wave, "
+            f"{blocks} x 256 threads x {iters} iterations", "launches": len(ts)}
+
+
+def _stats(ms):
+    a = np.asarray(ms, dtype=np.float64)
+    return {"median": float(np.median(a)), "p90": float(np.percentile(a, 90)), "mean": float(np.mean(a)),
+            "min": float(np.min(a)), "n": int(a.size)}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=100)
     # the first steps after process start run several percent slower (clocks and caches settle):
     # the default warm-up lets the timed steps see the steady state
     ap.add_argument("--warmup", type=int, default=20)
@@ -313,7 +409,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     # legs outside the step, timed the same way after it
-    extra_ms = {}
+    extra_ms, extra_stats = {}, {}
     if extra and len(legs) == 3:  # (also in a counter pass, so its kernels are sampled)
         print("bench: timing the gated legs", file=sys.stderr, flush=True)
         for _ in range(args.warmup):
@@ -328,12 +424,15 @@ def main():
                 fn()
                 xev[name][i][1].record()
         torch.cuda.synchronize()
-        extra_ms = {name: float(np.mean([a.elapsed_time(b) for a, b in xev[name]])) for name, _ in extra}
+        extra_stats = {name: _stats([a.elapsed_time(b) for a, b in xev[name]]) for name, _ in extra}
+        extra_ms = {name: st["mean"] for name, st in extra_stats.items()}
     if len(legs) < 3 or args.calib_copy_mib:
         print(json.dumps({"profiling_pass": [n for n, _ in legs], "steps": K}))
         return
-    leg_ms = {name: float(np.mean([a.elapsed_time(b) for a, b in ev[name]])) for name, _ in legs}
-    leg_ms_min = {name: float(np.min([a.elapsed_time(b) for a, b in ev[name]])) for name, _ in legs}
+    # every figure below uses the mean launch time (what rocprofv3's average duration reports);
+    # median, p90 and min sit beside it in leg_stats_ms
+    leg_stats = {name: _stats([a.elapsed_time(b) for a, b in ev[name]]) for name, _ in legs}
+    leg_ms = {name: st["mean"] for name, st in leg_stats.items()}
 
     b_pre = _alg_bytes_prefill(pp)
     f_pre = _alg_flops_prefill(pp)
@@ -399,7 +498,7 @@ def main():
     dominant = max(step_legs, key=lambda n: leg_info[n]["secs"])
     roof = roofline(dominant)
     roof_legs = {n: roofline(n) for n in step_legs}
-    extra_legs = {n: {"ms": extra_ms[n], "roofline": roofline(n)} for n in extra_ms}
+    extra_legs = {n: {"ms": extra_ms[n], "stats_ms": extra_stats[n], "roofline": roofline(n)} for n in extra_ms}
     if "kda" in extra_legs:
         extra_legs["kda"]["tokens_per_s"] = pk.T / (extra_ms["kda"] / 1e3)
     roof_legs["prefill"]["frac_bf16_mfma_full_tile"] = f_pre_full / s_pre / BF16_MFMA_PEAK
@@ -431,12 +530,22 @@ def main():
                                "bf16 pool, bf16 per-token states [1025,12,32,128,128], no commit",
                    "global_batch": pp.N, "seq_len": pp.T, "parallelism": "none (1 GPU)"},
         "decode_state_GBps": state_bytes_dec / s_dec / 1e9,
+        "ms_per_step_note": "host wall time per step: the three legs' launches plus, outside their event "
+                            "windows, three 512 MiB cache-flush reads and Python launch overhead; the legs' own "
+                            "HIP-event times are in leg_ms",
         "leg_ms": leg_ms,
-        "leg_ms_min": leg_ms_min,
+        "leg_stats_ms": leg_stats,
         "roofline": roof,
         "roofline_legs": roof_legs,
         "extra_legs": extra_legs,
     }
+    mp = _measured_mfma_peak(dev)
+    if mp is not None:
+        mp["prefill_frac"] = f_pre / s_pre / (mp["tflops"] * 1e12)
+        mp["prefill_frac_full_tile"] = f_pre_full / s_pre / (mp["tflops"] * 1e12)
+        roof_legs["prefill"]["frac_measured_mfma"] = mp["prefill_frac"]
+    out["measured_bf16_mfma_peak"] = mp
+    out["provenance"] = _provenance()
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = _cpu_baseline(pp)

@@ -3,7 +3,8 @@
     python -m gated_delta_rule_63_amd.build
 
 Each ``csrc/*.hip`` file is compiled to an object under ``_build/`` (in parallel),
-then linked into ``gated_delta_rule_63_amd/libgdr.so``.  Packed-fp32 instruction
+then linked into ``gated_delta_rule_63_amd/libgdr.so``.  The benchmark's MFMA-rate probe
+(``csrc/probe/mfma_peak.hip``) is built into ``libgdr_probe.so`` beside it.  Packed-fp32 instruction
 selection is switched off for every device compile.
 """
 from __future__ import annotations
@@ -20,6 +21,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgdr.so")
+# measurement probe (a dense-MFMA rate kernel for the benchmark), a library of its own
+PROBE_SRC = os.path.join(CSRC, "probe", "mfma_peak.hip")
+PROBE_LIB = os.path.join(PKG, "libgdr_probe.so")
 ARCH = "gfx950"
 
 COMMON = [
@@ -57,8 +61,13 @@ def build(verbose: bool = True) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
+    tmp = PROBE_LIB + ".tmp"
+    r = subprocess.run([_hipcc(), *COMMON, "-shared", PROBE_SRC, "-o", tmp], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {PROBE_SRC}:\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 

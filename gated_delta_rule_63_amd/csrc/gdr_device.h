@@ -281,8 +281,10 @@ __device__ __forceinline__ float exp_f32(float x) {
 
 // ---- gating front (FlashQLA PR #1: host-gating and in-kernel gated verify commits) ----
 // log(1 + e) for e >= 0 from the hardware log2: log(u) e / (u - 1) with u = fl(1 + e) cancels
-// the rounding of 1 + e (the classic correction for small e), and u == 1 means log(1 + e) = e to
-// fp32 precision.  A few ulps; no table constants, so it costs few registers.
+// the rounding of 1 + e, and u == 1 means log(1 + e) = e to fp32 precision.  This is the method of
+// D. Goldberg, "What Every Computer Scientist Should Know About Floating-Point Arithmetic" (ACM
+// Computing Surveys 23(1), 1991), Theorem 4.  A few ulps; no table constants, so it costs few
+// registers.
 __device__ __forceinline__ float log1p_nonneg_f32(float e) {
     const float u = 1.0f + e;
     const float d = u - 1.0f;

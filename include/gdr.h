@@ -32,7 +32,11 @@
  * Supported: K, V in {64, 128}; HV % HK == 0; io_dtype fp32 or bf16; every
  * fp32 -> bf16 store rounds to nearest even.
  *
- * Ownership and behaviour common to every entry point:
+ * Ownership and behaviour common to every entry point (the graph-safe entry that neither
+ * allocates nor synchronises: FlashQLA PR #1, verify integration spec commit, shared
+ * infrastructure; the caller-preallocated path that avoids any allocation and the default
+ * that never validates device contents or synchronises: cuLA PR #113, final-source
+ * validation section):
  *   - every pointer is device memory owned by the caller; the library never
  *     allocates, frees, retains or synchronises: it validates metadata on the host,
  *     enqueues kernels on `hip_stream` (NULL = the legacy default stream) and returns,
@@ -108,6 +112,12 @@ GDR_API gdr_status gdr_recurrent_fwd(const gdr_problem* p,
 /*
  * gdr_chunk_workspace_size -- bytes of device workspace gdr_chunk_fwd needs for this
  * problem (depends on T, N, HV, K, V and io_dtype).  Returns 0 for invalid metadata.
+ * The workspace follows the caller-preallocated path of the chunked forward (cuLA PR #113,
+ * final-source validation section: the preallocated path issues no allocation); here it
+ * holds the segment table, per-segment offsets and linear maps and the chained start states
+ * of the context-parallel route for a few long sequences (FlashQLA PR #1, decode design
+ * commit: occupancy by splitting work, the decode analogue of automatic context
+ * parallelism), and is 0 when that route is not taken.
  */
 GDR_API size_t gdr_chunk_workspace_size(const gdr_problem* p, int32_t chunk_size);
 
@@ -237,7 +247,11 @@ GDR_API gdr_status gdr_decode_paged_gated(const gdr_problem* p, int32_t max_q_le
                                   const int32_t* inter_state_indices,
                                   void* o, void* hip_stream);
 
-/* Human-readable name of a status code (static string). */
+/* Human-readable name of a status code (static string, never NULL; unknown codes map to
+ * "GDR_ERROR_UNKNOWN").  The codes stand for the loud contract checks of the pages' entry
+ * points: a device-capability check (cuLA PR #113, review thread on SM90 availability) and a
+ * wrapper that rejects unsupported dtypes, shapes and capabilities while empty inputs return
+ * early on the host (attention-gym PR #344, pull-request description). */
 GDR_API const char* gdr_status_string(gdr_status s);
 
 #ifdef __cplusplus

@@ -39,3 +39,19 @@ def max_rel_l2_states(x, ref) -> float:
     xs = x.reshape((-1,) + ref.shape[-2:])
     rs = ref.reshape((-1,) + ref.shape[-2:])
     return max((rel_l2(a, b) for a, b in zip(xs, rs)), default=0.0) if len(lead) else rel_l2(x, ref)
+
+
+def max_rel_l2_slices(x, ref, nd: int) -> float:
+    """Max relL2 over every slice formed by the last ``nd`` axes (all leading indices), vectorised;
+    the same per-slice rule as rel_l2."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert x.shape == ref.shape
+    inner = int(np.prod(ref.shape[-nd:])) if nd else 1
+    xs = x.reshape(-1, inner)
+    rs = ref.reshape(-1, inner)
+    if xs.shape[0] == 0:
+        return 0.0
+    num = np.linalg.norm(xs - rs, axis=1)
+    den = np.maximum(np.linalg.norm(rs, axis=1), 1e-6 * np.sqrt(max(inner, 1)))
+    return float(np.max(num / den))

@@ -5,7 +5,7 @@ import pytest
 import torch
 
 import oracle
-from _cmp import TOL, max_rel_l2_tokens, rel_l2
+from _cmp import TOL, max_rel_l2_slices, max_rel_l2_tokens, rel_l2
 from _dev import f64, oracle_inputs, to_dev, to_host
 from gated_delta_rule_63_amd import gdr, inputs
 
@@ -193,59 +193,76 @@ def test_graph_capture_replay_equals_eager():
         assert torch.equal(o, o_ref) and torch.equal(ib, ib_ref)
 
 
-def _sampled_oracle(p, sample):
-    """Oracle on a subset of sequences only (every (sequence, head) is independent)."""
-    cu = p.cu_seqlens
-    sub_idx = np.full(p.N, -1, dtype=np.int32)
-    sub_idx[sample] = p.state_indices[sample]
-    q, k, v, g, beta = oracle_inputs(p)
-    pool = {int(p.state_indices[b]): inputs.widen(p.pool[int(p.state_indices[b])]) for b in sample}
-    return oracle.decode_paged(q, k, v, g, beta, cu, p.scale, pool, sub_idx, want_states=True)
-
-
-def test_decode_full_size_sampled():
-    """256 sequences, 1024-slot fp32 pool, 26 padded, commit: all slot handling checked exactly,
-    values checked against the oracle on a sample of sequences."""
+def test_decode_full_size_every_sequence():
+    """256 sequences, 1024-slot fp32 pool, 26 padded, commit: slot handling checked exactly, and every
+    active (sequence, head) output and committed state against the oracle."""
     p = inputs.decode()
     before = p.pool
     o, pool, _ = _run(p)
     after = to_host(pool)
     act = sorted(int(s) for s in p.state_indices if s >= 0)
+    assert len(act) == 230
     untouched = np.array(sorted(set(range(1024)) - set(act)))
     assert np.array_equal(after[untouched], before[untouched])
-    rng = np.random.default_rng(0)
+    q, k, v, g, beta = oracle_inputs(p)
+    pool_act = {s: inputs.widen(p.pool[s]) for s in act}
+    ref = oracle.decode_paged(q, k, v, g, beta, p.cu_seqlens, p.scale, pool_act, p.state_indices)
     active_b = [b for b in range(p.N) if p.state_indices[b] >= 0]
-    sample = sorted(rng.choice(active_b, size=8, replace=False).tolist())
-    ref = _sampled_oracle(p, sample)
     oh = f64(o)
-    worst = 0.0
-    for b in sample:
-        s = int(p.state_indices[b])
-        for h in range(p.HV):
-            worst = max(worst, rel_l2(oh[b, h], ref["o"][b, h]), rel_l2(inputs.widen(after[s, h]), ref["final"][s][h]))
-    assert worst <= TOL["bf16"], worst
+    assert np.all(np.isfinite(oh[active_b]))
+    eo = max_rel_l2_slices(oh[active_b], ref["o"][active_b], 1)
+    got = inputs.widen(after[act])
+    assert np.all(np.isfinite(got))
+    es = max_rel_l2_slices(got, np.stack([ref["final"][s] for s in act]), 2)
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"], (eo, es)
     ohb = to_host(o)
     for b in range(p.N):
         if p.state_indices[b] < 0:
             assert np.all(ohb[b] == SENT_O)
 
 
-def test_verify_full_size_sampled():
-    """64 sequences x 12 tokens, bf16 pool, bf16 intermediate buffer [1025, 12, 32, 128, 128], no commit."""
-    p = inputs.verify()
+def _verify_full_size(p):
+    """Full-size verify (64 x 12 tokens, bf16 pool [1024, 32, 128, 128], bf16 intermediate buffer
+    [1025, 12, 32, 128, 128], no commit): every active sequence's outputs and every intermediate row
+    against the oracle, streamed one sequence at a time; every other intermediate row and the o rows
+    of padded sequences keep their sentinel bytes; the pool is unchanged."""
     o, pool, ib = _run(p, with_ibuf=torch.bfloat16)
     assert torch.equal(pool, to_dev(p.pool)), "verify must not write the pool"
-    # untouched: cache slot 64 (one past the dense arange) keeps its sentinel
-    assert torch.all(ib[64].view(torch.int16) == SENT_IB)
-    sample = [0, 17, 40, 63]
-    ref = _sampled_oracle(p, sample)
+    q, k, v, g, beta = oracle_inputs(p)
     oh = f64(o)
+    ohb = to_host(o)
+    cu = p.cu_seqlens
+    written = set()
     worst = 0.0
-    for b in sample:
-        s, e = p.cu_seqlens[b], p.cu_seqlens[b + 1]
-        row = f64(ib[b])
-        for h in range(p.HV):
-            worst = max(worst, rel_l2(oh[s:e, h], ref["o"][s:e, h]))
-            for t in range(12):
-                worst = max(worst, rel_l2(row[t, h], ref["states"][b][t, h]))
+    for b in range(p.N):
+        s, e = int(cu[b]), int(cu[b + 1])
+        if p.state_indices[b] < 0:
+            assert np.all(ohb[s:e] == SENT_O)
+            continue
+        sub = np.full(p.N, -1, dtype=np.int32)
+        sub[b] = p.state_indices[b]
+        ref = oracle.decode_paged(q, k, v, g, beta, cu, p.scale, {int(sub[b]): inputs.widen(p.pool[int(sub[b])])},
+                                  sub, want_states=True)
+        row = int(p.inter_state_indices[b])
+        written.add(row)
+        got = f64(ib[row, : e - s])
+        assert np.all(np.isfinite(got)) and np.all(np.isfinite(oh[s:e]))
+        worst = max(worst, max_rel_l2_slices(oh[s:e].transpose(1, 0, 2), ref["o"][s:e].transpose(1, 0, 2), 2),
+                    max_rel_l2_slices(got, ref["states"][b], 2))
     assert worst <= TOL["bf16"], worst
+    # every intermediate row not written above keeps its sentinel (checked on the device in slices)
+    rows = [r for r in range(ib.shape[0]) if r not in written]
+    for i in range(0, len(rows), 64):
+        sel = torch.tensor(rows[i:i + 64], dtype=torch.int64, device=ib.device)
+        assert bool(torch.all(ib.index_select(0, sel).view(torch.int16) == SENT_IB)), f"rows {rows[i]}.."
+
+
+def test_verify_full_size_every_sequence():
+    _verify_full_size(inputs.verify())
+
+
+def test_verify_padded_full_size_every_sequence():
+    """The verify workload with 10% (6 of 64) of the state indices set to -1."""
+    p = inputs.verify(pad=True)
+    assert int(np.sum(p.state_indices < 0)) == 6
+    _verify_full_size(p)
