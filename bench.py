@@ -215,8 +215,10 @@ def _provenance():
 
 
 def _measured_mfma_peak(dev):
-    """Dense bf16 MFMA rate measured on this GPU by the probe kernel (back-to-back 16x16x32 products
-    on every SIMD), median of 5 launches; None when the probe library is missing."""
+    """Dense bf16 MFMA rate measured on this GPU by the probe kernel (back-to-back 16x16x32 products,
+    8 independent accumulators per wave, 16 waves per CU), best of 5 launches after 2 warm-up launches,
+    for low-toggle operands (mode 0, the peak) and random-looking operands (mode 1, closer to real
+    data); None when the probe library is missing."""
     import ctypes
     import torch
     path = os.path.join(_HERE, "gated_delta_rule_63_amd", "libgdr_probe.so")
@@ -224,26 +226,31 @@ def _measured_mfma_peak(dev):
         return None
     L = ctypes.CDLL(path)
     L.gdr_probe_mfma_bf16.restype = ctypes.c_int
-    L.gdr_probe_mfma_bf16.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    L.gdr_probe_mfma_bf16.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                      ctypes.c_void_p]
     L.gdr_probe_mfma_bf16_flops.restype = ctypes.c_double
     L.gdr_probe_mfma_bf16_flops.argtypes = [ctypes.c_int32, ctypes.c_int32]
     blocks, iters = 4096, 2048
     out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
-    ts = []
-    for i in range(7):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        rc = L.gdr_probe_mfma_bf16(blocks, iters, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stream))
-        e1.record()
-        torch.cuda.synchronize()
-        if rc != 0:
-            return None
-        if i >= 2:
-            ts.append(e0.elapsed_time(e1) / 1e3)
     fl = L.gdr_probe_mfma_bf16_flops(blocks, iters)
-    return {"tflops": fl / float(np.median(ts)) / 1e12, "kernel": "v_mfma_f32_16x16x32_bf16, 8 chains per wave, "
-            f"{blocks} x 256 threads x {iters} iterations", "launches": len(ts)}
+    res = {}
+    for mode, name in ((0, "tflops"), (1, "tflops_random_operands")):
+        ts = []
+        for i in range(7):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            rc = L.gdr_probe_mfma_bf16(blocks, iters, mode, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stream))
+            e1.record()
+            torch.cuda.synchronize()
+            if rc != 0:
+                return None
+            if i >= 2:
+                ts.append(e0.elapsed_time(e1) / 1e3)
+        res[name] = fl / float(np.min(ts)) / 1e12
+    res["kernel"] = (f"v_mfma_f32_16x16x32_bf16, 8 chains per wave, {blocks} x 256 threads x {iters} iterations; "
+                     "best of 5 launches")
+    return res
 
 
 def _stats(ms):
