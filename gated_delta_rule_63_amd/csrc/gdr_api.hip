@@ -10,6 +10,29 @@ namespace {
 
 using gdr::RecurrentArgs;
 
+// Scratch of gdr_chunk_fwd_noalloc: a fixed device array instead of a caller's workspace, for
+// callers that cannot allocate.  Each GPU the library runs on holds its own copy until the process
+// ends.  In host code the array's name is only a stand-in for the symbol: its device address, per
+// device, comes from hipGetSymbolAddress and is the only form ever passed to a kernel.
+static __device__ __align__(256) char scratch[GDR_NOALLOC_SCRATCH_BYTES];
+
+std::atomic<char*> g_scratch_ptr[64];
+
+// Device address of this device's scratch array (looked up once per device, with it current).
+gdr_status scratch_address(char** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return GDR_ERROR_NOT_SUPPORTED;
+    char* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!ptr) {
+        void* sym = nullptr;
+        if (hipGetSymbolAddress(&sym, HIP_SYMBOL(scratch)) != hipSuccess || !sym) return GDR_ERROR_LAUNCH_FAILED;
+        ptr = static_cast<char*>(sym);
+        g_scratch_ptr[dev].store(ptr, std::memory_order_release);  // every thread finds the same address
+    }
+    *out = ptr;
+    return GDR_SUCCESS;
+}
+
 bool head_dim_ok(int32_t d) { return d == 64 || d == 128; }
 
 bool dtype_ok(int d) { return d == GDR_F32 || d == GDR_BF16; }
@@ -122,6 +145,7 @@ const char* gdr_status_string(gdr_status s) {
         case GDR_ERROR_INVALID_VALUE: return "GDR_ERROR_INVALID_VALUE";
         case GDR_ERROR_NOT_SUPPORTED: return "GDR_ERROR_NOT_SUPPORTED";
         case GDR_ERROR_LAUNCH_FAILED: return "GDR_ERROR_LAUNCH_FAILED";
+        case GDR_ERROR_SCRATCH_LIMIT: return "GDR_ERROR_SCRATCH_LIMIT";
         default: return "GDR_ERROR_UNKNOWN";
     }
 }
@@ -217,9 +241,13 @@ size_t gdr_chunk_workspace_size(const gdr_problem* p, int32_t chunk_size) {
     return pl.P > 1 ? pl.total : 0;
 }
 
-gdr_status gdr_chunk_fwd(const gdr_problem* p, int32_t chunk_size, const void* q, const void* k, const void* v,
-                         const float* g, const void* beta, const int32_t* cu_seqlens, const float* initial_state,
-                         void* o, float* final_state, void* workspace, size_t workspace_bytes, void* hip_stream) {
+}  // extern "C"
+
+namespace {
+
+// Metadata checks of gdr_chunk_fwd that do not involve the workspace.
+gdr_status check_chunk(const gdr_problem* p, int32_t chunk_size, const void* q, const void* k, const void* v,
+                       const float* g, const void* beta, const int32_t* cu_seqlens, const void* o) {
     gdr_status st = check_problem(p);
     if (st != GDR_SUCCESS) return st;
     if (chunk_size != 64) return GDR_ERROR_INVALID_VALUE;
@@ -228,9 +256,14 @@ gdr_status gdr_chunk_fwd(const gdr_problem* p, int32_t chunk_size, const void* q
     if (p->total_tokens > 0 && !o) return GDR_ERROR_INVALID_VALUE;
     if (p->num_seqs > 1 && !cu_seqlens) return GDR_ERROR_INVALID_VALUE;
     if (p->num_seqs == 0 && p->total_tokens > 0) return GDR_ERROR_INVALID_VALUE;
-    const size_t need = gdr_chunk_workspace_size(p, chunk_size);
-    if (need > 0 && (!workspace || workspace_bytes < need)) return GDR_ERROR_INVALID_VALUE;
-    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return GDR_ERROR_INVALID_VALUE;
+    return GDR_SUCCESS;
+}
+
+// Body of gdr_chunk_fwd after validation; `workspace` holds at least gdr_chunk_workspace_size bytes.
+gdr_status chunk_fwd_impl(const gdr_problem* p, const void* q, const void* k, const void* v, const float* g,
+                          const void* beta, const int32_t* cu_seqlens, const float* initial_state, void* o,
+                          float* final_state, void* workspace, void* hip_stream) {
+    gdr_status st;
     if (p->num_seqs == 0) return GDR_SUCCESS;
     if (p->total_tokens == 0) {
         // every sequence is empty: final state = initial state
@@ -286,6 +319,36 @@ gdr_status gdr_chunk_fwd(const gdr_problem* p, int32_t chunk_size, const void* q
         e = gdr::launch_state_copy(Ss + (int64_t)(pl.P - 1) * hvk, final_state, hvk, stream);
     }
     return status_of(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+gdr_status gdr_chunk_fwd(const gdr_problem* p, int32_t chunk_size, const void* q, const void* k, const void* v,
+                         const float* g, const void* beta, const int32_t* cu_seqlens, const float* initial_state,
+                         void* o, float* final_state, void* workspace, size_t workspace_bytes, void* hip_stream) {
+    gdr_status st = check_chunk(p, chunk_size, q, k, v, g, beta, cu_seqlens, o);
+    if (st != GDR_SUCCESS) return st;
+    const size_t need = gdr_chunk_workspace_size(p, chunk_size);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return GDR_ERROR_INVALID_VALUE;
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return GDR_ERROR_INVALID_VALUE;
+    return chunk_fwd_impl(p, q, k, v, g, beta, cu_seqlens, initial_state, o, final_state, workspace, hip_stream);
+}
+
+gdr_status gdr_chunk_fwd_noalloc(const gdr_problem* p, int32_t chunk_size, const void* q, const void* k,
+                                 const void* v, const float* g, const void* beta, const int32_t* cu_seqlens,
+                                 const float* initial_state, void* o, float* final_state, void* hip_stream) {
+    gdr_status st = check_chunk(p, chunk_size, q, k, v, g, beta, cu_seqlens, o);
+    if (st != GDR_SUCCESS) return st;
+    const size_t need = gdr_chunk_workspace_size(p, chunk_size);
+    if (need > (size_t)GDR_NOALLOC_SCRATCH_BYTES) return GDR_ERROR_SCRATCH_LIMIT;
+    char* ws = nullptr;
+    if (need > 0 && p->num_seqs > 0 && p->total_tokens > 0) {
+        if ((st = check_device()) != GDR_SUCCESS) return st;
+        if ((st = scratch_address(&ws)) != GDR_SUCCESS) return st;
+    }
+    return chunk_fwd_impl(p, q, k, v, g, beta, cu_seqlens, initial_state, o, final_state, ws, hip_stream);
 }
 
 }  // extern "C"

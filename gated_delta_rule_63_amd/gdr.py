@@ -7,8 +7,8 @@ given are contiguous device tensors of the documented shape and dtype, builds th
 HIP kernels.  If the library has not been built, loading it raises immediately.
 
 Names follow the C entry points: ``gdr_recurrent_fwd``, ``gdr_chunk_fwd``,
-``gdr_chunk_workspace_size``, ``gdr_decode_paged``, ``gdr_gating_prepass``,
-``gdr_decode_paged_gated``, ``gdr_status_string``.
+``gdr_chunk_fwd_noalloc``, ``gdr_chunk_workspace_size``, ``gdr_decode_paged``,
+``gdr_gating_prepass``, ``gdr_decode_paged_gated``, ``gdr_status_string``.
 """
 from __future__ import annotations
 
@@ -23,6 +23,8 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdr.so"
 _lib = None
 
 GDR_SUCCESS, GDR_ERROR_INVALID_VALUE, GDR_ERROR_NOT_SUPPORTED, GDR_ERROR_LAUNCH_FAILED = 0, 1, 2, 3
+GDR_ERROR_SCRATCH_LIMIT = 4
+GDR_NOALLOC_SCRATCH_BYTES = 64 << 20
 GDR_F32, GDR_BF16 = 0, 1
 GDR_GATE_SCALAR, GDR_GATE_PER_K = 0, 1
 
@@ -80,6 +82,8 @@ def lib():
         L.gdr_chunk_workspace_size.argtypes = [P, i32]
         L.gdr_chunk_fwd.restype = ctypes.c_int
         L.gdr_chunk_fwd.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.gdr_chunk_fwd_noalloc.restype = ctypes.c_int
+        L.gdr_chunk_fwd_noalloc.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.gdr_decode_paged.restype = ctypes.c_int
         L.gdr_decode_paged.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, i32, vp, i32,
                                        vp, ctypes.c_int, i32, i32, vp, vp, vp]
@@ -217,6 +221,24 @@ def gdr_chunk_fwd(q, k, v, g, beta, cu_seqlens=None, scale=None, initial_state=N
                              _ptr(cu_seqlens), _ptr(initial_state), _ptr(o), _ptr(final_state), _ptr(workspace),
                              workspace.numel(), _stream(stream))
     _raise(st, "gdr_chunk_fwd")
+    return o, final_state
+
+
+def gdr_chunk_fwd_noalloc(q, k, v, g, beta, cu_seqlens=None, scale=None, initial_state=None, o=None,
+                          final_state=None, chunk_size: int = 64, stream=None):
+    """gdr_chunk_fwd without a workspace argument: the library's fixed per-GPU scratch array
+    (GDR_NOALLOC_SCRATCH_BYTES) stands in for it.  ``o`` must be given; the C call allocates
+    nothing.  Calls that overlap on one GPU race on the scratch."""
+    T, HK, HV, K, V = _check_tokens(q, k, v, g, beta)
+    N = _num_seqs(cu_seqlens, 1)
+    _check(initial_state, "initial_state", (N, HV, V, K), torch.float32, optional=True)
+    _check(o, "o", (T, HV, V), q.dtype)
+    _check(final_state, "final_state", (N, HV, V, K), torch.float32, optional=True)
+    p = _problem(q, k, v, g, N, scale)
+    st = lib().gdr_chunk_fwd_noalloc(ctypes.byref(p), int(chunk_size), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                     _ptr(beta), _ptr(cu_seqlens), _ptr(initial_state), _ptr(o), _ptr(final_state),
+                                     _stream(stream))
+    _raise(st, "gdr_chunk_fwd_noalloc")
     return o, final_state
 
 

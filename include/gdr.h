@@ -69,8 +69,13 @@ typedef enum gdr_status {
     GDR_SUCCESS = 0,
     GDR_ERROR_INVALID_VALUE = 1,   /* bad metadata: null pointer, size, enum, workspace */
     GDR_ERROR_NOT_SUPPORTED = 2,   /* valid but unsupported: head dim, dtype combo, device */
-    GDR_ERROR_LAUNCH_FAILED = 3    /* hipGetLastError reported a failure after a launch */
+    GDR_ERROR_LAUNCH_FAILED = 3,   /* hipGetLastError reported a failure after a launch */
+    GDR_ERROR_SCRATCH_LIMIT = 4    /* gdr_chunk_fwd_noalloc: the problem needs more scratch than
+                                      GDR_NOALLOC_SCRATCH_BYTES                              */
 } gdr_status;
+
+/* Size of the fixed device scratch array behind gdr_chunk_fwd_noalloc (per GPU). */
+#define GDR_NOALLOC_SCRATCH_BYTES (64u << 20)
 
 typedef enum gdr_dtype { GDR_F32 = 0, GDR_BF16 = 1 } gdr_dtype;
 
@@ -147,6 +152,27 @@ GDR_API gdr_status gdr_chunk_fwd(const gdr_problem* p, int32_t chunk_size,
                          void* o, float* final_state,
                          void* workspace, size_t workspace_bytes,
                          void* hip_stream);
+
+/*
+ * gdr_chunk_fwd_noalloc -- gdr_chunk_fwd for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, and harnesses that forbid hipMalloc.  Same
+ * arguments and result as gdr_chunk_fwd, minus the workspace: the scratch that
+ * gdr_chunk_workspace_size reports comes from a fixed device array inside the library,
+ * GDR_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU, reserved on each GPU the library runs on until
+ * the process ends.  The call allocates nothing (no hipMalloc, no allocating library routine).
+ *   - a problem whose workspace exceeds GDR_NOALLOC_SCRATCH_BYTES returns
+ *     GDR_ERROR_SCRATCH_LIMIT without launching anything;
+ *   - every call on one GPU shares that GPU's array, which keeps the last call's contents (each
+ *     call writes every scratch byte it reads before reading it); calls that overlap on one GPU
+ *     (concurrent streams or host threads) race on the array and give undefined results.
+ */
+GDR_API gdr_status gdr_chunk_fwd_noalloc(const gdr_problem* p, int32_t chunk_size,
+                                 const void* q, const void* k, const void* v,
+                                 const float* g, const void* beta,
+                                 const int32_t* cu_seqlens,
+                                 const float* initial_state,
+                                 void* o, float* final_state,
+                                 void* hip_stream);
 
 /*
  * gdr_decode_paged -- decode (q_len 1) and speculative verify (q_len up to 12) against a

@@ -35,6 +35,8 @@ def test_status_strings():
     assert gdr.gdr_status_string(1) == "GDR_ERROR_INVALID_VALUE"
     assert gdr.gdr_status_string(2) == "GDR_ERROR_NOT_SUPPORTED"
     assert gdr.gdr_status_string(3) == "GDR_ERROR_LAUNCH_FAILED"
+    assert gdr.gdr_status_string(4) == "GDR_ERROR_SCRATCH_LIMIT"
+    assert gdr.gdr_status_string(99) == "GDR_ERROR_UNKNOWN"
 
 
 def _p(T=8, N=1, HK=1, HV=2, K=128, V=128, gate=0, io=1):
@@ -122,6 +124,32 @@ def test_chunk_workspace_and_rejections():
     assert call(p, cu=None) == 1                        # N > 1 needs cu_seqlens
     assert call(_p(K=96)) == 2
     assert call(_p(K=128, io=0)) == 2                   # fp32 operands need K = 64
+
+
+def test_chunk_noalloc_rejects_bad_metadata_before_the_device():
+    L = gdr.lib()
+
+    def call(p, cs=64, cu=DUMMY, o=DUMMY):
+        return L.gdr_chunk_fwd_noalloc(ctypes.byref(p), cs, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, cu, None, o, None, None)
+    p = _p(T=1000, N=3, HV=4)
+    assert call(p, cs=32) == 1
+    assert call(p, cu=None) == 1                        # N > 1 needs cu_seqlens
+    assert call(p, o=None) == 1
+    assert call(_p(K=96)) == 2
+    assert call(_p(K=128, io=0)) == 2
+    assert call(_p(T=0, N=0), cu=None) == 0             # nothing to do, no device needed
+    assert L.gdr_chunk_fwd_noalloc(None, 64, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, None, DUMMY, None, None) == 1
+
+
+@pytest.mark.parametrize("T,N,HV,K,V,io", [(65573, 1, 16, 128, 128, 1), (1 << 22, 1, 1, 128, 128, 1),
+                                          (1 << 22, 1, 2, 128, 128, 1), (1 << 22, 1, 3, 128, 128, 1),
+                                          (1 << 20, 1, 1, 64, 64, 0), (1 << 20, 1, 1, 128, 64, 1)])
+def test_noalloc_scratch_covers_the_segmented_route(T, N, HV, K, V, io):
+    """The fixed scratch of the no-alloc entry covers the workspace the segmented route plans for
+    long sequences (its largest is one round of 256 segment-heads of 64 KiB states)."""
+    p = gdr.Problem(T, N, 1, HV, K, V, 0.1, 0, io)
+    need = gdr.lib().gdr_chunk_workspace_size(ctypes.byref(p), 64)
+    assert 0 < need <= gdr.GDR_NOALLOC_SCRATCH_BYTES
 
 
 def _gating(**kw):
