@@ -1846,12 +1846,524 @@ __global__ __launch_bounds__(512) void chunk_pipe_kernel(const ChunkArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Flow form for the common case (scalar gate, bf16 operands, K = V = 128): v_new is solved from the
+// state directly, so no W is formed.  With R = diag(beta) V - diag(beta e^gamma) K S^T,
+//
+//     v_new = (I + L)^-1 R,
+//
+// which equals U - W S^T of the WY form: one triangular solve per chunk instead of two (one for U,
+// one for W).  The solve sits on the state-dependent path, but it is short: 20 products of
+// 16x16x16 per wave over four block rows.  Every iteration has two workgroup barriers:
+//
+//            waves 0-3 (state, 32 columns each)              waves 4-7 (prep)
+//   phase X  E1(c-1): Y = K S^T and S Q^T from one packing   L(c) and the four diagonal inverses;
+//            of the state, R, v_new, the state update        loads of chunk c + 2 into registers
+//   phase Y  E2(c-1): the P v_new part of the output and     chunk c + 1 from registers into LDS,
+//            its stores; the ten P tiles of chunk c          its gate tables
+//
+// Q, K, V, -L, the inverses, P and the gate tables are double-buffered, and the prep waves keep two
+// register sets of raw rows, so a chunk's loads are in flight for a whole iteration.  L and P tiles
+// are formed transposed (K_J K_I^T, K_J Q_I^T), so that each lane holds four consecutive columns of
+// one row and writes them with one 8-byte store.  The output scale is folded into the e^gamma table
+// and into P.
+//
+// Lazy decay: the state waves hold S / sigma.  The prep waves, which form the gate tables in chunk
+// order, track sigma (the product of the chunk decays e^{gamma_last}) and fold it into the factors
+// that touch the state: beta e^gamma sigma_c for R, scale e^gamma sigma_c for the output, and
+// e^{gamma_last - gamma} / sigma_{c+1} for the update.  When sigma would fall below 2^-40 (or
+// underflow, with the strongest decays), the chunk's table asks the state waves to multiply the
+// registers by sigma_c e^{gamma_last} and sigma restarts at 1; the final state is written as
+// sigma * registers.  This replaces a multiply of the whole state by e^{gamma_last} in every chunk.
+struct FlowLayout {
+    static constexpr int K = 128, V = 128;
+    static constexpr int LDK = K + 16, LDT = CH + 16, LDO = CH + 16, LDD = 16 + 8;
+    static constexpr size_t ROWK = 2 * CH * LDK;          // [64][LDK] bf16
+    static constexpr size_t ROWT = 2 * CH * LDT;          // [64][LDT] bf16
+    static constexpr size_t ROWO = 2 * (CH - 16) * LDO;   // rows 16..63 of -L (row 0..15 has no off-diagonal block)
+    static constexpr size_t ROWD = 2 * CH * LDD;          // the four 16x16 diagonal inverses, bf16
+    static constexpr int TABF = 9 * CH + 4;               // floats per gate-table set
+    static constexpr int t_g = 0, t_b = CH, t_be = 2 * CH, t_egs = 3 * CH, t_ed = 4 * CH, t_fa = 5 * CH, t_fb = 8 * CH,
+                         t_x = 9 * CH;                    // [0] explicit state rescale of the chunk, [1] sigma after it
+    static constexpr size_t q0 = 0;                       // Q rows, two buffers
+    static constexpr size_t k0 = q0 + 2 * ROWK;           // K rows, two buffers
+    static constexpr size_t v0 = k0 + 2 * ROWK;           // V rows, two buffers
+    static constexpr size_t lo = v0 + 2 * ROWK;           // -L off-diagonal blocks, two buffers
+    static constexpr size_t dd = lo + 2 * ROWO;           // diagonal inverses, two buffers
+    static constexpr size_t ld = dd + 2 * ROWD;           // diagonal blocks of L, fp32 (prep scratch)
+    static constexpr size_t p0 = ld + sizeof(float) * 4 * 16 * LDN;  // P rows, two buffers
+    static constexpr size_t tab = p0 + 2 * ROWT;          // gate tables, two sets
+    static constexpr size_t total = tab + 2 * sizeof(float) * TABF;
+};
+
+template <typename IO>
+__global__ __launch_bounds__(512) void chunk_flow_kernel(const ChunkArgs a) {
+    typedef FlowLayout L;
+    typedef MM<bf16_t> M;
+    typedef uint16_t S;
+    constexpr int K = L::K, KT = K / 16;
+    constexpr int LDK = L::LDK, LDT = L::LDT, LDO = L::LDO, LDD = L::LDD;
+    static_assert(L::total <= 160 * 1024, "LDS budget");
+    static_assert(std::is_same<IO, bf16_t>::value, "bf16 I/O");
+    __shared__ __align__(16) char smem[L::total];
+    auto SP = [&](size_t off) { return reinterpret_cast<S*>(smem + off); };
+    auto FP = [&](size_t off) { return reinterpret_cast<float*>(smem + off); };
+
+    const int h = blockIdx.y, n = blockIdx.z;
+    const int tid = threadIdx.x, l = tid & 63, g4 = l >> 4, lr = l & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t s0 = a.cu_seqlens ? a.cu_seqlens[n] : 0;
+    const int64_t s1 = a.cu_seqlens ? a.cu_seqlens[n + 1] : a.T;
+    const int nc = (int)((s1 - s0 + CH - 1) / CH);
+    // without outputs (the segment runs of context parallelism) the S Q^T products, P and the output
+    // stage are left out.  A run-time flag on purpose: as a template parameter the branch-free product
+    // loop measured about 4% slower end to end
+    const bool want_o = a.o != nullptr;
+    auto chunk_len = [&](int ci) {
+        const int64_t bos = s0 + (int64_t)CH * ci;
+        return (s1 - bos) < CH ? (int)(s1 - bos) : CH;
+    };
+    float* const sLd = FP(L::ld);
+
+    if (w < 4) {
+        // ================= state waves =================
+        // hs[j][kt][e] = S[32w + 16j + lane%16][16kt + 4(l/16) + e]
+        f32x4_t hs[2][KT];
+        const int64_t sbase = ((int64_t)n * a.HV + h) * a.V * K;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt)
+                hs[j][kt] = a.h0 ? *reinterpret_cast<const f32x4_t*>(a.h0 + sbase + (int64_t)(32 * w + 16 * j + lr) * K +
+                                                                    16 * kt + 4 * g4)
+                                 : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        f32x4_t ot[2][4];   // O^T tiles of chunk c - 1 between E1 and E2: lane (g, i) holds value columns
+                            // 32w + 16j + 4g .. +3 of token 16i + lane%16
+        uint4 na[2][2];     // v_new of chunk c - 1 packed as the A operand of the P v_new product
+        // zero the strictly upper tiles of both P buffers once (the P v_new product reads (0,1) and (2,3))
+        for (int idx = tid; idx < 2 * CH * CH; idx += 256) {
+            const int b = idx / (CH * CH), r = (idx / CH) % CH, j = idx % CH;
+            if ((j >> 4) > (r >> 4)) SP(L::p0 + b * L::ROWT)[r * LDT + perm<bf16_t>(j)] = M::cvt(0.0f);
+        }
+        __syncthreads();  // prologue: chunk 0 staged, tables of chunk 0 formed
+        for (int it = 0; it <= nc; ++it) {
+            const int b1 = it & 1, b0 = b1 ^ 1;  // buffers of chunk it and of chunk it - 1
+            // ===== phase X: E1(it - 1) =====
+            if (it >= 1) {
+                const S* sQ0 = SP(L::q0 + b0 * L::ROWK);
+                const S* sK0 = SP(L::k0 + b0 * L::ROWK);
+                const S* sV0 = SP(L::v0 + b0 * L::ROWK);
+                const S* sLo0 = SP(L::lo + b0 * L::ROWO);
+                const S* sD0 = SP(L::dd + b0 * L::ROWD);
+                const float* tb0 = FP(L::tab) + b0 * L::TABF;
+                // Y[r][v] = sum_k K[r][k] S[v][k] and O^T[v][r] = sum_k S[v][k] Q[r][k], sharing each packing of S
+                f32x4_t y[2][4];
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        y[j][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                        ot[j][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                    }
+#pragma unroll
+                for (int m = 0; m < K / 32; ++m) {
+                    bf16x8_t av[4], bq[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        av[i] = *reinterpret_cast<const bf16x8_t*>(sK0 + (16 * i + lr) * LDK + 32 * m + 8 * g4);
+                        if (want_o) bq[i] = *reinterpret_cast<const bf16x8_t*>(sQ0 + (16 * i + lr) * LDK + 32 * m + 8 * g4);
+                    }
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const bf16x8_t sv = __builtin_bit_cast(
+                            bf16x8_t, uint4{pack_tile_lo(hs[j][2 * m]), pack_tile_hi(hs[j][2 * m]),
+                                            pack_tile_lo(hs[j][2 * m + 1]), pack_tile_hi(hs[j][2 * m + 1])});
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            y[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i], sv, y[j][i], 0, 0, 0);
+                            if (want_o) ot[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sv, bq[i], ot[j][i], 0, 0, 0);
+                        }
+                    }
+                }
+                // R = beta V - beta e^gamma Y (rows 16I + 4(l/16) + e, column 32w + 16j + lane%16), then
+                // v_new = (I + L)^-1 R by blocked forward substitution (-L and the inverses from LDS)
+                s16x4_t lv[6], dv[4];
+#pragma unroll
+                for (int I = 0; I < 4; ++I) {
+                    dv[I] = *reinterpret_cast<const s16x4_t*>(sD0 + (16 * I + lr) * LDD + 4 * g4);
+#pragma unroll
+                    for (int J = 0; J < I; ++J)
+                        lv[I * (I - 1) / 2 + J] =
+                            *reinterpret_cast<const s16x4_t*>(sLo0 + (16 * I - 16 + lr) * LDO + 16 * J + 4 * g4);
+                }
+                f32x4_t x[2][4];
+#pragma unroll
+                for (int I = 0; I < 4; ++I) {
+                    const int t0 = 16 * I + 4 * g4;
+                    const f32x4_t bb = *reinterpret_cast<const f32x4_t*>(tb0 + L::t_b + t0);
+                    const f32x4_t be = *reinterpret_cast<const f32x4_t*>(tb0 + L::t_be + t0);
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const uint2 vr = ld_tr4<true>(sV0, LDK, t0, 32 * w + 16 * j);
+                        const float vv[4] = {__uint_as_float(vr.x << 16), __uint_as_float(vr.x & 0xFFFF0000u),
+                                             __uint_as_float(vr.y << 16), __uint_as_float(vr.y & 0xFFFF0000u)};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) y[j][I][e] = fmaf(-be[e], y[j][I][e], bb[e] * vv[e]);
+                    }
+                }
+#pragma unroll
+                for (int I = 0; I < 4; ++I) {
+#pragma unroll
+                    for (int J = 0; J < I; ++J)
+#pragma unroll
+                        for (int j = 0; j < 2; ++j) {
+                            const s16x4_t bv = __builtin_bit_cast(s16x4_t, uint2{pack_tile_lo(x[j][J]), pack_tile_hi(x[j][J])});
+                            y[j][I] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lv[I * (I - 1) / 2 + J], bv, y[j][I], 0, 0, 0);
+                        }
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const s16x4_t rv = __builtin_bit_cast(s16x4_t, uint2{pack_tile_lo(y[j][I]), pack_tile_hi(y[j][I])});
+                        x[j][I] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(dv[I], rv, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                    }
+                }
+                if (want_o) {
+                    // the S Q^T part scaled by scale e^gamma_r; v_new packed for E2
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float f = tb0[L::t_egs + 16 * i + lr];
+#pragma unroll
+                        for (int j = 0; j < 2; ++j) ot[j][i] *= f;
+                    }
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+#pragma unroll
+                        for (int m = 0; m < 2; ++m)
+                            na[j][m] = uint4{pack_tile_lo(x[j][2 * m]), pack_tile_hi(x[j][2 * m]),
+                                             pack_tile_lo(x[j][2 * m + 1]), pack_tile_hi(x[j][2 * m + 1])};
+                }
+                // S <- e^{gamma_last} S + sum_r v_new_r (k_r e^{gamma_last - gamma_r})^T, the K^T operand read
+                // from the row-major K rows with transposing reads
+                // the registers hold S / sigma; the decay of the chunk only moves sigma, except when sigma would
+                // leave the safe range: then the table holds the factor that folds it into the registers
+                const float resc = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(tb0[L::t_x])));
+                if (resc != 1.0f) {
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+#pragma unroll
+                        for (int kt = 0; kt < KT; ++kt) hs[j][kt] *= resc;
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const f32x4_t f = *reinterpret_cast<const f32x4_t*>(tb0 + L::t_ed + 16 * i + 4 * g4);
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) x[j][i] *= f;
+                }
+#pragma unroll
+                for (int m = 0; m < CH / 32; ++m) {
+                    bf16x8_t bw[2];
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        bw[j] = __builtin_bit_cast(bf16x8_t, uint4{pack_tile_lo(x[j][2 * m]), pack_tile_hi(x[j][2 * m]),
+                                                                   pack_tile_lo(x[j][2 * m + 1]),
+                                                                   pack_tile_hi(x[j][2 * m + 1])});
+#pragma unroll
+                    for (int kt = 0; kt < KT; ++kt) {
+                        const uint2 lo = ld_tr4<true>(sK0, LDK, 32 * m + 4 * g4, 16 * kt);
+                        const uint2 hi = ld_tr4<true>(sK0, LDK, 32 * m + 16 + 4 * g4, 16 * kt);
+                        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, uint4{lo.x, lo.y, hi.x, hi.y});
+#pragma unroll
+                        for (int j = 0; j < 2; ++j) hs[j][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bw[j], hs[j][kt], 0, 0, 0);
+                    }
+                }
+            }
+            __syncthreads();  // end of phase X
+            // ===== phase Y: E2(it - 1), then the P tiles of chunk it =====
+            if (it >= 1 && want_o) {
+                const int ce = it - 1;
+                const int64_t bos = s0 + (int64_t)CH * ce;
+                const int len = chunk_len(ce);
+                const S* sP0 = SP(L::p0 + b0 * L::ROWT);
+                // O^T_j += v_new^T P^T (P holds scale e^{gamma_r - gamma_t} q_r . k_t); P is lower triangular:
+                // token tile i needs the steps m with 32m <= 16i + 15
+                bf16x8_t bp[2][4];
+#pragma unroll
+                for (int m = 0; m < 2; ++m)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (32 * m <= 16 * i + 15)
+                            bp[m][i] = *reinterpret_cast<const bf16x8_t*>(sP0 + (16 * i + lr) * LDT + 32 * m + 8 * g4);
+#pragma unroll
+                for (int m = 0; m < 2; ++m)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const bf16x8_t nv = __builtin_bit_cast(bf16x8_t, na[j][m]);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (32 * m <= 16 * i + 15)
+                                ot[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(nv, bp[m][i], ot[j][i], 0, 0, 0);
+                    }
+                // rows g and g + 1 of a lane pair exchange halves (v_permlane16_swap), so that each lane holds
+                // eight consecutive value columns of its token: columns 32w + {0, 16, 8, 24}[g] .. +7, one 16-byte
+                // store per token tile, 64 contiguous bytes per token and store instruction
+                uint16_t* const obase = static_cast<uint16_t*>(a.o) + (bos * a.HV + h) * a.V + 32 * w +
+                                        ((g4 & 1) ? 16 + 4 * (g4 - 1) : 4 * g4);
+                const int64_t ostride = (int64_t)a.HV * a.V;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t x0 = pack_bf16x2(ot[0][i][0], ot[0][i][1]), x1 = pack_bf16x2(ot[0][i][2], ot[0][i][3]);
+                    const uint32_t y0 = pack_bf16x2(ot[1][i][0], ot[1][i][1]), y1 = pack_bf16x2(ot[1][i][2], ot[1][i][3]);
+                    const auto s0 = __builtin_amdgcn_permlane16_swap(x0, y0, false, false);
+                    const auto s1 = __builtin_amdgcn_permlane16_swap(x1, y1, false, false);
+                    const int r = 16 * i + lr;
+                    if (r < len)
+                        *reinterpret_cast<uint4*>(obase + r * ostride) = uint4{s0[0], s1[0], s0[1], s1[1]};
+                }
+            }
+            if (it < nc && want_o) {
+                // P tiles of chunk it, transposed products K_J Q_I^T: lane (g, i) holds P[16I + lane%16][16J + 4g + e]
+                const S* sQ1 = SP(L::q0 + b1 * L::ROWK);
+                const S* sK1 = SP(L::k0 + b1 * L::ROWK);
+                S* const sP1 = SP(L::p0 + b1 * L::ROWT);
+                const float* tb1 = FP(L::tab) + b1 * L::TABF;
+                auto store_off = [&](int q, const f32x4_t& cp) {
+                    int I, J;
+                    strict_tile(q, I, J);
+                    const int r = 16 * I + lr;
+                    const float fa = tb1[L::t_fa + J * CH + r] * a.scale;
+                    const f32x4_t fb = *reinterpret_cast<const f32x4_t*>(tb1 + L::t_fb + 16 * J + 4 * g4);
+                    *reinterpret_cast<uint2*>(sP1 + r * LDT + perm<bf16_t>(16 * J + 4 * g4)) =
+                        uint2{pack_bf16x2(fa * fb[0] * cp[0], fa * fb[1] * cp[1]),
+                              pack_bf16x2(fa * fb[2] * cp[2], fa * fb[3] * cp[3])};
+                };
+                int I0, J0;
+                strict_tile(w, I0, J0);
+                f32x4_t cd = {0.f, 0.f, 0.f, 0.f}, c0 = {0.f, 0.f, 0.f, 0.f};
+                M::template nt2<K>(cd, sK1 + 16 * w * LDK, sQ1 + 16 * w * LDK, c0, sK1 + 16 * J0 * LDK, sQ1 + 16 * I0 * LDK,
+                                   LDK);
+                {
+                    const int r = 16 * w + lr;
+                    const float gr = tb1[L::t_g + r];
+                    const f32x4_t gj = *reinterpret_cast<const f32x4_t*>(tb1 + L::t_g + 16 * w + 4 * g4);
+                    float x[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float v = exp_f32(gr - gj[e]) * cd[e] * a.scale;  // inf above the diagonal is discarded
+                        x[e] = (lr >= 4 * g4 + e) ? v : 0.0f;
+                    }
+                    *reinterpret_cast<uint2*>(sP1 + r * LDT + perm<bf16_t>(16 * w + 4 * g4)) =
+                        uint2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+                }
+                store_off(w, c0);
+                if (w < 2) {
+                    int I1, J1;
+                    strict_tile(w + 4, I1, J1);
+                    f32x4_t c1 = {0.f, 0.f, 0.f, 0.f};
+                    M::nt(c1, sK1 + 16 * J1 * LDK, LDK, sQ1 + 16 * I1 * LDK, LDK, K);
+                    store_off(w + 4, c1);
+                }
+            }
+            __syncthreads();  // end of phase Y
+        }
+        if (a.ht) {
+            // S = sigma * registers, sigma after the last chunk (1 for an empty sequence)
+            const float sig = nc > 0 ? FP(L::tab)[((nc - 1) & 1) * L::TABF + L::t_x + 1] : 1.0f;
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int kt = 0; kt < KT; ++kt)
+                    *reinterpret_cast<f32x4_t*>(a.ht + sbase + (int64_t)(32 * w + 16 * j + lr) * K + 16 * kt + 4 * g4) =
+                        hs[j][kt] * sig;
+        }
+    } else {
+        // ================= prep waves =================
+        constexpr int NLD = 256;
+        const int lt = tid - 256;  // thread index among waves 4-7
+        const int u = w - 4;
+        const int hk = h / (a.HV / a.HK);
+        typedef Tile<CH, K, NLD> TQ;
+        typedef PairTile<K, NLD> PK;
+        typedef PairTile<128, NLD> PV;
+        // one chunk's q, k, v rows (and, on wave 4, g and beta) held raw in registers; two sets, so that
+        // the loads of chunk c + 2 are in flight while chunk c + 1 is written to LDS
+        struct Regs {
+            Raw8<IO> qn[TQ::NV], kn[2 * PK::NPASS], vn[2 * PV::NPASS];
+            float gn;
+            uint32_t bn;
+        };
+        Regs ra, rb;
+        // sigma: the state waves hold S / sigma.  The tables of chunk c carry sigma_c (the value at the start of
+        // the chunk) in beta e^gamma and scale e^gamma, and 1 / sigma_{c+1} in e^{gamma_last - gamma}; sigma
+        // follows the chunk decays and is folded back into the registers (reset to 1) whenever it would fall
+        // below 2^-40, so that every factor stays far from overflow and underflow
+        float sig = 1.0f;
+        constexpr int ESZ = 2;
+        const int qk_row = a.HK * K * ESZ, v_row = a.HV * a.V * ESZ;
+        auto load = [&](int ci, Regs& r) {  // global -> registers: chunk ci
+            const int64_t bos = s0 + (int64_t)CH * ci;
+            const int len = chunk_len(ci);
+            const __amdgpu_buffer_rsrc_t rq =
+                chunk_rsrc(static_cast<const char*>(a.q) + ((bos * a.HK + hk) * K) * ESZ, len, qk_row);
+#pragma unroll
+            for (int i = 0; i < TQ::NV; ++i) r.qn[i].load(rq, TQ::row(lt, i) * qk_row + TQ::col(lt) * ESZ);
+            const __amdgpu_buffer_rsrc_t rk =
+                chunk_rsrc(static_cast<const char*>(a.k) + ((bos * a.HK + hk) * K) * ESZ, len, qk_row);
+#pragma unroll
+            for (int i = 0; i < PK::NPASS; ++i)
+#pragma unroll
+                for (int q = 0; q < 2; ++q)
+                    r.kn[2 * i + q].load(rk, (2 * PK::pair(lt, i) + q) * qk_row + PK::col(lt, i) * ESZ);
+            // v == NULL reads as zeros (a zero-byte range): the run that forms a segment's linear map
+            const __amdgpu_buffer_rsrc_t rv = chunk_rsrc(
+                a.v ? static_cast<const char*>(a.v) + ((bos * a.HV + h) * a.V) * ESZ : nullptr, a.v ? len : 0, v_row);
+#pragma unroll
+            for (int i = 0; i < PV::NPASS; ++i)
+#pragma unroll
+                for (int q = 0; q < 2; ++q)
+                    r.vn[2 * i + q].load(rv, (2 * PV::pair(lt, i) + q) * v_row + PV::col(lt, i) * ESZ);
+            if (u == 0) {
+                const __amdgpu_buffer_rsrc_t rg = chunk_rsrc(a.g + bos * a.HV + h, len, a.HV * 4);
+                r.gn = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, l * a.HV * 4, 0, 0));
+                const __amdgpu_buffer_rsrc_t rbt =
+                    chunk_rsrc(static_cast<const char*>(a.beta) + (bos * a.HV + h) * 2, len, a.HV * 2);
+                r.bn = __builtin_amdgcn_raw_buffer_load_b16(rbt, l * a.HV * 2, 0, 0);
+            }
+        };
+        auto stage = [&](int b, const Regs& r) {  // registers -> LDS buffers b; wave 4 forms the gate tables
+            S* const sQ = SP(L::q0 + b * L::ROWK);
+            S* const sK = SP(L::k0 + b * L::ROWK);
+            S* const sV = SP(L::v0 + b * L::ROWK);
+#pragma unroll
+            for (int i = 0; i < TQ::NV; ++i) st8_perm<bf16_t, IO>(sQ + TQ::row(lt, i) * LDK, TQ::col(lt), r.qn[i]);
+#pragma unroll
+            for (int i = 0; i < PK::NPASS; ++i) {
+                if (PK::valid(lt, i)) {
+                    const int c8 = PK::col(lt, i), pr0 = 2 * PK::pair(lt, i);
+                    st8_perm<bf16_t, IO>(sK + pr0 * LDK, c8, r.kn[2 * i]);
+                    st8_perm<bf16_t, IO>(sK + (pr0 + 1) * LDK, c8, r.kn[2 * i + 1]);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < PV::NPASS; ++i) {
+                if (PV::valid(lt, i)) {
+                    const int c8 = PV::col(lt, i), pr0 = 2 * PV::pair(lt, i);
+                    st8_perm<bf16_t, IO>(sV + pr0 * LDK, c8, r.vn[2 * i]);
+                    st8_perm<bf16_t, IO>(sV + (pr0 + 1) * LDK, c8, r.vn[2 * i + 1]);
+                }
+            }
+            if (u == 0) {  // inclusive prefix of the 64 gates (rows past the end are 0) and the factor tables
+                float* const tb = FP(L::tab) + b * L::TABF;
+                const float br = __uint_as_float(r.bn << 16);
+                const float x = wave_inclusive_sum(r.gn);
+                const float xl = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), CH - 1));
+                const float ex = exp_f32(x);
+                const float prod = sig * exp_f32(xl);          // sigma_c times the chunk's decay
+                const bool fold = !(prod >= 0x1p-40f);
+                const float sig_next = fold ? 1.0f : prod;
+                tb[L::t_g + l] = x;
+                tb[L::t_b + l] = br;
+                tb[L::t_be + l] = br * ex * sig;
+                tb[L::t_egs + l] = a.scale * ex * sig;
+                tb[L::t_ed + l] = exp_f32(xl - x) * __builtin_amdgcn_rcpf(sig_next);
+                if (l == 0) {
+                    tb[L::t_x] = fold ? prod : 1.0f;
+                    tb[L::t_x + 1] = sig_next;
+                }
+                sig = sig_next;
+                float rho[4];
+#pragma unroll
+                for (int J = 0; J < 4; ++J) rho[J] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16 * J + 15));
+#pragma unroll
+                for (int J = 0; J < 3; ++J) tb[L::t_fa + J * CH + l] = exp_f32(fminf(x - rho[J], 0.0f));
+                const int jb = l >> 4;
+                const float rj = jb == 0 ? rho[0] : jb == 1 ? rho[1] : jb == 2 ? rho[2] : rho[3];
+                tb[L::t_fb + l] = exp_f32(rj - x);
+            }
+        };
+        // phase X of iteration it: L of chunk it (transposed products K_J K_I^T), the diagonal inverses,
+        // the P tiles of chunk it, then the loads of chunk it + 2
+        auto phase_x = [&](int it, Regs& nxt) {
+            const int b1 = it & 1;
+            if (it < nc) {
+                const S* sK1 = SP(L::k0 + b1 * L::ROWK);
+                S* const sLo1 = SP(L::lo + b1 * L::ROWO);
+                S* const sD1 = SP(L::dd + b1 * L::ROWD);
+                const float* tb1 = FP(L::tab) + b1 * L::TABF;
+                auto store_off = [&](int q, const f32x4_t& cl) {
+                    int I, J;
+                    strict_tile(q, I, J);
+                    const int r = 16 * I + lr;
+                    const float fr = -tb1[L::t_b + r] * tb1[L::t_fa + J * CH + r];
+                    const f32x4_t fb = *reinterpret_cast<const f32x4_t*>(tb1 + L::t_fb + 16 * J + 4 * g4);
+                    *reinterpret_cast<uint2*>(sLo1 + (r - 16) * LDO + 16 * J + 4 * g4) =
+                        uint2{pack_bf16x2(fr * fb[0] * cl[0], fr * fb[1] * cl[1]),
+                              pack_bf16x2(fr * fb[2] * cl[2], fr * fb[3] * cl[3])};
+                };
+                int I0, J0;
+                strict_tile(u, I0, J0);
+                f32x4_t cd = {0.f, 0.f, 0.f, 0.f}, c0 = {0.f, 0.f, 0.f, 0.f};
+                M::template nt2<K>(cd, sK1 + 16 * u * LDK, sK1 + 16 * u * LDK, c0, sK1 + 16 * J0 * LDK, sK1 + 16 * I0 * LDK,
+                                   LDK);
+                float* sN = sLd + u * 16 * LDN;
+                {
+                    const int r = 16 * u + lr;
+                    const float gr = tb1[L::t_g + r], br = tb1[L::t_b + r];
+                    const f32x4_t gj = *reinterpret_cast<const f32x4_t*>(tb1 + L::t_g + 16 * u + 4 * g4);
+                    f32x4_t x;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float v = br * exp_f32(gr - gj[e]) * cd[e];  // inf above the diagonal is discarded
+                        x[e] = (lr > 4 * g4 + e) ? v : 0.0f;
+                    }
+                    *reinterpret_cast<f32x4_t*>(sN + lr * LDN + 4 * g4) = x;
+                }
+                // the tile's LDS writes complete before this wave's lanes read other lanes' entries
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                invert_unit_lower_16<bf16_t>(sN, sD1 + 16 * u * LDD, LDD);
+                store_off(u, c0);
+                if (u < 2) {
+                    int I1, J1;
+                    strict_tile(u + 4, I1, J1);
+                    f32x4_t c1 = {0.f, 0.f, 0.f, 0.f};
+                    M::nt(c1, sK1 + 16 * J1 * LDK, LDK, sK1 + 16 * I1 * LDK, LDK, K);
+                    store_off(u + 4, c1);
+                }
+            }
+            if (it + 2 < nc) load(it + 2, nxt);
+            __syncthreads();  // end of phase X
+        };
+        // phase Y of iteration it: chunk it + 1 from registers into LDS
+        auto phase_y = [&](int it, const Regs& cur) {
+            if (it + 1 < nc) stage((it & 1) ^ 1, cur);
+            __syncthreads();  // end of phase Y
+        };
+        if (nc > 0) {
+            load(0, ra);
+            stage(0, ra);
+        }
+        if (nc > 1) load(1, rb);
+        __syncthreads();  // prologue
+        // chunk c lives in register set ra for even c, rb for odd c
+        for (int it = 0; it <= nc; it += 2) {
+            phase_x(it, ra);
+            phase_y(it, rb);
+            if (it + 1 <= nc) {
+                phase_x(it + 1, rb);
+                phase_y(it + 1, ra);
+            }
+        }
+    }
+}
+
 template <int K, int V, typename IO, bool PER_K>
 hipError_t launch_fused(const ChunkArgs& a, hipStream_t stream) {
     // bf16: the workgroup owns all V columns; fp32 operands (K = 64 only) use 64-column tiles
     constexpr int BV = std::is_same<IO, float>::value ? 64 : V;
     if constexpr (K == 128 && V == 128 && std::is_same<IO, bf16_t>::value && !PER_K) {
+#ifdef GDR_CHUNK_PIPE
         hipLaunchKernelGGL(chunk_pipe_kernel<IO>, dim3(1, a.HV, a.N), dim3(512), 0, stream, a);
+#else
+        hipLaunchKernelGGL(chunk_flow_kernel<IO>, dim3(1, a.HV, a.N), dim3(512), 0, stream, a);
+#endif
         return hipGetLastError();
     }
     hipLaunchKernelGGL((chunk_fused_kernel<K, BV, IO, IO, PER_K>), dim3(V / BV, a.HV, a.N), dim3(4 * BV), 0, stream,
