@@ -269,10 +269,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--legs", default="prefill,decode,verify",
                     help="comma-separated subset of legs to run (profiling passes); the JSON line needs all three")
-    ap.add_argument("--extra-legs", default="decode_gated,verify_gated,verify_prepass,kda",
+    ap.add_argument("--extra-legs", default="decode_gated,verify_gated,verify_prepass,kda,cp_segmented,cp_direct",
                     help="legs outside the step, timed after it: the gating front fused into the decode and verify "
-                         "launches, the gating pass followed by the plain verify launch, and the per-channel-gate "
-                         "(KDA) chunked forward over one 65573-token sequence ('' for none)")
+                         "launches, the gating pass followed by the plain verify launch, the per-channel-gate "
+                         "(KDA) chunked forward over one 65573-token sequence, and 4 x 16384-token GDN sequences "
+                         "with 16 heads on the segmented and the single-pass route ('' for none)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before the legs, run one device-to-device copy of this many MiB (a plain copy kernel of "
                          "known size, used to scale the HBM byte counters of a profiling pass) and stop after the legs")
@@ -331,6 +332,25 @@ def main():
           "g": torch.empty((pv.T, pv.HV), dtype=torch.float32, device=dev),
           "beta": torch.empty((pv.T, pv.HV), dtype=torch.bfloat16, device=dev)}
 
+    C_ = None
+    if {"cp_segmented", "cp_direct"} & set(args.extra_legs.split(",")):
+        pc = inputs.long_batch()
+        C_ = {k: to_dev(getattr(pc, k)) for k in ("q", "k", "v", "g", "beta")}
+        C_["cu"] = to_dev(pc.cu_seqlens.astype(np.int32))
+        C_["h0"] = to_dev(pc.initial_state)
+        C_["o"] = torch.empty((pc.T, pc.HV, pc.V), dtype=torch.bfloat16, device=dev)
+        C_["ht"] = torch.empty((pc.N, pc.HV, pc.V, pc.K), dtype=torch.float32, device=dev)
+        C_["ws"] = torch.empty(max(256, gdr.gdr_chunk_workspace_size(C_["q"], C_["v"], C_["g"], pc.N)),
+                               dtype=torch.uint8, device=dev)
+
+    def cp_segmented():
+        gdr.gdr_chunk_fwd(C_["q"], C_["k"], C_["v"], C_["g"], C_["beta"], C_["cu"], pc.scale, C_["h0"], o=C_["o"],
+                          final_state=C_["ht"], workspace=C_["ws"])
+
+    def cp_direct():
+        gdr.gdr_chunk_fwd(C_["q"], C_["k"], C_["v"], C_["g"], C_["beta"], C_["cu"], pc.scale, C_["h0"], o=C_["o"],
+                          final_state=C_["ht"], segmented=False)
+
     K_ = None
     if "kda" in args.extra_legs.split(","):
         pk = inputs.kda()
@@ -378,7 +398,8 @@ def main():
     legs = [(n, f) for n, f in (("prefill", prefill), ("decode", decode), ("verify", verify))
             if n in args.legs.split(",")]
     extra = [(n, f) for n, f in (("decode_gated", decode_gated), ("verify_gated", verify_gated),
-                                 ("verify_prepass", verify_prepass), ("kda", kda)) if n in args.extra_legs.split(",")]
+                                 ("verify_prepass", verify_prepass), ("kda", kda), ("cp_segmented", cp_segmented),
+                                 ("cp_direct", cp_direct)) if n in args.extra_legs.split(",")]
     if args.calib_copy_mib:
         n = args.calib_copy_mib << 20
         src = torch.ones(n // 4, dtype=torch.float32, device=dev)
@@ -477,6 +498,14 @@ def main():
                                      "copy (1 x 65573 tokens, 16 heads; bytes, time and traffic per call)",
                            "bytes": _alg_bytes_prefill(pk, with_cu=False), "flops": None, "secs": extra_ms["kda"] / 1e3,
                            "sources": ["gdr_chunk.hip", "gdr_device.h", "gdr_cp.hip", "gdr_api.hip"]}
+    for leg, route in (("cp_segmented", "segmented route: setup, chunk kernel x3 (offsets, maps, outputs), scan, "
+                                         "final-state copy"),
+                       ("cp_direct", "single pass: one chunk-kernel launch, one workgroup per (sequence, head)")):
+        if leg in extra_ms:
+            leg_info[leg] = {"kernel": f"{route} (4 x 16384 tokens, 16 heads, K=V=128, bf16; per call)",
+                             "bytes": _alg_bytes_prefill(pc), "flops": _alg_flops_prefill(pc),
+                             "secs": extra_ms[leg] / 1e3,
+                             "sources": ["gdr_chunk.hip", "gdr_device.h", "gdr_cp.hip", "gdr_api.hip"]}
     traffic = _measured_traffic()
 
     def roofline(leg):
@@ -508,6 +537,9 @@ def main():
     extra_legs = {n: {"ms": extra_ms[n], "stats_ms": extra_stats[n], "roofline": roofline(n)} for n in extra_ms}
     if "kda" in extra_legs:
         extra_legs["kda"]["tokens_per_s"] = pk.T / (extra_ms["kda"] / 1e3)
+    for leg in ("cp_segmented", "cp_direct"):
+        if leg in extra_legs:
+            extra_legs[leg]["tokens_per_s"] = pc.T / (extra_ms[leg] / 1e3)
     roof_legs["prefill"]["frac_bf16_mfma_full_tile"] = f_pre_full / s_pre / BF16_MFMA_PEAK
     roof_legs["prefill"]["alg_flops_full_tile"] = f_pre_full
     roof_legs["decode"]["state_GBps"] = state_bytes_dec / s_dec / 1e9

@@ -285,27 +285,30 @@ gdr_status chunk_fwd_impl(const gdr_problem* p, const void* q, const void* k, co
 
     const gdr::CpPlan pl = gdr::cp_plan(p->total_tokens, p->num_seqs, p->num_v_heads, p->head_dim_k,
                                         p->head_dim_v, p->io_dtype == GDR_BF16 ? 2 : 4);
-    if (pl.P <= 1) return status_of(gdr::launch_chunk(a, p->io_dtype, per_k, stream));
+    // the segmented route needs its workspace; without one the call runs the single-pass route
+    if (pl.P <= 1 || !workspace) return status_of(gdr::launch_chunk(a, p->io_dtype, per_k, stream));
 
-    // One long sequence, few heads: cut it into P segments and run them in parallel.
+    // Few long sequences, few heads: cut every sequence into segments that run in parallel.
+    //   0. segment table from cu_seqlens (device side), identity maps
     //   1. B_s = end state of segment s from zero; M_s = end state of segment s from the identity
-    //      with v = 0 (the K x K linear part of its map), for s < P - 1; outputs discarded
-    //   2. scan: S_0 = initial state, S_{s+1} = S_s M_s + B_s
+    //      with v = 0 (the K x K linear part of its map); outputs discarded
+    //   2. scan per sequence: S_first = initial state, S_{s+1} = S_s M_s + B_s
     //   3. every segment from its true start state: outputs, and the end state in place
+    //   4. each sequence's final state = the end state of its last segment
     char* ws = static_cast<char*>(workspace);
     const int32_t* cu_seg = reinterpret_cast<const int32_t*>(ws + pl.cu_seg);
     float* Bs = reinterpret_cast<float*>(ws + pl.B);
     float* Ms = reinterpret_cast<float*>(ws + pl.M);
     float* Ss = reinterpret_cast<float*>(ws + pl.S);
-    hipError_t e = gdr::launch_cp_setup(pl, ws, p->total_tokens, p->num_v_heads, p->head_dim_k, stream);
+    hipError_t e = gdr::launch_cp_setup(pl, ws, cu_seqlens, p->total_tokens, p->num_v_heads, p->head_dim_k, stream);
     if (e != hipSuccess) return status_of(e);
 
     gdr::ChunkArgs b = a;  // 1a: offsets B_s
-    b.cu_seqlens = cu_seg; b.N = pl.P - 1; b.h0 = nullptr; b.o = nullptr; b.ht = Bs;
+    b.cu_seqlens = cu_seg; b.N = pl.P; b.h0 = nullptr; b.o = nullptr; b.ht = Bs;
     if ((e = gdr::launch_chunk(b, p->io_dtype, per_k, stream)) != hipSuccess) return status_of(e);
 
     gdr::ChunkArgs m = a;  // 1b: linear parts M_s (a K-row state, v = 0), in place from the identity
-    m.cu_seqlens = cu_seg; m.N = pl.P - 1; m.v = nullptr; m.V = p->head_dim_k; m.h0 = Ms; m.o = nullptr; m.ht = Ms;
+    m.cu_seqlens = cu_seg; m.N = pl.P; m.v = nullptr; m.V = p->head_dim_k; m.h0 = Ms; m.o = nullptr; m.ht = Ms;
     if ((e = gdr::launch_chunk(m, p->io_dtype, per_k, stream)) != hipSuccess) return status_of(e);
 
     e = gdr::launch_cp_scan(pl, ws, initial_state, p->num_v_heads, p->head_dim_k, p->head_dim_v, stream);
@@ -314,10 +317,7 @@ gdr_status chunk_fwd_impl(const gdr_problem* p, const void* q, const void* k, co
     gdr::ChunkArgs f = a;  // 3: outputs from the true start states; end states in place
     f.cu_seqlens = cu_seg; f.N = pl.P; f.h0 = Ss; f.ht = Ss;
     if ((e = gdr::launch_chunk(f, p->io_dtype, per_k, stream)) != hipSuccess) return status_of(e);
-    if (final_state) {
-        const int64_t hvk = (int64_t)p->num_v_heads * p->head_dim_v * p->head_dim_k;
-        e = gdr::launch_state_copy(Ss + (int64_t)(pl.P - 1) * hvk, final_state, hvk, stream);
-    }
+    if (final_state) e = gdr::launch_cp_final(pl, ws, final_state, p->num_v_heads, p->head_dim_k, p->head_dim_v, stream);
     return status_of(e);
 }
 
@@ -331,9 +331,10 @@ gdr_status gdr_chunk_fwd(const gdr_problem* p, int32_t chunk_size, const void* q
     gdr_status st = check_chunk(p, chunk_size, q, k, v, g, beta, cu_seqlens, o);
     if (st != GDR_SUCCESS) return st;
     const size_t need = gdr_chunk_workspace_size(p, chunk_size);
-    if (need > 0 && (!workspace || workspace_bytes < need)) return GDR_ERROR_INVALID_VALUE;
+    if (need > 0 && workspace && workspace_bytes < need) return GDR_ERROR_INVALID_VALUE;
     if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return GDR_ERROR_INVALID_VALUE;
-    return chunk_fwd_impl(p, q, k, v, g, beta, cu_seqlens, initial_state, o, final_state, workspace, hip_stream);
+    return chunk_fwd_impl(p, q, k, v, g, beta, cu_seqlens, initial_state, o, final_state, need > 0 ? workspace : nullptr,
+                          hip_stream);
 }
 
 gdr_status gdr_chunk_fwd_noalloc(const gdr_problem* p, int32_t chunk_size, const void* q, const void* k,

@@ -87,21 +87,26 @@ struct ChunkArgs {
 
 hipError_t launch_chunk(const ChunkArgs& a, int io_dtype, bool per_k, hipStream_t stream);
 
-// Context parallelism for one long sequence (gdr_cp.hip): the sequence is cut into P segments of
-// seg_tokens tokens (a multiple of 64; the last may be shorter) and run as P sequences.
+// Context parallelism for a few long sequences (gdr_cp.hip): every sequence is cut into segments of
+// seg_tokens tokens (a multiple of 64; a sequence's last segment may be shorter) that run as the
+// sequences of three chunk-kernel launches.
 constexpr int kCpWorkgroups = 256;   // target chunk-kernel workgroups per run: one per CU of the part
 constexpr int kCpMinChunks = 8;      // at least this many chunks per segment
-constexpr int kCpMinSegments = 6;    // below this the three runs cost more than they save
+constexpr int kCpMinSegments = 4;    // segments per sequence; below this the three runs cost more than they save
 
 struct CpPlan {
-    int P;                           // segments; 1 = no context parallelism
+    int P;                           // segments the workspace holds (an upper bound on the real count); 1 = no CP
+    int N;                           // sequences
     int64_t seg_tokens;
-    size_t cu_seg, B, M, S, total;   // workspace offsets (256-byte aligned) and size
+    size_t cu_seg, seg_first, B, M, S, total;   // workspace offsets (256-byte aligned) and size
 };
 
 CpPlan cp_plan(int64_t T, int32_t N, int32_t HV, int32_t K, int32_t V, int io_bytes);
-hipError_t launch_cp_setup(const CpPlan& pl, char* ws, int64_t T, int32_t HV, int32_t K, hipStream_t stream);
+hipError_t launch_cp_setup(const CpPlan& pl, char* ws, const int32_t* cu, int64_t T, int32_t HV, int32_t K,
+                           hipStream_t stream);
 hipError_t launch_cp_scan(const CpPlan& pl, char* ws, const float* h0, int32_t HV, int32_t K, int32_t V,
                           hipStream_t stream);
+hipError_t launch_cp_final(const CpPlan& pl, const char* ws, float* out, int32_t HV, int32_t K, int32_t V,
+                           hipStream_t stream);
 
 }  // namespace gdr

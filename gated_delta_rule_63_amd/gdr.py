@@ -200,9 +200,11 @@ def gdr_chunk_workspace_size(q, v, g, num_seqs: int, chunk_size: int = 64) -> in
 
 def gdr_chunk_fwd(q, k, v, g, beta, cu_seqlens=None, scale=None, initial_state=None, o=None,
                   final_state=None, output_final_state: bool = True, workspace=None, chunk_size: int = 64,
-                  stream=None):
+                  stream=None, segmented: bool = True):
     """Chunked (64-token) forward.  Returns (o, final_state or None).  ``workspace`` is a
-    uint8 device tensor of at least gdr_chunk_workspace_size bytes (allocated here if absent)."""
+    uint8 device tensor of at least gdr_chunk_workspace_size bytes (allocated here if absent).
+    ``segmented=False`` passes no workspace, which makes the library run every sequence in one
+    pass even where it would cut few long sequences into segments."""
     T, HK, HV, K, V = _check_tokens(q, k, v, g, beta)
     N = _num_seqs(cu_seqlens, 1)
     _check(initial_state, "initial_state", (N, HV, V, K), torch.float32, optional=True)
@@ -214,12 +216,14 @@ def gdr_chunk_fwd(q, k, v, g, beta, cu_seqlens=None, scale=None, initial_state=N
     _check(final_state, "final_state", (N, HV, V, K), torch.float32, optional=True)
     p = _problem(q, k, v, g, N, scale)
     need = int(lib().gdr_chunk_workspace_size(ctypes.byref(p), int(chunk_size)))
-    if workspace is None:
+    if not segmented:
+        workspace = None
+    elif workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    _check(workspace, "workspace", dtype=torch.uint8)
+    _check(workspace, "workspace", dtype=torch.uint8, optional=True)
     st = lib().gdr_chunk_fwd(ctypes.byref(p), int(chunk_size), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                              _ptr(cu_seqlens), _ptr(initial_state), _ptr(o), _ptr(final_state), _ptr(workspace),
-                             workspace.numel(), _stream(stream))
+                             0 if workspace is None else workspace.numel(), _stream(stream))
     _raise(st, "gdr_chunk_fwd")
     return o, final_state
 

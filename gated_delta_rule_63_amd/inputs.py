@@ -19,6 +19,8 @@ Workloads (sizes as named in the problem statement of the build):
                  heads, bf16 pool, bf16 per-token intermediate buffer, no commit.
 * ``prefill``    8 ragged sequences summing to 32768 tokens (two of length 64 and
                  65), 32 heads, K=V=128, bf16, fp32 initial state ~ N(0, 0.1).
+* ``long_batch`` 4 sequences of 16384 tokens, 16 heads, K=V=128, bf16, fp32 initial state
+                 (few long sequences: the segmented route of the chunked forward).
 * ``kda``        1 sequence of 65536+37 tokens, 16 heads, per-channel decay gk
                  (50% U[-2,0], 25% exactly 0, 25% exactly -2), beta 25% 0 /
                  25% 1 / 50% sigmoid(N(0,1)), zero initial state.
@@ -208,6 +210,13 @@ def prefill(seed: int = 4, adversarial: bool = False, lengths=None, HV: int = 32
                              g_range=(-2.0, 0.0), g_endpoints=0.25, name="prefill_adv")
     return dense_problem(seed, lengths, HK=HK, HV=HV, K=128, V=128, io_dtype=BF16,
                          g_range=(-0.1, 0.0), name="prefill")
+
+
+def long_batch(seed: int = 6, N: int = 4, length: int = 16384, HV: int = 16) -> Problem:
+    """A few long GDN sequences with few heads (the case the segmented route exists for): 4 x 16384
+    tokens, 16 heads, K=V=128, bf16, g ~ U[-0.1, 0], fp32 initial state."""
+    return dense_problem(seed, [length] * N, HK=HV, HV=HV, K=128, V=128, io_dtype=BF16,
+                         g_range=(-0.1, 0.0), name="long_batch")
 
 
 def kda(seed: int = 5, T: int = 65536 + 37, HV: int = 16) -> Problem:

@@ -139,9 +139,14 @@ GDR_API size_t gdr_chunk_workspace_size(const gdr_problem* p, int32_t chunk_size
  *   chunk_size     must be 64
  *   cu_seqlens, initial_state, o, final_state: as gdr_recurrent_fwd
  *   workspace      device buffer of at least gdr_chunk_workspace_size(p, 64) bytes,
- *                  caller-owned, contents need not be initialised, 256-byte aligned;
- *                  may be NULL when that size is 0 (the current kernels keep every
- *                  intermediate on chip)
+ *                  caller-owned, contents need not be initialised, 256-byte aligned, or NULL.
+ *                  A non-zero size means the problem has few, long sequences for the number of
+ *                  heads; with the workspace the call cuts every sequence into segments that run
+ *                  in parallel (segment offsets and linear maps, a scan over each sequence's
+ *                  segments, then every segment from its true start state), with NULL it runs
+ *                  every sequence's chunks in one pass.  A non-NULL workspace smaller than the
+ *                  size returns GDR_ERROR_INVALID_VALUE.
+ * fp32 I/O is supported for K = 64 only (K = 128 returns GDR_ERROR_NOT_SUPPORTED).
  * The result matches gdr_recurrent_fwd to the chunked method's rounding, not bitwise.
  */
 GDR_API gdr_status gdr_chunk_fwd(const gdr_problem* p, int32_t chunk_size,

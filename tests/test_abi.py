@@ -209,33 +209,52 @@ def _cp_size(T, N, HV, K=128, V=128, io=1):
     return gdr.lib().gdr_chunk_workspace_size(ctypes.byref(p), 64)
 
 
-def _cp_expected(T, HV, K, V, io_bytes):
+def _cp_expected(T, N, HV, K, V, io_bytes):
     """Workspace of the segmented path, written out from its definition: segments target one
-    workgroup per (segment, head) on 256 CUs with at least 8 chunks each, at least 6 of them; the
-    workspace holds the segment table, P-1 offsets [HV, V, K], P-1 maps [HV, K, K] and P start
-    states [HV, V, K], each rounded up to 256 bytes."""
-    nchunks = (T + 63) // 64
+    workgroup per (segment, head) on 256 CUs (at least 4 segments per sequence in that round), with
+    at least 8 chunks each, and at least 4 segments per sequence on average; the workspace holds
+    the segment table, the per-sequence first-segment indices, and P offsets [HV, V, K], P maps
+    [HV, K, K] and P start states [HV, V, K], where P = floor(T / segment) + N bounds the segment
+    count for any lengths; each part rounded up to 256 bytes."""
     vt = V // 64 if io_bytes == 4 else 1
-    P = min(256 // (HV * vt), nchunks // 8)
-    if P < 6:
+    per_seq = 256 // (N * HV * vt)
+    if per_seq < 4:
         return 0
-    seg = -(-nchunks // P)
-    P = -(-nchunks // seg)
-    if P < 6:
+    nchunks = (T + 63) // 64
+    seg = 64 * max(8, -(-nchunks // (per_seq * N)))
+    if T // seg // N < 4:
         return 0
+    P = T // seg + N
     up = lambda x: -(-x // 256) * 256
-    return up(4 * (P + 1)) + up(4 * (P - 1) * HV * V * K) + up(4 * (P - 1) * HV * K * K) + up(4 * P * HV * V * K)
+    return (up(4 * (P + 1)) + up(4 * (N + 1)) + up(4 * P * HV * V * K) + up(4 * P * HV * K * K)
+            + up(4 * P * HV * V * K))
+
+
+def test_segment_bound_covers_every_length_split():
+    """P = floor(T / seg) + N is at least sum_n max(1, ceil(len_n / seg)) for any lengths summing to T
+    (brute force over small cases, empty sequences included)."""
+    import itertools
+    for seg in (3, 4, 7):
+        for N in (1, 2, 3):
+            for lens in itertools.product(range(0, 13), repeat=N):
+                T = sum(lens)
+                need = sum(max(1, -(-x // seg)) for x in lens)
+                assert need <= T // seg + N, (seg, lens)
 
 
 @pytest.mark.parametrize("T,N,HV,K,V,io", [(65573, 1, 16, 128, 128, 1), (6417, 1, 2, 128, 128, 1),
                                           (3845, 1, 2, 64, 64, 0), (65573, 2, 16, 128, 128, 1),
                                           (2000, 1, 16, 128, 128, 1), (64, 1, 2, 64, 64, 0),
-                                          (32768, 1, 32, 128, 128, 1), (65573, 1, 64, 128, 128, 1)])
+                                          (32768, 1, 32, 128, 128, 1), (65573, 1, 64, 128, 128, 1),
+                                          (65536, 4, 16, 128, 128, 1), (32768, 8, 32, 128, 128, 1),
+                                          (9000, 3, 2, 128, 128, 1), (9000, 3, 2, 64, 128, 0),
+                                          (1 << 20, 16, 4, 128, 128, 1)])
 def test_segmented_workspace_size(T, N, HV, K, V, io):
-    """Host-side planning of the context-parallel route: only one sequence, enough chunks and few
-    enough heads take it; everything else needs no workspace."""
+    """Host-side planning of the context-parallel route: few long sequences with few heads take it;
+    everything else needs no workspace."""
     got = _cp_size(T, N, HV, K, V, io)
-    want = _cp_expected(T, HV, K, V, 4 if io == 0 else 2) if N == 1 else 0
-    assert got == want
-    if (T, N, HV) == (65573, 1, 16):
-        assert got > 0  # the KDA stress shape is segmented (16 segments)
+    assert got == _cp_expected(T, N, HV, K, V, 4 if io == 0 else 2)
+    if (T, N, HV) in ((65573, 1, 16), (65573, 2, 16), (65536, 4, 16)):
+        assert got > 0  # the KDA stress shape and a few long GDN sequences are segmented
+    if (T, N, HV) in ((32768, 8, 32), (2000, 1, 16)):
+        assert got == 0  # the prefill workload (8 sequences, 32 heads) and short sequences are not

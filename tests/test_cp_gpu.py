@@ -1,7 +1,8 @@
-"""Context-parallel chunked path: one long sequence with few heads is cut into segments that run
-in parallel (segment offsets, segment linear maps, a scan, then every segment from its true start
-state).  Checked against the fp64 token oracle, with and without an initial state, for both gate
-kinds and for fp32 operands."""
+"""Context-parallel chunked path: few long sequences with few heads are cut into segments that run
+in parallel (segment offsets, segment linear maps, a scan over each sequence's segments, then every
+segment from its true start state).  Checked against the fp64 token oracle, with and without an
+initial state, for both gate kinds, for fp32 operands, and for batches of several sequences
+(ragged, with an empty and a short one)."""
 import numpy as np
 import pytest
 import torch
@@ -16,7 +17,7 @@ pytestmark = pytest.mark.gpu
 
 def _run_and_check(p, h0=True, with_cu=True):
     d = problem_to_dev(p)
-    need = gdr.gdr_chunk_workspace_size(d["q"], d["v"], d["g"], 1)
+    need = gdr.gdr_chunk_workspace_size(d["q"], d["v"], d["g"], p.N)
     assert need > 0, "this shape is expected to take the segmented path"
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     o, ht = gdr.gdr_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"] if with_cu else None, p.scale,
@@ -128,3 +129,61 @@ def test_gating_prepass_graph_capture_replay_equals_eager():
         graph.replay()
         torch.cuda.synchronize()
         assert all(torch.equal(t, r_) for t, r_ in zip((qo, ko, g, beta), refs))
+
+
+def _direct(p, h0=True):
+    d = problem_to_dev(p)
+    o, ht = gdr.gdr_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], p.scale,
+                              d.get("h0") if h0 else None, segmented=False)
+    torch.cuda.synchronize()
+    return o, ht
+
+
+@pytest.mark.parametrize("h0", [True, False])
+def test_gdn_bf16_two_long_sequences(h0):
+    p = inputs.dense_problem(85, [64 * 40 + 7, 64 * 30 + 33], HK=1, HV=2, K=128, V=128, io_dtype="bf16",
+                             g_range=(-0.5, 0.0))
+    o, ht = _run_and_check(p, h0=h0)
+    # the single-pass route (no workspace) agrees to the bf16 bar
+    o2, ht2 = _direct(p, h0=h0)
+    assert max_rel_l2_tokens(f64(o), f64(o2), p.cu_seqlens) <= TOL["bf16"]
+    assert max_rel_l2_states(f64(ht), f64(ht2)) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("h0", [True, False])
+def test_gdn_bf16_four_ragged_sequences_with_empty_and_short(h0):
+    """Four sequences: long, empty, shorter than one segment, long; GQA 2:1."""
+    p = inputs.dense_problem(86, [6000, 0, 100, 5000], HK=1, HV=2, K=128, V=128, io_dtype="bf16",
+                             g_range=(-1.0, 0.0))
+    _run_and_check(p, h0=h0)
+
+
+@pytest.mark.parametrize("h0", [True, False])
+def test_kda_bf16_two_long_sequences(h0):
+    p = inputs.dense_problem(87, [64 * 50, 64 * 33 + 9], HK=2, HV=2, K=128, V=128, io_dtype="bf16",
+                             g_range=(-2.0, 0.0), g_endpoints=0.25, per_k_gate=True, beta_mode="mixed",
+                             with_initial_state=h0)
+    _run_and_check(p, h0=h0)
+
+
+def test_gdn_bf16_four_sequences_gqa_adversarial():
+    p = inputs.dense_problem(88, [2600, 2700, 64 * 45, 2500], HK=1, HV=2, K=128, V=128, io_dtype="bf16",
+                             g_range=(-2.0, 0.0), g_endpoints=0.25)
+    _run_and_check(p)
+
+
+def test_fp32_k64_two_sequences():
+    p = inputs.dense_problem(89, [64 * 40 + 5, 64 * 36], HK=1, HV=1, K=64, V=64, io_dtype="f32", g_range=(-0.5, 0.0))
+    _run_and_check(p)
+
+
+def test_long_batch_full_size_every_head_both_routes():
+    """4 x 16384 tokens, 16 heads: the segmented route on every (sequence, head) against the oracle,
+    and the single-pass route against it too."""
+    p = inputs.long_batch()
+    o, ht = _run_and_check(p)
+    o2, ht2 = _direct(p)
+    q, k, v, g, beta = oracle_inputs(p)
+    o_ref, f_ref, _ = oracle.recurrent(q, k, v, g, beta, p.cu_seqlens, p.scale, p.initial_state)
+    assert max_rel_l2_tokens(f64(o2), o_ref, p.cu_seqlens) <= TOL["bf16"]
+    assert max_rel_l2_states(f64(ht2), f_ref) <= TOL["bf16"]
