@@ -1,6 +1,6 @@
 """Benchmark of the gated-delta-rule hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--no-cpu-baseline]
 
 One step is one pass of the whole hot path over one batch of synthetic inputs,
 already resident in HBM:
@@ -12,10 +12,12 @@ already resident in HBM:
   verify   gdr_decode_paged  64 sequences x 12 tokens, bf16 pool, bf16 per-token states
                              [1025, 12, 32, 128, 128], no commit  (speculative verify)
 
-After the step, four legs outside it are timed the same way: the decode and verify launches
-with the gating front fused into the token loop (raw q, k, a, b in; gdr_decode_paged_gated),
-the gating pass followed by the plain verify launch (gdr_gating_prepass + gdr_decode_paged),
-and the per-channel-gate (KDA) chunked forward over one sequence of 65573 tokens, 16 heads.
+After the step, legs outside it are timed the same way: the decode and verify launches with the
+gating front fused into the token loop (raw q, k, a, b in; gdr_decode_paged_gated), the gating
+pass followed by the plain verify launch (gdr_gating_prepass + gdr_decode_paged), the
+per-channel-gate (KDA) chunked forward over one sequence of 65573 tokens with 16 heads, 4 x 16384
+GDN tokens with 16 heads on the segmented and the single-pass route, and the fused KDA decode
+front (gdr_kda_decode_fused) at 1, 16 and 64 sequences x 1 token with 32 heads.
 
 The JSON line reports prefill tokens/s as ``value`` and the decode state GB/s beside it,
 each leg's time from HIP events recorded on the stream the library launches on (torch's
@@ -98,6 +100,27 @@ def _alg_bytes_prepass(p):
     """Gating pass: q, k read and written, a and b read, g (fp32) and beta written, A_log and dt_bias."""
     io = 2 if p.io_dtype == "bf16" else 4
     return p.T * (4 * p.HK * p.K * io + 3 * p.HV * io + p.HV * 4) + p.HV * 8
+
+
+def _alg_bytes_kda_front(p):
+    """Fused KDA decode front, per call: for each active sequence the state read and written once per
+    head (commit), the convolution windows read and written, and per token the raw q, k, v, the gate
+    input, b, the epilogue gate (when on) and o; once per call the convolution taps and bias, the gate
+    projection, A_log, dt_bias and the norm weight; 4 bytes of index per sequence and the cu_seqlens."""
+    io = 2 if p.io_dtype == "bf16" else 4
+    st = 4 if p.pool_dtype == "f32" else 2
+    C = 2 * p.H * p.K + p.H * p.V
+    epi = p.norm_weight is not None
+    once = C * p.W * io + (C * io if p.conv_bias is not None else 0) + p.H * p.K * p.R * io + p.H * 4 \
+        + p.H * p.K * 4 + (p.V * io if epi else 0) + 4 * (p.N + 1)
+    per_tok = C * io + p.R * io + p.H * io + p.H * p.V * io * (2 if epi else 1)
+    per_seq = 2 * p.H * p.V * p.K * st + 2 * C * (p.W - 1) * io
+    lens = np.diff(p.cu_seqlens.astype(np.int64))
+    total = once + 4 * p.N
+    for n in range(p.N):
+        if p.state_indices[n] >= 0:
+            total += per_seq + int(lens[n]) * per_tok
+    return total
 
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -269,11 +292,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--legs", default="prefill,decode,verify",
                     help="comma-separated subset of legs to run (profiling passes); the JSON line needs all three")
-    ap.add_argument("--extra-legs", default="decode_gated,verify_gated,verify_prepass,kda,cp_segmented,cp_direct",
+    ap.add_argument("--extra-legs", default="decode_gated,verify_gated,verify_prepass,kda,cp_segmented,cp_direct,"
+                                            "kda_front_b1,kda_front_b16,kda_front_b64",
                     help="legs outside the step, timed after it: the gating front fused into the decode and verify "
                          "launches, the gating pass followed by the plain verify launch, the per-channel-gate "
                          "(KDA) chunked forward over one 65573-token sequence, and 4 x 16384-token GDN sequences "
-                         "with 16 heads on the segmented and the single-pass route ('' for none)")
+                         "with 16 heads on the segmented and the single-pass route, and the fused KDA decode front at "
+                         "1, 16 and 64 sequences x 1 token with 32 heads ('' for none)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before the legs, run one device-to-device copy of this many MiB (a plain copy kernel of "
                          "known size, used to scale the HBM byte counters of a profiling pass) and stop after the legs")
@@ -351,6 +376,27 @@ def main():
         gdr.gdr_chunk_fwd(C_["q"], C_["k"], C_["v"], C_["g"], C_["beta"], C_["cu"], pc.scale, C_["h0"], o=C_["o"],
                           final_state=C_["ht"], segmented=False)
 
+    # fused KDA decode front at decode shapes: 1, 16 and 64 sequences x 1 token, 32 heads, K=V=128,
+    # gate rank 128, convolution width 4, epilogue on, fp32 pool, commit
+    KF = {}
+    for nb in (1, 16, 64):
+        if f"kda_front_b{nb}" not in args.extra_legs.split(","):
+            continue
+        pf = inputs.kda_front_problem(560 + nb, B=nb, q_len=1, H=32, R=128, num_slots=max(2 * nb, 8))
+        dd = {n: to_dev(getattr(pf, n)) for n in ("q", "k", "v", "conv_weight", "conv_bias", "conv_state", "gate_in",
+                                                 "gate_weight", "A_log", "dt_bias", "b", "norm_weight", "norm_gate",
+                                                 "pool", "state_indices")}
+        dd["o"] = torch.empty((pf.T, pf.H, pf.V), dtype=torch.bfloat16, device=dev)
+        KF[nb] = (pf, dd)
+
+    def kda_front(nb):
+        pf, dd = KF[nb]
+        gdr.gdr_kda_decode_fused(dd["q"], dd["k"], dd["v"], dd["conv_weight"], dd["conv_state"], dd["gate_in"],
+                                 dd["gate_weight"], dd["A_log"], dd["dt_bias"], dd["b"], dd["pool"], dd["state_indices"],
+                                 max_q_len=1, commit=True, scale=pf.scale, conv_bias=dd["conv_bias"],
+                                 l2norm_eps=pf.l2_eps, norm_weight=dd["norm_weight"], norm_gate=dd["norm_gate"],
+                                 norm_eps=pf.norm_eps, o=dd["o"])
+
     K_ = None
     if "kda" in args.extra_legs.split(","):
         pk = inputs.kda()
@@ -399,7 +445,9 @@ def main():
             if n in args.legs.split(",")]
     extra = [(n, f) for n, f in (("decode_gated", decode_gated), ("verify_gated", verify_gated),
                                  ("verify_prepass", verify_prepass), ("kda", kda), ("cp_segmented", cp_segmented),
-                                 ("cp_direct", cp_direct)) if n in args.extra_legs.split(",")]
+                                 ("cp_direct", cp_direct), ("kda_front_b1", lambda: kda_front(1)),
+                                 ("kda_front_b16", lambda: kda_front(16)), ("kda_front_b64", lambda: kda_front(64)))
+             if n in args.extra_legs.split(",")]
     if args.calib_copy_mib:
         n = args.calib_copy_mib << 20
         src = torch.ones(n // 4, dtype=torch.float32, device=dev)
@@ -506,6 +554,13 @@ def main():
                              "bytes": _alg_bytes_prefill(pc), "flops": _alg_flops_prefill(pc),
                              "secs": extra_ms[leg] / 1e3,
                              "sources": ["gdr_chunk.hip", "gdr_device.h", "gdr_cp.hip", "gdr_api.hip"]}
+    for nb in (1, 16, 64):
+        leg = f"kda_front_b{nb}"
+        if leg in extra_ms:
+            leg_info[leg] = {"kernel": f"kda_decode_kernel (fused KDA decode front: {nb} x 1 token, 32 heads, K=V=128, "
+                                       "gate rank 128, width 4, epilogue, fp32 pool, commit)",
+                             "bytes": _alg_bytes_kda_front(KF[nb][0]), "flops": None, "secs": extra_ms[leg] / 1e3,
+                             "sources": ["gdr_kda.hip", "gdr_device.h"]}
     traffic = _measured_traffic()
 
     def roofline(leg):

@@ -212,6 +212,43 @@ gdr_status gdr_decode_paged_gated(const gdr_problem* p, int32_t max_q_len, const
                              cache_steps, inter_state_indices, o, hip_stream);
 }
 
+gdr_status gdr_kda_decode_fused(const gdr_problem* p, int32_t max_q_len, const void* q, const void* k, const void* v,
+                                const gdr_kda_front* f, const int32_t* cu_seqlens, void* pool, gdr_dtype pool_dtype,
+                                int32_t num_slots, const int32_t* state_indices, int32_t commit, void* o,
+                                void* hip_stream) {
+    gdr_status st = check_problem(p);
+    if (st != GDR_SUCCESS) return st;
+    if (!f) return GDR_ERROR_INVALID_VALUE;
+    if (p->gate != GDR_GATE_PER_K || p->num_k_heads != p->num_v_heads) return GDR_ERROR_NOT_SUPPORTED;
+    if (max_q_len < 1 || max_q_len > 12) return GDR_ERROR_INVALID_VALUE;
+    if (!pool || num_slots <= 0 || !state_indices) return GDR_ERROR_INVALID_VALUE;
+    if (!dtype_ok(pool_dtype)) return GDR_ERROR_INVALID_VALUE;
+    if (commit != 0 && commit != 1) return GDR_ERROR_INVALID_VALUE;
+    if (!cu_seqlens && p->total_tokens != p->num_seqs) return GDR_ERROR_INVALID_VALUE;
+    if (p->total_tokens > (int64_t)p->num_seqs * max_q_len) return GDR_ERROR_INVALID_VALUE;
+    if (f->conv_width < 1 || f->conv_width > 4) return GDR_ERROR_INVALID_VALUE;
+    if (f->conv_width > 1 && !f->conv_state) return GDR_ERROR_INVALID_VALUE;
+    if (f->gate_rank <= 0 || f->gate_rank > 4096 || f->gate_rank % 8 != 0) return GDR_ERROR_INVALID_VALUE;
+    if (!(f->l2norm_eps >= 0.0f) || f->l2norm_eps > 3.0e38f) return GDR_ERROR_INVALID_VALUE;
+    if (f->norm_weight && (!f->norm_gate || !(f->norm_eps >= 0.0f) || f->norm_eps > 3.0e38f))
+        return GDR_ERROR_INVALID_VALUE;
+    if (p->total_tokens > 0 && !(q && k && v && o && f->conv_weight && f->gate_in && f->gate_weight && f->A_log &&
+                                 f->dt_bias && f->b))
+        return GDR_ERROR_INVALID_VALUE;
+    if (p->num_seqs == 0 || p->total_tokens == 0) return GDR_SUCCESS;
+    if ((st = check_device()) != GDR_SUCCESS) return st;
+    gdr::KdaArgs a{};
+    a.q = q; a.k = k; a.v = v; a.cu_seqlens = cu_seqlens; a.pool = pool; a.slots = state_indices;
+    a.commit = commit; a.o = o;
+    a.conv_width = f->conv_width; a.conv_weight = f->conv_weight; a.conv_bias = f->conv_bias;
+    a.conv_state = f->conv_state; a.gate_in = f->gate_in; a.gate_weight = f->gate_weight;
+    a.gate_rank = f->gate_rank; a.A_log = f->A_log; a.dt_bias = f->dt_bias; a.b = f->b;
+    a.l2_eps = f->l2norm_eps; a.norm_weight = f->norm_weight; a.norm_gate = f->norm_gate; a.norm_eps = f->norm_eps;
+    a.scale = p->scale; a.N = p->num_seqs; a.HV = p->num_v_heads;
+    return status_of(gdr::launch_kda(a, p->head_dim_k, p->head_dim_v, p->io_dtype, pool_dtype,
+                                     static_cast<hipStream_t>(hip_stream)));
+}
+
 gdr_status gdr_gating_prepass(const gdr_problem* p, const void* q, const void* k, const gdr_gating* gating,
                               void* q_out, void* k_out, float* g_out, void* beta_out, void* hip_stream) {
     gdr_status st = check_problem(p);

@@ -87,6 +87,37 @@ struct ChunkArgs {
 
 hipError_t launch_chunk(const ChunkArgs& a, int io_dtype, bool per_k, hipStream_t stream);
 
+// Fused KDA decode front (gdr_kda.hip): convolution + SiLU, gate projection, q/k l2 norm, beta,
+// per-key-channel recurrence against the paged state, optional gated RMSNorm epilogue.
+struct KdaArgs {
+    const void* q;               // [T, HV, K] io dtype, raw (before the convolution)
+    const void* k;               // [T, HV, K]
+    const void* v;               // [T, HV, V]
+    const int32_t* cu_seqlens;   // [N + 1] or NULL (one token per sequence)
+    void* pool;                  // [slots, HV, V, K] state dtype
+    const int32_t* slots;        // [N]; negative = padded sequence
+    int32_t commit;              // write the state and the convolution windows back
+    void* o;                     // [T, HV, V] io dtype
+    int32_t conv_width;          // 1..4
+    const void* conv_weight;     // [C, W] io dtype, C = 2 HV K + HV V (q | k | v)
+    const void* conv_bias;       // [C] or NULL
+    void* conv_state;            // [slots, C, W - 1] io dtype
+    const void* gate_in;         // [T, R] io dtype
+    const void* gate_weight;     // [HV K, R] io dtype
+    int32_t gate_rank;           // R, a multiple of 8
+    const float* A_log;          // [HV]
+    const float* dt_bias;        // [HV K]
+    const void* b;               // [T, HV] io dtype
+    float l2_eps;
+    const void* norm_weight;     // [V] io dtype, or NULL: no epilogue
+    const void* norm_gate;       // [T, HV, V] io dtype
+    float norm_eps;
+    float scale;
+    int32_t N, HV;
+};
+
+hipError_t launch_kda(const KdaArgs& a, int K, int V, int io_dtype, int st_dtype, hipStream_t stream);
+
 // Context parallelism for a few long sequences (gdr_cp.hip): every sequence is cut into segments of
 // seg_tokens tokens (a multiple of 64; a sequence's last segment may be shorter) that run as the
 // sequences of three chunk-kernel launches.

@@ -8,7 +8,7 @@ HIP kernels.  If the library has not been built, loading it raises immediately.
 
 Names follow the C entry points: ``gdr_recurrent_fwd``, ``gdr_chunk_fwd``,
 ``gdr_chunk_fwd_noalloc``, ``gdr_chunk_workspace_size``, ``gdr_decode_paged``,
-``gdr_gating_prepass``, ``gdr_decode_paged_gated``, ``gdr_status_string``.
+``gdr_gating_prepass``, ``gdr_decode_paged_gated``, ``gdr_kda_decode_fused``, ``gdr_status_string``.
 """
 from __future__ import annotations
 
@@ -44,6 +44,25 @@ class Gating(ctypes.Structure):
         ("l2norm_eps", ctypes.c_float),
         ("qk_l2norm", ctypes.c_int32),
         ("allow_neg_eigval", ctypes.c_int32),
+    ]
+
+
+class KdaFront(ctypes.Structure):
+    _fields_ = [
+        ("conv_width", ctypes.c_int32),
+        ("conv_weight", ctypes.c_void_p),
+        ("conv_bias", ctypes.c_void_p),
+        ("conv_state", ctypes.c_void_p),
+        ("gate_in", ctypes.c_void_p),
+        ("gate_weight", ctypes.c_void_p),
+        ("gate_rank", ctypes.c_int32),
+        ("A_log", ctypes.c_void_p),
+        ("dt_bias", ctypes.c_void_p),
+        ("b", ctypes.c_void_p),
+        ("l2norm_eps", ctypes.c_float),
+        ("norm_weight", ctypes.c_void_p),
+        ("norm_gate", ctypes.c_void_p),
+        ("norm_eps", ctypes.c_float),
     ]
 
 
@@ -93,6 +112,9 @@ def lib():
         L.gdr_decode_paged_gated.restype = ctypes.c_int
         L.gdr_decode_paged_gated.argtypes = [P, i32, vp, vp, vp, G, vp, vp, ctypes.c_int, i32, vp, i32,
                                              vp, ctypes.c_int, i32, i32, vp, vp, vp]
+        L.gdr_kda_decode_fused.restype = ctypes.c_int
+        L.gdr_kda_decode_fused.argtypes = [P, i32, vp, vp, vp, ctypes.POINTER(KdaFront), vp, vp, ctypes.c_int, i32, vp,
+                                           i32, vp, vp]
         _lib = L
     return _lib
 
@@ -367,4 +389,47 @@ def gdr_decode_paged_gated(q, k, v, a, b, A_log, dt_bias, pool, state_indices, c
                                       1 if commit else 0, _ptr(inter_states), inter_dt, ncs, steps,
                                       _ptr(inter_state_indices), _ptr(o), _stream(stream))
     _raise(st, "gdr_decode_paged_gated")
+    return o
+
+
+def gdr_kda_decode_fused(q, k, v, conv_weight, conv_state, gate_in, gate_weight, A_log, dt_bias, b, pool,
+                         state_indices, cu_seqlens=None, max_q_len: int = 1, commit: bool = True, scale=None,
+                         conv_bias=None, l2norm_eps: float = 1e-6, norm_weight=None, norm_gate=None,
+                         norm_eps: float = 1e-6, o=None, stream=None):
+    """Fused KDA decode front (raw q, k, v [T, H, K|V]; conv_weight [C, W]; conv_state
+    [slots, C, W-1]; gate_in [T, R]; gate_weight [H*K, R]; A_log [H]; dt_bias [H*K]; b [T, H];
+    optional norm_weight [V] with norm_gate [T, H, V]).  Returns o."""
+    T, H, K = q.shape
+    V = v.shape[2]
+    _check(q, "q", (T, H, K))
+    _check(k, "k", (T, H, K), q.dtype)
+    _check(v, "v", (T, H, V), q.dtype)
+    C, W = conv_weight.shape
+    assert C == 2 * H * K + H * V, "conv_weight rows: q | k | v channels"
+    _check(conv_weight, "conv_weight", (C, W), q.dtype)
+    _check(conv_bias, "conv_bias", (C,), q.dtype, optional=True)
+    _check(conv_state, "conv_state", (pool.shape[0], C, W - 1), q.dtype, optional=(W == 1))
+    R = gate_in.shape[1]
+    _check(gate_in, "gate_in", (T, R), q.dtype)
+    _check(gate_weight, "gate_weight", (H * K, R), q.dtype)
+    _check(A_log, "A_log", (H,), torch.float32)
+    _check(dt_bias, "dt_bias", (H * K,), torch.float32)
+    _check(b, "b", (T, H), q.dtype)
+    _check(norm_weight, "norm_weight", (V,), q.dtype, optional=True)
+    _check(norm_gate, "norm_gate", (T, H, V), q.dtype, optional=True)
+    N = int(state_indices.shape[0])
+    _check(state_indices, "state_indices", (N,), torch.int32)
+    _check(pool, "pool", (pool.shape[0], H, V, K))
+    if o is None:
+        o = torch.empty((T, H, V), dtype=q.dtype, device=q.device)
+    _check(o, "o", (T, H, V), q.dtype)
+    p = Problem(T, N, H, H, K, V, float(1.0 / math.sqrt(K) if scale is None else scale), GDR_GATE_PER_K,
+                _dtype_code(q.dtype))
+    f = KdaFront(W, _ptr(conv_weight), _ptr(conv_bias), _ptr(conv_state), _ptr(gate_in), _ptr(gate_weight), R,
+                 _ptr(A_log), _ptr(dt_bias), _ptr(b), float(l2norm_eps), _ptr(norm_weight), _ptr(norm_gate),
+                 float(norm_eps))
+    st = lib().gdr_kda_decode_fused(ctypes.byref(p), int(max_q_len), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(f),
+                                    _ptr(cu_seqlens), _ptr(pool), _dtype_code(pool.dtype), int(pool.shape[0]),
+                                    _ptr(state_indices), int(bool(commit)), _ptr(o), _stream(stream))
+    _raise(st, "gdr_kda_decode_fused")
     return o

@@ -329,3 +329,83 @@ def raw_gating(seed: int, T: int, HK: int, HV: int, K: int, io_dtype: str = BF16
     return RawGating(q=cast_io(q, io_dtype), k=cast_io(k, io_dtype), a=cast_io(a, io_dtype),
                      b=cast_io(b, io_dtype), A_log=A_log, dt_bias=dt_bias, eps=float(eps),
                      qk_l2norm=bool(qk_l2norm), allow_neg_eigval=bool(allow_neg_eigval))
+
+
+@dataclasses.dataclass
+class KdaFrontProblem:
+    """Inputs of the fused KDA decode front (raw projections, convolution, gate, paged state):
+
+    q, k [T, H, K], v [T, H, V] io dtype (raw, before the convolution); conv_weight [C, W],
+    conv_bias [C] or None, conv_state [slots, C, W-1] io dtype with C = 2HK + HV (q | k | v);
+    gate_in [T, R], gate_weight [H*K, R] io dtype; A_log [H], dt_bias [H*K] fp32; b [T, H];
+    norm_weight [V] and norm_gate [T, H, V] io dtype (or None: no epilogue); pool
+    [slots, H, V, K] (pool_dtype); state_indices int32 [N] with -1 for padded sequences."""
+    T: int
+    N: int
+    H: int
+    K: int
+    V: int
+    R: int
+    W: int
+    io_dtype: str
+    pool_dtype: str
+    scale: float
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    conv_weight: np.ndarray
+    conv_bias: Optional[np.ndarray]
+    conv_state: np.ndarray
+    gate_in: np.ndarray
+    gate_weight: np.ndarray
+    A_log: np.ndarray
+    dt_bias: np.ndarray
+    b: np.ndarray
+    norm_weight: Optional[np.ndarray]
+    norm_gate: Optional[np.ndarray]
+    pool: np.ndarray
+    state_indices: np.ndarray
+    cu_seqlens: np.ndarray
+    max_q_len: int
+    l2_eps: float = 1e-6
+    norm_eps: float = 1e-6
+
+
+def kda_front_problem(seed: int, B: int, q_len: int, H: int, K: int = 128, V: int = 128, R: int = 128,
+                      W: int = 4, num_slots: Optional[int] = None, io_dtype: str = BF16, pool_dtype: str = F32,
+                      pad_count: int = 0, ragged: bool = False, with_bias: bool = True,
+                      with_epilogue: bool = True) -> KdaFrontProblem:
+    """Seeded draws: raw q, k, v ~ N(0, 1); taps ~ N(0, 0.5^2), bias ~ N(0, 0.1^2); windows ~ N(0, 1);
+    gate input ~ N(0, 1) and projection ~ N(0, 1/R) (unit-variance projections); A_log = ln U[1, 16];
+    dt_bias ~ U[-5, -1]; b ~ N(0, 1.5^2); norm weight ~ U[0.5, 1.5], norm gate ~ N(0, 1); state pool
+    ~ N(0, 0.1^2); distinct slots, pad_count of them -1."""
+    rng = np.random.default_rng(seed)
+    num_slots = num_slots if num_slots is not None else max(2 * B, 4)
+    lengths = rng.integers(1, q_len + 1, size=B) if ragged else np.full(B, q_len, dtype=np.int64)
+    T = int(lengths.sum())
+    cu = np.zeros(B + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lengths)
+    C = 2 * H * K + H * V
+    f = lambda *shape: rng.standard_normal(shape, dtype=np.float32)
+    q = cast_io(f(T, H, K), io_dtype)
+    k = cast_io(f(T, H, K), io_dtype)
+    v = cast_io(f(T, H, V), io_dtype)
+    conv_weight = cast_io(f(C, W) * np.float32(0.5), io_dtype)
+    conv_bias = cast_io(f(C) * np.float32(0.1), io_dtype) if with_bias else None
+    conv_state = cast_io(f(num_slots, C, W - 1), io_dtype)
+    gate_in = cast_io(f(T, R), io_dtype)
+    gate_weight = cast_io(f(H * K, R) * np.float32(1.0 / math.sqrt(R)), io_dtype)
+    A_log = np.log(rng.uniform(1.0, 16.0, H)).astype(np.float32)
+    dt_bias = rng.uniform(-5.0, -1.0, H * K).astype(np.float32)
+    b = cast_io(f(T, H) * np.float32(1.5), io_dtype)
+    norm_weight = cast_io(rng.uniform(0.5, 1.5, V).astype(np.float32), io_dtype) if with_epilogue else None
+    norm_gate = cast_io(f(T, H, V), io_dtype) if with_epilogue else None
+    pool = cast_io(f(num_slots, H, V, K) * np.float32(0.1), pool_dtype)
+    idx = rng.choice(num_slots, size=B, replace=False).astype(np.int32)
+    if pad_count:
+        idx[rng.choice(B, size=pad_count, replace=False)] = -1
+    return KdaFrontProblem(T=T, N=B, H=H, K=K, V=V, R=R, W=W, io_dtype=io_dtype, pool_dtype=pool_dtype,
+                           scale=1.0 / math.sqrt(K), q=q, k=k, v=v, conv_weight=conv_weight, conv_bias=conv_bias,
+                           conv_state=conv_state, gate_in=gate_in, gate_weight=gate_weight, A_log=A_log,
+                           dt_bias=dt_bias, b=b, norm_weight=norm_weight, norm_gate=norm_gate, pool=pool,
+                           state_indices=idx, cu_seqlens=cu, max_q_len=int(lengths.max()) if B else 1)

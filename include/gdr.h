@@ -278,6 +278,63 @@ GDR_API gdr_status gdr_decode_paged_gated(const gdr_problem* p, int32_t max_q_le
                                   const int32_t* inter_state_indices,
                                   void* o, void* hip_stream);
 
+/*
+ * Fused KDA decode front (tokenspeed PR #834 "[WIP] perf(k3): optimize decode": the commit that
+ * rewrites the single-launch KDA decode -- causal convolution with SiLU, the gate projection, q/k
+ * l2 normalisation and the delta-rule recurrence against the paged fp32 state -- and the commit
+ * that folds rmsnorm(o) * w * sigmoid(gate) into its epilogue).  The page names the steps but
+ * not their formulas; the readings taken here, per token t of sequence n and head h (one key head
+ * per value head, HK == HV):
+ *
+ *     conv     y[c] = silu(bias[c] + sum_{i<W} w[c][i] x_{t-(W-1)+i}[c]) for every channel c of
+ *              q, k and v (raw projections), with the tokens before the call taken from the
+ *              slot's window (the W-1 latest raw inputs, oldest first); silu(z) = z sigmoid(z)
+ *     gate     gk[h][c] = -exp(A_log[h]) softplus((gate_weight gate_in[t])[h K + c] + dt_bias[h K + c])
+ *              (softplus with threshold 20, as gdr_gating)
+ *     norm     q, k <- y / sqrt(sum y^2 + l2norm_eps) per (token, head)
+ *     beta     sigmoid(b[t, h])
+ *     state    the recurrence of gdr_decode_paged with the per-key-channel gate
+ *     epilogue optional: o <- o / sqrt(mean_v o^2 + norm_eps) * norm_weight[v] * sigmoid(norm_gate[t,h,v])
+ */
+typedef struct gdr_kda_front {
+    int32_t      conv_width;   /* W in 1..4                                                      */
+    const void*  conv_weight;  /* [C, W] io_dtype, C = 2*HV*K + HV*V channels: q | k | v, each   */
+                               /* head-major (q channel h*K + c, then k, then v); taps oldest first */
+    const void*  conv_bias;    /* [C] io_dtype, or NULL (no bias)                                */
+    void*        conv_state;   /* [num_slots, C, W-1] io_dtype: each slot's window, oldest first;  */
+                               /* rewritten in place on commit; may be NULL when W == 1            */
+    const void*  gate_in;      /* [T, R] io_dtype: the low-rank gate input of each token           */
+    const void*  gate_weight;  /* [HV*K, R] io_dtype: the gate projection                          */
+    int32_t      gate_rank;    /* R, a positive multiple of 8, at most 4096                        */
+    const float* A_log;        /* [HV] fp32                                                        */
+    const float* dt_bias;      /* [HV*K] fp32                                                      */
+    const void*  b;            /* [T, HV] io_dtype: beta input before the sigmoid                  */
+    float        l2norm_eps;   /* finite, >= 0                                                     */
+    const void*  norm_weight;  /* [V] io_dtype, or NULL: no epilogue                               */
+    const void*  norm_gate;    /* [T, HV, V] io_dtype (required with norm_weight)                  */
+    float        norm_eps;     /* finite, >= 0                                                     */
+} gdr_kda_front;
+
+/*
+ * gdr_kda_decode_fused -- decode (q_len 1) and multi-token decode (q_len up to 12) of the KDA layer
+ * from the raw projections, in one launch.  q, k [T, HV, K] and v [T, HV, V] are the raw inputs of
+ * the convolution; p->gate must be GDR_GATE_PER_K and p->num_k_heads == p->num_v_heads (otherwise
+ * GDR_ERROR_NOT_SUPPORTED).  cu_seqlens, pool, pool_dtype, num_slots, state_indices (-1 = padded:
+ * the sequence is skipped, its o rows untouched), commit and o behave as in gdr_decode_paged;
+ * commit also writes each active slot's convolution window back, and commit = 0 leaves both the
+ * pool and the windows unchanged.  There is no per-token intermediate-state buffer here.
+ * The workgroup of a (sequence, head) owns every convolution channel of that head, so the window
+ * update does not race between heads or sequences; distinct slots are required as in
+ * gdr_decode_paged.
+ */
+GDR_API gdr_status gdr_kda_decode_fused(const gdr_problem* p, int32_t max_q_len,
+                                const void* q, const void* k, const void* v,
+                                const gdr_kda_front* front,
+                                const int32_t* cu_seqlens,
+                                void* pool, gdr_dtype pool_dtype, int32_t num_slots,
+                                const int32_t* state_indices, int32_t commit,
+                                void* o, void* hip_stream);
+
 /* Human-readable name of a status code (static string, never NULL; unknown codes map to
  * "GDR_ERROR_UNKNOWN").  The codes stand for the loud contract checks of the pages' entry
  * points: a device-capability check (cuLA PR #113, review thread on SM90 availability) and a

@@ -258,3 +258,42 @@ def test_segmented_workspace_size(T, N, HV, K, V, io):
         assert got > 0  # the KDA stress shape and a few long GDN sequences are segmented
     if (T, N, HV) in ((32768, 8, 32), (2000, 1, 16)):
         assert got == 0  # the prefill workload (8 sequences, 32 heads) and short sequences are not
+
+
+def _kda_front(**kw):
+    f = dict(conv_width=4, conv_weight=0x1000, conv_bias=None, conv_state=0x1000, gate_in=0x1000,
+             gate_weight=0x1000, gate_rank=128, A_log=0x1000, dt_bias=0x1000, b=0x1000, l2norm_eps=1e-6,
+             norm_weight=None, norm_gate=None, norm_eps=1e-6)
+    f.update(kw)
+    return gdr.KdaFront(f["conv_width"], f["conv_weight"], f["conv_bias"], f["conv_state"], f["gate_in"],
+                        f["gate_weight"], f["gate_rank"], f["A_log"], f["dt_bias"], f["b"], f["l2norm_eps"],
+                        f["norm_weight"], f["norm_gate"], f["norm_eps"])
+
+
+def _kda(p, front, max_q_len=1, cu=None, pool=DUMMY, idx=DUMMY, commit=1, o=DUMMY, slots=8):
+    return gdr.lib().gdr_kda_decode_fused(ctypes.byref(p), max_q_len, DUMMY, DUMMY, DUMMY,
+                                          ctypes.byref(front) if front is not None else None, cu, pool, 0, slots, idx,
+                                          commit, o, None)
+
+
+def test_kda_front_rejects_bad_metadata_before_the_device():
+    p = _p(T=4, N=4, HK=2, HV=2, gate=1)
+    assert _kda(p, None) == 1
+    assert _kda(p, _kda_front(conv_width=5)) == 1
+    assert _kda(p, _kda_front(conv_width=0)) == 1
+    assert _kda(p, _kda_front(conv_state=None)) == 1                 # W > 1 needs the windows
+    assert _kda(p, _kda_front(gate_rank=12)) == 1                    # a multiple of 8
+    assert _kda(p, _kda_front(gate_rank=0)) == 1
+    assert _kda(p, _kda_front(l2norm_eps=-1.0)) == 1
+    assert _kda(p, _kda_front(norm_weight=0x1000)) == 1              # the epilogue needs its gate
+    assert _kda(p, _kda_front(b=None)) == 1
+    assert _kda(p, _kda_front(), max_q_len=13) == 1
+    assert _kda(p, _kda_front(), commit=2) == 1
+    assert _kda(p, _kda_front(), pool=None) == 1
+    assert _kda(p, _kda_front(), o=None) == 1
+    assert _kda(_p(T=5, N=4, HK=2, HV=2, gate=1), _kda_front()) == 1  # T != N without cu_seqlens
+    # the front is defined for the per-key-channel gate with one key head per value head
+    assert _kda(_p(T=4, N=4, HK=2, HV=2, gate=0), _kda_front()) == 2
+    assert _kda(_p(T=4, N=4, HK=1, HV=2, gate=1), _kda_front()) == 2
+    # empty batch: nothing to do, no device needed
+    assert _kda(_p(T=0, N=4, HK=2, HV=2, gate=1), _kda_front(), cu=DUMMY) == 0

@@ -46,3 +46,15 @@ def test_decode_and_verify_bytes():
     per_seq = 4 + 32 * 128 * 128 * 2 + 12 * (2 * 16 * 128 * 2 + 2 * 32 * 128 * 2 + 32 * 4 + 32 * 2) \
         + 12 * 32 * 128 * 128 * 2 + 4
     assert bench._alg_bytes_paged(v, with_ibuf=True) == 64 * per_seq + 4 * 65 == 891_437_828
+
+
+def test_kda_front_bytes():
+    p = inputs.kda_front_problem(564, B=64, q_len=1, H=32, R=128, num_slots=128)
+    # once per call: taps [C, 4] and bias [C] in bf16 (C = 2*32*128 + 32*128 = 12288 channels), the gate
+    # projection [4096, 128] bf16, A_log and dt_bias fp32, the norm weight [128] bf16, cu_seqlens (65)
+    once = 12288 * 4 * 2 + 12288 * 2 + 4096 * 128 * 2 + 32 * 4 + 4096 * 4 + 128 * 2 + 4 * 65
+    # per sequence: index; fp32 state read and written (32 heads of 128 x 128); windows (12288 x 3 bf16)
+    # read and written; one token's raw q, k, v (12288 bf16), gate input (128), b (32), epilogue gate and
+    # o (32 x 128 each)
+    per_seq = 4 + 2 * 32 * 128 * 128 * 4 + 2 * 12288 * 3 * 2 + (12288 + 128 + 32 + 2 * 32 * 128) * 2
+    assert bench._alg_bytes_kda_front(p) == once + 64 * per_seq == 281_703_300
