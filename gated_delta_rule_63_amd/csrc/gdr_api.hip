@@ -288,7 +288,8 @@ gdr_status check_chunk(const gdr_problem* p, int32_t chunk_size, const void* q, 
     gdr_status st = check_problem(p);
     if (st != GDR_SUCCESS) return st;
     if (chunk_size != 64) return GDR_ERROR_INVALID_VALUE;
-    if (p->io_dtype == GDR_F32 && p->head_dim_k != 64) return GDR_ERROR_NOT_SUPPORTED;
+    // fp32 operands with the per-key-channel gate need K = 64 (the LDS layout of K = 128 does not fit)
+    if (p->io_dtype == GDR_F32 && p->gate == GDR_GATE_PER_K && p->head_dim_k != 64) return GDR_ERROR_NOT_SUPPORTED;
     if (!token_inputs_ok(p, q, k, v, g, beta)) return GDR_ERROR_INVALID_VALUE;
     if (p->total_tokens > 0 && !o) return GDR_ERROR_INVALID_VALUE;
     if (p->num_seqs > 1 && !cu_seqlens) return GDR_ERROR_INVALID_VALUE;

@@ -503,6 +503,21 @@ struct RhsFromRows {                               // row-major bf16 rows (perm(
     }
 };
 
+struct RhsFromRowsF32 {                            // row-major fp32 rows (natural columns), columns c0 .. c0+15
+    const float* m;
+    int ld, c0;
+    const float* sc;
+    struct Raw {
+        f32x4_t f, x;
+    };
+    __device__ __forceinline__ Raw raw(int I) const {
+        const int t0 = 16 * I + 4 * ((threadIdx.x & 63) >> 4), c = c0 + (threadIdx.x & 15);
+        return Raw{*reinterpret_cast<const f32x4_t*>(sc + t0),
+                   f32x4_t{m[t0 * ld + c], m[(t0 + 1) * ld + c], m[(t0 + 2) * ld + c], m[(t0 + 3) * ld + c]}};
+    }
+    __device__ __forceinline__ static f32x4_t value(const Raw& r) { return r.x * r.f; }
+};
+
 // X = (I + L)^-1 B for NR 16-column tiles of B (64 rows each), by blocked forward substitution:
 // X_I = D_I (B_I - sum_{J<I} L_IJ X_J), D_I = (I + L_II)^-1.  L's off-diagonal blocks are read
 // negated from sLo (row-major, stride ldo), the D_I from sD (block I at sD + 16*I*ldd); rhs[n].raw(I)
@@ -633,16 +648,20 @@ struct Layout {
     static constexpr int LDV = BV + MM<MT>::PAD;
     static constexpr bool TRK = !PER_K && BF && K / 16 == BV / 16;
     static_assert(!TRK || sizeof(S) * CH * LDV <= VT_, "row-major V fits the V^T area");
+    // fp32 operands at K = 128 (scalar gate): an fp32 MFMA operand is one element per lane, so K^T is
+    // read from the row-major K rows with transposed indexing and no K^T copy is built; the fp32
+    // diagonal blocks of L live in the -W area (W is dead from E until D rewrites it)
+    static constexpr bool KROW = !PER_K && !BF && K == 128;
 
     // ---- scalar gate ----
     static constexpr size_t g_q = 0;              // Q rows
     static constexpr size_t g_k = g_q + ROWK;     // K rows
     static constexpr size_t g_w = g_k + ROWK;     // -W rows
     static constexpr size_t g_kt = g_w + ROWK;    // K^T
-    static constexpr size_t g_vt = g_kt + KT_;    // V^T
+    static constexpr size_t g_vt = g_kt + (KROW ? 0 : KT_);  // V^T
     static constexpr size_t g_lo = g_vt + VT_;
-    static constexpr size_t g_ld = g_lo + LO_;
-    static constexpr size_t g_d = g_ld + LD_;
+    static constexpr size_t g_ld = KROW ? g_w : g_lo + LO_;
+    static constexpr size_t g_d = g_lo + LO_ + (KROW ? 0 : LD_);
     static constexpr size_t g_p = g_d + D_;       // P rows
     static constexpr size_t g_g = g_p + ROWT;     // gamma [64]
     static constexpr size_t g_b = g_g + sizeof(float) * CH;    // beta [64]
@@ -686,6 +705,7 @@ struct Layout {
     // written at the end of E and flushed at the start of the next iteration; the -L and
     // diagonal-inverse area it overlays is rewritten only in B/C, after the next phase-A barrier.
     static constexpr size_t o_stage = PER_K ? k_lo : g_lo;
+    static constexpr size_t o_room = PER_K ? LO_ + LD_ + D_ : g_d + D_ - g_lo;  // bytes the staging may overlay
     static constexpr size_t total = PER_K ? k_total : g_total;
 };
 
@@ -720,7 +740,8 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
     typedef OStage<BV, IO> OS;
     constexpr bool TRK = Lay::TRK;
     static_assert(Lay::total <= 160 * 1024, "LDS budget");
-    static_assert(OS::bytes <= Lay::LO_ + Lay::LD_ + Lay::D_, "output staging overlays -L and the inverses");
+    static_assert(OS::bytes <= Lay::o_room, "output staging overlays -L and the inverses");
+    constexpr bool KROW = Lay::KROW;
     __shared__ __align__(16) char smem[Lay::total];
     auto SP = [&](size_t off) { return reinterpret_cast<S*>(smem + off); };
     auto FP = [&](size_t off) { return reinterpret_cast<float*>(smem + off); };
@@ -877,7 +898,7 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
                 const int c8 = PK::col(tid, i), pr0 = 2 * PK::pair(tid, i);
                 st8_perm<MT, IO>(sK + pr0 * LDK, c8, kr[2 * i]);
                 st8_perm<MT, IO>(sK + (pr0 + 1) * LDK, c8, kr[2 * i + 1]);
-                if constexpr (!PER_K && !TRK) st_pair_t<MT, IO>(SP(Lay::g_kt), LDT, c8, pr0, kr[2 * i], kr[2 * i + 1]);
+                if constexpr (!PER_K && !TRK && !KROW) st_pair_t<MT, IO>(SP(Lay::g_kt), LDT, c8, pr0, kr[2 * i], kr[2 * i + 1]);
             }
         }
         if constexpr (!PER_K) {
@@ -1288,8 +1309,13 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
             } else {
                 for (int jt = w; jt < KT; jt += NW) {
                     f32x4_t X[1][4];
-                    const RhsFromTransposed<MT> rhs[1] = {{sKb + (16 * jt + lr) * LDT, wsc}};
-                    block_solve<MT, 1>(X, sLo, LDO, sD, LDD, rhs);
+                    if constexpr (KROW) {
+                        const RhsFromRowsF32 rhs[1] = {{FP(Lay::g_k), LDK, 16 * jt, wsc}};
+                        block_solve<MT, 1>(X, sLo, LDO, sD, LDD, rhs);
+                    } else {
+                        const RhsFromTransposed<MT> rhs[1] = {{sKb + (16 * jt + lr) * LDT, wsc}};
+                        block_solve<MT, 1>(X, sLo, LDO, sD, LDD, rhs);
+                    }
                     store_w(jt, X[0]);
                 }
                 f32x4_t X[1][4];
@@ -1361,6 +1387,17 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
                         hs[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, hs[kt], 0, 0, 0);
                     }
                 }
+            } else if constexpr (KROW) {
+                // hs[kt] += K[:, 16 kt ..]^T v_new~: A[c][t] = K[t][c] read with transposed indexing
+                const float* sKf = FP(Lay::g_k);
+#pragma unroll
+                for (int t = 0; t < CH / 16; ++t)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+#pragma unroll
+                        for (int kt = 0; kt < KT; ++kt)
+                            hs[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(sKf[(16 * t + 4 * g4 + e) * LDK + 16 * kt + lr],
+                                                                          nu[t][e], hs[kt], 0, 0, 0);
             } else {
                 gemm_regs<MT, CH, KT>(hs, SP(Lay::g_kt), LDT, nu);
             }
@@ -2374,9 +2411,10 @@ hipError_t launch_fused(const ChunkArgs& a, hipStream_t stream) {
 template <int K, int V>
 hipError_t launch_kv(const ChunkArgs& a, int io, bool per_k, hipStream_t s) {
     if (io == 0) {
-        // fp32 operands at K = 128 do not fit the 160 KiB of LDS in this design
+        // fp32 operands: every shape with the scalar gate; the per-channel gate at K = 128 does not
+        // fit the 160 KiB of LDS in this design
         if constexpr (K == 64) return per_k ? launch_fused<K, V, float, true>(a, s) : launch_fused<K, V, float, false>(a, s);
-        else return hipErrorNotSupported;
+        else return per_k ? hipErrorNotSupported : launch_fused<K, V, float, false>(a, s);
     }
     return per_k ? launch_fused<K, V, bf16_t, true>(a, s) : launch_fused<K, V, bf16_t, false>(a, s);
 }

@@ -146,7 +146,8 @@ GDR_API size_t gdr_chunk_workspace_size(const gdr_problem* p, int32_t chunk_size
  *                  segments, then every segment from its true start state), with NULL it runs
  *                  every sequence's chunks in one pass.  A non-NULL workspace smaller than the
  *                  size returns GDR_ERROR_INVALID_VALUE.
- * fp32 I/O is supported for K = 64 only (K = 128 returns GDR_ERROR_NOT_SUPPORTED).
+ * fp32 I/O is supported for every K, V with the scalar gate; with the per-key-channel gate it
+ * needs K = 64 (K = 128 returns GDR_ERROR_NOT_SUPPORTED).
  * The result matches gdr_recurrent_fwd to the chunked method's rounding, not bitwise.
  */
 GDR_API gdr_status gdr_chunk_fwd(const gdr_problem* p, int32_t chunk_size,

@@ -123,7 +123,7 @@ def test_chunk_workspace_and_rejections():
     assert call(p, ws=ctypes.c_void_p(0x1010)) == 1    # not 256-byte aligned
     assert call(p, cu=None) == 1                        # N > 1 needs cu_seqlens
     assert call(_p(K=96)) == 2
-    assert call(_p(K=128, io=0)) == 2                   # fp32 operands need K = 64
+    assert call(_p(K=128, io=0, gate=1)) == 2           # fp32 with the per-channel gate needs K = 64
 
 
 def test_chunk_noalloc_rejects_bad_metadata_before_the_device():
@@ -136,7 +136,7 @@ def test_chunk_noalloc_rejects_bad_metadata_before_the_device():
     assert call(p, cu=None) == 1                        # N > 1 needs cu_seqlens
     assert call(p, o=None) == 1
     assert call(_p(K=96)) == 2
-    assert call(_p(K=128, io=0)) == 2
+    assert call(_p(K=128, io=0, gate=1)) == 2
     assert call(_p(T=0, N=0), cu=None) == 0             # nothing to do, no device needed
     assert L.gdr_chunk_fwd_noalloc(None, 64, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, None, DUMMY, None, None) == 1
 

@@ -60,6 +60,23 @@ def test_head_dims_bf16(K, V):
     _check(p, o, ht)
 
 
+@pytest.mark.parametrize("V,lengths,h0", [(128, [70, 5, 64, 200], True), (64, [130, 1, 63], True),
+                                           (128, [65, 0, 37], False)])
+def test_fp32_k128(V, lengths, h0):
+    """fp32 I/O at K = 128 (scalar gate): fp32 MFMA, K^T read from the row-major rows."""
+    p = inputs.dense_problem(65 + V + len(lengths), lengths, HK=2, HV=4, K=128, V=V, io_dtype="f32",
+                             g_range=(-0.5, 0.0), with_initial_state=h0)
+    o, ht = _chunk(p, h0=h0)
+    _check(p, o, ht, h0=h0)
+
+
+def test_fp32_k128_adversarial_decay():
+    p = inputs.dense_problem(66, [200, 64, 65], HK=1, HV=2, K=128, V=128, io_dtype="f32", g_range=(-2.0, 0.0),
+                             g_endpoints=0.25)
+    o, ht = _chunk(p)
+    _check(p, o, ht)
+
+
 @pytest.mark.parametrize("V", [64, 128])
 def test_fp32_k64(V):
     p = inputs.dense_problem(61 + V, [70, 5, 64], HK=1, HV=2, K=64, V=V, io_dtype="f32", g_range=(-0.5, 0.0))

@@ -187,3 +187,8 @@ def test_long_batch_full_size_every_head_both_routes():
     o_ref, f_ref, _ = oracle.recurrent(q, k, v, g, beta, p.cu_seqlens, p.scale, p.initial_state)
     assert max_rel_l2_tokens(f64(o2), o_ref, p.cu_seqlens) <= TOL["bf16"]
     assert max_rel_l2_states(f64(ht2), f_ref) <= TOL["bf16"]
+
+
+def test_fp32_k128_long_sequence():
+    p = inputs.dense_problem(90, [64 * 70 + 11], HK=1, HV=2, K=128, V=128, io_dtype="f32", g_range=(-0.5, 0.0))
+    _run_and_check(p)
