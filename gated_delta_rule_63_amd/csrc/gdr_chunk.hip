@@ -1,8 +1,9 @@
 // Chunked gated delta rule for gfx950: one fused kernel over 64-token chunks (WY/UT form).
 //
-// Two kernels: chunk_pipe_kernel (below, near the end) for bf16 I/O with the scalar gate at K = V = 128,
-// which overlaps the state-dependent step of one chunk with the state-independent steps of the next,
-// and chunk_fused_kernel for every other configuration, described here.
+// Two kernels: chunk_flow_kernel (below, near the end) for bf16 I/O with the scalar gate at K = V = 128,
+// which solves v_new from the state and overlaps the state-dependent step of one chunk with the
+// state-independent steps of the next, and chunk_fused_kernel for every other configuration,
+// described here.
 //
 // One workgroup owns the whole state S[V][K] of one (sequence, value head) -- or a 64-wide
 // V tile of it -- and walks the sequence's chunks in order.  Wave w keeps the 16 state
@@ -231,13 +232,13 @@ __device__ __forceinline__ uint32_t pack_tile_hi(const f32x4_t& t) { return pack
 // 32m + 4*(l/16) + e (e < 4) or 32m + 16 + 4*(l/16) + e - 4 (e >= 4) -- one 16-byte read of a
 // perm()-ordered A row; for an fp32 step (t, e) position l/16 is index 16t + 4*(l/16) + e.
 // With LOWER, A is lower triangular (A[r][j] = 0 for j > r): reduction steps entirely above the
-// diagonal of a 16-row tile are skipped.
-template <typename MT, int NP, int NI, bool LOWER = false>
+// diagonal of a 16-row tile are skipped.  GMAX k-steps of A reads are issued together, before
+// their products (GMAX = 1 where registers are short).
+template <typename MT, int NP, int NI, bool LOWER = false, int GMAX = 2>
 __device__ __forceinline__ void gemm_regs(f32x4_t* acc, const typename MM<MT>::S* sA, int lda, const f32x4_t* Bt) {
     const int l = threadIdx.x & 63, g4 = l >> 4, lr = l & 15;
     if constexpr (sizeof(typename MM<MT>::S) == 2) {
-        // the A reads of two k-steps are issued together, before their products
-        constexpr int MS = NP / 32, G = MS < 2 ? MS : 2;
+        constexpr int MS = NP / 32, G = MS < GMAX ? MS : GMAX;
 #pragma unroll
         for (int m0 = 0; m0 < MS; m0 += G) {
             bf16x8_t av[G][NI];
@@ -299,6 +300,14 @@ template <> struct Raw8<bf16_t> {
             x[2 * j + 1] = __uint_as_float(ws[j] & 0xFFFF0000u);
         }
     }
+    // elements 4hh .. 4hh+3
+    __device__ __forceinline__ void get4(float* x, int hh) const {
+        const uint32_t w0 = hh ? w.z : w.x, w1 = hh ? w.w : w.y;
+        x[0] = __uint_as_float(w0 << 16);
+        x[1] = __uint_as_float(w0 & 0xFFFF0000u);
+        x[2] = __uint_as_float(w1 << 16);
+        x[3] = __uint_as_float(w1 & 0xFFFF0000u);
+    }
 };
 template <> struct Raw8<float> {
     f32x4_t a, b;
@@ -312,6 +321,10 @@ template <> struct Raw8<float> {
             x[e] = a[e];
             x[4 + e] = b[e];
         }
+    }
+    __device__ __forceinline__ void get4(float* x, int hh) const {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = hh ? b[e] : a[e];
     }
 };
 
@@ -524,10 +537,8 @@ struct RhsFromRowsF32 {                            // row-major fp32 rows (natur
 // returns block I of tile n.  X stays in registers in C layout; with v_mfma_f32_16x16x16_bf16 the
 // C layout of one block is the B operand layout of the next product, so each wave solves its own
 // columns without synchronising with the others.  The NR tiles share every read of L and D, and
-// their dependency chains interleave.  With FENCE the chain is kept behind the reads (a scheduling
-// barrier); without it the compiler interleaves the two, which the pipelined kernel prefers (its
-// solve shares the SIMD with a wave of the other role).
-template <typename MT, int NR, typename Rhs, bool FENCE = true>
+// their dependency chains interleave.  A scheduling barrier keeps the chain behind the reads.
+template <typename MT, int NR, typename Rhs>
 __device__ __forceinline__ void block_solve(f32x4_t (*X)[4], const typename MM<MT>::S* sLo, int ldo,
                                             const typename MM<MT>::S* sD, int ldd, const Rhs* rhs) {
     const int l = threadIdx.x & 63, g4 = l >> 4, lr = l & 15;
@@ -548,7 +559,7 @@ __device__ __forceinline__ void block_solve(f32x4_t (*X)[4], const typename MM<M
             for (int J = 0; J < I; ++J)
                 lv[I * (I - 1) / 2 + J] = *reinterpret_cast<const s16x4_t*>(sLo + (16 * I + lr) * ldo + 16 * J + 4 * g4);
         }
-        if constexpr (FENCE) __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_sched_barrier(0);
         f32x4_t R[NR][4];
 #pragma unroll
         for (int I = 0; I < 4; ++I)
@@ -571,7 +582,7 @@ __device__ __forceinline__ void block_solve(f32x4_t (*X)[4], const typename MM<M
             }
         }
     } else {
-        if constexpr (FENCE) __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_sched_barrier(0);
         f32x4_t R[NR][4];
 #pragma unroll
         for (int I = 0; I < 4; ++I)
@@ -622,6 +633,28 @@ __device__ __forceinline__ void st8_perm(typename MM<MT>::S* row, int c8, const 
     } else {
         float f[8];
         x.get(f);
+        MM<MT>::st8(row + c8, f);
+    }
+}
+
+// Four fp32 values of logical columns c4 .. c4+3 (c4 a multiple of 4) into an operand row, in the
+// operand's type and column order (the four stay adjacent under perm()).
+template <typename MT>
+__device__ __forceinline__ void st4f_perm(typename MM<MT>::S* row, int c4, const float* f) {
+    if constexpr (sizeof(typename MM<MT>::S) == 2)
+        *reinterpret_cast<uint2*>(row + perm<MT>(c4)) = uint2{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3])};
+    else
+        *reinterpret_cast<f32x4_t*>(row + c4) = f32x4_t{f[0], f[1], f[2], f[3]};
+}
+
+// Eight fp32 values of logical columns c8 .. c8+7 into an operand row, in the operand's type and
+// column order.
+template <typename MT>
+__device__ __forceinline__ void st8f_perm(typename MM<MT>::S* row, int c8, const float* f) {
+    if constexpr (sizeof(typename MM<MT>::S) == 2) {
+        *reinterpret_cast<uint2*>(row + perm<MT>(c8)) = uint2{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3])};
+        *reinterpret_cast<uint2*>(row + perm<MT>(c8 + 4)) = uint2{pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])};
+    } else {
         MM<MT>::st8(row + c8, f);
     }
 }
@@ -699,6 +732,7 @@ struct Layout {
     static constexpr size_t k_d = k_ld + LD_;
     static constexpr size_t k_w = k_d + D_;
     static constexpr size_t k_part = k_w;                             // gamma partial sums (phase A)
+    static constexpr size_t k_fp = k_lk;                              // [7][K] pair factors (A to B/C, MFMA form)
     static constexpr size_t k_total = k_w + ROWK;
 
     // output tile staging [64][BV] in the IO type, 16-byte granules XOR-swizzled by row.  It is
@@ -737,6 +771,8 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
     typedef Layout<K, BV, MT, PER_K> Lay;
     constexpr int LDK = Lay::LDK, LDT = Lay::LDT, LDO = Lay::LDO, LDD = Lay::LDD;
     static_assert(NW >= 4, "four waves invert the diagonal blocks");
+    // without outputs (the segment-offset and segment-map runs) q, P and the output are skipped
+    const bool want_o = a.o != nullptr;
     typedef OStage<BV, IO> OS;
     constexpr bool TRK = Lay::TRK;
     static_assert(Lay::total <= 160 * 1024, "LDS budget");
@@ -748,7 +784,7 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
 
     const int vt = blockIdx.x, h = blockIdx.y, n = blockIdx.z;
     const int hk = h / (a.HV / a.HK);
-    const int tid = threadIdx.x, l = tid & 63, g4 = l >> 4, lr = l & 15;
+    int tid = threadIdx.x, l = tid & 63, g4 = l >> 4, lr = l & 15;  // laundered each chunk (below)
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in a scalar register
     const int v0 = vt * BV;
     const int vcol = v0 + 16 * w + lr;
@@ -780,7 +816,9 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
     typedef PairTile<BV, NTHR> PV;           // v row pairs
     constexpr int GQ = NTHR / K;                   // per-K gate: row groups per channel
     constexpr int RPQ = PER_K ? CH / GQ : 1;       // gate values per thread
-    Raw8<IO> qn[TQ::NV], kn[2 * PK::NPASS], vn[2 * PV::NPASS];
+    // per-K gate: q in the row-pair mapping of k, so that both share the decay factors of a unit
+    constexpr int NQ = PER_K ? 2 * PK::NPASS : TQ::NV;
+    Raw8<IO> qn[NQ], kn[2 * PK::NPASS], vn[2 * PV::NPASS];
     float gn[RPQ] = {};
     uint32_t bn = 0;  // beta kept as loaded (bf16 bits or fp32 bits): converting here would wait on the load
     // byte strides of one token row and this thread's byte offsets inside a chunk (fixed)
@@ -796,11 +834,19 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
         return (s1 - bos) < CH ? (int)(s1 - bos) : CH;
     };
     auto load_q = [&](int ci) {
+        if (!want_o) return;  // q only feeds P and the output
         const int64_t bos = s0 + (int64_t)CH * ci;
         const __amdgpu_buffer_rsrc_t rq =
             chunk_rsrc(static_cast<const char*>(a.q) + ((bos * a.HK + hk) * K) * ESZ, chunk_len(ci), qk_row);
+        if constexpr (PER_K) {
 #pragma unroll
-        for (int i = 0; i < TQ::NV; ++i) qn[i].load(rq, TQ::row(tid, i) * qk_row + TQ::col(tid) * ESZ);
+            for (int i = 0; i < PK::NPASS; ++i)
+#pragma unroll
+                for (int u = 0; u < 2; ++u) qn[2 * i + u].load(rq, (2 * PK::pair(tid, i) + u) * qk_row + PK::col(tid, i) * ESZ);
+        } else {
+#pragma unroll
+            for (int i = 0; i < TQ::NV; ++i) qn[i].load(rq, TQ::row(tid, i) * qk_row + TQ::col(tid) * ESZ);
+        }
     };
     auto load_k = [&](int ci) {
         const int64_t bos = s0 + (int64_t)CH * ci;
@@ -849,7 +895,7 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
     // staged output rows of a chunk -> o, one 16-byte granule per thread and pass
     char* const so = smem + Lay::o_stage;
     auto flush_o = [&](int64_t bos, int len) {
-        if (!a.o) return;  // outputs not wanted (the segment-map runs)
+        if (!want_o) return;  // outputs not wanted (the segment-offset and segment-map runs)
         for (int idx = tid; idx < CH * OS::NG; idx += NTHR) {
             const int r = idx / OS::NG, gi = idx % OS::NG;
             if (r < len) {
@@ -862,13 +908,22 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
 
     for (int ci = 0; ci < nc; ++ci) {
         const int64_t bos = s0 + (int64_t)CH * ci;
+        if constexpr (PER_K) {
+            // the lane indices look new to the compiler in every chunk: the many per-lane addresses
+            // derived from them are then recomputed where used instead of being hoisted out of the
+            // loop and held in registers (the per-K form has too few to spare)
+            asm volatile("" : "+v"(tid));
+            l = tid & 63;
+            g4 = l >> 4;
+            lr = l & 15;
+        }
 
         // current chunk <- prefetched registers (the next chunk's loads are issued in B/C, D and E)
-        Raw8<IO> qr[TQ::NV], kr[2 * PK::NPASS], vr[2 * PV::NPASS];
+        Raw8<IO> qr[NQ], kr[2 * PK::NPASS], vr[2 * PV::NPASS];
         float gr[RPQ];
         const float br = std::is_same<IO, float>::value ? __uint_as_float(bn) : __uint_as_float(bn << 16);
 #pragma unroll
-        for (int i = 0; i < TQ::NV; ++i) qr[i] = qn[i];
+        for (int i = 0; i < NQ; ++i) qr[i] = qn[i];
 #pragma unroll
         for (int i = 0; i < 2 * PK::NPASS; ++i) kr[i] = kn[i];
 #pragma unroll
@@ -887,13 +942,17 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
         float* sg = FP(PER_K ? Lay::k_g : Lay::g_g);
         float* sb = FP(PER_K ? Lay::k_b : Lay::g_b);
 
-        // ===== A: raw rows into LDS, gate prefix =====
+        // ===== A: raw rows into LDS (scalar gate; the per-K gate scales them from registers in B),
+        //       gate prefix =====
+        bool wide = false;  // per-K gate: some 16-row block spans more decay than its MFMA form accepts
 #pragma unroll
         for (int i = 0; i < TQ::NV; ++i) {
+            if (PER_K || !want_o) break;
             st8_perm<MT, IO>(sQ + TQ::row(tid, i) * LDK, TQ::col(tid), qr[i]);
         }
 #pragma unroll
         for (int i = 0; i < PK::NPASS; ++i) {
+            if (PER_K) break;
             if (PK::valid(tid, i)) {
                 const int c8 = PK::col(tid, i), pr0 = 2 * PK::pair(tid, i);
                 st8_perm<MT, IO>(sK + pr0 * LDK, c8, kr[2 * i]);
@@ -950,8 +1009,21 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
             for (int j = 0; j < qd; ++j) off += part[j * K + c];
 #pragma unroll
             for (int i = 0; i < RPQ; ++i) sg[(qd * RPQ + i) * K + c] = gr[i] + off;
+            // decay across the 16-row blocks this thread's rows close: with reference point
+            // rho = gamma[16I - 1] the right factor of block I's own rows reaches e^(-(block sum))
+            if constexpr (RPQ >= 16) {
+#pragma unroll
+                for (int b = 0; b < RPQ / 16; ++b)
+                    wide = wide || (-(gr[16 * b + 15] - (b ? gr[16 * b - 1] : 0.0f)) > kKdaDiagRange);
+            } else {
+                static_assert(RPQ == 8, "row groups of 8, 16 or 32");
+                if (qd & 1) wide = -(part[(qd - 1) * K + c] + part[qd * K + c]) > kKdaDiagRange;
+            }
         }
-        __syncthreads();
+        // the per-K form learns here whether any block of the chunk needs the element-wise form
+        int wide_any = 0;
+        if constexpr (PER_K) wide_any = __syncthreads_or(wide);
+        else __syncthreads();
 
         // ===== B/C: L = beta (K K^T) decay (strictly lower), P = (Q K^T) decay (lower incl. diag);
         //       waves 0-3 also invert the diagonal block of L they computed =====
@@ -1043,170 +1115,6 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
             S* sLK = SP(Lay::k_lk);
             S* sLQ = SP(Lay::k_lq);
             S* sRG = SP(Lay::k_rg);
-            // Row block I against blocks J <= I on MFMA, reference point rho = gamma[16I - 1]
-            // (0 for I = 0): e^(gamma_r - gamma_j) = e^(gamma_r - rho) e^(rho - gamma_j).  The left
-            // factor is <= 1; the right one is <= 1 for J < I and exceeds 1 only on block I's own
-            // rows, by at most e^(rho - gamma[16I + 15]).  While that range stays below
-            // kKdaDiagRange on every channel (checked here) both operands stay far inside the bf16 /
-            // fp32 range; otherwise the diagonal blocks are evaluated element-wise and only the
-            // blocks J < I use MFMA.
-            bool wide = false;
-            if (tid < K) {
-#pragma unroll
-                for (int I = 0; I < 4; ++I) {
-                    const float rho = I ? sg[(16 * I - 1) * K + tid] : 0.0f;
-                    wide = wide || (rho - sg[(16 * I + 15) * K + tid] > kKdaDiagRange);
-                }
-            }
-            if (!__syncthreads_or(wide)) {
-                // One pass scales the operands for every block pair, in physical column order:
-                //   left  (in place)  K_r, Q_r times e^(gamma_r - rho_I),  rho_I = gamma[16I - 1] (0 for I = 0)
-                //   right (into sRG)  K_j times e^(rho'_J - gamma_j),      rho'_J = gamma[16J + 15]
-                // and the pair (I, J) multiplies the right operand's columns by
-                //   f_IJ = e^(rho_I - rho'_J): 1 for J = I - 1, <= 1 for J < I - 1, and bounded by
-                //   e^kKdaDiagRange for J = I,
-                // so every product is k_r k_j e^(gamma_r - gamma_j) and every operand stays in range.
-                float* fperm = FP(Lay::k_lk);  // [7][K]: pairs (0,0) (1,1) (2,2) (3,3) (2,0) (3,0) (3,1)
-                static_assert(7 * K * sizeof(float) <= 2 * 16 * LDK * sizeof(S), "pair factors fit the left-operand rows");
-                constexpr int GP = 8;  // physical columns per work unit (16 bytes of bf16, 32 of fp32)
-                for (int u = tid; u < CH * (K / GP); u += NTHR) {
-                    const int r = u / (K / GP), p0 = (u % (K / GP)) * GP, I = r >> 4;
-                    float kv[GP], qv[GP];
-                    if constexpr (Lay::BF) {
-                        const uint4 kw = *reinterpret_cast<const uint4*>(sK + r * LDK + p0);
-                        const uint4 qw = *reinterpret_cast<const uint4*>(sQ + r * LDK + p0);
-                        const uint32_t ka[4] = {kw.x, kw.y, kw.z, kw.w}, qa[4] = {qw.x, qw.y, qw.z, qw.w};
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            kv[2 * i] = __uint_as_float(ka[i] << 16);
-                            kv[2 * i + 1] = __uint_as_float(ka[i] & 0xFFFF0000u);
-                            qv[2 * i] = __uint_as_float(qa[i] << 16);
-                            qv[2 * i + 1] = __uint_as_float(qa[i] & 0xFFFF0000u);
-                        }
-                    } else {
-#pragma unroll
-                        for (int i = 0; i < GP; ++i) {
-                            kv[i] = M::back(sK[r * LDK + p0 + i]);
-                            qv[i] = M::back(sQ[r * LDK + p0 + i]);
-                        }
-                    }
-                    // the 8 physical columns are two runs of 4 logical channels: gamma of row r, of
-                    // row 16I - 1 and of row 16I + 15 come in as 16-byte reads
-                    float gv[GP], rv0[GP], rv1[GP];
-#pragma unroll
-                    for (int hh = 0; hh < 2; ++hh) {
-                        const int c0 = iperm<MT>(p0 + 4 * hh);
-                        const f32x4_t a = *reinterpret_cast<const f32x4_t*>(sg + r * K + c0);
-                        const f32x4_t b = I ? *reinterpret_cast<const f32x4_t*>(sg + (16 * I - 1) * K + c0)
-                                            : f32x4_t{0.f, 0.f, 0.f, 0.f};
-                        const f32x4_t d = *reinterpret_cast<const f32x4_t*>(sg + (16 * I + 15) * K + c0);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            gv[4 * hh + e] = a[e];
-                            rv0[4 * hh + e] = b[e];
-                            rv1[4 * hh + e] = d[e];
-                        }
-                    }
-                    float lk[GP], lq[GP], rk[GP];
-#pragma unroll
-                    for (int i = 0; i < GP; ++i) {
-                        const float el = exp_f32(gv[i] - rv0[i]);
-                        const float er = exp_f32(rv1[i] - gv[i]);
-                        lk[i] = kv[i] * el;
-                        lq[i] = qv[i] * el;
-                        rk[i] = kv[i] * er;
-                    }
-                    M::st8(sK + r * LDK + p0, lk);
-                    if (a.o) M::st8(sQ + r * LDK + p0, lq);  // P only feeds the output
-                    M::st8(sRG + r * LDK + p0, rk);
-                }
-                for (int u = tid; u < 7 * K; u += NTHR) {
-                    const int pi = u / K, pcol = u % K, c = iperm<MT>(pcol);
-                    const int I = pi < 4 ? pi : (pi == 4 ? 2 : 3), J = pi < 4 ? pi : (pi == 6 ? 1 : 0);
-                    const float rho = I ? sg[(16 * I - 1) * K + c] : 0.0f;
-                    fperm[pi * K + pcol] = exp_f32(rho - sg[(16 * J + 15) * K + c]);
-                }
-                __syncthreads();
-                // the pairs (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3); each pair's L and P
-                // tiles share the scaled right operand; wave w takes pairs w and w + NW
-                for (int tp = w; tp < 10; tp += NW) {
-                    int I, J;
-                    lower_tile(tp, I, J);
-                    const int fi = J == I ? I : J == I - 1 ? -1 : (I == 2 ? 4 : (J == 0 ? 5 : 6));
-                    f32x4_t cl = {0.f, 0.f, 0.f, 0.f}, cp = {0.f, 0.f, 0.f, 0.f};
-                    if (a.o)
-                        nt2_bscaled<MT, K>(cl, sK + 16 * I * LDK, cp, sQ + 16 * I * LDK, LDK, sRG + 16 * J * LDK, LDK,
-                                           fi >= 0 ? fperm + fi * K : nullptr);
-                    else  // no outputs: P is not needed
-                        nt2_bscaled<MT, K, false>(cl, sK + 16 * I * LDK, cp, sQ + 16 * I * LDK, LDK, sRG + 16 * J * LDK,
-                                                  LDK, fi >= 0 ? fperm + fi * K : nullptr);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int rr = 4 * g4 + e, r = 16 * I + rr, j = 16 * J + lr;
-                        if (J < I) {
-                            sLo[r * LDO + j] = M::cvt(-sb[r] * cl[e]);
-                            if (a.o) sP[r * LDT + perm<MT>(j)] = M::cvt(cp[e]);
-                        } else {  // diagonal blocks: L in fp32, strictly lower, for the inversion; P lower
-                            sLd[I * 16 * LDN + rr * LDN + lr] = (lr < rr) ? sb[r] * cl[e] : 0.0f;
-                            if (a.o) sP[r * LDT + perm<MT>(j)] = M::cvt((lr <= rr) ? cp[e] : 0.0f);
-                        }
-                    }
-                }
-                __syncthreads();
-            } else {
-            // diagonal 16x16 blocks, element-wise: (r, j) in the same block, j <= r
-            for (int p = tid; p < 4 * 256; p += NTHR) {
-                const int b = p >> 8, rr = (p >> 4) & 15, jj = p & 15;
-                const int r = 16 * b + rr, j = 16 * b + jj;
-                float accp = 0.0f, accl = 0.0f;
-                if (jj <= rr) {
-                    for (int c = 0; c < K; ++c) {
-                        const int pc = perm<MT>(c);
-                        const float d = exp_f32(sg[r * K + c] - sg[j * K + c]);
-                        const float kj = M::back(sK[j * LDK + pc]) * d;
-                        accp = fmaf(M::back(sQ[r * LDK + pc]), kj, accp);
-                        accl = fmaf(M::back(sK[r * LDK + pc]), kj, accl);
-                    }
-                }
-                sP[r * LDT + perm<MT>(j)] = M::cvt(accp);  // zero above the diagonal
-                sLd[b * 16 * LDN + rr * LDN + jj] = (jj < rr) ? sb[r] * accl : 0.0f;
-            }
-            // off-diagonal blocks (I > J) through MFMA, reference point rho = gamma[16I - 1]
-            for (int I = 1; I < 4; ++I) {
-                const int rho_row = 16 * I - 1;
-                for (int idx = tid; idx < 16 * K; idx += NTHR) {
-                    const int r = idx / K, c = idx % K, rr = 16 * I + r, pc = perm<MT>(c);
-                    const float f = exp_f32(sg[rr * K + c] - sg[rho_row * K + c]);
-                    sLK[r * LDK + pc] = M::cvt(M::back(sK[rr * LDK + pc]) * f);
-                    sLQ[r * LDK + pc] = M::cvt(M::back(sQ[rr * LDK + pc]) * f);
-                }
-                for (int idx = tid; idx < 16 * I * K; idx += NTHR) {
-                    const int j = idx / K, c = idx % K, pc = perm<MT>(c);
-                    sRG[j * LDK + pc] =
-                        M::cvt(M::back(sK[j * LDK + pc]) * exp_f32(sg[rho_row * K + c] - sg[j * K + c]));
-                }
-                __syncthreads();
-                for (int t = w; t < 2 * I; t += NW) {
-                    const int J = t >> 1;
-                    const bool isL = (t & 1) == 0;
-                    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-                    M::nt(acc, isL ? sLK : sLQ, LDK, sRG + 16 * J * LDK, LDK, K);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = 16 * I + 4 * g4 + e, j = 16 * J + lr;
-                        if (isL) sLo[r * LDO + j] = M::cvt(-sb[r] * acc[e]);
-                        else sP[r * LDT + perm<MT>(j)] = M::cvt(acc[e]);
-                    }
-                }
-                __syncthreads();
-            }
-            }
-            if (w < 4) invert_unit_lower_16<MT>(sLd + w * 16 * LDN, sD + 16 * w * LDD, LDD);
-            // the transposed / scaled operands of D and E, from this chunk's registers
-            S* sKgT = SP(Lay::k_kgt);
-            S* sVT = SP(Lay::k_vt);
-            S* sQt = SP(Lay::k_qt);
-            S* sKdT = SP(Lay::k_kdt);
             // 8 consecutive channels of gamma in two 16-byte reads
             auto g8 = [&](int r, int c8, float* x) {
                 const f32x4_t a = *reinterpret_cast<const f32x4_t*>(sg + r * K + c8);
@@ -1217,29 +1125,220 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
                     x[4 + e] = b[e];
                 }
             };
-            // (K e^gamma)^T and (K e^(gamma_last - gamma))^T, a row pair per thread and pass
+            if (!wide_any) {
+                // Row block I against blocks J <= I on MFMA with reference points: e^(gamma_r - gamma_j) =
+                // e^(gamma_r - rho_I) f_IJ e^(G_J - gamma_j), rho_I = gamma[16I - 1] (0 for I = 0),
+                // G_J = gamma[16J + 15], f_IJ = e^(rho_I - G_J): 1 for J = I - 1, <= 1 for J < I - 1, and
+                // below e^kKdaDiagRange for J = I (the test of phase A).  The two outer factors are <= 1
+                // and scale the operands: each thread scales its own row pair of k (and q) from the
+                // registers, so the two operands of a unit share one set of exponentials.
+                static_assert(7 * K * sizeof(float) <= 2 * 16 * LDK * sizeof(S), "pair factors fit the left-operand rows");
+                if (tid < K) {  // f_IJ of the pairs (0,0) (1,1) (2,2) (3,3) (2,0) (3,0) (3,1), physical column order
+                    const int c = tid, pc = perm<MT>(c);
+                    const float G0 = sg[15 * K + c], G1 = sg[31 * K + c], G2 = sg[47 * K + c], G3 = sg[63 * K + c];
+                    float* fp = FP(Lay::k_fp);
+                    fp[0 * K + pc] = exp_f32(-G0);
+                    fp[1 * K + pc] = exp_f32(G0 - G1);
+                    fp[2 * K + pc] = exp_f32(G1 - G2);
+                    fp[3 * K + pc] = exp_f32(G2 - G3);
+                    fp[4 * K + pc] = exp_f32(G1 - G0);
+                    fp[5 * K + pc] = exp_f32(G2 - G0);
+                    fp[6 * K + pc] = exp_f32(G2 - G1);
+                }
+#pragma unroll
+                for (int i = 0; i < PK::NPASS; ++i) {
+                    if (!PK::valid(tid, i)) continue;
+                    const int c8 = PK::col(tid, i), r0 = 2 * PK::pair(tid, i), I = r0 >> 4;
+                    // two halves of four channels keep the temporaries few
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const int c4 = c8 + 4 * hh;
+                        const f32x4_t ga = *reinterpret_cast<const f32x4_t*>(sg + r0 * K + c4);
+                        const f32x4_t gb = *reinterpret_cast<const f32x4_t*>(sg + (r0 + 1) * K + c4);
+                        const f32x4_t g0 = I ? *reinterpret_cast<const f32x4_t*>(sg + (16 * I - 1) * K + c4)
+                                             : f32x4_t{0.f, 0.f, 0.f, 0.f};
+                        const f32x4_t g1 = *reinterpret_cast<const f32x4_t*>(sg + (16 * I + 15) * K + c4);
+                        float ka[4], kb[4], la[4], lb[4], y[4];
+                        kr[2 * i].get4(ka, hh);
+                        kr[2 * i + 1].get4(kb, hh);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            la[e] = exp_f32(ga[e] - g0[e]);
+                            lb[e] = exp_f32(gb[e] - g0[e]);
+                        }
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) y[e] = ka[e] * la[e];
+                        st4f_perm<MT>(sK + r0 * LDK, c4, y);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) y[e] = kb[e] * lb[e];
+                        st4f_perm<MT>(sK + (r0 + 1) * LDK, c4, y);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) y[e] = ka[e] * exp_f32(g1[e] - ga[e]);
+                        st4f_perm<MT>(sRG + r0 * LDK, c4, y);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) y[e] = kb[e] * exp_f32(g1[e] - gb[e]);
+                        st4f_perm<MT>(sRG + (r0 + 1) * LDK, c4, y);
+                        if (want_o) {  // P only feeds the output
+                            qr[2 * i].get4(y, hh);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) y[e] *= la[e];
+                            st4f_perm<MT>(sQ + r0 * LDK, c4, y);
+                            qr[2 * i + 1].get4(y, hh);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) y[e] *= lb[e];
+                            st4f_perm<MT>(sQ + (r0 + 1) * LDK, c4, y);
+                        }
+                    }
+                }
+                __syncthreads();
+                // the pairs (I, J): L and P tiles share the scaled right operand.  Waves 0-3 take the
+                // diagonal pair (w, w) and invert their diagonal block of L right away; the six
+                // off-diagonal pairs go to waves 4.. (or, with four waves, to the same waves afterwards).
+                const float* fperm = FP(Lay::k_fp);
+                auto do_pair = [&](int I, int J) {
+                    const int fi = J == I ? I : J == I - 1 ? -1 : (I == 2 ? 4 : (J == 0 ? 5 : 6));
+                    f32x4_t cl = {0.f, 0.f, 0.f, 0.f}, cp = {0.f, 0.f, 0.f, 0.f};
+                    if (want_o)
+                        nt2_bscaled<MT, K>(cl, sK + 16 * I * LDK, cp, sQ + 16 * I * LDK, LDK, sRG + 16 * J * LDK, LDK,
+                                           fi >= 0 ? fperm + fi * K : nullptr);
+                    else  // no outputs: P is not needed
+                        nt2_bscaled<MT, K, false>(cl, sK + 16 * I * LDK, cp, sQ + 16 * I * LDK, LDK, sRG + 16 * J * LDK,
+                                                  LDK, fi >= 0 ? fperm + fi * K : nullptr);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int rr = 4 * g4 + e, r = 16 * I + rr, j = 16 * J + lr;
+                        if (J < I) {
+                            sLo[r * LDO + j] = M::cvt(-sb[r] * cl[e]);
+                            if (want_o) sP[r * LDT + perm<MT>(j)] = M::cvt(cp[e]);
+                        } else {  // diagonal blocks: L in fp32, strictly lower, for the inversion; P lower
+                            sLd[I * 16 * LDN + rr * LDN + lr] = (lr < rr) ? sb[r] * cl[e] : 0.0f;
+                            if (want_o) sP[r * LDT + perm<MT>(j)] = M::cvt((lr <= rr) ? cp[e] : 0.0f);
+                        }
+                    }
+                };
+                if (w < 4) {
+                    do_pair(w, w);
+                    // the block's LDS writes complete before this wave's lanes read other lanes' entries
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                    invert_unit_lower_16<MT>(sLd + w * 16 * LDN, sD + 16 * w * LDD, LDD);
+                }
+                constexpr int OW = NW > 4 ? NW - 4 : NW;  // waves that take off-diagonal pairs
+                for (int q = NW > 4 ? w - 4 : w; q < 6; q += OW) {
+                    if (q < 0) break;
+                    int I, J;
+                    strict_tile(q, I, J);
+                    do_pair(I, J);
+                }
+                __syncthreads();
+            } else {
+                // raw rows for the element-wise form
+#pragma unroll
+                for (int i = 0; i < PK::NPASS; ++i) {
+                    if (!PK::valid(tid, i)) continue;
+                    const int c8 = PK::col(tid, i), pr0 = 2 * PK::pair(tid, i);
+                    st8_perm<MT, IO>(sK + pr0 * LDK, c8, kr[2 * i]);
+                    st8_perm<MT, IO>(sK + (pr0 + 1) * LDK, c8, kr[2 * i + 1]);
+                    if (want_o) {
+                        st8_perm<MT, IO>(sQ + pr0 * LDK, c8, qr[2 * i]);
+                        st8_perm<MT, IO>(sQ + (pr0 + 1) * LDK, c8, qr[2 * i + 1]);
+                    }
+                }
+                __syncthreads();
+                // diagonal 16x16 blocks, element-wise: (r, j) in the same block, j <= r
+                for (int p = tid; p < 4 * 256; p += NTHR) {
+                    const int b = p >> 8, rr = (p >> 4) & 15, jj = p & 15;
+                    const int r = 16 * b + rr, j = 16 * b + jj;
+                    float accp = 0.0f, accl = 0.0f;
+                    if (jj <= rr) {
+                        for (int c = 0; c < K; ++c) {
+                            const int pc = perm<MT>(c);
+                            const float d = exp_f32(sg[r * K + c] - sg[j * K + c]);
+                            const float kj = M::back(sK[j * LDK + pc]) * d;
+                            if (want_o) accp = fmaf(M::back(sQ[r * LDK + pc]), kj, accp);
+                            accl = fmaf(M::back(sK[r * LDK + pc]), kj, accl);
+                        }
+                    }
+                    sP[r * LDT + perm<MT>(j)] = M::cvt(accp);  // zero above the diagonal
+                    sLd[b * 16 * LDN + rr * LDN + jj] = (jj < rr) ? sb[r] * accl : 0.0f;
+                }
+                // off-diagonal blocks (I > J) through MFMA, reference point rho = gamma[16I - 1]
+                for (int I = 1; I < 4; ++I) {
+                    const int rho_row = 16 * I - 1;
+                    for (int idx = tid; idx < 16 * K; idx += NTHR) {
+                        const int r = idx / K, c = idx % K, rr = 16 * I + r, pc = perm<MT>(c);
+                        const float f = exp_f32(sg[rr * K + c] - sg[rho_row * K + c]);
+                        sLK[r * LDK + pc] = M::cvt(M::back(sK[rr * LDK + pc]) * f);
+                        if (want_o) sLQ[r * LDK + pc] = M::cvt(M::back(sQ[rr * LDK + pc]) * f);
+                    }
+                    for (int idx = tid; idx < 16 * I * K; idx += NTHR) {
+                        const int j = idx / K, c = idx % K, pc = perm<MT>(c);
+                        sRG[j * LDK + pc] =
+                            M::cvt(M::back(sK[j * LDK + pc]) * exp_f32(sg[rho_row * K + c] - sg[j * K + c]));
+                    }
+                    __syncthreads();
+                    for (int t = w; t < 2 * I; t += NW) {
+                        const int J = t >> 1;
+                        const bool isL = (t & 1) == 0;
+                        if (!want_o && !isL) continue;
+                        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+                        M::nt(acc, isL ? sLK : sLQ, LDK, sRG + 16 * J * LDK, LDK, K);
+    #pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int r = 16 * I + 4 * g4 + e, j = 16 * J + lr;
+                            if (isL) sLo[r * LDO + j] = M::cvt(-sb[r] * acc[e]);
+                            else sP[r * LDT + perm<MT>(j)] = M::cvt(acc[e]);
+                        }
+                    }
+                    __syncthreads();
+                }
+                if (w < 4) invert_unit_lower_16<MT>(sLd + w * 16 * LDN, sD + 16 * w * LDD, LDD);
+            }
+            // the transposed / scaled operands of D and E, from this chunk's registers (the scaled rows
+            // of B are dead): (K e^gamma)^T, (K e^(gamma_last - gamma))^T and Q e^gamma from one row pair
+            // and 8 channels per unit, V^T
+            S* sKgT = SP(Lay::k_kgt);
+            S* sVT = SP(Lay::k_vt);
+            S* sQt = SP(Lay::k_qt);
+            S* sKdT = SP(Lay::k_kdt);
 #pragma unroll
             for (int i = 0; i < PK::NPASS; ++i) {
                 if (PK::valid(tid, i)) {
                     const int c8 = PK::col(tid, i), pr0 = 2 * PK::pair(tid, i);
-                    float ka[8], kb[8], ga[8], gb[8], gl[8];
-                    kr[2 * i].get(ka);
-                    kr[2 * i + 1].get(kb);
-                    g8(pr0, c8, ga);
-                    g8(pr0 + 1, c8, gb);
-                    g8(CH - 1, c8, gl);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float ya = ka[e] * exp_f32(ga[e]), yb = kb[e] * exp_f32(gb[e]);
-                        const float da = ka[e] * exp_f32(gl[e] - ga[e]), db = kb[e] * exp_f32(gl[e] - gb[e]);
-                        if constexpr (Lay::BF) {
-                            *reinterpret_cast<uint32_t*>(sKgT + (c8 + e) * LDT + perm<MT>(pr0)) = pack_bf16x2(ya, yb);
-                            *reinterpret_cast<uint32_t*>(sKdT + (c8 + e) * LDT + perm<MT>(pr0)) = pack_bf16x2(da, db);
-                        } else {
-                            sKgT[(c8 + e) * LDT + pr0] = ya;
-                            sKgT[(c8 + e) * LDT + pr0 + 1] = yb;
-                            sKdT[(c8 + e) * LDT + pr0] = da;
-                            sKdT[(c8 + e) * LDT + pr0 + 1] = db;
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const int c4 = c8 + 4 * hh;
+                        const f32x4_t ga = *reinterpret_cast<const f32x4_t*>(sg + pr0 * K + c4);
+                        const f32x4_t gb = *reinterpret_cast<const f32x4_t*>(sg + (pr0 + 1) * K + c4);
+                        const f32x4_t gl = *reinterpret_cast<const f32x4_t*>(sg + (CH - 1) * K + c4);
+                        float ka[4], kb[4], ea[4], eb[4];
+                        kr[2 * i].get4(ka, hh);
+                        kr[2 * i + 1].get4(kb, hh);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            ea[e] = exp_f32(ga[e]);
+                            eb[e] = exp_f32(gb[e]);
+                            const float ya = ka[e] * ea[e], yb = kb[e] * eb[e];
+                            const float da = ka[e] * exp_f32(gl[e] - ga[e]), db = kb[e] * exp_f32(gl[e] - gb[e]);
+                            if constexpr (Lay::BF) {
+                                *reinterpret_cast<uint32_t*>(sKgT + (c4 + e) * LDT + perm<MT>(pr0)) = pack_bf16x2(ya, yb);
+                                *reinterpret_cast<uint32_t*>(sKdT + (c4 + e) * LDT + perm<MT>(pr0)) = pack_bf16x2(da, db);
+                            } else {
+                                sKgT[(c4 + e) * LDT + pr0] = ya;
+                                sKgT[(c4 + e) * LDT + pr0 + 1] = yb;
+                                sKdT[(c4 + e) * LDT + pr0] = da;
+                                sKdT[(c4 + e) * LDT + pr0 + 1] = db;
+                            }
+                        }
+                        if (want_o) {  // Q e^gamma only feeds the output
+                            float y[4];
+                            qr[2 * i].get4(y, hh);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) y[e] *= ea[e];
+                            st4f_perm<MT>(sQt + pr0 * LDK, c4, y);
+                            qr[2 * i + 1].get4(y, hh);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) y[e] *= eb[e];
+                            st4f_perm<MT>(sQt + (pr0 + 1) * LDK, c4, y);
                         }
                     }
                 }
@@ -1248,23 +1347,6 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
             for (int i = 0; i < PV::NPASS; ++i) {
                 if (PV::valid(tid, i))
                     st_pair_t<MT, IO>(sVT, LDT, PV::col(tid, i), 2 * PV::pair(tid, i), vr[2 * i], vr[2 * i + 1]);
-            }
-            // Q e^gamma only feeds the output: skipped when no outputs are wanted (segment-map runs)
-#pragma unroll
-            for (int i = 0; i < TQ::NV; ++i) {
-                if (!a.o) break;
-                const int r = TQ::row(tid, i), c8 = TQ::col(tid);
-                float y[8], gq[8];
-                qr[i].get(y);
-                g8(r, c8, gq);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) y[e] *= exp_f32(gq[e]);
-                if constexpr (Lay::BF) {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) sQt[r * LDK + perm<MT>(c8 + e)] = M::cvt(y[e]);
-                } else {
-                    M::st8(sQt + r * LDK + c8, y);
-                }
             }
             for (int c = tid; c < K; c += NTHR) FP(Lay::k_gl)[c] = exp_f32(sg[(CH - 1) * K + c]);
         }
@@ -1332,7 +1414,7 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
         gemm_regs<MT, K, 4>(nu, sW, LDK, hs);
         if (ci + 1 < nc) load_vgb(ci + 1);
         // O = scale (diag(e^gamma) Q S^T + P v_new), when outputs are wanted
-        if (a.o) {
+        if (want_o) {
         f32x4_t oa[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) oa[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -1419,467 +1501,6 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
     if (a.ht) {
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) *reinterpret_cast<f32x4_t*>(a.ht + sidx + 16 * kt + 4 * g4) = hs[kt];
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Pipelined form for the common case (scalar gate, bf16 operands, K = V = 128).
-//
-// B, C and D of a chunk depend only on that chunk's inputs, and E is the only step that needs
-// the state.  Each iteration therefore overlaps E of chunk c with the L products and inverses of
-// chunk c + 1:
-//
-//   phase 1  waves 4-7:   A(c+1)  raw q, k, v rows of chunk c + 1 into LDS (loaded one chunk ahead)
-//            wave 0:              gate prefix and factor tables of chunk c + 1
-//   phase 2  waves 0-3:   E(c)    v_new, output, state update; wave w owns the 32 state columns
-//                                 32w .. 32w+31 (two 16-column groups)
-//            waves 4-7:   B/C(c+1) L and the diagonal inverses of chunk c + 1
-//   phase 3  waves 0-3:   D(c+1)  U for the wave's own columns (kept in registers until E(c+1)),
-//                                 then the ten P tiles of chunk c + 1
-//            waves 4-7:   D(c+1)  the eight W tiles, two per wave, into LDS
-//
-// The two roles run loops of their own, with one workgroup barrier after each phase.  Q, K, P and
-// the gate tables are double-buffered (chunk c is read by E while chunk c + 1 is written).  With
-// four state waves instead of eight, every wave of E reads the shared operands W, Q, K and P for
-// 32 columns at once, which halves E's LDS operand traffic.  The output is formed transposed
-// (O^T = S Q^T + v_new^T P^T, the state and v_new tiles as the A operand) so that each lane holds
-// four consecutive value columns of one token and writes them to o with one 8-byte store: no
-// staging area.
-struct PipeLayout {
-    static constexpr int K = 128, V = 128;
-    static constexpr int LDK = K + 16, LDT = CH + 16, LDO = CH + 16, LDD = 16 + 16, LDV = V + 16;
-    static constexpr size_t ROWK = 2 * CH * LDK;          // [64][LDK] bf16
-    static constexpr size_t ROWT = 2 * CH * LDT;          // [64][LDT] bf16
-    static constexpr int TABF = 10 * CH;                  // floats per gate-table set
-    // gate tables (floats, offsets inside one set)
-    static constexpr int t_g = 0, t_b = CH, t_be = 2 * CH, t_eg = 3 * CH, t_ed = 4 * CH, t_fa = 5 * CH,
-                         t_fb = 8 * CH;
-    static constexpr size_t q0 = 0;                        // Q rows, two buffers
-    static constexpr size_t k0 = q0 + 2 * ROWK;            // K rows, two buffers
-    static constexpr size_t vr = k0 + 2 * ROWK;            // V rows
-    static constexpr size_t w = vr + 2 * CH * LDV;         // -W rows
-    static constexpr size_t lo = w + ROWK;                 // -L off-diagonal blocks
-    static constexpr size_t ld = lo + 2 * CH * LDO;        // diagonal L blocks, fp32
-    static constexpr size_t dd = ld + sizeof(float) * 4 * 16 * LDN;  // diagonal-block inverses
-    static constexpr size_t p0 = dd + 2 * CH * LDD;        // P rows, two buffers
-    static constexpr size_t tab = p0 + 2 * ROWT;           // gate tables, two sets
-    static constexpr size_t total = tab + 2 * sizeof(float) * TABF;
-};
-
-template <typename IO>
-__global__ __launch_bounds__(512) void chunk_pipe_kernel(const ChunkArgs a) {
-    typedef PipeLayout L;
-    typedef MM<bf16_t> M;
-    typedef uint16_t S;
-    constexpr int K = L::K, KT = K / 16;
-    constexpr int LDK = L::LDK, LDT = L::LDT, LDO = L::LDO, LDD = L::LDD, LDV = L::LDV;
-    static_assert(L::total <= 160 * 1024, "LDS budget");
-    static_assert(std::is_same<IO, bf16_t>::value, "bf16 I/O");
-    __shared__ __align__(16) char smem[L::total];
-    auto SP = [&](size_t off) { return reinterpret_cast<S*>(smem + off); };
-    auto FP = [&](size_t off) { return reinterpret_cast<float*>(smem + off); };
-
-    const int h = blockIdx.y, n = blockIdx.z;
-    const int tid = threadIdx.x, l = tid & 63, g4 = l >> 4, lr = l & 15;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int64_t s0 = a.cu_seqlens ? a.cu_seqlens[n] : 0;
-    const int64_t s1 = a.cu_seqlens ? a.cu_seqlens[n + 1] : a.T;
-    const int nc = (int)((s1 - s0 + CH - 1) / CH);
-    auto chunk_len = [&](int ci) {
-        const int64_t bos = s0 + (int64_t)CH * ci;
-        return (s1 - bos) < CH ? (int)(s1 - bos) : CH;
-    };
-    S* const sV = SP(L::vr);
-    S* const sW = SP(L::w);
-    S* const sLo = SP(L::lo);
-    float* const sLd = FP(L::ld);
-    S* const sD = SP(L::dd);
-
-    // The two roles run loops of their own (so that neither holds the other's registers); both take
-    // the same three workgroup barriers per iteration, nc + 1 iterations.
-    if (w < 4) {
-        // ---- state waves 0-3: phase 1 the tables of chunk it (wave 0), phase 2 E(it - 1),
-        //      phase 3 U and P of chunk it ----
-        // hs[j][kt][e] = S[32w + 16j + lane%16][16kt + 4(l/16) + e]
-        f32x4_t hs[2][KT];
-        const int64_t sbase = ((int64_t)n * a.HV + h) * a.V * K;
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int kt = 0; kt < KT; ++kt)
-                hs[j][kt] = a.h0 ? *reinterpret_cast<const f32x4_t*>(a.h0 + sbase + (int64_t)(32 * w + 16 * j + lr) * K +
-                                                                    16 * kt + 4 * g4)
-                                 : f32x4_t{0.f, 0.f, 0.f, 0.f};
-        f32x4_t nu[2][4];  // U of the chunk solved in the last phase 3, then v_new
-        // wave 0 reads the gate and beta of a chunk (one value per row) one chunk ahead and forms the
-        // chunk's factor tables in phase 1
-        float gn = 0.0f;
-        uint32_t bn = 0;
-        auto load_gb = [&](int ci) {
-            if (w != 0) return;
-            const int64_t bos = s0 + (int64_t)CH * ci;
-            const int len = chunk_len(ci);
-            const __amdgpu_buffer_rsrc_t rg = chunk_rsrc(a.g + bos * a.HV + h, len, a.HV * 4);
-            gn = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, l * a.HV * 4, 0, 0));
-            const __amdgpu_buffer_rsrc_t rb =
-                chunk_rsrc(static_cast<const char*>(a.beta) + (bos * a.HV + h) * 2, len, a.HV * 2);
-            bn = __builtin_amdgcn_raw_buffer_load_b16(rb, l * a.HV * 2, 0, 0);
-        };
-        if (nc > 0) load_gb(0);
-        for (int it = 0; it <= nc; ++it) {
-            const int b1 = it & 1, b0 = b1 ^ 1;  // buffers of chunk it and of chunk it - 1
-            float* const tb1 = FP(L::tab) + b1 * L::TABF;
-            if (w == 0 && it < nc) {  // inclusive prefix of the 64 gates (rows past the end are 0), factor tables
-                const float br = __uint_as_float(bn << 16);
-                const float x = wave_inclusive_sum(gn);
-                const float xl = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), CH - 1));
-                const float ex = exp_f32(x);
-                tb1[L::t_g + l] = x;
-                tb1[L::t_b + l] = br;
-                tb1[L::t_be + l] = br * ex;
-                tb1[L::t_eg + l] = ex;
-                tb1[L::t_ed + l] = exp_f32(xl - x);
-                float rho[4];
-#pragma unroll
-                for (int J = 0; J < 4; ++J) rho[J] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16 * J + 15));
-#pragma unroll
-                for (int J = 0; J < 3; ++J) tb1[L::t_fa + J * CH + l] = exp_f32(fminf(x - rho[J], 0.0f));
-                const int jb = l >> 4;
-                const float rj = jb == 0 ? rho[0] : jb == 1 ? rho[1] : jb == 2 ? rho[2] : rho[3];
-                tb1[L::t_fb + l] = exp_f32(rj - x);
-            }
-            __syncthreads();  // end of phase 1
-            if (it >= 1) {
-                const int ce = it - 1;
-                const int64_t bos = s0 + (int64_t)CH * ce;
-                const int len = chunk_len(ce);
-                const S* sQ0 = SP(L::q0 + b0 * L::ROWK);
-                const S* sK0 = SP(L::k0 + b0 * L::ROWK);
-                const S* sP0 = SP(L::p0 + b0 * L::ROWT);
-                const float* tb0 = FP(L::tab) + b0 * L::TABF;
-                // v_new_j = U_j - W S_j^T  (LDS holds -W); the A reads of two k-steps are issued together
-#pragma unroll
-                for (int m0 = 0; m0 < K / 32; m0 += 2) {
-                    bf16x8_t av[2][4];
-#pragma unroll
-                    for (int m = 0; m < 2; ++m)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            av[m][i] = *reinterpret_cast<const bf16x8_t*>(sW + (16 * i + lr) * LDK + 32 * (m0 + m) + 8 * g4);
-                    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                    for (int m = 0; m < 2; ++m)
-#pragma unroll
-                        for (int j = 0; j < 2; ++j) {
-                            const int t = 2 * (m0 + m);
-                            const bf16x8_t bv = __builtin_bit_cast(
-                                bf16x8_t, uint4{pack_tile_lo(hs[j][t]), pack_tile_hi(hs[j][t]), pack_tile_lo(hs[j][t + 1]),
-                                                pack_tile_hi(hs[j][t + 1])});
-#pragma unroll
-                            for (int i = 0; i < 4; ++i)
-                                nu[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[m][i], bv, nu[j][i], 0, 0, 0);
-                        }
-                }
-                if (a.o) {
-                    // O^T_j[v][r] = e^{gamma_r} sum_k S[v][k] q_r[k] + sum_t v_new[t][v] P[r][t]; lane (g, i) holds
-                    // value columns 32w + 16j + 4g .. +3 of token 16i + lane%16
-                    f32x4_t ot[2][4];
-#pragma unroll
-                    for (int j = 0; j < 2; ++j)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) ot[j][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int m0 = 0; m0 < K / 32; m0 += 2) {
-                        bf16x8_t bq[2][4];
-#pragma unroll
-                        for (int m = 0; m < 2; ++m)
-#pragma unroll
-                            for (int i = 0; i < 4; ++i)
-                                bq[m][i] = *reinterpret_cast<const bf16x8_t*>(sQ0 + (16 * i + lr) * LDK + 32 * (m0 + m) + 8 * g4);
-                        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                        for (int m = 0; m < 2; ++m)
-#pragma unroll
-                            for (int j = 0; j < 2; ++j) {
-                                const int t = 2 * (m0 + m);
-                                const bf16x8_t sa = __builtin_bit_cast(
-                                    bf16x8_t, uint4{pack_tile_lo(hs[j][t]), pack_tile_hi(hs[j][t]),
-                                                    pack_tile_lo(hs[j][t + 1]), pack_tile_hi(hs[j][t + 1])});
-#pragma unroll
-                                for (int i = 0; i < 4; ++i)
-                                    ot[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sa, bq[m][i], ot[j][i], 0, 0, 0);
-                            }
-                    }
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float f = tb0[L::t_eg + 16 * i + lr];
-#pragma unroll
-                        for (int j = 0; j < 2; ++j) ot[j][i] *= f;
-                    }
-                    {
-                        // P is lower triangular: token tile i needs the steps m with 32m <= 16i + 15
-                        bf16x8_t bp[2][4];
-#pragma unroll
-                        for (int m = 0; m < 2; ++m)
-#pragma unroll
-                            for (int i = 0; i < 4; ++i)
-                                if (32 * m <= 16 * i + 15)
-                                    bp[m][i] = *reinterpret_cast<const bf16x8_t*>(sP0 + (16 * i + lr) * LDT + 32 * m + 8 * g4);
-                        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                        for (int m = 0; m < 2; ++m)
-#pragma unroll
-                            for (int j = 0; j < 2; ++j) {
-                                const bf16x8_t na = __builtin_bit_cast(
-                                    bf16x8_t, uint4{pack_tile_lo(nu[j][2 * m]), pack_tile_hi(nu[j][2 * m]),
-                                                    pack_tile_lo(nu[j][2 * m + 1]), pack_tile_hi(nu[j][2 * m + 1])});
-#pragma unroll
-                                for (int i = 0; i < 4; ++i)
-                                    if (32 * m <= 16 * i + 15)
-                                        ot[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(na, bp[m][i], ot[j][i], 0, 0, 0);
-                            }
-                    }
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int r = 16 * i + lr;
-                        if (r < len) {
-                            uint16_t* dst = static_cast<uint16_t*>(a.o) + ((bos + r) * a.HV + h) * a.V + 32 * w + 4 * g4;
-#pragma unroll
-                            for (int j = 0; j < 2; ++j) {
-                                const f32x4_t x = ot[j][i] * a.scale;
-                                *reinterpret_cast<uint2*>(dst + 16 * j) = uint2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
-                            }
-                        }
-                    }
-                }
-                // S <- e^{gamma_last} S + sum_r v_new_r (k_r e^{gamma_last - gamma_r})^T, the K^T operand read
-                // from the row-major K rows with transposing reads
-                const float dec = tb0[L::t_eg + CH - 1];
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-#pragma unroll
-                    for (int kt = 0; kt < KT; ++kt) hs[j][kt] *= dec;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const f32x4_t f = *reinterpret_cast<const f32x4_t*>(tb0 + L::t_ed + 16 * i + 4 * g4);
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) nu[j][i] *= f;
-                }
-#pragma unroll
-                for (int m = 0; m < CH / 32; ++m) {
-                    bf16x8_t bw[2];
-#pragma unroll
-                    for (int j = 0; j < 2; ++j)
-                        bw[j] = __builtin_bit_cast(bf16x8_t, uint4{pack_tile_lo(nu[j][2 * m]), pack_tile_hi(nu[j][2 * m]),
-                                                                   pack_tile_lo(nu[j][2 * m + 1]),
-                                                                   pack_tile_hi(nu[j][2 * m + 1])});
-#pragma unroll
-                    for (int kt = 0; kt < KT; ++kt) {
-                        const uint2 lo = ld_tr4<true>(sK0, LDK, 32 * m + 4 * g4, 16 * kt);
-                        const uint2 hi = ld_tr4<true>(sK0, LDK, 32 * m + 16 + 4 * g4, 16 * kt);
-                        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, uint4{lo.x, lo.y, hi.x, hi.y});
-#pragma unroll
-                        for (int j = 0; j < 2; ++j) hs[j][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bw[j], hs[j][kt], 0, 0, 0);
-                    }
-                }
-            }
-            __syncthreads();  // end of phase 2
-            if (it + 1 < nc) load_gb(it + 1);
-            if (it < nc) {
-                // U for the wave's own 32 value columns
-                f32x4_t X[2][4];
-                const RhsFromRows rhs[2] = {{sV, LDV, 32 * w, tb1 + L::t_b}, {sV, LDV, 32 * w + 16, tb1 + L::t_b}};
-                block_solve<bf16_t, 2, RhsFromRows, false>(X, sLo, LDO, sD, LDD, rhs);
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) nu[j][i] = X[j][i];
-                // P of chunk it (read by E in the next iteration): the diagonal tile (w, w) with element-wise
-                // decay, masked above the diagonal, and the off-diagonal tiles q = w (and w + 4 for w < 2) of
-                // (1,0),(2,0),(2,1),(3,0),(3,1),(3,2) with the factor tables
-                const S* sQ1 = SP(L::q0 + b1 * L::ROWK);
-                const S* sK1 = SP(L::k0 + b1 * L::ROWK);
-                S* const sP1 = SP(L::p0 + b1 * L::ROWT);
-                auto store_off = [&](int q, const f32x4_t& cp) {
-                    int I, J;
-                    strict_tile(q, I, J);
-                    const f32x4_t fa = *reinterpret_cast<const f32x4_t*>(tb1 + L::t_fa + J * CH + 16 * I + 4 * g4);
-                    const float fb = tb1[L::t_fb + 16 * J + lr];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        sP1[(16 * I + 4 * g4 + e) * LDT + perm<bf16_t>(16 * J + lr)] = M::cvt((fa[e] * fb) * cp[e]);
-                };
-                int I0, J0;
-                strict_tile(w, I0, J0);
-                f32x4_t cd = {0.f, 0.f, 0.f, 0.f}, c0 = {0.f, 0.f, 0.f, 0.f};
-                M::template nt2<K>(cd, sQ1 + 16 * w * LDK, sK1 + 16 * w * LDK, c0, sQ1 + 16 * I0 * LDK, sK1 + 16 * J0 * LDK,
-                                   LDK);
-                {
-                    const f32x4_t gr = *reinterpret_cast<const f32x4_t*>(tb1 + L::t_g + 16 * w + 4 * g4);
-                    const float gj = tb1[L::t_g + 16 * w + lr];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = 16 * w + 4 * g4 + e, jj = 16 * w + lr;
-                        const float x = exp_f32(gr[e] - gj) * cd[e];  // inf above the diagonal is discarded
-                        sP1[r * LDT + perm<bf16_t>(jj)] = M::cvt((r >= jj) ? x : 0.0f);
-                    }
-                }
-                store_off(w, c0);
-                if (w < 2) {
-                    int I1, J1;
-                    strict_tile(w + 4, I1, J1);
-                    f32x4_t c1 = {0.f, 0.f, 0.f, 0.f};
-                    M::nt(c1, sQ1 + 16 * I1 * LDK, LDK, sK1 + 16 * J1 * LDK, LDK, K);
-                    store_off(w + 4, c1);
-                }
-            }
-            __syncthreads();  // end of phase 3
-        }
-        if (a.ht) {
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int kt = 0; kt < KT; ++kt)
-                    *reinterpret_cast<f32x4_t*>(a.ht + sbase + (int64_t)(32 * w + 16 * j + lr) * K + 16 * kt + 4 * g4) =
-                        hs[j][kt];
-        }
-    } else {
-        // ---- waves 4-7: loads, phase 1 A(it), phase 2 L and the inverses of chunk it, phase 3 W of chunk it ----
-        constexpr int NLD = 256;
-        const int lt = tid - 256;  // thread index among waves 4-7
-        const int u = w - 4;
-        const int hk = h / (a.HV / a.HK);
-        // strictly upper tiles of both P buffers are never written: zero them once
-        for (int idx = lt; idx < 2 * CH * CH; idx += NLD) {
-            const int b = idx / (CH * CH), r = (idx / CH) % CH, j = idx % CH;
-            if ((j >> 4) > (r >> 4)) SP(L::p0 + b * L::ROWT)[r * LDT + perm<bf16_t>(j)] = M::cvt(0.0f);
-        }
-        typedef Tile<CH, K, NLD> TQ;
-        typedef PairTile<K, NLD> PK;
-        typedef PairTile<128, NLD> PV;
-        Raw8<IO> qn[TQ::NV], kn[2 * PK::NPASS], vn[2 * PV::NPASS];
-        constexpr int ESZ = 2;
-        const int qk_row = a.HK * K * ESZ, v_row = a.HV * a.V * ESZ;
-        auto load_qk = [&](int ci) {
-            const int64_t bos = s0 + (int64_t)CH * ci;
-            const int len = chunk_len(ci);
-            const __amdgpu_buffer_rsrc_t rq =
-                chunk_rsrc(static_cast<const char*>(a.q) + ((bos * a.HK + hk) * K) * ESZ, len, qk_row);
-#pragma unroll
-            for (int i = 0; i < TQ::NV; ++i) qn[i].load(rq, TQ::row(lt, i) * qk_row + TQ::col(lt) * ESZ);
-            const __amdgpu_buffer_rsrc_t rk =
-                chunk_rsrc(static_cast<const char*>(a.k) + ((bos * a.HK + hk) * K) * ESZ, len, qk_row);
-#pragma unroll
-            for (int i = 0; i < PK::NPASS; ++i)
-#pragma unroll
-                for (int q = 0; q < 2; ++q)
-                    kn[2 * i + q].load(rk, (2 * PK::pair(lt, i) + q) * qk_row + PK::col(lt, i) * ESZ);
-        };
-        auto load_vgb = [&](int ci) {
-            const int64_t bos = s0 + (int64_t)CH * ci;
-            const int len = chunk_len(ci);
-            // v == NULL reads as zeros (a zero-byte range): the run that forms a segment's linear map
-            const __amdgpu_buffer_rsrc_t rv = chunk_rsrc(
-                a.v ? static_cast<const char*>(a.v) + ((bos * a.HV + h) * a.V) * ESZ : nullptr, a.v ? len : 0, v_row);
-#pragma unroll
-            for (int i = 0; i < PV::NPASS; ++i)
-#pragma unroll
-                for (int q = 0; q < 2; ++q)
-                    vn[2 * i + q].load(rv, (2 * PV::pair(lt, i) + q) * v_row + PV::col(lt, i) * ESZ);
-        };
-        if (nc > 0) {
-            load_qk(0);
-            load_vgb(0);
-        }
-        for (int it = 0; it <= nc; ++it) {
-            const int b1 = it & 1;
-            S* const sQ1 = SP(L::q0 + b1 * L::ROWK);
-            S* const sK1 = SP(L::k0 + b1 * L::ROWK);
-            float* const tb1 = FP(L::tab) + b1 * L::TABF;
-            // ===== phase 1: A(it) =====
-            if (it < nc) {
-#pragma unroll
-                for (int i = 0; i < TQ::NV; ++i) st8_perm<bf16_t, IO>(sQ1 + TQ::row(lt, i) * LDK, TQ::col(lt), qn[i]);
-#pragma unroll
-                for (int i = 0; i < PK::NPASS; ++i) {
-                    if (PK::valid(lt, i)) {
-                        const int c8 = PK::col(lt, i), pr0 = 2 * PK::pair(lt, i);
-                        st8_perm<bf16_t, IO>(sK1 + pr0 * LDK, c8, kn[2 * i]);
-                        st8_perm<bf16_t, IO>(sK1 + (pr0 + 1) * LDK, c8, kn[2 * i + 1]);
-                    }
-                }
-#pragma unroll
-                for (int i = 0; i < PV::NPASS; ++i) {
-                    if (PV::valid(lt, i)) {
-                        const int c8 = PV::col(lt, i), pr0 = 2 * PV::pair(lt, i);
-                        st8_perm<bf16_t, IO>(sV + pr0 * LDV, c8, vn[2 * i]);
-                        st8_perm<bf16_t, IO>(sV + (pr0 + 1) * LDV, c8, vn[2 * i + 1]);
-                    }
-                }
-            }
-            __syncthreads();  // end of phase 1
-            // ===== phase 2: L of chunk it: wave u forms L(u, u) and inverts I + L(u, u), and one or two of the
-            // six off-diagonal blocks (1,0),(2,0),(2,1),(3,0),(3,1),(3,2) =====
-            if (it + 1 < nc) load_qk(it + 1);
-            if (it < nc) {
-                const float* sg = tb1 + L::t_g;
-                const float* sb = tb1 + L::t_b;
-                auto store_off = [&](int q, const f32x4_t& cl) {
-                    int I, J;
-                    strict_tile(q, I, J);
-                    const f32x4_t fa = *reinterpret_cast<const f32x4_t*>(tb1 + L::t_fa + J * CH + 16 * I + 4 * g4);
-                    const f32x4_t br = *reinterpret_cast<const f32x4_t*>(sb + 16 * I + 4 * g4);
-                    const float fb = tb1[L::t_fb + 16 * J + lr];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float d = fa[e] * fb;
-                        sLo[(16 * I + 4 * g4 + e) * LDO + 16 * J + lr] = M::cvt(-br[e] * d * cl[e]);
-                    }
-                };
-                int I0, J0;
-                strict_tile(u, I0, J0);
-                f32x4_t cd = {0.f, 0.f, 0.f, 0.f}, c0 = {0.f, 0.f, 0.f, 0.f};
-                M::template nt2<K>(cd, sK1 + 16 * u * LDK, sK1 + 16 * u * LDK, c0, sK1 + 16 * I0 * LDK, sK1 + 16 * J0 * LDK,
-                                   LDK);
-                float* sN = sLd + u * 16 * LDN;
-                const f32x4_t gr = *reinterpret_cast<const f32x4_t*>(sg + 16 * u + 4 * g4);
-                const f32x4_t br = *reinterpret_cast<const f32x4_t*>(sb + 16 * u + 4 * g4);
-                const float gj = sg[16 * u + lr];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int rr = 4 * g4 + e;
-                    const float x = br[e] * exp_f32(gr[e] - gj) * cd[e];  // inf above the diagonal is discarded
-                    sN[rr * LDN + lr] = (rr > lr) ? x : 0.0f;
-                }
-                // the tile's LDS writes complete before this wave's lanes read other lanes' entries
-                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                invert_unit_lower_16<bf16_t>(sN, sD + 16 * u * LDD, LDD);
-                store_off(u, c0);
-                if (u < 2) {
-                    int I1, J1;
-                    strict_tile(u + 4, I1, J1);
-                    f32x4_t c1 = {0.f, 0.f, 0.f, 0.f};
-                    M::nt(c1, sK1 + 16 * I1 * LDK, LDK, sK1 + 16 * J1 * LDK, LDK, K);
-                    store_off(u + 4, c1);
-                }
-            }
-            __syncthreads();  // end of phase 2
-            // ===== phase 3: W tiles 2u and 2u + 1 of chunk it =====
-            if (it + 1 < nc) load_vgb(it + 1);
-            if (it < nc) {
-                f32x4_t X[2][4];
-                const RhsFromRows rhs[2] = {{sK1, LDK, 32 * u, tb1 + L::t_be}, {sK1, LDK, 32 * u + 16, tb1 + L::t_be}};
-                block_solve<bf16_t, 2, RhsFromRows, false>(X, sLo, LDO, sD, LDD, rhs);
-#pragma unroll
-                for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            sW[(16 * i + 4 * g4 + e) * LDK + perm<bf16_t>(32 * u + 16 * jt + lr)] = M::cvt(-X[jt][i][e]);
-            }
-            __syncthreads();  // end of phase 3
-        }
     }
 }
 
@@ -2238,8 +1859,9 @@ __global__ __launch_bounds__(512) void chunk_flow_kernel(const ChunkArgs a) {
         auto load = [&](int ci, Regs& r) {  // global -> registers: chunk ci
             const int64_t bos = s0 + (int64_t)CH * ci;
             const int len = chunk_len(ci);
-            const __amdgpu_buffer_rsrc_t rq =
-                chunk_rsrc(static_cast<const char*>(a.q) + ((bos * a.HK + hk) * K) * ESZ, len, qk_row);
+            // without outputs q reads as zeros (a zero-byte range): it only feeds P and the output
+            const __amdgpu_buffer_rsrc_t rq = chunk_rsrc(
+                want_o ? static_cast<const char*>(a.q) + ((bos * a.HK + hk) * K) * ESZ : nullptr, want_o ? len : 0, qk_row);
 #pragma unroll
             for (int i = 0; i < TQ::NV; ++i) r.qn[i].load(rq, TQ::row(lt, i) * qk_row + TQ::col(lt) * ESZ);
             const __amdgpu_buffer_rsrc_t rk =
@@ -2396,11 +2018,7 @@ hipError_t launch_fused(const ChunkArgs& a, hipStream_t stream) {
     // bf16: the workgroup owns all V columns; fp32 operands (K = 64 only) use 64-column tiles
     constexpr int BV = std::is_same<IO, float>::value ? 64 : V;
     if constexpr (K == 128 && V == 128 && std::is_same<IO, bf16_t>::value && !PER_K) {
-#ifdef GDR_CHUNK_PIPE
-        hipLaunchKernelGGL(chunk_pipe_kernel<IO>, dim3(1, a.HV, a.N), dim3(512), 0, stream, a);
-#else
         hipLaunchKernelGGL(chunk_flow_kernel<IO>, dim3(1, a.HV, a.N), dim3(512), 0, stream, a);
-#endif
         return hipGetLastError();
     }
     hipLaunchKernelGGL((chunk_fused_kernel<K, BV, IO, IO, PER_K>), dim3(V / BV, a.HV, a.N), dim3(4 * BV), 0, stream,

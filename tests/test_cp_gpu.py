@@ -189,6 +189,28 @@ def test_long_batch_full_size_every_head_both_routes():
     assert max_rel_l2_states(f64(ht2), f_ref) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("K,V,HK,HV", [(64, 64, 1, 2), (128, 128, 1, 4), (128, 64, 2, 2), (64, 128, 1, 1)])
+def test_kda_bf16_segmented_shapes(K, V, HK, HV):
+    """Per-channel gate, bf16, two sequences on the segmented route at every head-dimension pair, GQA,
+    with an initial state; the single-pass route agrees."""
+    p = inputs.dense_problem(91 + K + V, [64 * 61 + 21, 64 * 40], HK=HK, HV=HV, K=K, V=V, io_dtype="bf16",
+                             g_range=(-2.0, 0.0), g_endpoints=0.25, per_k_gate=True, beta_mode="mixed")
+    o, ht = _run_and_check(p)
+    o2, ht2 = _direct(p)
+    assert max_rel_l2_tokens(f64(o), f64(o2), p.cu_seqlens) <= TOL["bf16"]
+    assert max_rel_l2_states(f64(ht), f64(ht2)) <= TOL["bf16"]
+
+
+def test_kda_bf16_segmented_strong_decay_elementwise_diagonal():
+    """Decays of -5 per token and channel on one head exceed the range the MFMA form of a diagonal
+    block accepts, so every chunk of that head takes the element-wise diagonal path, in the runs without
+    outputs too; the other head keeps the MFMA form."""
+    p = inputs.dense_problem(95, [64 * 48 + 7], HK=2, HV=2, K=128, V=128, io_dtype="bf16", per_k_gate=True,
+                             beta_mode="mixed", g_range=(-0.3, 0.0))
+    p.g[:, 1, :] = np.float32(-5.0)
+    _run_and_check(p)
+
+
 def test_fp32_k128_long_sequence():
     p = inputs.dense_problem(90, [64 * 70 + 11], HK=1, HV=2, K=128, V=128, io_dtype="f32", g_range=(-0.5, 0.0))
     _run_and_check(p)
