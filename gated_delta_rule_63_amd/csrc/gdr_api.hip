@@ -338,16 +338,24 @@ gdr_status chunk_fwd_impl(const gdr_problem* p, const void* q, const void* k, co
     float* Bs = reinterpret_cast<float*>(ws + pl.B);
     float* Ms = reinterpret_cast<float*>(ws + pl.M);
     float* Ss = reinterpret_cast<float*>(ws + pl.S);
-    hipError_t e = gdr::launch_cp_setup(pl, ws, cu_seqlens, p->total_tokens, p->num_v_heads, p->head_dim_k, stream);
+    // the per-channel gate with K = V forms B_s and M_s in one paired run, M_s from an identity it holds itself
+    const bool paired = per_k && p->io_dtype == GDR_BF16 && p->head_dim_k == p->head_dim_v;
+    hipError_t e = gdr::launch_cp_setup(pl, ws, cu_seqlens, p->total_tokens, p->num_v_heads, p->head_dim_k, !paired,
+                                        stream);
     if (e != hipSuccess) return status_of(e);
 
     gdr::ChunkArgs b = a;  // 1a: offsets B_s
     b.cu_seqlens = cu_seg; b.N = pl.P; b.h0 = nullptr; b.o = nullptr; b.ht = Bs;
-    if ((e = gdr::launch_chunk(b, p->io_dtype, per_k, stream)) != hipSuccess) return status_of(e);
-
-    gdr::ChunkArgs m = a;  // 1b: linear parts M_s (a K-row state, v = 0), in place from the identity
-    m.cu_seqlens = cu_seg; m.N = pl.P; m.v = nullptr; m.V = p->head_dim_k; m.h0 = Ms; m.o = nullptr; m.ht = Ms;
-    if ((e = gdr::launch_chunk(m, p->io_dtype, per_k, stream)) != hipSuccess) return status_of(e);
+    if (paired) {
+        // 1: one paired run forms B_s and M_s, sharing every chunk's reads and intra-chunk transform
+        b.q = nullptr; b.map = Ms;
+        if ((e = gdr::launch_chunk(b, p->io_dtype, per_k, stream)) != hipSuccess) return status_of(e);
+    } else {
+        if ((e = gdr::launch_chunk(b, p->io_dtype, per_k, stream)) != hipSuccess) return status_of(e);
+        gdr::ChunkArgs m = a;  // 1b: linear parts M_s (a K-row state, v = 0), in place from the identity
+        m.cu_seqlens = cu_seg; m.N = pl.P; m.v = nullptr; m.V = p->head_dim_k; m.h0 = Ms; m.o = nullptr; m.ht = Ms;
+        if ((e = gdr::launch_chunk(m, p->io_dtype, per_k, stream)) != hipSuccess) return status_of(e);
+    }
 
     e = gdr::launch_cp_scan(pl, ws, initial_state, p->num_v_heads, p->head_dim_k, p->head_dim_v, stream);
     if (e != hipSuccess) return status_of(e);

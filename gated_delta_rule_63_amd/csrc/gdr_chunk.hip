@@ -277,6 +277,64 @@ __device__ __forceinline__ void gemm_regs(f32x4_t* acc, const typename MM<MT>::S
     }
 }
 
+// acc0[i] += A[16*i + .., :] B0 and acc1[i] += A[16*i + .., :] B1 (gemm_regs for two right operands
+// from registers with one left operand from LDS, bf16): each A read feeds both products.
+template <typename MT, int NP, int NI>
+__device__ __forceinline__ void gemm_regs_2b(f32x4_t* acc0, const f32x4_t* Bt0, f32x4_t* acc1, const f32x4_t* Bt1,
+                                             const typename MM<MT>::S* sA, int lda) {
+    static_assert(sizeof(typename MM<MT>::S) == 2, "bf16 operands");
+    const int l = threadIdx.x & 63, g4 = l >> 4, lr = l & 15;
+#pragma unroll
+    for (int m = 0; m < NP / 32; ++m) {
+        bf16x8_t av[NI];
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+            av[i] = *reinterpret_cast<const bf16x8_t*>(sA + (16 * i + lr) * lda + 32 * m + 8 * g4);
+        __builtin_amdgcn_sched_barrier(0);
+        const uint4 b0 = {pack_tile_lo(Bt0[2 * m]), pack_tile_hi(Bt0[2 * m]), pack_tile_lo(Bt0[2 * m + 1]),
+                          pack_tile_hi(Bt0[2 * m + 1])};
+        const uint4 b1 = {pack_tile_lo(Bt1[2 * m]), pack_tile_hi(Bt1[2 * m]), pack_tile_lo(Bt1[2 * m + 1]),
+                          pack_tile_hi(Bt1[2 * m + 1])};
+        const bf16x8_t bv0 = __builtin_bit_cast(bf16x8_t, b0), bv1 = __builtin_bit_cast(bf16x8_t, b1);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            acc0[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i], bv0, acc0[i], 0, 0, 0);
+            acc1[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i], bv1, acc1[i], 0, 0, 0);
+        }
+    }
+}
+
+// acc0[i] += A0[16*i + .., :] B and acc1[i] += A1[16*i + .., :] B (gemm_regs for two left operands with
+// one right operand): each packing of B feeds both, and the two accumulator chains interleave.
+template <typename MT, int NP, int NI>
+__device__ __forceinline__ void gemm_regs2(f32x4_t* acc0, const typename MM<MT>::S* sA0, f32x4_t* acc1,
+                                           const typename MM<MT>::S* sA1, int lda, const f32x4_t* Bt) {
+    if constexpr (sizeof(typename MM<MT>::S) == 2) {
+        const int l = threadIdx.x & 63, g4 = l >> 4, lr = l & 15;
+#pragma unroll
+        for (int m = 0; m < NP / 32; ++m) {
+            bf16x8_t a0[NI], a1[NI];
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                a0[i] = *reinterpret_cast<const bf16x8_t*>(sA0 + (16 * i + lr) * lda + 32 * m + 8 * g4);
+                a1[i] = *reinterpret_cast<const bf16x8_t*>(sA1 + (16 * i + lr) * lda + 32 * m + 8 * g4);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            const uint4 bw = {pack_tile_lo(Bt[2 * m]), pack_tile_hi(Bt[2 * m]), pack_tile_lo(Bt[2 * m + 1]),
+                              pack_tile_hi(Bt[2 * m + 1])};
+            const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, bw);
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                acc0[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[i], bv, acc0[i], 0, 0, 0);
+                acc1[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[i], bv, acc1[i], 0, 0, 0);
+            }
+        }
+    } else {
+        gemm_regs<MT, NP, NI>(acc0, sA0, lda, Bt);
+        gemm_regs<MT, NP, NI>(acc1, sA1, lda, Bt);
+    }
+}
+
 // Buffer resource over the rows of one chunk: `rows` rows of `row_bytes` starting at `base`.
 // Loads at byte offsets past rows * row_bytes return zeros, so rows past the end of a short
 // chunk read as zero without a clamp, a select or a branch.
@@ -761,10 +819,17 @@ struct OStage {
 // products well inside the fp32 / bf16 exponent range.
 constexpr float kKdaDiagRange = 64.0f;
 
-template <int K, int BV, typename IO, typename MT, bool PER_K>
+// With MAP (per-channel gate, bf16, K = V; the segmented route), one run forms both end-of-segment
+// quantities of a (segment, head): the state reached from h0 with the inputs (ht) and the linear part
+// of the segment's map, the state reached from the identity with v = 0 (map [N, HV, K, K]).  Wave w
+// holds value columns 16w .. 16w+15 of the first and rows 16w .. 16w+15 of the second; the two share
+// every chunk's k, gate and beta reads and the whole intra-chunk transform, and each product of E
+// reads its LDS operand once for both.  No q is read and no output is formed.
+template <int K, int BV, typename IO, typename MT, bool PER_K, bool MAP = false>
 __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) {
     constexpr int NW = BV / 16;       // waves; wave w owns value columns 16w .. 16w+15 of the tile
     constexpr int NTHR = 64 * NW;
+    static_assert(!MAP || (PER_K && K == BV && sizeof(typename MM<MT>::S) == 2), "paired run: per-K gate, K = V, bf16");
     constexpr int KT = K / 16;
     typedef MM<MT> M;
     typedef typename M::S S;
@@ -772,7 +837,7 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
     constexpr int LDK = Lay::LDK, LDT = Lay::LDT, LDO = Lay::LDO, LDD = Lay::LDD;
     static_assert(NW >= 4, "four waves invert the diagonal blocks");
     // without outputs (the segment-offset and segment-map runs) q, P and the output are skipped
-    const bool want_o = a.o != nullptr;
+    const bool want_o = !MAP && a.o != nullptr;
     typedef OStage<BV, IO> OS;
     constexpr bool TRK = Lay::TRK;
     static_assert(Lay::total <= 160 * 1024, "LDS budget");
@@ -799,6 +864,14 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
     for (int kt = 0; kt < KT; ++kt) {
         hs[kt] = a.h0 ? *reinterpret_cast<const f32x4_t*>(a.h0 + sidx + 16 * kt + 4 * g4)
                       : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    // MAP: rows 16w .. 16w+15 of the segment map, from the identity (row 16w + l%16 of the K x K map)
+    f32x4_t hm[MAP ? KT : 1];
+    if constexpr (MAP) {
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) hm[kt][e] = (16 * kt + 4 * g4 + e == 16 * w + lr) ? 1.0f : 0.0f;
     }
 
     // strictly upper tiles of P are never written: zero them once
@@ -1410,15 +1483,36 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
         __syncthreads();
 
         // ===== E: v_new, output, state update (wave w: columns 16w .. 16w+15) =====
-        // v_new = U - W S^T  (LDS holds -W)
-        gemm_regs<MT, K, 4>(nu, sW, LDK, hs);
-        if (ci + 1 < nc) load_vgb(ci + 1);
-        // O = scale (diag(e^gamma) Q S^T + P v_new), when outputs are wanted
-        if (want_o) {
+        // v_new = U - W S^T (LDS holds -W) and, when outputs are wanted, the Q S^T part of
+        // O = scale (diag(e^gamma) Q S^T + P v_new): one packing of the state feeds both
+        if constexpr (MAP) {
+            // both states: v_new = U - W S^T and, for the map rows (U = 0), -W M^T; then the decays and
+            // the rank-64 updates with (K e^(gamma_last - gamma))^T, each LDS operand read once
+            f32x4_t nm[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) nm[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            gemm_regs_2b<MT, K, 4>(nu, hs, nm, hm, sW, LDK);
+            if (ci + 1 < nc) load_vgb(ci + 1);
+            const float* sgl = FP(Lay::k_gl);
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float d = sgl[16 * kt + 4 * g4 + e];
+                    hs[kt][e] *= d;
+                    hm[kt][e] *= d;
+                }
+            gemm_regs_2b<MT, CH, KT>(hs, nu, hm, nm, SP(Lay::k_kdt), LDT);
+            __syncthreads();
+            continue;
+        }
         f32x4_t oa[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) oa[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        gemm_regs<MT, K, 4>(oa, SP(PER_K ? Lay::k_qt : Lay::g_q), LDK, hs);
+        if (want_o) gemm_regs2<MT, K, 4>(nu, sW, oa, SP(PER_K ? Lay::k_qt : Lay::g_q), LDK, hs);
+        else gemm_regs<MT, K, 4>(nu, sW, LDK, hs);
+        if (ci + 1 < nc) load_vgb(ci + 1);
+        if (want_o) {
         if constexpr (!PER_K) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -1501,6 +1595,11 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
     if (a.ht) {
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) *reinterpret_cast<f32x4_t*>(a.ht + sidx + 16 * kt + 4 * g4) = hs[kt];
+    }
+    if constexpr (MAP) {
+        float* const dm = a.map + (((int64_t)n * a.HV + h) * K + 16 * w + lr) * K;
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) *reinterpret_cast<f32x4_t*>(dm + 16 * kt + 4 * g4) = hm[kt];
     }
 }
 
@@ -2019,15 +2118,25 @@ hipError_t launch_fused(const ChunkArgs& a, hipStream_t stream) {
     constexpr int BV = std::is_same<IO, float>::value ? 64 : V;
     if constexpr (K == 128 && V == 128 && std::is_same<IO, bf16_t>::value && !PER_K) {
         hipLaunchKernelGGL(chunk_flow_kernel<IO>, dim3(1, a.HV, a.N), dim3(512), 0, stream, a);
-        return hipGetLastError();
+    } else {
+        hipLaunchKernelGGL((chunk_fused_kernel<K, BV, IO, IO, PER_K>), dim3(V / BV, a.HV, a.N), dim3(4 * BV), 0,
+                           stream, a);
     }
-    hipLaunchKernelGGL((chunk_fused_kernel<K, BV, IO, IO, PER_K>), dim3(V / BV, a.HV, a.N), dim3(4 * BV), 0, stream,
-                       a);
     return hipGetLastError();
 }
 
 template <int K, int V>
 hipError_t launch_kv(const ChunkArgs& a, int io, bool per_k, hipStream_t s) {
+    if (a.map) {  // the paired offset/map run of the segmented route
+        if constexpr (K == V) {
+            if (io == 1 && per_k) {
+                hipLaunchKernelGGL((chunk_fused_kernel<K, V, bf16_t, bf16_t, true, true>), dim3(1, a.HV, a.N),
+                                   dim3(4 * V), 0, s, a);
+                return hipGetLastError();
+            }
+        }
+        return hipErrorNotSupported;
+    }
     if (io == 0) {
         // fp32 operands: every shape with the scalar gate; the per-channel gate at K = 128 does not
         // fit the 160 KiB of LDS in this design

@@ -27,8 +27,8 @@ namespace gdr {
 // nseg_n = max(1, ceil(len_n / seg_tokens)) segments; seg_first[n] = sum of nseg over the earlier
 // sequences, seg_first[N] = the real segment count.  cu_seg[seg_first[n] + j] = start of segment j of
 // sequence n, cu_seg[s] = T for every s from the real count up to P_max (empty trailing segments).
-// M[s][h] = I (K x K) for every segment and head.  One thread forms seg_first (N is small on this
-// route); every thread fills cu_seg and M.
+// M[s][h] = I (K x K) for every segment and head when the maps are formed by a run of their own.  One
+// thread forms seg_first (N is small on this route); every thread fills cu_seg and M.
 __global__ __launch_bounds__(256) void cp_setup_kernel(const int32_t* __restrict__ cu, int32_t N,
                                                        int32_t* __restrict__ cu_seg, int32_t* __restrict__ seg_first,
                                                        int P_max, int64_t seg_tokens, int64_t T,
@@ -164,8 +164,8 @@ CpPlan cp_plan(int64_t T, int32_t N, int32_t HV, int32_t K, int32_t V, int io_by
 }
 
 hipError_t launch_cp_setup(const CpPlan& pl, char* ws, const int32_t* cu, int64_t T, int32_t HV, int32_t K,
-                           hipStream_t stream) {
-    const int64_t maps = (int64_t)pl.P * HV;
+                           bool identity, hipStream_t stream) {
+    const int64_t maps = identity ? (int64_t)pl.P * HV : 0;
     int64_t blocks = (maps * K * K + 255) / 256;
     if (blocks < 1) blocks = 1;
     if (blocks > 65536) blocks = 65536;

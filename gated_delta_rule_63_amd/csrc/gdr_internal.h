@@ -80,6 +80,9 @@ struct ChunkArgs {
     const float* h0;             // [N, HV, V, K] or NULL (zeros)
     void* o;                     // NULL: outputs not written
     float* ht;                   // [N, HV, V, K] or NULL; may equal h0 (each thread reads its part first)
+    // non-NULL selects the paired run of the segmented route (per-channel gate, bf16, K = V): besides
+    // ht, map [N, HV, K, K] receives the end state from the identity with v = 0; q and o are unused
+    float* map;
     int64_t T;
     int32_t N, HK, HV, K, V;
     float scale;
@@ -133,8 +136,9 @@ struct CpPlan {
 };
 
 CpPlan cp_plan(int64_t T, int32_t N, int32_t HV, int32_t K, int32_t V, int io_bytes);
+// identity: also set every segment map to the identity (the start state of the separate map run)
 hipError_t launch_cp_setup(const CpPlan& pl, char* ws, const int32_t* cu, int64_t T, int32_t HV, int32_t K,
-                           hipStream_t stream);
+                           bool identity, hipStream_t stream);
 hipError_t launch_cp_scan(const CpPlan& pl, char* ws, const float* h0, int32_t HV, int32_t K, int32_t V,
                           hipStream_t stream);
 hipError_t launch_cp_final(const CpPlan& pl, const char* ws, float* out, int32_t HV, int32_t K, int32_t V,
