@@ -30,6 +30,11 @@ CPU oracle timed on a bounded sample of the prefill workload.
 Profiling passes: ``--legs prefill`` runs only that leg, ``--calib-copy-mib N`` first runs one
 device copy of N MiB (known traffic, to scale FETCH_SIZE / WRITE_SIZE); both print a short
 JSON line instead of the full report.
+
+Summaries (host only, no GPU): ``--summarize-counters FETCH_DIR WRITE_DIR`` turns the two counter
+passes' CSV output into profiles/hbm_traffic.md (bytes per launch per leg, and the records this
+script reads back), ``--summarize-trace TRACE_DIR PROFILED_LOG PLAIN_LOG`` turns a kernel trace of a
+bench run into profiles/bench_kernel_trace.md.
 """
 from __future__ import annotations
 
@@ -282,6 +287,209 @@ def _stats(ms):
             "min": float(np.min(a)), "n": int(a.size)}
 
 
+# Kernels each leg launches per call: (name fragment, grid size in work-items or None, dispatches per
+# call).  A leg's dispatches are told apart from another leg's launches of the same kernel by the
+# grid; a spec without a grid takes every dispatch of that name that no gridded spec claimed.
+_VERIFY_K = "recurrent_kernel<128, gdr::bf16_t, gdr::bf16_t, gdr::bf16_t, gdr::bf16_t, false, 4, true, 0>"
+
+
+def _leg_kernel_specs():
+    from gated_delta_rule_63_amd import inputs
+    pp, pk, pc = inputs.prefill(), inputs.kda(), inputs.long_batch()
+    flow = "chunk_flow_kernel<gdr::bf16_t>"
+    specs = {
+        "prefill": [(flow, 512 * pp.HV * pp.N, 1)],
+        "decode": [("recurrent_kernel<128, gdr::bf16_t, float, float, void, false, 4, false, 0>", None, 1)],
+        "verify": [(_VERIFY_K, None, 1)],
+        "decode_gated": [("recurrent_kernel<128, gdr::bf16_t, float, float, void, false, 4, false, 2>", None, 1)],
+        "verify_gated": [("recurrent_kernel<128, gdr::bf16_t, gdr::bf16_t, gdr::bf16_t, gdr::bf16_t, false, 4, true, 2>",
+                          None, 1)],
+        "verify_prepass": [("gating_prepass_kernel<128, gdr::bf16_t>", None, 1), (_VERIFY_K, None, 1)],
+        "kda": [("chunk_fused_kernel<128, 128, gdr::bf16_t, gdr::bf16_t, true, true>", None, 1),
+                ("chunk_fused_kernel<128, 128, gdr::bf16_t, gdr::bf16_t, true, false>", None, 1),
+                ("cp_scan_kernel<128>", 256 * (pk.V // 16) * pk.HV * pk.N, 1), ("cp_setup_kernel", 256, 1),
+                ("cp_final_kernel", 256 * 256 * pk.N, 1)],
+        "cp_segmented": [(flow, None, 3), ("cp_scan_kernel<128>", None, 1), ("cp_setup_kernel", None, 1),
+                         ("cp_final_kernel", None, 1)],
+        "cp_direct": [(flow, 512 * pc.HV * pc.N, 1)],
+    }
+    for nb in (1, 16, 64):
+        specs[f"kda_front_b{nb}"] = [("kda_decode_kernel", 512 * 32 * nb, 1)]
+    return specs
+
+
+def _leg_sources():
+    chunk = ["gdr_chunk.hip", "gdr_device.h"]
+    cp = ["gdr_chunk.hip", "gdr_device.h", "gdr_cp.hip", "gdr_api.hip"]
+    rec = ["gdr_recurrent.hip", "gdr_device.h"]
+    out = {"prefill": chunk, "decode": rec, "verify": rec, "decode_gated": rec, "verify_gated": rec,
+           "verify_prepass": ["gdr_gating.hip"] + rec, "kda": cp, "cp_segmented": cp, "cp_direct": cp}
+    for nb in (1, 16, 64):
+        out[f"kda_front_b{nb}"] = ["gdr_kda.hip", "gdr_device.h"]
+    return out
+
+
+def _assign_dispatches(dispatches, specs):
+    """dispatches: list of (kernel name, grid, value).  Returns {leg: [(fragment, count, values)]}."""
+    claimed = set()
+    out = {leg: [None] * len(sp) for leg, sp in specs.items()}
+    for leg, sp in specs.items():
+        for j, (frag, grid, cnt) in enumerate(sp):
+            if grid is not None:
+                idx = [i for i, (nm, g, _) in enumerate(dispatches) if frag in nm and g == grid]
+                claimed.update(idx)
+                out[leg][j] = (frag, cnt, [dispatches[i][2] for i in idx])
+    for leg, sp in specs.items():
+        for j, (frag, grid, cnt) in enumerate(sp):
+            if grid is None:
+                idx = [i for i, (nm, g, _) in enumerate(dispatches) if frag in nm and i not in claimed]
+                out[leg][j] = (frag, cnt, [dispatches[i][2] for i in idx])
+    return out
+
+
+def _summarize_counters(fetch_dir, write_dir):
+    """profiles/hbm_traffic.md from the FETCH_SIZE and WRITE_SIZE passes (rocprofv3 csv output)."""
+    import csv
+    import glob
+    from gated_delta_rule_63_amd import inputs
+
+    def load(d, counter):
+        f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
+        per = {}
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter:
+                key = (r["Dispatch_Id"], r["Kernel_Name"], int(r["Grid_Size"]))
+                per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+        return [(nm, g, v) for (_, nm, g), v in sorted(per.items(), key=lambda kv: int(kv[0][0]))]
+
+    fe, wr = load(fetch_dir, "FETCH_SIZE"), load(write_dir, "WRITE_SIZE")
+    cf = max(v for nm, _, v in fe if "copyBuffer" in nm)
+    cw = max(v for nm, _, v in wr if "copyBuffer" in nm)
+    copy_kib = 1024 * 1024  # the --calib-copy-mib 1024 copy reads and writes 1 GiB
+    ff, wf = copy_kib / cf, copy_kib / cw
+    specs = _leg_kernel_specs()
+    af, aw = _assign_dispatches(fe, specs), _assign_dispatches(wr, specs)
+    pp, pd, pv, pk, pc = inputs.prefill(), inputs.decode(), inputs.verify(), inputs.kda(), inputs.long_batch()
+    alg = {"prefill": _alg_bytes_prefill(pp), "decode": _alg_bytes_paged(pd, with_ibuf=False),
+           "verify": _alg_bytes_paged(pv, with_ibuf=True),
+           "decode_gated": _alg_bytes_paged(pd, with_ibuf=False, gated=True),
+           "verify_gated": _alg_bytes_paged(pv, with_ibuf=True, gated=True),
+           "verify_prepass": _alg_bytes_prepass(pv) + _alg_bytes_paged(pv, with_ibuf=True),
+           "kda": _alg_bytes_prefill(pk, with_cu=False), "cp_segmented": _alg_bytes_prefill(pc),
+           "cp_direct": _alg_bytes_prefill(pc)}
+    for nb in (1, 16, 64):
+        alg[f"kda_front_b{nb}"] = _alg_bytes_kda_front(
+            inputs.kda_front_problem(560 + nb, B=nb, q_len=1, H=32, R=128, num_slots=max(2 * nb, 8)))
+    srcs = _leg_sources()
+    rows, recs = [], []
+    for leg in specs:
+        fk = wk = 0.0
+        parts, ok = [], True
+        for (frag, cnt, fv), (_, _, wv) in zip(af[leg], aw[leg]):
+            if not fv or not wv:
+                ok = False
+                break
+            fk += cnt * sum(fv) / len(fv)
+            wk += cnt * sum(wv) / len(wv)
+            parts.append(f"`{frag}` x{cnt} ({len(fv)})")
+        if not ok:
+            continue
+        b = (fk * ff + wk * wf) * 1024
+        rows.append(f"| {leg} | {', '.join(parts)} | {fk:.1f} | {wk:.1f} | {b:.4e} | {alg[leg]:.4e} | "
+                    f"{b / alg[leg]:.3f} |")
+        recs.append(json.dumps({"leg": leg, "kernels": [f for f, _, _ in specs[leg]],
+                                "source_sha256": _source_digest(srcs[leg]), "fetch_kib_raw": fk, "write_kib_raw": wk,
+                                "fetch_factor": ff, "write_factor": wf, "bytes_per_launch": b,
+                                "alg_bytes_per_launch": alg[leg]}))
+    cmd = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 240 rocprofv3 --pmc {c} --output-format csv -d "
+           "/root/repo/gpurun_out/prof_{d} -o run -- python3 /root/repo/bench.py --steps 2 --warmup 1 "
+           "--no-cpu-baseline --calib-copy-mib 1024")
+    out = f"""# HBM traffic per call (rocprofv3 FETCH_SIZE / WRITE_SIZE), MI355X
+
+Two counter passes, each in a run of its own, then this summary (host only):
+
+```
+{cmd.format(c='FETCH_SIZE', d='fetch')}
+{cmd.format(c='WRITE_SIZE', d='write')}
+python3 bench.py --summarize-counters gpurun_out/prof_fetch gpurun_out/prof_write
+```
+
+Scaling: the run first copies 1 GiB device-to-device (`__amd_rocclr_copyBuffer`, reads and writes 1048576 KiB). FETCH_SIZE reads {cf:.1f} KiB and WRITE_SIZE {cw:.1f} KiB for it, so the factors are {ff:.4f} (fetch) and {wf:.4f} (write).
+
+Each leg sums, per call, the kernels it launches (the count after each kernel is the dispatches per call; the number in parentheses, the dispatches averaged). Launches of one kernel by two legs are told apart by their grids.
+
+| leg | kernels per call | FETCH_SIZE KiB (raw) | WRITE_SIZE KiB (raw) | scaled bytes/call | algorithmic bytes | ratio |
+|---|---|---|---|---|---|---|
+""" + "\n".join(rows) + """
+
+Records read by bench.py (`traffic` is reported only while the sha256 of the leg's kernel sources still matches):
+
+""" + "\n".join(recs) + "\n"
+    with open(_TRAFFIC, "w") as f:
+        f.write(out)
+    print(out)
+
+
+def _summarize_trace(trace_dir, profiled_log, plain_log):
+    """profiles/bench_kernel_trace.md from a kernel trace of a bench run and two bench JSON lines."""
+    import csv
+    import glob
+
+    def jl(p):
+        with open(p) as f:
+            for line in f:
+                if line.startswith("{") and '"metric"' in line:
+                    return json.loads(line)
+        raise SystemExit(f"no bench line in {p}")
+    stats = list(csv.DictReader(open(glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)[0])))
+    trace = list(csv.DictReader(open(glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)[0])))
+    disp = [(r["Kernel_Name"], int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]),
+             (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3) for r in trace]
+    specs = _leg_kernel_specs()
+    per_leg = _assign_dispatches(disp, specs)
+    pr, un = jl(profiled_log), jl(plain_log)
+    nm = lambda x: x if len(x) <= 110 else x[:107] + "..."
+    t = "\n".join(f"| `{nm(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                  f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f}% |" for r in stats)
+    legs = {**{k: v for k, v in pr["leg_ms"].items()}, **{k: v["ms"] for k, v in pr["extra_legs"].items()}}
+    plain = {**{k: v for k, v in un["leg_ms"].items()}, **{k: v["ms"] for k, v in un["extra_legs"].items()}}
+    lines = []
+    for leg, parts in per_leg.items():
+        if leg not in legs:
+            continue
+        # the timed calls come after the warm-up ones: keep each kernel's last steps x count dispatches
+        parts = [(frag, cnt, v[-pr["steps"] * cnt:]) for frag, cnt, v in parts]
+        us = [f"`{frag}` x{cnt}: {sum(v) / len(v):.1f} us over {len(v)}" for frag, cnt, v in parts if v]
+        tot = sum(cnt * sum(v) / len(v) for frag, cnt, v in parts if v)
+        lines.append(f"| {leg} | {'; '.join(us)} | {tot / 1e3:.4f} | {legs[leg]:.4f} | {plain.get(leg, float('nan')):.4f} |")
+    cmd = (f"cd /tmp && export TMPDIR=/tmp && timeout -k 10 600 rocprofv3 --kernel-trace --stats --output-format csv -d "
+           f"/root/repo/gpurun_out/prof_trace -o run -- python3 /root/repo/bench.py --no-cpu-baseline "
+           f"--steps {pr['steps']} --warmup {pr['warmup']}")
+    out = f"""# Kernel trace of a bench run, MI355X
+
+```
+{cmd}
+python3 bench.py --summarize-trace gpurun_out/prof_trace PROFILED_LOG PLAIN_LOG
+```
+
+PROFILED_LOG is the bench line the profiled run printed, PLAIN_LOG the line of an unprofiled
+`python3 bench.py` on the same box.  `run_kernel_stats.csv` ({pr['warmup']} warm-up and {pr['steps']} timed calls per leg; `reduce_kernel` is torch's sum that cleans the cache before each timed launch):
+
+| kernel | calls | avg us | min us | max us | share |
+|---|---|---|---|---|---|
+{t}
+
+Per leg, from `run_kernel_trace.csv` (each kernel's mean over the leg's timed dispatches, the last ones of the run; a leg's launches of a kernel are told apart from another leg's by the grid), against the HIP-event times (ms, mean over the timed calls) of the profiled and the unprofiled run:
+
+| leg | kernels per call | kernel sum ms | HIP events, profiled | HIP events, plain |
+|---|---|---|---|---|
+""" + "\n".join(lines) + "\n"
+    path = os.path.join(_HERE, "profiles", "bench_kernel_trace.md")
+    with open(path, "w") as f:
+        f.write(out)
+    print(out)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -302,7 +510,17 @@ def main():
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before the legs, run one device-to-device copy of this many MiB (a plain copy kernel of "
                          "known size, used to scale the HBM byte counters of a profiling pass) and stop after the legs")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="host only: write profiles/hbm_traffic.md from the two counter passes and stop")
+    ap.add_argument("--summarize-trace", nargs=3, metavar=("TRACE_DIR", "PROFILED_LOG", "PLAIN_LOG"),
+                    help="host only: write profiles/bench_kernel_trace.md from a kernel trace of a bench run and stop")
     args = ap.parse_args()
+    if args.summarize_counters:
+        _summarize_counters(*args.summarize_counters)
+        return
+    if args.summarize_trace:
+        _summarize_trace(*args.summarize_trace)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: the gated-delta-rule path here is built and timed on a single "
               "MI355X (every (sequence, head) state is independent; sharding is described, not run). "
@@ -520,7 +738,7 @@ def main():
 
     prefill_tps = pp.T / s_pre
     leg_info = {
-        "prefill": {"kernel": "chunk_pipe_kernel<bf16> (one launch per call)", "bytes": b_pre,
+        "prefill": {"kernel": "chunk_flow_kernel<bf16> (one launch per call)", "bytes": b_pre,
                     "flops": f_pre, "secs": s_pre, "sources": ["gdr_chunk.hip", "gdr_device.h"]},
         "decode": {"kernel": "recurrent_kernel (256 x 1 token, fp32 pool, commit)", "bytes": b_dec, "flops": None,
                    "secs": s_dec, "sources": ["gdr_recurrent.hip", "gdr_device.h"]},
@@ -542,13 +760,14 @@ def main():
                                       "secs": extra_ms["verify_prepass"] / 1e3,
                                       "sources": ["gdr_gating.hip"] + gated_sources}
     if "kda" in extra_ms:
-        leg_info["kda"] = {"kernel": "segmented route: chunk_fused_kernel<128,128,bf16,per-K gate> x3, scan, setup, "
-                                     "copy (1 x 65573 tokens, 16 heads; bytes, time and traffic per call)",
+        leg_info["kda"] = {"kernel": "segmented route: setup, paired offset/map run and outputs run of "
+                                     "chunk_fused_kernel<128,128,bf16,per-K gate>, scan, final-state copy "
+                                     "(1 x 65573 tokens, 16 heads; bytes, time and traffic per call)",
                            "bytes": _alg_bytes_prefill(pk, with_cu=False), "flops": None, "secs": extra_ms["kda"] / 1e3,
                            "sources": ["gdr_chunk.hip", "gdr_device.h", "gdr_cp.hip", "gdr_api.hip"]}
-    for leg, route in (("cp_segmented", "segmented route: setup, chunk kernel x3 (offsets, maps, outputs), scan, "
+    for leg, route in (("cp_segmented", "segmented route: setup, chunk_flow_kernel x3 (offsets, maps, outputs), scan, "
                                          "final-state copy"),
-                       ("cp_direct", "single pass: one chunk-kernel launch, one workgroup per (sequence, head)")):
+                       ("cp_direct", "single pass: one chunk_flow_kernel launch, one workgroup per (sequence, head)")):
         if leg in extra_ms:
             leg_info[leg] = {"kernel": f"{route} (4 x 16384 tokens, 16 heads, K=V=128, bf16; per call)",
                              "bytes": _alg_bytes_prefill(pc), "flops": _alg_flops_prefill(pc),
