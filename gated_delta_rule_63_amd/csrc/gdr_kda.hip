@@ -15,9 +15,10 @@
 //    and written back at the end by the same workgroup, and no other workgroup touches it (the page
 //    reports a race where column-split programs shared an in-place window shift);
 //  * per token, threads 0 .. 2K+V-1 each run one convolution channel (taps, bias and window in
-//    registers), threads 2K+V .. 3K+V-1 each form one key channel's decay (a dot product of length R
-//    with the gate projection row), thread 0 also forms beta; results go through LDS
-//    (double-buffered by token parity);
+//    registers); every thread also takes a 1/TPC share of one key channel's gate projection (a dot
+//    product of length R; TPC = 512/K threads per channel, their partial sums reduced across the
+//    consecutive lanes); thread 0 also forms beta.  All of a token's front loads are independent, so
+//    they are in flight together.  Results go through LDS (double-buffered by token parity);
 //  * the recurrence runs on 16-lane row groups as in the token-loop kernel: lane j holds K/16 key
 //    channels of SLOTS = V/32 rows, the two row GEMVs reduce with DPP, q and k are normalised with
 //    one more 16-lane reduction each;
@@ -31,6 +32,42 @@ namespace {
 
 constexpr int kKdaThreads = 512;
 
+// Eight consecutive elements held as loaded (bf16 pairs stay packed), so that a slice of the gate
+// projection costs 4 registers in bf16.
+template <typename IO> struct Slice8;
+template <> struct Slice8<bf16_t> {
+    uint4 w;
+    __device__ __forceinline__ void load(const void* p, int64_t i) {
+        w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p) + i);
+    }
+    __device__ __forceinline__ void zero() { w = uint4{0u, 0u, 0u, 0u}; }
+    __device__ __forceinline__ float dot(const Slice8& o, float acc) const {
+        const uint32_t a[4] = {w.x, w.y, w.z, w.w}, b[4] = {o.w.x, o.w.y, o.w.z, o.w.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            acc = fmaf(__uint_as_float(a[j] << 16), __uint_as_float(b[j] << 16), acc);
+            acc = fmaf(__uint_as_float(a[j] & 0xFFFF0000u), __uint_as_float(b[j] & 0xFFFF0000u), acc);
+        }
+        return acc;
+    }
+};
+template <> struct Slice8<float> {
+    f32x4_t x, y;
+    __device__ __forceinline__ void load(const void* p, int64_t i) {
+        const f32x4_t* s = reinterpret_cast<const f32x4_t*>(static_cast<const float*>(p) + i);
+        x = s[0];
+        y = s[1];
+    }
+    __device__ __forceinline__ void zero() { x = y = f32x4_t{0.f, 0.f, 0.f, 0.f}; }
+    __device__ __forceinline__ float dot(const Slice8& o, float acc) const {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc = fmaf(x[j], o.x[j], acc);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc = fmaf(y[j], o.y[j], acc);
+        return acc;
+    }
+};
+
 template <int K, int V, typename IO, typename ST, bool EPI>
 __global__ __launch_bounds__(kKdaThreads) void kda_decode_kernel(const KdaArgs a) {
     constexpr int EPL = K / 16;                                  // key channels per lane
@@ -38,7 +75,9 @@ __global__ __launch_bounds__(kKdaThreads) void kda_decode_kernel(const KdaArgs a
     constexpr int UNITS = EPL / VW;
     constexpr int SLOTS = V / 32;                                // rows per row group (32 row groups)
     constexpr int C = 2 * K + V;                                 // convolution channels of one head
-    static_assert(C + K <= kKdaThreads, "one thread per convolution channel and per decay");
+    static_assert(C <= kKdaThreads, "one thread per convolution channel");
+    constexpr int TPC = kKdaThreads / K;                         // threads per key channel of the gate
+    constexpr int GSLOTS = 4;                                    // 8-input slices per thread kept in registers
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -57,9 +96,8 @@ __global__ __launch_bounds__(kKdaThreads) void kda_decode_kernel(const KdaArgs a
     __shared__ float sb[2];                                      // beta
     __shared__ __align__(16) float so[EPI ? 2 : 1][EPI ? V : 1]; // outputs before the epilogue
 
-    // ---- this thread's front role ----
+    // ---- this thread's front roles ----
     const bool conv_thread = tid < C;
-    const bool gate_thread = tid >= C && tid < C + K;
     int64_t gchan = 0;                                           // global convolution channel
     const void* src = nullptr;                                   // raw input tensor of the channel
     int64_t src_row = 0, src_col = 0;                            // element (t * src_row + src_col)
@@ -84,9 +122,14 @@ __global__ __launch_bounds__(kKdaThreads) void kda_decode_kernel(const KdaArgs a
         for (int i = 0; i < W - 1; ++i) win[3 - (W - 1) + i] = Elem<IO>::load(a.conv_state, win_base + i);
         if (a.conv_bias) bias = Elem<IO>::load(a.conv_bias, gchan);
     }
-    const int gc = tid - C;                                      // key channel of a gate thread
+    const int gc = tid / TPC, gq = tid % TPC;                    // gate: key channel and share of it
     const float neg_exp_a_log = -exp_f32(a.A_log[h]);
-    const float dtb = gate_thread ? a.dt_bias[(int64_t)h * K + gc] : 0.f;
+    const float dtb = a.dt_bias[(int64_t)h * K + gc];
+    const int R = a.gate_rank;
+    const int64_t wrow = ((int64_t)h * K + gc) * R;
+    // this thread's slices of the projection row are (gq + i TPC) * 8 .. +7; up to GSLOTS of them are read
+    // per token with every load in flight together
+    const bool gate_short = R <= 8 * TPC * GSLOTS;
 
     // ---- state tile (all V rows of the head) through a buffer resource ----
     int cols[UNITS];
@@ -109,26 +152,42 @@ __global__ __launch_bounds__(kKdaThreads) void kda_decode_kernel(const KdaArgs a
     for (int64_t t = bos; t < eos; ++t) {
         const int pb = (int)((t - bos) & 1);
         // ===== front =====
+        float x = 0.f;
+        if (conv_thread) x = Elem<IO>::load(src, t * src_row + src_col);
+        // raw = gate_weight[h K + c, :] . gate_in[t, :]: this thread's slices, then the channel's TPC lanes
+        float acc = 0.f;
+        if (gate_short) {
+            Slice8<IO> wv[GSLOTS], av[GSLOTS];
+#pragma unroll
+            for (int i = 0; i < GSLOTS; ++i) {
+                const int r = (gq + i * TPC) * 8;
+                if (r < R) {
+                    wv[i].load(a.gate_weight, wrow + r);
+                    av[i].load(a.gate_in, t * R + r);
+                } else {
+                    wv[i].zero();
+                    av[i].zero();
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < GSLOTS; ++i) acc = wv[i].dot(av[i], acc);
+        } else {
+            for (int r = gq * 8; r < R; r += 8 * TPC) {
+                Slice8<IO> wv, av;
+                wv.load(a.gate_weight, wrow + r);
+                av.load(a.gate_in, t * R + r);
+                acc = wv.dot(av, acc);
+            }
+        }
+#pragma unroll
+        for (int m = 1; m < TPC; m <<= 1) acc += __shfl_xor(acc, m);
+        if (gq == 0) sd[pb][gc] = exp_f32(gate_decay(acc, neg_exp_a_log, dtb));
         if (conv_thread) {
-            const float x = Elem<IO>::load(src, t * src_row + src_col);
             const float z = bias + taps[0] * win[0] + taps[1] * win[1] + taps[2] * win[2] + taps[3] * x;
             sx[pb][tid] = z * sigmoid_f32(z);
             win[0] = win[1];
             win[1] = win[2];
             win[2] = x;
-        } else if (gate_thread) {
-            // raw = gate_weight[h K + c, :] . gate_in[t, :], 8 elements per step
-            const int R = a.gate_rank;
-            const int64_t wrow = ((int64_t)h * K + gc) * R;
-            float acc = 0.f;
-            for (int r = 0; r < R; r += 8) {
-                float wv[8], av[8];
-                Vec<IO, 8>::load(a.gate_weight, wrow + r, wv);
-                Vec<IO, 8>::load(a.gate_in, t * R + r, av);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc = fmaf(wv[e], av[e], acc);
-            }
-            sd[pb][gc] = exp_f32(gate_decay(acc, neg_exp_a_log, dtb));
         }
         if (tid == 0) sb[pb] = sigmoid_f32(Elem<IO>::load(a.b, t * a.HV + h));
         __syncthreads();  // the token's front is in LDS

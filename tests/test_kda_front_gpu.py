@@ -118,6 +118,16 @@ def test_fp32_io_and_bf16_pool():
     _check(p, o, pool, conv)
 
 
+@pytest.mark.parametrize("K,V,R,io", [(128, 128, 200, "bf16"), (64, 64, 264, "bf16"), (128, 64, 136, "f32"),
+                                      (64, 128, 40, "f32")])
+def test_gate_ranks_past_and_inside_the_per_token_slices(K, V, R, io):
+    """Gate ranks beyond what one token's slice loads cover (the streaming form: 128 at K = 128, 256 at
+    K = 64) and a rank that ends inside a thread's slices, for both I/O types."""
+    p = inputs.kda_front_problem(545 + R, B=3, q_len=3, H=2, K=K, V=V, R=R, io_dtype=io, ragged=True)
+    o, pool, conv = _run(p)
+    _check(p, o, pool, conv)
+
+
 @pytest.mark.parametrize("B", [1, 16, 64])
 def test_decode_shapes_every_head(B):
     """32 heads, K=V=128, gate rank 128, width 4, epilogue on, one token per sequence."""
