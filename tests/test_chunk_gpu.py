@@ -137,6 +137,18 @@ def test_chunked_matches_recurrent_on_gpu_and_repeats_bitwise():
     assert max_rel_l2_states(f64(h1), f64(hr)) <= TOL["bf16"]
 
 
+def test_inputs_untouched_flow_and_per_key_gate():
+    """q, k, v, g, beta, cu_seqlens and the initial state are byte-identical after a call, on the flow
+    kernel (scalar gate, bf16, K = V = 128) and on the per-key-channel kernel."""
+    for per_k, seed in ((False, 75), (True, 76)):
+        p = inputs.dense_problem(seed, [150, 64, 3], HK=2, HV=4, K=128, V=128, io_dtype="bf16", per_k_gate=per_k)
+        d = problem_to_dev(p)
+        snap = {k: v.clone() for k, v in d.items()}
+        _chunk(p, d)
+        for k in d:
+            assert torch.equal(d[k], snap[k]), (per_k, k)
+
+
 def test_empty_sequences_and_no_initial_state():
     p = inputs.dense_problem(74, [0, 70, 0, 5], HK=2, HV=2, K=128, V=128, io_dtype="bf16")
     o, ht = _chunk(p)

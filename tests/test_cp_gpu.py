@@ -211,6 +211,22 @@ def test_kda_bf16_segmented_strong_decay_elementwise_diagonal():
     _run_and_check(p)
 
 
+def test_kda_paired_route_repeats_bitwise_and_leaves_inputs_untouched():
+    """The paired offset/map run, the scan and the outputs run: two calls give the same bytes, and q,
+    k, v, g, beta, cu_seqlens and the initial state are byte-identical afterwards."""
+    p = inputs.dense_problem(96, [64 * 40 + 11, 64 * 30], HK=2, HV=2, K=128, V=128, io_dtype="bf16",
+                             g_range=(-2.0, 0.0), g_endpoints=0.25, per_k_gate=True, beta_mode="mixed")
+    d = problem_to_dev(p)
+    snap = {k: v.clone() for k, v in d.items()}
+    ws = torch.empty(gdr.gdr_chunk_workspace_size(d["q"], d["v"], d["g"], p.N), dtype=torch.uint8, device="cuda")
+    runs = [gdr.gdr_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], p.scale, d["h0"], workspace=ws)
+            for _ in range(2)]
+    torch.cuda.synchronize()
+    assert torch.equal(runs[0][0], runs[1][0]) and torch.equal(runs[0][1], runs[1][1])
+    for k in d:
+        assert torch.equal(d[k], snap[k]), k
+
+
 def test_fp32_k128_long_sequence():
     p = inputs.dense_problem(90, [64 * 70 + 11], HK=1, HV=2, K=128, V=128, io_dtype="f32", g_range=(-0.5, 0.0))
     _run_and_check(p)

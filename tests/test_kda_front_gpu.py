@@ -1,7 +1,7 @@
 """Fused KDA decode front on the GPU (gdr_kda_decode_fused) against the fp64 oracle of
 oracle/kda_front.py composed with the recurrence oracle: outputs per (sequence, head) at the
 stated tolerance, committed states, and the convolution windows bit for bit (they hold raw
-inputs); untouched slots, windows and padded o rows keep their bytes."""
+inputs); untouched slots, windows and padded o rows keep their bytes, and so do the read-only inputs."""
 import numpy as np
 import pytest
 import torch
@@ -33,6 +33,13 @@ def _run(p, commit=True):
                              conv_bias=opt["conv_bias"], l2norm_eps=p.l2_eps, norm_weight=opt["norm_weight"],
                              norm_gate=opt["norm_gate"], norm_eps=p.norm_eps, o=o)
     torch.cuda.synchronize()
+    # the read-only inputs keep their bytes
+    for n in ("q", "k", "v", "conv_weight", "gate_in", "gate_weight", "A_log", "dt_bias", "b", "state_indices"):
+        assert np.array_equal(to_host(d[n]), np.ascontiguousarray(getattr(p, n))), f"input {n} changed"
+    for n, t in opt.items():
+        if t is not None:
+            assert np.array_equal(to_host(t), np.ascontiguousarray(getattr(p, n))), f"input {n} changed"
+    assert np.array_equal(to_host(cu), p.cu_seqlens.astype(np.int32)), "cu_seqlens changed"
     return o, d["pool"], d["conv_state"]
 
 
