@@ -338,8 +338,8 @@ gdr_status chunk_fwd_impl(const gdr_problem* p, const void* q, const void* k, co
     float* Bs = reinterpret_cast<float*>(ws + pl.B);
     float* Ms = reinterpret_cast<float*>(ws + pl.M);
     float* Ss = reinterpret_cast<float*>(ws + pl.S);
-    // the per-channel gate with K = V forms B_s and M_s in one paired run, M_s from an identity it holds itself
-    const bool paired = per_k && p->io_dtype == GDR_BF16 && p->head_dim_k == p->head_dim_v;
+    // bf16 with K = V forms B_s and M_s in one paired run, M_s from an identity it holds itself
+    const bool paired = p->io_dtype == GDR_BF16 && p->head_dim_k == p->head_dim_v;
     hipError_t e = gdr::launch_cp_setup(pl, ws, cu_seqlens, p->total_tokens, p->num_v_heads, p->head_dim_k, !paired,
                                         stream);
     if (e != hipSuccess) return status_of(e);

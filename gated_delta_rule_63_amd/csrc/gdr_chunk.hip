@@ -819,7 +819,7 @@ struct OStage {
 // products well inside the fp32 / bf16 exponent range.
 constexpr float kKdaDiagRange = 64.0f;
 
-// With MAP (per-channel gate, bf16, K = V; the segmented route), one run forms both end-of-segment
+// With MAP (bf16, K = V, either gate; the segmented route), one run forms both end-of-segment
 // quantities of a (segment, head): the state reached from h0 with the inputs (ht) and the linear part
 // of the segment's map, the state reached from the identity with v = 0 (map [N, HV, K, K]).  Wave w
 // holds value columns 16w .. 16w+15 of the first and rows 16w .. 16w+15 of the second; the two share
@@ -829,7 +829,7 @@ template <int K, int BV, typename IO, typename MT, bool PER_K, bool MAP = false>
 __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) {
     constexpr int NW = BV / 16;       // waves; wave w owns value columns 16w .. 16w+15 of the tile
     constexpr int NTHR = 64 * NW;
-    static_assert(!MAP || (PER_K && K == BV && sizeof(typename MM<MT>::S) == 2), "paired run: per-K gate, K = V, bf16");
+    static_assert(!MAP || (K == BV && sizeof(typename MM<MT>::S) == 2), "paired run: K = V, bf16");
     constexpr int KT = K / 16;
     typedef MM<MT> M;
     typedef typename M::S S;
@@ -1106,8 +1106,11 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
             auto pair = [&](int I, int J, f32x4_t& cl, f32x4_t& cp) {
                 cl = f32x4_t{0.f, 0.f, 0.f, 0.f};
                 cp = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                M::template nt2<K>(cl, sK + 16 * I * LDK, sK + 16 * J * LDK, cp, sQ + 16 * I * LDK, sK + 16 * J * LDK,
-                                   LDK);
+                if (want_o)
+                    M::template nt2<K>(cl, sK + 16 * I * LDK, sK + 16 * J * LDK, cp, sQ + 16 * I * LDK,
+                                       sK + 16 * J * LDK, LDK);
+                else  // P only feeds the output
+                    M::nt(cl, sK + 16 * I * LDK, LDK, sK + 16 * J * LDK, LDK, K);
             };
             auto store_p_diag = [&](int I, const f32x4_t& acc) {  // element-wise decay, masked
                 const f32x4_t gr = *reinterpret_cast<const f32x4_t*>(sg + 16 * I + 4 * g4);
@@ -1129,7 +1132,7 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
                     const int r = 16 * I + 4 * g4 + e, j = 16 * J + lr;
                     const float d = fa[e] * fb;
                     sLo[r * LDO + j] = M::cvt(-br[e] * d * cl[e]);
-                    sP[r * LDT + perm<MT>(j)] = M::cvt(d * cp[e]);
+                    if (want_o) sP[r * LDT + perm<MT>(j)] = M::cvt(d * cp[e]);
                 }
             };
             auto off_pair = [&](int q) {  // q-th of the pairs (1,0),(2,0),(2,1),(3,0),(3,1),(3,2)
@@ -1159,7 +1162,9 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
                     const float x = br[e] * exp_f32(gr[e] - gj) * cl[e];
                     sN[rr * LDN + lr] = (rr > lr) ? x : 0.0f;
                 }
-                if constexpr (NW == 4) store_p_diag(w, cp);
+                if constexpr (NW == 4) {
+                    if (want_o) store_p_diag(w, cp);
+                }
                 // the tile's LDS writes complete before this wave's lanes read other lanes' entries
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
                 invert_unit_lower_16<MT>(sN, sD + 16 * w * LDD, LDD);
@@ -1170,7 +1175,7 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
                     off_pair(w - 4);
                     if (w < 6) {
                         off_pair(w - 4 + 4);
-                    } else {  // waves 6 and 7: diagonal P tiles (I, I), I = 2 (w - 6), 2 (w - 6) + 1
+                    } else if (want_o) {  // waves 6 and 7: diagonal P tiles (I, I), I = 2 (w - 6), 2 (w - 6) + 1
                         const int I0 = 2 * (w - 6);
                         f32x4_t c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
                         M::template nt2<K>(c0, sQ + 16 * I0 * LDK, sK + 16 * I0 * LDK, c1, sQ + 16 * (I0 + 1) * LDK,
@@ -1493,16 +1498,56 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
             for (int i = 0; i < 4; ++i) nm[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             gemm_regs_2b<MT, K, 4>(nu, hs, nm, hm, sW, LDK);
             if (ci + 1 < nc) load_vgb(ci + 1);
-            const float* sgl = FP(Lay::k_gl);
+            if constexpr (PER_K) {
+                const float* sgl = FP(Lay::k_gl);
 #pragma unroll
-            for (int kt = 0; kt < KT; ++kt)
+                for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float d = sgl[16 * kt + 4 * g4 + e];
-                    hs[kt][e] *= d;
-                    hm[kt][e] *= d;
+                    for (int e = 0; e < 4; ++e) {
+                        const float d = sgl[16 * kt + 4 * g4 + e];
+                        hs[kt][e] *= d;
+                        hm[kt][e] *= d;
+                    }
+                gemm_regs_2b<MT, CH, KT>(hs, nu, hm, nm, SP(Lay::k_kdt), LDT);
+            } else {
+                // scalar gate: S <- e^{gamma_last} S + K^T (v_new * e^{gamma_last - gamma}), the K^T operand read
+                // from the row-major K rows with transposing reads, once for both states
+                static_assert(!MAP || TRK, "the paired scalar-gate run reads K^T from the row-major K rows");
+                const float dec = FP(Lay::g_eg)[CH - 1];
+#pragma unroll
+                for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        hs[kt][e] *= dec;
+                        hm[kt][e] *= dec;
+                    }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const f32x4_t f = *reinterpret_cast<const f32x4_t*>(FP(Lay::g_ed) + 16 * i + 4 * g4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        nu[i][e] *= f[e];
+                        nm[i][e] *= f[e];
+                    }
                 }
-            gemm_regs_2b<MT, CH, KT>(hs, nu, hm, nm, SP(Lay::k_kdt), LDT);
+#pragma unroll
+                for (int m = 0; m < CH / 32; ++m) {
+                    const bf16x8_t b0 = __builtin_bit_cast(bf16x8_t, uint4{pack_tile_lo(nu[2 * m]), pack_tile_hi(nu[2 * m]),
+                                                                          pack_tile_lo(nu[2 * m + 1]),
+                                                                          pack_tile_hi(nu[2 * m + 1])});
+                    const bf16x8_t b1 = __builtin_bit_cast(bf16x8_t, uint4{pack_tile_lo(nm[2 * m]), pack_tile_hi(nm[2 * m]),
+                                                                          pack_tile_lo(nm[2 * m + 1]),
+                                                                          pack_tile_hi(nm[2 * m + 1])});
+#pragma unroll
+                    for (int kt = 0; kt < KT; ++kt) {
+                        const uint2 lo = ld_tr4<true>(sK, LDK, 32 * m + 4 * g4, 16 * kt);
+                        const uint2 hi = ld_tr4<true>(sK, LDK, 32 * m + 16 + 4 * g4, 16 * kt);
+                        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, uint4{lo.x, lo.y, hi.x, hi.y});
+                        hs[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b0, hs[kt], 0, 0, 0);
+                        hm[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b1, hm[kt], 0, 0, 0);
+                    }
+                }
+            }
             __syncthreads();
             continue;
         }
@@ -2129,9 +2174,13 @@ template <int K, int V>
 hipError_t launch_kv(const ChunkArgs& a, int io, bool per_k, hipStream_t s) {
     if (a.map) {  // the paired offset/map run of the segmented route
         if constexpr (K == V) {
-            if (io == 1 && per_k) {
-                hipLaunchKernelGGL((chunk_fused_kernel<K, V, bf16_t, bf16_t, true, true>), dim3(1, a.HV, a.N),
-                                   dim3(4 * V), 0, s, a);
+            if (io == 1) {
+                if (per_k)
+                    hipLaunchKernelGGL((chunk_fused_kernel<K, V, bf16_t, bf16_t, true, true>), dim3(1, a.HV, a.N),
+                                       dim3(4 * V), 0, s, a);
+                else
+                    hipLaunchKernelGGL((chunk_fused_kernel<K, V, bf16_t, bf16_t, false, true>), dim3(1, a.HV, a.N),
+                                       dim3(4 * V), 0, s, a);
                 return hipGetLastError();
             }
         }

@@ -80,7 +80,7 @@ struct ChunkArgs {
     const float* h0;             // [N, HV, V, K] or NULL (zeros)
     void* o;                     // NULL: outputs not written
     float* ht;                   // [N, HV, V, K] or NULL; may equal h0 (each thread reads its part first)
-    // non-NULL selects the paired run of the segmented route (per-channel gate, bf16, K = V): besides
+    // non-NULL selects the paired run of the segmented route (bf16, K = V, either gate): besides
     // ht, map [N, HV, K, K] receives the end state from the identity with v = 0; q and o are unused
     float* map;
     int64_t T;
