@@ -309,7 +309,8 @@ def _leg_kernel_specs():
                 ("chunk_fused_kernel<128, 128, gdr::bf16_t, gdr::bf16_t, true, false>", None, 1),
                 ("cp_scan_kernel<128>", 256 * (pk.V // 16) * pk.HV * pk.N, 1), ("cp_setup_kernel", 256, 1),
                 ("cp_final_kernel", 256 * 256 * pk.N, 1)],
-        "cp_segmented": [(flow, None, 3), ("cp_scan_kernel<128>", None, 1), ("cp_setup_kernel", None, 1),
+        "cp_segmented": [("chunk_fused_kernel<128, 128, gdr::bf16_t, gdr::bf16_t, false, true>", None, 1),
+                         (flow, None, 1), ("cp_scan_kernel<128>", None, 1), ("cp_setup_kernel", None, 1),
                          ("cp_final_kernel", None, 1)],
         "cp_direct": [(flow, 512 * pc.HV * pc.N, 1)],
     }
@@ -765,8 +766,8 @@ def main():
                                      "(1 x 65573 tokens, 16 heads; bytes, time and traffic per call)",
                            "bytes": _alg_bytes_prefill(pk, with_cu=False), "flops": None, "secs": extra_ms["kda"] / 1e3,
                            "sources": ["gdr_chunk.hip", "gdr_device.h", "gdr_cp.hip", "gdr_api.hip"]}
-    for leg, route in (("cp_segmented", "segmented route: setup, chunk_flow_kernel x3 (offsets, maps, outputs), scan, "
-                                         "final-state copy"),
+    for leg, route in (("cp_segmented", "segmented route: setup, paired offset/map run (chunk_fused_kernel), scan, "
+                                         "outputs run (chunk_flow_kernel), final-state copy"),
                        ("cp_direct", "single pass: one chunk_flow_kernel launch, one workgroup per (sequence, head)")):
         if leg in extra_ms:
             leg_info[leg] = {"kernel": f"{route} (4 x 16384 tokens, 16 heads, K=V=128, bf16; per call)",
