@@ -232,13 +232,13 @@ __device__ __forceinline__ uint32_t pack_tile_hi(const f32x4_t& t) { return pack
 // 32m + 4*(l/16) + e (e < 4) or 32m + 16 + 4*(l/16) + e - 4 (e >= 4) -- one 16-byte read of a
 // perm()-ordered A row; for an fp32 step (t, e) position l/16 is index 16t + 4*(l/16) + e.
 // With LOWER, A is lower triangular (A[r][j] = 0 for j > r): reduction steps entirely above the
-// diagonal of a 16-row tile are skipped.  GMAX k-steps of A reads are issued together, before
-// their products (GMAX = 1 where registers are short).
-template <typename MT, int NP, int NI, bool LOWER = false, int GMAX = 2>
+// diagonal of a 16-row tile are skipped.  The A reads of two k-steps are issued together, before
+// their products.
+template <typename MT, int NP, int NI, bool LOWER = false>
 __device__ __forceinline__ void gemm_regs(f32x4_t* acc, const typename MM<MT>::S* sA, int lda, const f32x4_t* Bt) {
     const int l = threadIdx.x & 63, g4 = l >> 4, lr = l & 15;
     if constexpr (sizeof(typename MM<MT>::S) == 2) {
-        constexpr int MS = NP / 32, G = MS < GMAX ? MS : GMAX;
+        constexpr int MS = NP / 32, G = MS < 2 ? MS : 2;
 #pragma unroll
         for (int m0 = 0; m0 < MS; m0 += G) {
             bf16x8_t av[G][NI];
