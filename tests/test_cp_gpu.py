@@ -211,6 +211,18 @@ def test_kda_bf16_segmented_strong_decay_elementwise_diagonal():
     _run_and_check(p)
 
 
+@pytest.mark.parametrize("K,V,HK,HV", [(64, 64, 1, 2), (128, 64, 2, 2), (64, 128, 1, 1)])
+def test_gdn_bf16_segmented_shapes(K, V, HK, HV):
+    """Scalar gate, bf16, two sequences on the segmented route: the paired run on the four-wave kernel at
+    K = V = 64, two separate runs at K != V; the single-pass route agrees."""
+    p = inputs.dense_problem(97 + K + V, [64 * 61 + 21, 64 * 40], HK=HK, HV=HV, K=K, V=V, io_dtype="bf16",
+                             g_range=(-1.0, 0.0), g_endpoints=0.25)
+    o, ht = _run_and_check(p)
+    o2, ht2 = _direct(p)
+    assert max_rel_l2_tokens(f64(o), f64(o2), p.cu_seqlens) <= TOL["bf16"]
+    assert max_rel_l2_states(f64(ht), f64(ht2)) <= TOL["bf16"]
+
+
 def test_kda_paired_route_repeats_bitwise_and_leaves_inputs_untouched():
     """The paired offset/map run, the scan and the outputs run: two calls give the same bytes, and q,
     k, v, g, beta, cu_seqlens and the initial state are byte-identical afterwards."""
