@@ -289,7 +289,8 @@ def _stats(ms):
 
 # Kernels each leg launches per call: (name fragment, grid size in work-items or None, dispatches per
 # call).  A leg's dispatches are told apart from another leg's launches of the same kernel by the
-# grid; a spec without a grid takes every dispatch of that name that no gridded spec claimed.
+# grid; a spec without a grid takes every dispatch of that name that no gridded spec claimed (two
+# such specs share them: the segment-setup kernel has one block in both segmented legs).
 _VERIFY_K = "recurrent_kernel<128, gdr::bf16_t, gdr::bf16_t, gdr::bf16_t, gdr::bf16_t, false, 4, true, 0>"
 
 
@@ -307,7 +308,7 @@ def _leg_kernel_specs():
         "verify_prepass": [("gating_prepass_kernel<128, gdr::bf16_t>", None, 1), (_VERIFY_K, None, 1)],
         "kda": [("chunk_fused_kernel<128, 128, gdr::bf16_t, gdr::bf16_t, true, true>", None, 1),
                 ("chunk_fused_kernel<128, 128, gdr::bf16_t, gdr::bf16_t, true, false>", None, 1),
-                ("cp_scan_kernel<128>", 256 * (pk.V // 16) * pk.HV * pk.N, 1), ("cp_setup_kernel", 256, 1),
+                ("cp_scan_kernel<128>", 256 * (pk.V // 16) * pk.HV * pk.N, 1), ("cp_setup_kernel", None, 1),
                 ("cp_final_kernel", 256 * 256 * pk.N, 1)],
         "cp_segmented": [("chunk_fused_kernel<128, 128, gdr::bf16_t, gdr::bf16_t, false, true>", None, 1),
                          (flow, None, 1), ("cp_scan_kernel<128>", None, 1), ("cp_setup_kernel", None, 1),
