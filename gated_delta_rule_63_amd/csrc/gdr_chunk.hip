@@ -671,15 +671,10 @@ __device__ __forceinline__ void block_solve(f32x4_t (*X)[4], const typename MM<M
     }
 }
 
-// The 6 strictly lower (I, J) tiles of a 64x64 matrix: (1,0),(2,0),(2,1),(3,0),(3,1),(3,2);
-// and the 10 lower tiles incl. the diagonal: (0,0),(1,0),(1,1),(2,0),...
+// The 6 strictly lower (I, J) tiles of a 64x64 matrix: (1,0),(2,0),(2,1),(3,0),(3,1),(3,2).
 __device__ __forceinline__ void strict_tile(int t, int& I, int& J) {
     I = t >= 3 ? 3 : t >= 1 ? 2 : 1;
     J = t - I * (I - 1) / 2;
-}
-__device__ __forceinline__ void lower_tile(int t, int& I, int& J) {
-    I = t >= 6 ? 3 : t >= 3 ? 2 : t >= 1 ? 1 : 0;
-    J = t - I * (I + 1) / 2;
 }
 
 // Store the 8 consecutive logical columns c8 .. c8+7 of a row into a perm()-ordered LDS row.
