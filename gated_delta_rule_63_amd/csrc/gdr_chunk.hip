@@ -1654,13 +1654,14 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
 // 16x16x16 per wave over four block rows.  Every iteration has two workgroup barriers:
 //
 //            waves 0-3 (state, 32 columns each)              waves 4-7 (prep)
-//   phase X  E1(c-1): Y = K S^T and S Q^T from one packing   L(c) and the four diagonal inverses;
-//            of the state, R, v_new, the state update        loads of chunk c + 2 into registers
+//   phase X  E1(c-1): Y = K S^T and S Q^T from one packing   loads of chunk c + 2 into registers;
+//            of the state, R, v_new, the state update        L(c) and the four diagonal inverses
 //   phase Y  E2(c-1): the P v_new part of the output and     chunk c + 1 from registers into LDS,
 //            its stores; the ten P tiles of chunk c          its gate tables
 //
 // Q, K, V, -L, the inverses, P and the gate tables are double-buffered, and the prep waves keep two
-// register sets of raw rows, so a chunk's loads are in flight for a whole iteration.  L and P tiles
+// register sets of raw rows, so a chunk's loads are in flight for three phases (issued at the start
+// of phase X two iterations ahead, written to LDS in the phase Y of the iteration before its use).  L and P tiles
 // are formed transposed (K_J K_I^T, K_J Q_I^T), so that each lane holds four consecutive columns of
 // one row and writes them with one 8-byte store.  The output scale is folded into the e^gamma table
 // and into P.
@@ -2077,10 +2078,13 @@ __global__ __launch_bounds__(512) void chunk_flow_kernel(const ChunkArgs a) {
                 tb[L::t_fb + l] = exp_f32(rj - x);
             }
         };
-        // phase X of iteration it: L of chunk it (transposed products K_J K_I^T), the diagonal inverses,
-        // the P tiles of chunk it, then the loads of chunk it + 2
+        // phase X of iteration it: the loads of chunk it + 2 first (their register set was written to LDS
+        // in the previous phase, and issuing them before the tile work gives them one more phase to
+        // arrive: with one phase less, the memory latency of a few heads delayed their staging and set
+        // the kernel's end), then L of chunk it (transposed products K_J K_I^T) and the diagonal inverses
         auto phase_x = [&](int it, Regs& nxt) {
             const int b1 = it & 1;
+            if (it + 2 < nc) load(it + 2, nxt);
             if (it < nc) {
                 const S* sK1 = SP(L::k0 + b1 * L::ROWK);
                 S* const sLo1 = SP(L::lo + b1 * L::ROWO);
@@ -2126,7 +2130,6 @@ __global__ __launch_bounds__(512) void chunk_flow_kernel(const ChunkArgs a) {
                     store_off(u + 4, c1);
                 }
             }
-            if (it + 2 < nc) load(it + 2, nxt);
             __syncthreads();  // end of phase X
         };
         // phase Y of iteration it: chunk it + 1 from registers into LDS
