@@ -1660,8 +1660,8 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
 //            its stores; the ten P tiles of chunk c          its gate tables
 //
 // Q, K, V, -L, the inverses, P and the gate tables are double-buffered, and the prep waves keep two
-// register sets of raw rows, so a chunk's loads are in flight for three phases (issued at the start
-// of phase X two iterations ahead, written to LDS in the phase Y of the iteration before its use).  L and P tiles
+// register sets of raw rows, so a chunk's loads are in flight for about three phases (issued during
+// phase X two iterations ahead, written to LDS in the phase Y of the iteration before its use).  L and P tiles
 // are formed transposed (K_J K_I^T, K_J Q_I^T), so that each lane holds four consecutive columns of
 // one row and writes them with one 8-byte store.  The output scale is folded into the e^gamma table
 // and into P.
@@ -1996,14 +1996,18 @@ __global__ __launch_bounds__(512) void chunk_flow_kernel(const ChunkArgs a) {
         float sig = 1.0f;
         constexpr int ESZ = 2;
         const int qk_row = a.HK * K * ESZ, v_row = a.HV * a.V * ESZ;
-        auto load = [&](int ci, Regs& r) {  // global -> registers: chunk ci
+        // global -> registers: the parts of chunk ci named in `part` (q: 1, k: 2, v with g and beta: 4)
+        auto load = [&](int ci, Regs& r, int part) {
             const int64_t bos = s0 + (int64_t)CH * ci;
             const int len = chunk_len(ci);
+            if (part & 1) {
             // without outputs q reads as zeros (a zero-byte range): it only feeds P and the output
             const __amdgpu_buffer_rsrc_t rq = chunk_rsrc(
                 want_o ? static_cast<const char*>(a.q) + ((bos * a.HK + hk) * K) * ESZ : nullptr, want_o ? len : 0, qk_row);
 #pragma unroll
             for (int i = 0; i < TQ::NV; ++i) r.qn[i].load(rq, TQ::row(lt, i) * qk_row + TQ::col(lt) * ESZ);
+            }
+            if (part & 2) {
             const __amdgpu_buffer_rsrc_t rk =
                 chunk_rsrc(static_cast<const char*>(a.k) + ((bos * a.HK + hk) * K) * ESZ, len, qk_row);
 #pragma unroll
@@ -2011,6 +2015,8 @@ __global__ __launch_bounds__(512) void chunk_flow_kernel(const ChunkArgs a) {
 #pragma unroll
                 for (int q = 0; q < 2; ++q)
                     r.kn[2 * i + q].load(rk, (2 * PK::pair(lt, i) + q) * qk_row + PK::col(lt, i) * ESZ);
+            }
+            if (part & 4) {
             // v == NULL reads as zeros (a zero-byte range): the run that forms a segment's linear map
             const __amdgpu_buffer_rsrc_t rv = chunk_rsrc(
                 a.v ? static_cast<const char*>(a.v) + ((bos * a.HV + h) * a.V) * ESZ : nullptr, a.v ? len : 0, v_row);
@@ -2025,6 +2031,7 @@ __global__ __launch_bounds__(512) void chunk_flow_kernel(const ChunkArgs a) {
                 const __amdgpu_buffer_rsrc_t rbt =
                     chunk_rsrc(static_cast<const char*>(a.beta) + (bos * a.HV + h) * 2, len, a.HV * 2);
                 r.bn = __builtin_amdgcn_raw_buffer_load_b16(rbt, l * a.HV * 2, 0, 0);
+            }
             }
         };
         auto stage = [&](int b, const Regs& r) {  // registers -> LDS buffers b; wave 4 forms the gate tables
@@ -2078,13 +2085,15 @@ __global__ __launch_bounds__(512) void chunk_flow_kernel(const ChunkArgs a) {
                 tb[L::t_fb + l] = exp_f32(rj - x);
             }
         };
-        // phase X of iteration it: the loads of chunk it + 2 first (their register set was written to LDS
-        // in the previous phase, and issuing them before the tile work gives them one more phase to
-        // arrive: with one phase less, the memory latency of a few heads delayed their staging and set
-        // the kernel's end), then L of chunk it (transposed products K_J K_I^T) and the diagonal inverses
+        // phase X of iteration it: L of chunk it (transposed products K_J K_I^T) and the diagonal inverses,
+        // with the loads of chunk it + 2 into the register set written to LDS in the previous phase: q and
+        // k before the tile work, v, g and beta after the inverses.  Issued at the end of the phase, the
+        // loads left too little time on the heads whose rows sit where memory answers slowest, and those
+        // heads set the kernel's end; issued all at once at the start, they stalled the wave behind the
+        // memory queue.  Split, no head lags.
         auto phase_x = [&](int it, Regs& nxt) {
             const int b1 = it & 1;
-            if (it + 2 < nc) load(it + 2, nxt);
+            if (it + 2 < nc) load(it + 2, nxt, 1 | 2);
             if (it < nc) {
                 const S* sK1 = SP(L::k0 + b1 * L::ROWK);
                 S* const sLo1 = SP(L::lo + b1 * L::ROWO);
@@ -2121,6 +2130,7 @@ __global__ __launch_bounds__(512) void chunk_flow_kernel(const ChunkArgs a) {
                 // the tile's LDS writes complete before this wave's lanes read other lanes' entries
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
                 invert_unit_lower_16<bf16_t>(sN, sD1 + 16 * u * LDD, LDD);
+                if (it + 2 < nc) load(it + 2, nxt, 4);
                 store_off(u, c0);
                 if (u < 2) {
                     int I1, J1;
@@ -2138,10 +2148,10 @@ __global__ __launch_bounds__(512) void chunk_flow_kernel(const ChunkArgs a) {
             __syncthreads();  // end of phase Y
         };
         if (nc > 0) {
-            load(0, ra);
+            load(0, ra, 7);
             stage(0, ra);
         }
-        if (nc > 1) load(1, rb);
+        if (nc > 1) load(1, rb, 7);
         __syncthreads();  // prologue
         // chunk c lives in register set ra for even c, rb for odd c
         for (int it = 0; it <= nc; it += 2) {
