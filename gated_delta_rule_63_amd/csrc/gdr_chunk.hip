@@ -1655,9 +1655,10 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
 //
 //            waves 0-3 (state, 32 columns each)              waves 4-7 (prep)
 //   phase X  E1(c-1): Y = K S^T and S Q^T from one packing   loads of chunk c + 2 into registers;
-//            of the state, R, v_new, the state update        L(c) and the four diagonal inverses
+//            of the state, R, v_new, the state update        L(c), the four diagonal inverses and
+//                                                            the four diagonal P tiles of chunk c
 //   phase Y  E2(c-1): the P v_new part of the output and     chunk c + 1 from registers into LDS,
-//            its stores; the ten P tiles of chunk c          its gate tables
+//            its stores; the six off-diagonal P tiles of c   its gate tables
 //
 // Q, K, V, -L, the inverses, P and the gate tables are double-buffered, and the prep waves keep two
 // register sets of raw rows, so a chunk's loads are in flight for about three phases (issued during
@@ -1918,7 +1919,8 @@ __global__ __launch_bounds__(512) void chunk_flow_kernel(const ChunkArgs a) {
                 }
             }
             if (it < nc && want_o) {
-                // P tiles of chunk it, transposed products K_J Q_I^T: lane (g, i) holds P[16I + lane%16][16J + 4g + e]
+                // the six off-diagonal P tiles of chunk it (the prep waves form the diagonal ones), transposed
+                // products K_J Q_I^T: lane (g, i) holds P[16I + lane%16][16J + 4g + e]
                 const S* sQ1 = SP(L::q0 + b1 * L::ROWK);
                 const S* sK1 = SP(L::k0 + b1 * L::ROWK);
                 S* const sP1 = SP(L::p0 + b1 * L::ROWT);
@@ -1935,22 +1937,8 @@ __global__ __launch_bounds__(512) void chunk_flow_kernel(const ChunkArgs a) {
                 };
                 int I0, J0;
                 strict_tile(w, I0, J0);
-                f32x4_t cd = {0.f, 0.f, 0.f, 0.f}, c0 = {0.f, 0.f, 0.f, 0.f};
-                M::template nt2<K>(cd, sK1 + 16 * w * LDK, sQ1 + 16 * w * LDK, c0, sK1 + 16 * J0 * LDK, sQ1 + 16 * I0 * LDK,
-                                   LDK);
-                {
-                    const int r = 16 * w + lr;
-                    const float gr = tb1[L::t_g + r];
-                    const f32x4_t gj = *reinterpret_cast<const f32x4_t*>(tb1 + L::t_g + 16 * w + 4 * g4);
-                    float x[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float v = exp_f32(gr - gj[e]) * cd[e] * a.scale;  // inf above the diagonal is discarded
-                        x[e] = (lr >= 4 * g4 + e) ? v : 0.0f;
-                    }
-                    *reinterpret_cast<uint2*>(sP1 + r * LDT + perm<bf16_t>(16 * w + 4 * g4)) =
-                        uint2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
-                }
+                f32x4_t c0 = {0.f, 0.f, 0.f, 0.f};
+                M::nt(c0, sK1 + 16 * J0 * LDK, LDK, sQ1 + 16 * I0 * LDK, LDK, K);
                 store_off(w, c0);
                 if (w < 2) {
                     int I1, J1;
@@ -2085,12 +2073,13 @@ __global__ __launch_bounds__(512) void chunk_flow_kernel(const ChunkArgs a) {
                 tb[L::t_fb + l] = exp_f32(rj - x);
             }
         };
-        // phase X of iteration it: L of chunk it (transposed products K_J K_I^T) and the diagonal inverses,
-        // with the loads of chunk it + 2 into the register set written to LDS in the previous phase: q and
-        // k before the tile work, v, g and beta after the inverses.  Issued at the end of the phase, the
-        // loads left too little time on the heads whose rows sit where memory answers slowest, and those
-        // heads set the kernel's end; issued all at once at the start, they stalled the wave behind the
-        // memory queue.  Split, no head lags.
+        // phase X of iteration it: L of chunk it (transposed products K_J K_I^T), the diagonal inverses and
+        // the diagonal P tiles (taken off the state waves, whose phase Y bounded the iteration), with the
+        // loads of chunk it + 2 into the register set written to LDS in the previous phase: q and k before
+        // the tile work, v, g and beta after the inverses.  Issued at the end of the phase, the loads left
+        // too little time on the heads whose rows sit where memory answers slowest, and those heads set
+        // the kernel's end; issued all at once at the start, they stalled the wave behind the memory
+        // queue.  Split, no head lags.
         auto phase_x = [&](int it, Regs& nxt) {
             const int b1 = it & 1;
             if (it + 2 < nc) load(it + 2, nxt, 1 | 2);
@@ -2114,6 +2103,10 @@ __global__ __launch_bounds__(512) void chunk_flow_kernel(const ChunkArgs a) {
                 f32x4_t cd = {0.f, 0.f, 0.f, 0.f}, c0 = {0.f, 0.f, 0.f, 0.f};
                 M::template nt2<K>(cd, sK1 + 16 * u * LDK, sK1 + 16 * u * LDK, c0, sK1 + 16 * J0 * LDK, sK1 + 16 * I0 * LDK,
                                    LDK);
+                const S* sQ1 = SP(L::q0 + b1 * L::ROWK);
+                S* const sP1 = SP(L::p0 + b1 * L::ROWT);
+                f32x4_t cq = {0.f, 0.f, 0.f, 0.f};  // the diagonal P tile, K_u Q_u^T
+                M::nt(cq, sK1 + 16 * u * LDK, LDK, sQ1 + 16 * u * LDK, LDK, K);
                 float* sN = sLd + u * 16 * LDN;
                 {
                     const int r = 16 * u + lr;
@@ -2138,6 +2131,19 @@ __global__ __launch_bounds__(512) void chunk_flow_kernel(const ChunkArgs a) {
                     f32x4_t c1 = {0.f, 0.f, 0.f, 0.f};
                     M::nt(c1, sK1 + 16 * J1 * LDK, LDK, sK1 + 16 * I1 * LDK, LDK, K);
                     store_off(u + 4, c1);
+                }
+                {   // the diagonal P tile of chunk it: scale e^{gamma_r - gamma_t} k_t . q_r, r >= t
+                    const int r = 16 * u + lr;
+                    const float gr = tb1[L::t_g + r];
+                    const f32x4_t gj = *reinterpret_cast<const f32x4_t*>(tb1 + L::t_g + 16 * u + 4 * g4);
+                    float x[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float v = exp_f32(gr - gj[e]) * cq[e] * a.scale;  // inf above the diagonal is discarded
+                        x[e] = (lr >= 4 * g4 + e) ? v : 0.0f;
+                    }
+                    *reinterpret_cast<uint2*>(sP1 + r * LDT + perm<bf16_t>(16 * u + 4 * g4)) =
+                        uint2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
                 }
             }
             __syncthreads();  // end of phase X
