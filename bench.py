@@ -35,6 +35,12 @@ Summaries (host only, no GPU): ``--summarize-counters FETCH_DIR WRITE_DIR`` turn
 passes' CSV output into profiles/hbm_traffic.md (bytes per launch per leg, and the records this
 script reads back), ``--summarize-trace TRACE_DIR PROFILED_LOG PLAIN_LOG`` turns a kernel trace of a
 bench run into profiles/bench_kernel_trace.md.
+
+Clock counters (GPU): ``--flow-stamps [SEQ HEAD]`` runs the prefill workload on libgdr_stamps.so (the
+flow kernel with shader-clock counters compiled in) and writes profiles/prefill_flow_stamps.md: the
+cycles of each phase of the two wave roles per chunk, for the workgroup of sequence SEQ and head HEAD
+(default 0 0: the longest sequence), and every workgroup's cycles and clock from entry to its last
+chunk.
 """
 from __future__ import annotations
 
@@ -432,6 +438,103 @@ Records read by bench.py (`traffic` is reported only while the sha256 of the leg
     print(out)
 
 
+def _flow_stamps(seq: int, head: int, reps: int = 6):
+    """Clock counters of chunk_flow_kernel on the prefill workload (measurement build); writes
+    profiles/prefill_flow_stamps.md."""
+    import ctypes
+    import torch
+    from gated_delta_rule_63_amd import gdr, inputs
+
+    gdr.use_library(os.path.join(_HERE, "gated_delta_rule_63_amd", "libgdr_stamps.so"))
+    L = gdr.lib()
+    L.gdr_dbg_flow_target.restype = ctypes.c_int
+    L.gdr_dbg_flow_target.argtypes = [ctypes.c_int, ctypes.c_int]
+    L.gdr_dbg_flow_stamps.restype = ctypes.c_int
+    L.gdr_dbg_flow_stamps.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+
+    def to_dev(x):
+        x = np.ascontiguousarray(x)
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(x).to(dev)
+
+    pp = inputs.prefill()
+    P = {k: to_dev(getattr(pp, k)) for k in ("q", "k", "v", "g", "beta")}
+    cu, h0 = to_dev(pp.cu_seqlens.astype(np.int32)), to_dev(pp.initial_state)
+    o = torch.empty((pp.T, pp.HV, pp.V), dtype=torch.bfloat16, device=dev)
+    ht = torch.empty((pp.N, pp.HV, pp.V, pp.K), dtype=torch.float32, device=dev)
+    flush = torch.ones((512 << 20) // 4, dtype=torch.float32, device=dev)
+    assert L.gdr_dbg_flow_target(seq, head) == 0
+    st = np.zeros((2, 128, 8), dtype=np.uint64)
+    wg = np.zeros((8, 32, 4), dtype=np.uint64)
+    ms = []
+    for _ in range(reps):  # the last launch is read; each starts from a clean cache, as in the bench
+        flush.sum()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        gdr.gdr_chunk_fwd(P["q"], P["k"], P["v"], P["g"], P["beta"], cu, pp.scale, h0, o=o, final_state=ht)
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    assert L.gdr_dbg_flow_stamps(ctypes.c_void_p(st.ctypes.data), ctypes.c_void_p(wg.ctypes.data)) == 0
+    s, w = st.astype(np.int64), wg.astype(np.int64)
+    lens = [int(x) for x in pp.lengths]
+    nc = (lens[seq] + 63) // 64
+    it = np.arange(1, nc + 1)
+    sl = it[(it >= 5) & (it <= nc - 5)]  # steady state: away from the first and last chunks
+    med = lambda x: float(np.median(x))
+    a, b = s[0], s[1]
+    rows = [
+        ("iteration", med(a[sl, 3] - a[sl - 1, 3]), med(b[sl, 3] - b[sl - 1, 3])),
+        ("phase X: work", med(a[sl, 0] - a[sl - 1, 3]), med(b[sl, 0] - b[sl - 1, 3])),
+        ("phase X: barrier wait", med(a[sl, 1] - a[sl, 0]), med(b[sl, 1] - b[sl, 0])),
+        ("phase Y: work", med(a[sl, 2] - a[sl, 1]), med(b[sl, 2] - b[sl, 1])),
+        ("phase Y: barrier wait", med(a[sl, 3] - a[sl, 2]), med(b[sl, 3] - b[sl, 2])),
+    ]
+    state_x = [("K S^T and S Q^T products", med(a[sl, 5] - a[sl - 1, 3])), ("R and the block solve", med(a[sl, 6] - a[sl, 5])),
+               ("output scaling, the state update", med(a[sl, 0] - a[sl, 6]))]
+    state_y = [("P v_new part of the output, its stores", med(a[sl, 4] - a[sl, 1])),
+               ("the off-diagonal P tiles", med(a[sl, 2] - a[sl, 4]))]
+    prep_x = [("q and k load issue", med(b[sl, 6] - b[sl, 5])),
+              ("L tiles, diagonal inverses, diagonal P tiles", med(b[sl, 4] - b[sl, 6])),
+              ("v, g, beta load issue", med(b[sl, 7] - b[sl, 4])), ("L stores, remaining L tiles, P stores", med(b[sl, 0] - b[sl, 7]))]
+    cyc = w[:, :, 2] - w[:, :, 0]
+    ns = (w[:, :, 3] - w[:, :, 1]) * 10.0  # the real-time clock counts at 100 MHz
+    t0 = w[:, :, 1].min()
+    end_us = (w[:, :, 3] - t0) * 10.0 / 1e3
+    cmd = "python3 bench.py --flow-stamps" + ("" if (seq, head) == (0, 0) else f" {seq} {head}")
+    out = ["# Clock counters of `chunk_flow_kernel<bf16>`, prefill workload, MI355X", "",
+           "```", cmd, "```", "",
+           f"The measurement build `libgdr_stamps.so` (the flow kernel compiled with `GDR_FLOW_STAMPS`: "
+           f"shader-clock reads at the phase boundaries and inside the phases, and each workgroup's entry "
+           f"and exit) runs the prefill workload {reps} times, each launch after a 512 MiB cache-flush "
+           f"read; the last launch is read. Launch times (HIP events): "
+           + ", ".join(f"{x:.3f}" for x in ms) + " ms.", "",
+           f"## Per chunk, workgroup of sequence {seq} ({lens[seq]} tokens, {nc} chunks), head {head}", "",
+           f"Medians over chunks 5 .. {nc - 5}, in shader-clock cycles. Waves 0 and 4 share a SIMD.", "",
+           "| | state waves (wave 0) | prep waves (wave 4) |", "|---|---|---|"]
+    out += [f"| {nm} | {x:.0f} | {y:.0f} |" for nm, x, y in rows]
+    out += ["", "Inside the phases:", "", "| role, phase | part | cycles |", "|---|---|---|"]
+    out += [f"| state, X | {nm} | {x:.0f} |" for nm, x in state_x]
+    out += [f"| state, Y | {nm} | {x:.0f} |" for nm, x in state_y]
+    out += [f"| prep, X | {nm} | {x:.0f} |" for nm, x in prep_x]
+    out += ["", "## Every workgroup: entry to the end of its last chunk", "",
+            "Cycles (shader clock), clock (cycles over the 100 MHz real-time clock) and end time after the "
+            "first workgroup's entry, over the heads of each sequence.", "",
+            "| sequence | tokens | chunks | cycles: min / median / max | clock GHz: median | end µs: median / max |",
+            "|---|---|---|---|---|---|"]
+    for n in range(min(pp.N, 8)):
+        c, g, e = cyc[n, :pp.HV], cyc[n, :pp.HV] / np.maximum(ns[n, :pp.HV], 1), end_us[n, :pp.HV]
+        out.append(f"| {n} | {lens[n]} | {(lens[n] + 63) // 64} | {c.min()} / {int(np.median(c))} / {c.max()} | "
+                   f"{np.median(g):.2f} | {np.median(e):.1f} / {e.max():.1f} |")
+    text = "\n".join(out) + "\n"
+    path = os.path.join(_HERE, "profiles", "prefill_flow_stamps.md")
+    with open(path, "w") as f:
+        f.write(text)
+    print(text)
+
+
 def _summarize_trace(trace_dir, profiled_log, plain_log):
     """profiles/bench_kernel_trace.md from a kernel trace of a bench run and two bench JSON lines."""
     import csv
@@ -516,7 +619,16 @@ def main():
                     help="host only: write profiles/hbm_traffic.md from the two counter passes and stop")
     ap.add_argument("--summarize-trace", nargs=3, metavar=("TRACE_DIR", "PROFILED_LOG", "PLAIN_LOG"),
                     help="host only: write profiles/bench_kernel_trace.md from a kernel trace of a bench run and stop")
+    ap.add_argument("--flow-stamps", nargs="*", type=int, metavar="SEQ_HEAD",
+                    help="GPU: per-phase clock counters of the prefill flow kernel (measurement build) into "
+                         "profiles/prefill_flow_stamps.md, for the workgroup of sequence SEQ and head HEAD "
+                         "(default 0 0), and stop")
     args = ap.parse_args()
+    if args.flow_stamps is not None:
+        if len(args.flow_stamps) not in (0, 2):
+            ap.error("--flow-stamps takes no value or SEQ HEAD")
+        _flow_stamps(*(args.flow_stamps or [0, 0]))
+        return
     if args.summarize_counters:
         _summarize_counters(*args.summarize_counters)
         return

@@ -3,9 +3,11 @@
     python -m gated_delta_rule_63_amd.build
 
 Each ``csrc/*.hip`` file is compiled to an object under ``_build/`` (in parallel),
-then linked into ``gated_delta_rule_63_amd/libgdr.so``.  The benchmark's MFMA-rate probe
-(``csrc/probe/mfma_peak.hip``) is built into ``libgdr_probe.so`` beside it.  Packed-fp32 instruction
-selection is switched off for every device compile.
+then linked into ``gated_delta_rule_63_amd/libgdr.so``.  Two measurement libraries are built beside
+it: the benchmark's MFMA-rate probe (``csrc/probe/mfma_peak.hip``) into ``libgdr_probe.so``, and
+``libgdr_stamps.so``, the same library with the flow kernel's clock counters compiled in
+(``GDR_FLOW_STAMPS``; read by ``bench.py --flow-stamps``).  Packed-fp32 instruction selection is
+switched off for every device compile.
 """
 from __future__ import annotations
 
@@ -24,6 +26,7 @@ LIB = os.path.join(PKG, "libgdr.so")
 # measurement probe (a dense-MFMA rate kernel for the benchmark), a library of its own
 PROBE_SRC = os.path.join(CSRC, "probe", "mfma_peak.hip")
 PROBE_LIB = os.path.join(PKG, "libgdr_probe.so")
+STAMPS_LIB = os.path.join(PKG, "libgdr_stamps.so")
 ARCH = "gfx950"
 
 COMMON = [
@@ -40,9 +43,9 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *COMMON, "-c", src, "-o", obj]
+def _compile(src: str, defines=(), suffix: str = "") -> str:
+    obj = os.path.join(BUILD, os.path.basename(src) + suffix + ".o")
+    cmd = [_hipcc(), *COMMON, *defines, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
@@ -53,8 +56,12 @@ def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     workers = min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
+    chunk = os.path.join(CSRC, "gdr_chunk.hip")
     with concurrent.futures.ThreadPoolExecutor(workers) as ex:
-        objs = list(ex.map(_compile, srcs))
+        futs = [ex.submit(_compile, src) for src in srcs]
+        fut_st = ex.submit(_compile, chunk, ("-DGDR_FLOW_STAMPS",), ".stamps")
+        objs = [f.result() for f in futs]
+        obj_st = fut_st.result()
     tmp = LIB + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -66,8 +73,15 @@ def build(verbose: bool = True) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {PROBE_SRC}:\n{r.stderr}")
     os.replace(tmp, PROBE_LIB)
+    tmp = STAMPS_LIB + ".tmp"
+    objs_st = [obj_st if os.path.basename(o) == "gdr_chunk.hip.o" else o for o in objs]
+    r = subprocess.run([_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs_st, "-o", tmp],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp, STAMPS_LIB)
     if verbose:
-        print(f"built {LIB} and {PROBE_LIB}")
+        print(f"built {LIB}, {PROBE_LIB} and {STAMPS_LIB}")
     return LIB
 
 

@@ -51,6 +51,37 @@ namespace {
 
 constexpr int CH = 64;  // chunk length
 
+#ifdef GDR_FLOW_STAMPS
+// Measurement build only (libgdr_stamps.so, never libgdr.so): shader-clock counters of the flow kernel.
+//   g_flow_stamps[role][iteration][slot]: lane 0 of wave 0 (role 0, state) and of wave 4 (role 1, prep)
+//     of the workgroup (sequence g_flow_target[0], head g_flow_target[1]), at the phase boundaries
+//     and inside the phases (slots listed where they are taken);
+//   g_flow_wg[sequence][head]: thread 0 of every workgroup, shader clock and 100 MHz real-time clock
+//     at entry and after the state waves' last iteration.
+constexpr int kStampIters = 128, kStampSeqs = 8, kStampHeads = 32;
+__device__ unsigned long long g_flow_stamps[2][kStampIters][8];
+__device__ unsigned long long g_flow_wg[kStampSeqs][kStampHeads][4];
+__device__ int g_flow_target[2];
+#define FLOW_STAMP(rec, role, it, slot)                                                                   \
+    do {                                                                                                  \
+        if ((rec) && (it) < kStampIters) g_flow_stamps[role][it][slot] = __builtin_amdgcn_s_memtime();    \
+    } while (0)
+#define FLOW_WG_CLOCK(first)                                                                              \
+    do {                                                                                                  \
+        if (threadIdx.x == 0 && blockIdx.z < kStampSeqs && blockIdx.y < kStampHeads) {                    \
+            g_flow_wg[blockIdx.z][blockIdx.y][(first) ? 0 : 2] = __builtin_amdgcn_s_memtime();            \
+            g_flow_wg[blockIdx.z][blockIdx.y][(first) ? 1 : 3] = __builtin_amdgcn_s_memrealtime();        \
+        }                                                                                                 \
+    } while (0)
+#else
+#define FLOW_STAMP(rec, role, it, slot) \
+    do {                                \
+    } while (0)
+#define FLOW_WG_CLOCK(first) \
+    do {                     \
+    } while (0)
+#endif
+
 // ---------------------------------------------------------------------------
 // MFMA tile products on LDS operands, "NT" form: C[i][j] += sum_k A[i][k] * Bt[j][k]
 // with A and Bt both row-major over the reduction index.  sA / sB point at the first
@@ -1723,6 +1754,12 @@ __global__ __launch_bounds__(512) void chunk_flow_kernel(const ChunkArgs a) {
         return (s1 - bos) < CH ? (int)(s1 - bos) : CH;
     };
     float* const sLd = FP(L::ld);
+#ifdef GDR_FLOW_STAMPS
+    const bool rec = (int)n == g_flow_target[0] && (int)h == g_flow_target[1] && l == 0;
+#else
+    constexpr bool rec = false;
+#endif
+    FLOW_WG_CLOCK(true);
 
     if (w < 4) {
         // ================= state waves =================
@@ -1784,6 +1821,7 @@ __global__ __launch_bounds__(512) void chunk_flow_kernel(const ChunkArgs a) {
                         }
                     }
                 }
+                FLOW_STAMP(rec && w == 0, 0, it, 5);  // products done
                 // R = beta V - beta e^gamma Y (rows 16I + 4(l/16) + e, column 32w + 16j + lane%16), then
                 // v_new = (I + L)^-1 R by blocked forward substitution (-L and the inverses from LDS)
                 s16x4_t lv[6], dv[4];
@@ -1825,6 +1863,7 @@ __global__ __launch_bounds__(512) void chunk_flow_kernel(const ChunkArgs a) {
                         x[j][I] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(dv[I], rv, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
                     }
                 }
+                FLOW_STAMP(rec && w == 0, 0, it, 6);  // R and the solve done
                 if (want_o) {
                     // the S Q^T part scaled by scale e^gamma_r; v_new packed for E2
 #pragma unroll
@@ -1875,7 +1914,9 @@ __global__ __launch_bounds__(512) void chunk_flow_kernel(const ChunkArgs a) {
                     }
                 }
             }
+            FLOW_STAMP(rec && w == 0, 0, it, 0);
             __syncthreads();  // end of phase X
+            FLOW_STAMP(rec && w == 0, 0, it, 1);
             // ===== phase Y: E2(it - 1), then the P tiles of chunk it =====
             if (it >= 1 && want_o) {
                 const int ce = it - 1;
@@ -1918,6 +1959,7 @@ __global__ __launch_bounds__(512) void chunk_flow_kernel(const ChunkArgs a) {
                         *reinterpret_cast<uint4*>(obase + r * ostride) = uint4{s0[0], s1[0], s0[1], s1[1]};
                 }
             }
+            FLOW_STAMP(rec && w == 0, 0, it, 4);  // the output part done
             if (it < nc && want_o) {
                 // the six off-diagonal P tiles of chunk it (the prep waves form the diagonal ones), transposed
                 // products K_J Q_I^T: lane (g, i) holds P[16I + lane%16][16J + 4g + e]
@@ -1948,8 +1990,11 @@ __global__ __launch_bounds__(512) void chunk_flow_kernel(const ChunkArgs a) {
                     store_off(w + 4, c1);
                 }
             }
+            FLOW_STAMP(rec && w == 0, 0, it, 2);
             __syncthreads();  // end of phase Y
+            FLOW_STAMP(rec && w == 0, 0, it, 3);
         }
+        FLOW_WG_CLOCK(false);
         if (a.ht) {
             // S = sigma * registers, sigma after the last chunk (1 for an empty sequence)
             const float sig = nc > 0 ? FP(L::tab)[((nc - 1) & 1) * L::TABF + L::t_x + 1] : 1.0f;
@@ -2082,7 +2127,9 @@ __global__ __launch_bounds__(512) void chunk_flow_kernel(const ChunkArgs a) {
         // queue.  Split, no head lags.
         auto phase_x = [&](int it, Regs& nxt) {
             const int b1 = it & 1;
+            FLOW_STAMP(rec && w == 4, 1, it, 5);
             if (it + 2 < nc) load(it + 2, nxt, 1 | 2);
+            FLOW_STAMP(rec && w == 4, 1, it, 6);
             if (it < nc) {
                 const S* sK1 = SP(L::k0 + b1 * L::ROWK);
                 S* const sLo1 = SP(L::lo + b1 * L::ROWO);
@@ -2123,7 +2170,9 @@ __global__ __launch_bounds__(512) void chunk_flow_kernel(const ChunkArgs a) {
                 // the tile's LDS writes complete before this wave's lanes read other lanes' entries
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
                 invert_unit_lower_16<bf16_t>(sN, sD1 + 16 * u * LDD, LDD);
+                FLOW_STAMP(rec && w == 4, 1, it, 4);
                 if (it + 2 < nc) load(it + 2, nxt, 4);
+                FLOW_STAMP(rec && w == 4, 1, it, 7);
                 store_off(u, c0);
                 if (u < 2) {
                     int I1, J1;
@@ -2146,12 +2195,16 @@ __global__ __launch_bounds__(512) void chunk_flow_kernel(const ChunkArgs a) {
                         uint2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
                 }
             }
+            FLOW_STAMP(rec && w == 4, 1, it, 0);
             __syncthreads();  // end of phase X
+            FLOW_STAMP(rec && w == 4, 1, it, 1);
         };
         // phase Y of iteration it: chunk it + 1 from registers into LDS
         auto phase_y = [&](int it, const Regs& cur) {
             if (it + 1 < nc) stage((it & 1) ^ 1, cur);
+            FLOW_STAMP(rec && w == 4, 1, it, 2);
             __syncthreads();  // end of phase Y
+            FLOW_STAMP(rec && w == 4, 1, it, 3);
         };
         if (nc > 0) {
             load(0, ra, 7);
@@ -2210,6 +2263,18 @@ hipError_t launch_kv(const ChunkArgs& a, int io, bool per_k, hipStream_t s) {
 }
 
 }  // namespace
+
+#ifdef GDR_FLOW_STAMPS
+extern "C" __attribute__((visibility("default"))) int gdr_dbg_flow_target(int seq, int head) {
+    const int t[2] = {seq, head};
+    return (int)hipMemcpyToSymbol(HIP_SYMBOL(g_flow_target), t, sizeof(t), 0, hipMemcpyHostToDevice);
+}
+extern "C" __attribute__((visibility("default"))) int gdr_dbg_flow_stamps(void* stamps, void* wg) {
+    hipError_t e = hipMemcpyFromSymbol(stamps, HIP_SYMBOL(g_flow_stamps), sizeof(g_flow_stamps), 0, hipMemcpyDeviceToHost);
+    if (e == hipSuccess) e = hipMemcpyFromSymbol(wg, HIP_SYMBOL(g_flow_wg), sizeof(g_flow_wg), 0, hipMemcpyDeviceToHost);
+    return (int)e;
+}
+#endif
 
 hipError_t launch_chunk(const ChunkArgs& a, int io_dtype, bool per_k, hipStream_t stream) {
     if (a.K == 64) {

@@ -19,7 +19,8 @@ from typing import Optional
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdr.so")
+_DEFAULT_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdr.so")
+_LIB_PATH = _DEFAULT_LIB_PATH
 _lib = None
 
 GDR_SUCCESS, GDR_ERROR_INVALID_VALUE, GDR_ERROR_NOT_SUPPORTED, GDR_ERROR_LAUNCH_FAILED = 0, 1, 2, 3
@@ -82,6 +83,15 @@ class Problem(ctypes.Structure):
 
 def library_path() -> str:
     return _LIB_PATH
+
+
+def use_library(path: Optional[str] = None) -> None:
+    """Bind to another build of the library from here on (the measurement build libgdr_stamps.so
+    exports the same entry points, with the flow kernel's clock counters compiled in); None binds
+    to libgdr.so again."""
+    global _lib, _LIB_PATH
+    _lib = None
+    _LIB_PATH = path if path is not None else _DEFAULT_LIB_PATH
 
 
 def lib():
