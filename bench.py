@@ -460,6 +460,8 @@ def _flow_stamps(seq: int, head: int, reps: int = 6):
         return torch.from_numpy(x).to(dev)
 
     pp = inputs.prefill()
+    if not (0 <= seq < pp.N and 0 <= head < pp.HV):
+        raise SystemExit(f"--flow-stamps: SEQ in 0..{pp.N - 1}, HEAD in 0..{pp.HV - 1}")
     P = {k: to_dev(getattr(pp, k)) for k in ("q", "k", "v", "g", "beta")}
     cu, h0 = to_dev(pp.cu_seqlens.astype(np.int32)), to_dev(pp.initial_state)
     o = torch.empty((pp.T, pp.HV, pp.V), dtype=torch.bfloat16, device=dev)
