@@ -25,7 +25,9 @@ current stream, passed explicitly to every call), every launch starting from a c
 512 MiB read outside the event window evicts L2 and the MALL and leaves no dirty lines), the roofline of the step's dominant kernel
 (the longest leg; each leg's own roofline beside it), HBM traffic per launch where the
 rocprofv3 counter passes recorded under profiles/ match the current kernel sources, and the
-CPU oracle timed on a bounded sample of the prefill workload.
+CPU oracle timed on a bounded sample of the prefill workload. Beside the nominal peaks it reports a
+measured dense bf16 MFMA rate (a probe kernel) and the HBM rates of the runtime's copy kernel and
+torch's fill.
 
 Profiling passes: ``--legs prefill`` runs only that leg, ``--calib-copy-mib N`` first runs one
 device copy of N MiB (known traffic, to scale FETCH_SIZE / WRITE_SIZE); both print a short
@@ -284,6 +286,34 @@ def _measured_mfma_peak(dev):
         res[name] = fl / float(np.min(ts)) / 1e12
     res["kernel"] = (f"v_mfma_f32_16x16x32_bf16, 8 chains per wave, {blocks} x 256 threads x {iters} iterations; "
                      "best of 5 launches")
+    return res
+
+
+def _measured_hbm_rates(dev):
+    """HBM rates of the runtime's own streaming kernels on 1 GiB buffers (far past L2 and the MALL),
+    best of 5 launches after 2 warm-up launches: a device-to-device copy (torch's copy_, which the HIP
+    runtime serves with its copy kernel; 1 GiB read and 1 GiB written) and torch's fill (1 GiB
+    written).  Context beside the nominal 8 TB/s: what a plain streaming kernel reaches here."""
+    import torch
+    n = (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty(n, dtype=torch.float32, device=dev)
+    res = {}
+    for name, fn, nbytes in (("runtime_copy_GBps", lambda: dst.copy_(src), 2 * 4 * n),
+                             ("torch_fill_GBps", lambda: dst.fill_(2.0), 4 * n)):
+        ts = []
+        for i in range(7):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            if i >= 2:
+                ts.append(e0.elapsed_time(e1) / 1e3)
+        res[name] = nbytes / float(np.min(ts)) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    res["buffers"] = "1 GiB fp32; the copy counts read + write bytes; best of 5 launches"
     return res
 
 
@@ -974,6 +1004,10 @@ def main():
         mp["prefill_frac_full_tile"] = f_pre_full / s_pre / (mp["tflops"] * 1e12)
         roof_legs["prefill"]["frac_measured_mfma"] = mp["prefill_frac"]
     out["measured_bf16_mfma_peak"] = mp
+    hb = _measured_hbm_rates(dev)
+    for leg in ("decode", "verify", "prefill"):
+        hb[f"{leg}_vs_runtime_copy"] = leg_info[leg]["bytes"] / leg_info[leg]["secs"] / 1e9 / hb["runtime_copy_GBps"]
+    out["measured_hbm"] = hb
     out["provenance"] = _provenance()
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
