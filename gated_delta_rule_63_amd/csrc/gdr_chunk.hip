@@ -1693,9 +1693,9 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
 //
 // Q, K, V, -L, the inverses, P and the gate tables are double-buffered, and the prep waves keep two
 // register sets of raw rows, so a chunk's loads are in flight for about three phases (issued during
-// phase X two iterations ahead, written to LDS in the phase Y of the iteration before its use).  L and P tiles
-// are formed transposed (K_J K_I^T, K_J Q_I^T), so that each lane holds four consecutive columns of
-// one row and writes them with one 8-byte store.  The output scale is folded into the e^gamma table
+// phase X two iterations ahead, written to LDS in the phase Y of the iteration before its use).  L
+// and P tiles are formed transposed (K_J K_I^T, K_J Q_I^T), so that each lane holds four consecutive
+// columns of one row and writes them with one 8-byte store.  The output scale is folded into the e^gamma table
 // and into P.
 //
 // Lazy decay: the state waves hold S / sigma.  The prep waves, which form the gate tables in chunk
@@ -1917,7 +1917,7 @@ __global__ __launch_bounds__(512) void chunk_flow_kernel(const ChunkArgs a) {
             FLOW_STAMP(rec && w == 0, 0, it, 0);
             __syncthreads();  // end of phase X
             FLOW_STAMP(rec && w == 0, 0, it, 1);
-            // ===== phase Y: E2(it - 1), then the P tiles of chunk it =====
+            // ===== phase Y: E2(it - 1), then the off-diagonal P tiles of chunk it =====
             if (it >= 1 && want_o) {
                 const int ce = it - 1;
                 const int64_t bos = s0 + (int64_t)CH * ce;
@@ -2034,37 +2034,39 @@ __global__ __launch_bounds__(512) void chunk_flow_kernel(const ChunkArgs a) {
             const int64_t bos = s0 + (int64_t)CH * ci;
             const int len = chunk_len(ci);
             if (part & 1) {
-            // without outputs q reads as zeros (a zero-byte range): it only feeds P and the output
-            const __amdgpu_buffer_rsrc_t rq = chunk_rsrc(
-                want_o ? static_cast<const char*>(a.q) + ((bos * a.HK + hk) * K) * ESZ : nullptr, want_o ? len : 0, qk_row);
+                // without outputs q reads as zeros (a zero-byte range): it only feeds P and the output
+                const __amdgpu_buffer_rsrc_t rq =
+                    chunk_rsrc(want_o ? static_cast<const char*>(a.q) + ((bos * a.HK + hk) * K) * ESZ : nullptr,
+                               want_o ? len : 0, qk_row);
 #pragma unroll
-            for (int i = 0; i < TQ::NV; ++i) r.qn[i].load(rq, TQ::row(lt, i) * qk_row + TQ::col(lt) * ESZ);
+                for (int i = 0; i < TQ::NV; ++i) r.qn[i].load(rq, TQ::row(lt, i) * qk_row + TQ::col(lt) * ESZ);
             }
             if (part & 2) {
-            const __amdgpu_buffer_rsrc_t rk =
-                chunk_rsrc(static_cast<const char*>(a.k) + ((bos * a.HK + hk) * K) * ESZ, len, qk_row);
+                const __amdgpu_buffer_rsrc_t rk =
+                    chunk_rsrc(static_cast<const char*>(a.k) + ((bos * a.HK + hk) * K) * ESZ, len, qk_row);
 #pragma unroll
-            for (int i = 0; i < PK::NPASS; ++i)
+                for (int i = 0; i < PK::NPASS; ++i)
 #pragma unroll
-                for (int q = 0; q < 2; ++q)
-                    r.kn[2 * i + q].load(rk, (2 * PK::pair(lt, i) + q) * qk_row + PK::col(lt, i) * ESZ);
+                    for (int q = 0; q < 2; ++q)
+                        r.kn[2 * i + q].load(rk, (2 * PK::pair(lt, i) + q) * qk_row + PK::col(lt, i) * ESZ);
             }
             if (part & 4) {
-            // v == NULL reads as zeros (a zero-byte range): the run that forms a segment's linear map
-            const __amdgpu_buffer_rsrc_t rv = chunk_rsrc(
-                a.v ? static_cast<const char*>(a.v) + ((bos * a.HV + h) * a.V) * ESZ : nullptr, a.v ? len : 0, v_row);
+                // v == NULL reads as zeros (a zero-byte range): the run that forms a segment's linear map
+                const __amdgpu_buffer_rsrc_t rv =
+                    chunk_rsrc(a.v ? static_cast<const char*>(a.v) + ((bos * a.HV + h) * a.V) * ESZ : nullptr,
+                               a.v ? len : 0, v_row);
 #pragma unroll
-            for (int i = 0; i < PV::NPASS; ++i)
+                for (int i = 0; i < PV::NPASS; ++i)
 #pragma unroll
-                for (int q = 0; q < 2; ++q)
-                    r.vn[2 * i + q].load(rv, (2 * PV::pair(lt, i) + q) * v_row + PV::col(lt, i) * ESZ);
-            if (u == 0) {
-                const __amdgpu_buffer_rsrc_t rg = chunk_rsrc(a.g + bos * a.HV + h, len, a.HV * 4);
-                r.gn = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, l * a.HV * 4, 0, 0));
-                const __amdgpu_buffer_rsrc_t rbt =
-                    chunk_rsrc(static_cast<const char*>(a.beta) + (bos * a.HV + h) * 2, len, a.HV * 2);
-                r.bn = __builtin_amdgcn_raw_buffer_load_b16(rbt, l * a.HV * 2, 0, 0);
-            }
+                    for (int q = 0; q < 2; ++q)
+                        r.vn[2 * i + q].load(rv, (2 * PV::pair(lt, i) + q) * v_row + PV::col(lt, i) * ESZ);
+                if (u == 0) {
+                    const __amdgpu_buffer_rsrc_t rg = chunk_rsrc(a.g + bos * a.HV + h, len, a.HV * 4);
+                    r.gn = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, l * a.HV * 4, 0, 0));
+                    const __amdgpu_buffer_rsrc_t rbt =
+                        chunk_rsrc(static_cast<const char*>(a.beta) + (bos * a.HV + h) * 2, len, a.HV * 2);
+                    r.bn = __builtin_amdgcn_raw_buffer_load_b16(rbt, l * a.HV * 2, 0, 0);
+                }
             }
         };
         auto stage = [&](int b, const Regs& r) {  // registers -> LDS buffers b; wave 4 forms the gate tables
