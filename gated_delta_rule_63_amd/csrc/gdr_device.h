@@ -154,12 +154,17 @@ template <int N> struct LdsVec<bf16_t, N> {
 // ---- loads through a buffer resource: bytes past the resource's range read as zero ----
 template <typename T, int N> struct BufVec;
 
+// cache-policy operand of the buffer loads: 0 = default, kNonTemporal = streaming data read once
+// (the nt bit: the lines are the first to be replaced)
+constexpr int kNonTemporal = 2;
+
 template <int N> struct BufVec<float, N> {
     static_assert(N % 4 == 0, "fp32 vectors are whole float4s");
+    template <int AUX = 0>
     __device__ __forceinline__ static void load(__amdgpu_buffer_rsrc_t r, uint32_t off, float* out) {
 #pragma unroll
         for (int j = 0; j < N / 4; ++j) {
-            const f32x4_t x = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * j, 0, 0));
+            const f32x4_t x = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * j, 0, AUX));
             out[4 * j + 0] = x[0];
             out[4 * j + 1] = x[1];
             out[4 * j + 2] = x[2];
@@ -170,9 +175,10 @@ template <int N> struct BufVec<float, N> {
 
 template <int N> struct BufVec<bf16_t, N> {
     static_assert(N == 4 || N == 8, "bf16 vectors are 8 or 16 bytes");
+    template <int AUX = 0>
     __device__ __forceinline__ static void load(__amdgpu_buffer_rsrc_t r, uint32_t off, float* out) {
         if constexpr (N == 8) {
-            const uint4 w = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+            const uint4 w = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX));
             const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -180,7 +186,7 @@ template <int N> struct BufVec<bf16_t, N> {
                 out[2 * j + 1] = __uint_as_float(ws[j] & 0xFFFF0000u);
             }
         } else {
-            const uint2 w = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+            const uint2 w = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, AUX));
             out[0] = __uint_as_float(w.x << 16);
             out[1] = __uint_as_float(w.x & 0xFFFF0000u);
             out[2] = __uint_as_float(w.y << 16);

@@ -146,7 +146,8 @@ __global__ __launch_bounds__(kKdaThreads) void kda_decode_kernel(const KdaArgs a
         for (int s = 0; s < SLOTS; ++s)
 #pragma unroll
             for (int u = 0; u < UNITS; ++u)
-                BufVec<ST, VW>::load(srs, (uint32_t)(((row0 + s) * K + cols[u]) * Elem<ST>::bytes), &S[s][u * VW]);
+                BufVec<ST, VW>::template load<kNonTemporal>(
+                    srs, (uint32_t)(((row0 + s) * K + cols[u]) * Elem<ST>::bytes), &S[s][u * VW]);
     }
 
     for (int64_t t = bos; t < eos; ++t) {

@@ -77,7 +77,8 @@ __global__ __launch_bounds__(256) void recurrent_kernel(const RecurrentArgs a) {
     const int64_t sbase = (((int64_t)slot * a.HV + h) * a.V + row0) * K;
     // The workgroup's state tile (BV rows of K) is read through a buffer resource that spans the
     // tile, or nothing when there is no source state: reads then return zeros, so the start state
-    // needs no branch and its loads schedule together with the first token's.
+    // needs no branch and its loads schedule together with the first token's.  The reads are
+    // non-temporal: each state byte is read once per call (decode 0.153 -> 0.146 ms).
     auto load_state = [&]() {
         const int64_t tile = (((int64_t)slot * a.HV + h) * a.V + vt * BV) * K;
         const char* tile_ptr = a.src ? static_cast<const char*>(a.src) + tile * Elem<ST>::bytes : nullptr;
@@ -87,7 +88,8 @@ __global__ __launch_bounds__(256) void recurrent_kernel(const RecurrentArgs a) {
         for (int s = 0; s < SLOTS; ++s)
 #pragma unroll
             for (int u = 0; u < UNITS; ++u)
-                BufVec<ST, VW>::load(srs, (uint32_t)(((rg * SLOTS + s) * K + cols[u]) * Elem<ST>::bytes), &S[s][u * VW]);
+                BufVec<ST, VW>::template load<kNonTemporal>(
+                    srs, (uint32_t)(((rg * SLOTS + s) * K + cols[u]) * Elem<ST>::bytes), &S[s][u * VW]);
     };
 
     // One token on this thread's SLOTS rows, from its unpacked inputs: k and q (this lane's
