@@ -195,6 +195,41 @@ template <int N> struct BufVec<bf16_t, N> {
     }
 };
 
+// Cache-policy operand of buffer stores: kWriteThrough = device scope (sc1), the store is written
+// through the caches toward memory.  For state written once and not read again in the call.
+constexpr int kWriteThrough = 16;
+
+// N converted elements of a row stored as one or two 16-byte (or one 8-byte) vectors through a
+// buffer resource, byte offset `off`, cache policy AUX
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+template <typename T, int N> struct BufStore;
+template <int N> struct BufStore<float, N> {
+    static_assert(N % 4 == 0, "fp32 vectors are whole float4s");
+    template <int AUX>
+    __device__ __forceinline__ static void store(__amdgpu_buffer_rsrc_t r, uint32_t off, const float* in) {
+#pragma unroll
+        for (int j = 0; j < N / 4; ++j)
+            __builtin_amdgcn_raw_buffer_store_b128(
+                __builtin_bit_cast(u32x4_t, f32x4_t{in[4 * j], in[4 * j + 1], in[4 * j + 2], in[4 * j + 3]}), r,
+                off + 16 * j, 0, AUX);
+    }
+};
+template <int N> struct BufStore<bf16_t, N> {
+    static_assert(N == 4 || N == 8, "bf16 vectors are 8 or 16 bytes");
+    template <int AUX>
+    __device__ __forceinline__ static void store(__amdgpu_buffer_rsrc_t r, uint32_t off, const float* in) {
+        if constexpr (N == 8) {
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{pack_bf16x2(in[0], in[1]), pack_bf16x2(in[2], in[3]),
+                                                           pack_bf16x2(in[4], in[5]), pack_bf16x2(in[6], in[7])},
+                                                   r, off, 0, AUX);
+        } else {
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(in[0], in[1]), pack_bf16x2(in[2], in[3])}, r,
+                                                  off, 0, AUX);
+        }
+    }
+};
+
 // ---- raw (unconverted) vectors, so loads can be issued well before their use ----
 template <typename T, int N> struct RawVec;
 template <int N> struct RawVec<float, N> {
