@@ -136,7 +136,6 @@ __global__ __launch_bounds__(kKdaThreads) void kda_decode_kernel(const KdaArgs a
 #pragma unroll
     for (int u = 0; u < UNITS; ++u) cols[u] = (u * 16 + j) * VW;
     float S[SLOTS][EPL];
-    const int64_t sbase = (((int64_t)slot * a.HV + h) * V + row0) * K;
     {
         const int64_t tile = ((int64_t)slot * a.HV + h) * V * K;
         const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
@@ -257,10 +256,17 @@ __global__ __launch_bounds__(kKdaThreads) void kda_decode_kernel(const KdaArgs a
     }
 
     if (a.commit) {
+        // written through (device scope): the state is not read again in this call (64 x 32 heads:
+        // unchanged at 0.063 ms; 16 x 32 heads: 0.021 -> 0.0205 ms)
+        const int64_t tile = ((int64_t)slot * a.HV + h) * V * K;
+        const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+            static_cast<char*>(a.pool) + tile * Elem<ST>::bytes, 0, V * K * Elem<ST>::bytes, 0x00020000);
 #pragma unroll
         for (int s = 0; s < SLOTS; ++s)
 #pragma unroll
-            for (int u = 0; u < UNITS; ++u) Vec<ST, VW>::store(a.pool, sbase + (int64_t)s * K + cols[u], &S[s][u * VW]);
+            for (int u = 0; u < UNITS; ++u)
+                BufStore<ST, VW>::template store<kWriteThrough>(
+                    crs, (uint32_t)(((row0 + s) * K + cols[u]) * Elem<ST>::bytes), &S[s][u * VW]);
         if (conv_thread)
             for (int i = 0; i < W - 1; ++i) Elem<IO>::store(a.conv_state, win_base + i, win[3 - (W - 1) + i]);
     }
