@@ -378,8 +378,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const void* base, i
 template <typename IO> struct Raw8;
 template <> struct Raw8<bf16_t> {
     uint4 w;
+    template <int AUX = 0>
     __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int voff) {
-        w = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+        w = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, AUX));
     }
     __device__ __forceinline__ void get(float* x) const {
         const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
@@ -400,9 +401,10 @@ template <> struct Raw8<bf16_t> {
 };
 template <> struct Raw8<float> {
     f32x4_t a, b;
+    template <int AUX = 0>
     __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int voff) {
-        a = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
-        b = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16, 0, 0));
+        a = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, AUX));
+        b = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16, 0, AUX));
     }
     __device__ __forceinline__ void get(float* x) const {
 #pragma unroll
@@ -1945,9 +1947,12 @@ __global__ __launch_bounds__(512) void chunk_flow_kernel(const ChunkArgs a) {
                 // rows g and g + 1 of a lane pair exchange halves (v_permlane16_swap), so that each lane holds
                 // eight consecutive value columns of its token: columns 32w + {0, 16, 8, 24}[g] .. +7, one 16-byte
                 // store per token tile, 64 contiguous bytes per token and store instruction
-                uint16_t* const obase = static_cast<uint16_t*>(a.o) + (bos * a.HV + h) * a.V + 32 * w +
-                                        ((g4 & 1) ? 16 + 4 * (g4 - 1) : 4 * g4);
-                const int64_t ostride = (int64_t)a.HV * a.V;
+                // written through (device scope, not read again in the call) by a buffer store over the chunk's
+                // len token rows: rows past a short chunk's end fall outside the range and are dropped
+                const int ostride = a.HV * a.V;
+                const int ocol = 32 * w + ((g4 & 1) ? 16 + 4 * (g4 - 1) : 4 * g4);
+                const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
+                    static_cast<uint16_t*>(a.o) + (bos * a.HV + h) * a.V, 0, len * ostride * 2, 0x00020000);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const uint32_t x0 = pack_bf16x2(ot[0][i][0], ot[0][i][1]), x1 = pack_bf16x2(ot[0][i][2], ot[0][i][3]);
@@ -1955,8 +1960,8 @@ __global__ __launch_bounds__(512) void chunk_flow_kernel(const ChunkArgs a) {
                     const auto s0 = __builtin_amdgcn_permlane16_swap(x0, y0, false, false);
                     const auto s1 = __builtin_amdgcn_permlane16_swap(x1, y1, false, false);
                     const int r = 16 * i + lr;
-                    if (r < len)
-                        *reinterpret_cast<uint4*>(obase + r * ostride) = uint4{s0[0], s1[0], s0[1], s1[1]};
+                    __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{s0[0], s1[0], s0[1], s1[1]}, ors,
+                                                           (uint32_t)(r * ostride * 2 + ocol * 2), 0, kWriteThrough);
                 }
             }
             FLOW_STAMP(rec && w == 0, 0, it, 4);  // the output part done
@@ -2039,7 +2044,7 @@ __global__ __launch_bounds__(512) void chunk_flow_kernel(const ChunkArgs a) {
                     chunk_rsrc(want_o ? static_cast<const char*>(a.q) + ((bos * a.HK + hk) * K) * ESZ : nullptr,
                                want_o ? len : 0, qk_row);
 #pragma unroll
-                for (int i = 0; i < TQ::NV; ++i) r.qn[i].load(rq, TQ::row(lt, i) * qk_row + TQ::col(lt) * ESZ);
+                for (int i = 0; i < TQ::NV; ++i) r.qn[i].template load<kNonTemporal>(rq, TQ::row(lt, i) * qk_row + TQ::col(lt) * ESZ);
             }
             if (part & 2) {
                 const __amdgpu_buffer_rsrc_t rk =
@@ -2048,7 +2053,7 @@ __global__ __launch_bounds__(512) void chunk_flow_kernel(const ChunkArgs a) {
                 for (int i = 0; i < PK::NPASS; ++i)
 #pragma unroll
                     for (int q = 0; q < 2; ++q)
-                        r.kn[2 * i + q].load(rk, (2 * PK::pair(lt, i) + q) * qk_row + PK::col(lt, i) * ESZ);
+                        r.kn[2 * i + q].template load<kNonTemporal>(rk, (2 * PK::pair(lt, i) + q) * qk_row + PK::col(lt, i) * ESZ);
             }
             if (part & 4) {
                 // v == NULL reads as zeros (a zero-byte range): the run that forms a segment's linear map
@@ -2059,7 +2064,7 @@ __global__ __launch_bounds__(512) void chunk_flow_kernel(const ChunkArgs a) {
                 for (int i = 0; i < PV::NPASS; ++i)
 #pragma unroll
                     for (int q = 0; q < 2; ++q)
-                        r.vn[2 * i + q].load(rv, (2 * PV::pair(lt, i) + q) * v_row + PV::col(lt, i) * ESZ);
+                        r.vn[2 * i + q].template load<kNonTemporal>(rv, (2 * PV::pair(lt, i) + q) * v_row + PV::col(lt, i) * ESZ);
                 if (u == 0) {
                     const __amdgpu_buffer_rsrc_t rg = chunk_rsrc(a.g + bos * a.HV + h, len, a.HV * 4);
                     r.gn = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, l * a.HV * 4, 0, 0));
