@@ -76,6 +76,13 @@ bool token_inputs_ok(const gdr_problem* p, const void* q, const void* k, const v
 
 gdr_status status_of(hipError_t e) { return e == hipSuccess ? GDR_SUCCESS : GDR_ERROR_LAUNCH_FAILED; }
 
+// fp32 operands with the per-key-channel gate at K = 128: the chunk kernel's fp32 per-channel tables
+// and operands do not fit the LDS, so gdr_chunk_fwd runs the token-serial recurrence kernel instead
+// (the same launch as gdr_recurrent_fwd, the exact recurrence rather than the chunked rounding)
+bool token_serial_chunk(const gdr_problem* p) {
+    return p->io_dtype == GDR_F32 && p->gate == GDR_GATE_PER_K && p->head_dim_k == 128;
+}
+
 // Gating-front metadata: scalar decay only, flags 0/1, eps finite and >= 0, pointers present.
 gdr_status check_gating(const gdr_problem* p, const gdr_gating* gt) {
     if (!gt) return GDR_ERROR_INVALID_VALUE;
@@ -273,6 +280,7 @@ gdr_status gdr_gating_prepass(const gdr_problem* p, const void* q, const void* k
 
 size_t gdr_chunk_workspace_size(const gdr_problem* p, int32_t chunk_size) {
     if (check_problem(p) != GDR_SUCCESS || chunk_size != 64) return 0;
+    if (token_serial_chunk(p)) return 0;  // no segmented route for this configuration
     const gdr::CpPlan pl = gdr::cp_plan(p->total_tokens, p->num_seqs, p->num_v_heads, p->head_dim_k,
                                         p->head_dim_v, p->io_dtype == GDR_BF16 ? 2 : 4);
     return pl.P > 1 ? pl.total : 0;
@@ -288,8 +296,6 @@ gdr_status check_chunk(const gdr_problem* p, int32_t chunk_size, const void* q, 
     gdr_status st = check_problem(p);
     if (st != GDR_SUCCESS) return st;
     if (chunk_size != 64) return GDR_ERROR_INVALID_VALUE;
-    // fp32 operands with the per-key-channel gate need K = 64 (the LDS layout of K = 128 does not fit)
-    if (p->io_dtype == GDR_F32 && p->gate == GDR_GATE_PER_K && p->head_dim_k != 64) return GDR_ERROR_NOT_SUPPORTED;
     if (!token_inputs_ok(p, q, k, v, g, beta)) return GDR_ERROR_INVALID_VALUE;
     if (p->total_tokens > 0 && !o) return GDR_ERROR_INVALID_VALUE;
     if (p->num_seqs > 1 && !cu_seqlens) return GDR_ERROR_INVALID_VALUE;
@@ -307,6 +313,8 @@ gdr_status chunk_fwd_impl(const gdr_problem* p, const void* q, const void* k, co
         // every sequence is empty: final state = initial state
         return gdr_recurrent_fwd(p, q, k, v, g, beta, cu_seqlens, initial_state, o, final_state, hip_stream);
     }
+    if (token_serial_chunk(p))
+        return gdr_recurrent_fwd(p, q, k, v, g, beta, cu_seqlens, initial_state, o, final_state, hip_stream);
     if ((st = check_device()) != GDR_SUCCESS) return st;
 
     const bool per_k = p->gate == GDR_GATE_PER_K;

@@ -146,9 +146,12 @@ GDR_API size_t gdr_chunk_workspace_size(const gdr_problem* p, int32_t chunk_size
  *                  segments, then every segment from its true start state), with NULL it runs
  *                  every sequence's chunks in one pass.  A non-NULL workspace smaller than the
  *                  size returns GDR_ERROR_INVALID_VALUE.
- * fp32 I/O is supported for every K, V with the scalar gate; with the per-key-channel gate it
- * needs K = 64 (K = 128 returns GDR_ERROR_NOT_SUPPORTED).
- * The result matches gdr_recurrent_fwd to the chunked method's rounding, not bitwise.
+ * Every K, V in {64, 128} and both I/O dtypes are accepted with either gate.  fp32 I/O with the
+ * per-key-channel gate at K = 128 runs the token-serial recurrence kernel of gdr_recurrent_fwd (the
+ * chunk kernel's fp32 per-channel operands do not fit the LDS): its result equals gdr_recurrent_fwd
+ * bitwise, it needs no workspace (gdr_chunk_workspace_size returns 0) and its time grows with the
+ * longest sequence token by token.  Every other configuration runs the chunked method, and its
+ * result matches gdr_recurrent_fwd to the chunked method's rounding, not bitwise.
  */
 GDR_API gdr_status gdr_chunk_fwd(const gdr_problem* p, int32_t chunk_size,
                          const void* q, const void* k, const void* v,

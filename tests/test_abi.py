@@ -260,6 +260,14 @@ def test_segmented_workspace_size(T, N, HV, K, V, io):
         assert got == 0  # the prefill workload (8 sequences, 32 heads) and short sequences are not
 
 
+def test_fp32_per_key_gate_k128_needs_no_workspace():
+    """fp32 I/O with the per-key-channel gate at K = 128 runs the token-serial kernel: no segmented
+    route, so no workspace even for one long sequence with few heads; K = 64 keeps its route."""
+    assert _cp_size(65573, 1, 16, 128, 128, io=0) == 0
+    assert _cp_size(65573, 1, 16, 128, 64, io=0) == 0
+    assert _cp_size(65573, 1, 16, 64, 64, io=0) == _cp_expected(65573, 1, 16, 64, 64, 4) > 0
+
+
 def _kda_front(**kw):
     f = dict(conv_width=4, conv_weight=0x1000, conv_bias=None, conv_state=0x1000, gate_in=0x1000,
              gate_weight=0x1000, gate_rank=128, A_log=0x1000, dt_bias=0x1000, b=0x1000, l2norm_eps=1e-6,

@@ -70,6 +70,25 @@ def test_fp32_k128(V, lengths, h0):
     _check(p, o, ht, h0=h0)
 
 
+@pytest.mark.parametrize("V,lengths", [(128, [300, 0, 65, 1]), (64, [129, 64])])
+def test_fp32_per_key_gate_k128_runs_the_token_kernel(V, lengths):
+    """fp32 I/O with the per-key-channel gate at K = 128 (no chunked kernel fits the LDS): the chunk
+    entry points run the token-serial kernel, so they equal gdr_recurrent_fwd bitwise, need no
+    workspace, and meet the fp32 tolerance against the oracle."""
+    p = inputs.dense_problem(67 + V, lengths, HK=2, HV=4, K=128, V=V, io_dtype="f32", g_range=(-2.0, 0.0),
+                             g_endpoints=0.25, per_k_gate=True, beta_mode="mixed")
+    d = problem_to_dev(p)
+    assert gdr.gdr_chunk_workspace_size(d["q"], d["v"], d["g"], p.N) == 0
+    o, ht = _chunk(p, d)
+    _check(p, o, ht)
+    o_r, ht_r = gdr.gdr_recurrent_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], p.scale, d["h0"])
+    o_n, ht_n = gdr.gdr_chunk_fwd_noalloc(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], p.scale, d["h0"],
+                                          o=torch.empty_like(o), final_state=torch.empty_like(ht))
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_r) and torch.equal(ht, ht_r)
+    assert torch.equal(o_n, o_r) and torch.equal(ht_n, ht_r)
+
+
 def test_fp32_k128_adversarial_decay():
     p = inputs.dense_problem(66, [200, 64, 65], HK=1, HV=2, K=128, V=128, io_dtype="f32", g_range=(-2.0, 0.0),
                              g_endpoints=0.25)
