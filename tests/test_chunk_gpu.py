@@ -156,6 +156,36 @@ def test_chunked_matches_recurrent_on_gpu_and_repeats_bitwise():
     assert max_rel_l2_states(f64(h1), f64(hr)) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("row", ["64", "1024", "packed4096", "boundary_x8", "gva2", "gva4"])
+def test_repeated_launches_stay_bitwise_identical(row):
+    """Determinism under repetition, scaled down from the cuLA PR #113 stress (100,000 launches over
+    six rows): 300 back-to-back launches of each row, every one bitwise equal to the first.  Rows: one
+    64-token sequence, one of 1024, 4096 tokens packed into sequences of 7..694, [1, 63, 64, 65] x 8,
+    and the GVA2 [1, 63, 65, 2] and GVA4 [65, 1, 129, 63] batches (16 key heads)."""
+    rng = np.random.default_rng(91)
+    if row == "packed4096":
+        lengths, left = [], 4096
+        while left > 0:
+            n = min(left, int(rng.integers(7, 695)))
+            lengths.append(n)
+            left -= n
+    else:
+        lengths = {"64": [64], "1024": [1024], "boundary_x8": [1, 63, 64, 65] * 8, "gva2": [1, 63, 65, 2],
+                   "gva4": [65, 1, 129, 63]}[row]
+    HV = {"gva2": 32, "gva4": 64}.get(row, 16)
+    p = inputs.dense_problem(92, lengths, HK=16, HV=HV, K=128, V=128, io_dtype="bf16")
+    d = problem_to_dev(p)
+    o_ref, h_ref = _chunk(p, d)
+    o, h = torch.empty_like(o_ref), torch.empty_like(h_ref)
+    bad = torch.zeros((), dtype=torch.int64, device="cuda")
+    for _ in range(300):
+        gdr.gdr_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], p.scale, d["h0"], o=o, final_state=h)
+        bad += (o.view(torch.int16) != o_ref.view(torch.int16)).any().long()
+        bad += (h.view(torch.int32) != h_ref.view(torch.int32)).any().long()
+    torch.cuda.synchronize()
+    assert int(bad) == 0
+
+
 def test_inputs_untouched_flow_and_per_key_gate():
     """q, k, v, g, beta, cu_seqlens and the initial state are byte-identical after a call, on the flow
     kernel (scalar gate, bf16, K = V = 128) and on the per-key-channel kernel."""
