@@ -68,31 +68,34 @@ __global__ __launch_bounds__(256) void cp_setup_kernel(const int32_t* __restrict
 
 // Per sequence n: S[f] = h0[n] (or zeros) and S[s+1] = S[s] M_s + B_s for the segments s = f .. l - 2 of
 // the sequence (f = seg_first[n], l = seg_first[n + 1]), per value head.  One workgroup owns 16 state rows
-// of one head of one sequence (grid: V/16 x HV x N) and keeps them in LDS between steps; wave w forms
+// of one head of one sequence (V/16 x HV x N workgroups) and keeps them in LDS between steps; wave w forms
 // output columns 32w .. 32w + 31 (two 16-column tiles; one tile when K = 64) with fp32 MFMA (16x16x4):
 // A = the 16 rows from LDS, B = M_s, C starting from B_s.  M_s and B_s do not depend on the chain, so
 // each lane holds its share of them for the next segment in registers, loaded while the current step's
-// products run: a step then waits on no global load (65573-token KDA call 1.2201 -> 1.2110 ms, results
-// bitwise unchanged).
+// products run: a step then waits on no global load.  With the XCD-aware grid below, the 65573-token
+// KDA call went from 1.2313 to 1.2024 ms (results bitwise unchanged), the 4 x 16384 GDN scan from 32 to
+// 20 us.
 template <int K>
 __global__ __launch_bounds__(256) void cp_scan_kernel(const float* __restrict__ h0, const float* __restrict__ B,
                                                       const float* __restrict__ M, float* __restrict__ S,
-                                                      const int32_t* __restrict__ seg_first, int HV, int V) {
+                                                      const int32_t* __restrict__ seg_first, int HV, int V,
+                                                      int nseq) {
     constexpr int LDR = K + 4;                  // padded LDS row: the A reads of a k-step hit 16 banks
     constexpr int TPW = K / 64;                 // 16-column tiles per wave (K / 16 tiles over 4 waves)
     constexpr int NK = K / 4;                   // k-steps of one product
     __shared__ __align__(16) float rows[16][LDR];
     const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
-    const int h = blockIdx.y, r0 = blockIdx.x * 16, n = blockIdx.z;
+    // one-dimensional grid, XCD-aware: workgroups are handed to the 8 XCDs in turn by linear index, so
+    // the V/16 row blocks of one (sequence, head) take indices congruent modulo 8 and share an XCD, and
+    // its M_s is fetched from memory once per step into that XCD's L2 instead of once per row block
+    constexpr int kXcds = 8;
+    const int nvt = V / 16;
+    const int i = blockIdx.x;
+    const int hs = (i / (kXcds * nvt)) * kXcds + i % kXcds;  // (sequence, head) pair
+    if (hs >= HV * nseq) return;                              // padding of the last group of 8 pairs
+    const int h = hs % HV, n = hs / HV, r0 = ((i / kXcds) % nvt) * 16;
     const int64_t vk = (int64_t)V * K;
     const int f = seg_first[n], last = seg_first[n + 1] - 1;
-    for (int e = tid; e < 16 * K; e += 256) {
-        const int rr = e / K, cc = e % K;
-        const int64_t row = (int64_t)h * V + r0 + rr;
-        const float x = h0 ? h0[((int64_t)n * HV * V + row) * K + cc] : 0.0f;
-        rows[rr][cc] = x;
-        S[((int64_t)f * HV * V + row) * K + cc] = x;  // the first segment's start state
-    }
     // this lane's operands of one step: M_s[4k + l/16][col_t] for every k-step k and tile t, and
     // B_s[4(l/16) + e][col_t]; two sets, for the current and the next segment
     float mb[2][TPW][NK];
@@ -147,7 +150,21 @@ __global__ __launch_bounds__(256) void cp_scan_kernel(const float* __restrict__ 
         }
         __syncthreads();
     };
+    // the first step's operands, then the start rows (every load of the prologue in flight together)
     if (f < last) fetch(std::integral_constant<int, 0>{}, f);
+    constexpr int IPT = 16 * K / 256;  // start-state elements per thread
+    float x0[IPT];
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+        const int e = tid + 256 * i, rr = e / K, cc = e % K;
+        x0[i] = h0 ? h0[((int64_t)n * HV * V + (int64_t)h * V + r0 + rr) * K + cc] : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+        const int e = tid + 256 * i, rr = e / K, cc = e % K;
+        rows[rr][cc] = x0[i];
+        S[((int64_t)f * HV * V + (int64_t)h * V + r0 + rr) * K + cc] = x0[i];  // the first segment's start state
+    }
     __syncthreads();
     for (int s = f; s < last; s += 2) {
         step(std::integral_constant<int, 0>{}, s);
@@ -210,15 +227,16 @@ hipError_t launch_cp_setup(const CpPlan& pl, char* ws, const int32_t* cu, int64_
 
 hipError_t launch_cp_scan(const CpPlan& pl, char* ws, const float* h0, int32_t HV, int32_t K, int32_t V,
                           hipStream_t stream) {
-    const dim3 grid(V / 16, HV, pl.N);
+    const int64_t pairs = (int64_t)HV * pl.N;
+    const dim3 grid((unsigned)(((pairs + 7) / 8) * 8 * (V / 16)));
     const float* B = reinterpret_cast<const float*>(ws + pl.B);
     const float* M = reinterpret_cast<const float*>(ws + pl.M);
     float* S = reinterpret_cast<float*>(ws + pl.S);
     const int32_t* sf = reinterpret_cast<const int32_t*>(ws + pl.seg_first);
     if (K == 64)
-        hipLaunchKernelGGL(cp_scan_kernel<64>, grid, dim3(256), 0, stream, h0, B, M, S, sf, HV, V);
+        hipLaunchKernelGGL(cp_scan_kernel<64>, grid, dim3(256), 0, stream, h0, B, M, S, sf, HV, V, pl.N);
     else
-        hipLaunchKernelGGL(cp_scan_kernel<128>, grid, dim3(256), 0, stream, h0, B, M, S, sf, HV, V);
+        hipLaunchKernelGGL(cp_scan_kernel<128>, grid, dim3(256), 0, stream, h0, B, M, S, sf, HV, V, pl.N);
     return hipGetLastError();
 }
 
