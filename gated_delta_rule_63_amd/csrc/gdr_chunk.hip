@@ -1251,10 +1251,18 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
                     fp[5 * K + pc] = exp_f32(G2 - G0);
                     fp[6 * K + pc] = exp_f32(G2 - G1);
                 }
+                // The diagonal of P is q_r . k_r: its decay factor is exactly 1, but the scaled bf16
+                // operands would round each factor on its own, which under cancellation (a small q_r . k_r)
+                // leaves a large relative error in a one-token output.  It is summed here from the unscaled
+                // rows in fp32 (partial sums of the 8 lanes of a row pair, one per 64-channel block, in the
+                // W area, free until D) and replaces the MFMA value below.
+                float* const sdg = FP(Lay::k_w);
+                static_assert(K / 64 * CH * sizeof(float) <= Lay::ROWK, "diagonal partial sums fit the W area");
 #pragma unroll
                 for (int i = 0; i < PK::NPASS; ++i) {
                     if (!PK::valid(tid, i)) continue;
                     const int c8 = PK::col(tid, i), r0 = 2 * PK::pair(tid, i), I = r0 >> 4;
+                    float dqa = 0.0f, dqb = 0.0f;  // this lane's part of q_r0 . k_r0 and q_r0+1 . k_r0+1
                     // two halves of four channels keep the temporaries few
 #pragma unroll
                     for (int hh = 0; hh < 2; ++hh) {
@@ -1287,12 +1295,31 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
                         if (want_o) {  // P only feeds the output
                             qr[2 * i].get4(y, hh);
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) y[e] *= la[e];
+                            for (int e = 0; e < 4; ++e) {
+                                dqa = fmaf(y[e], ka[e], dqa);
+                                y[e] *= la[e];
+                            }
                             st4f_perm<MT>(sQ + r0 * LDK, c4, y);
                             qr[2 * i + 1].get4(y, hh);
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) y[e] *= lb[e];
+                            for (int e = 0; e < 4; ++e) {
+                                dqb = fmaf(y[e], kb[e], dqb);
+                                y[e] *= lb[e];
+                            }
                             st4f_perm<MT>(sQ + (r0 + 1) * LDK, c4, y);
+                        }
+                    }
+                    if (want_o) {  // the 8 lanes of the row pair (consecutive lanes, whole waves valid or not)
+                        dqa += dpp_mov<0xB1>(dqa);   // quad_perm [1,0,3,2]
+                        dqb += dpp_mov<0xB1>(dqb);
+                        dqa += dpp_mov<0x4E>(dqa);   // quad_perm [2,3,0,1]
+                        dqb += dpp_mov<0x4E>(dqb);
+                        dqa += dpp_mov<0x141>(dqa);  // row_half_mirror: the other quad of the 8 lanes
+                        dqb += dpp_mov<0x141>(dqb);
+                        if ((tid & 7) == 0) {
+                            const int blk = (c8 / 64) * CH;
+                            sdg[blk + r0] = dqa;
+                            sdg[blk + r0 + 1] = dqb;
                         }
                     }
                 }
@@ -1318,7 +1345,15 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
                             if (want_o) sP[r * LDT + perm<MT>(j)] = M::cvt(cp[e]);
                         } else {  // diagonal blocks: L in fp32, strictly lower, for the inversion; P lower
                             sLd[I * 16 * LDN + rr * LDN + lr] = (lr < rr) ? sb[r] * cl[e] : 0.0f;
-                            if (want_o) sP[r * LDT + perm<MT>(j)] = M::cvt((lr <= rr) ? cp[e] : 0.0f);
+                            if (want_o) {
+                                float pv = (lr <= rr) ? cp[e] : 0.0f;
+                                if (lr == rr) {  // q_r . k_r from the unscaled rows
+                                    pv = sdg[r];
+#pragma unroll
+                                    for (int b = 1; b < K / 64; ++b) pv += sdg[b * CH + r];
+                                }
+                                sP[r * LDT + perm<MT>(j)] = M::cvt(pv);
+                            }
                         }
                     }
                 };

@@ -80,7 +80,8 @@ def _check(p, o, pool, conv, commit=True):
         got = inputs.widen(pool_after[act])
         want = np.stack([ref["final"][s] for s in act])
         es = max_rel_l2_slices(got, want, 2)
-        assert es <= tol, f"state relL2 {es}"
+        # the committed state is stored in the pool's dtype: a bf16 pool holds it to bf16's bar
+        assert es <= (TOL["bf16"] if p.pool.dtype == np.uint16 else tol), f"state relL2 {es}"
         # the window holds raw inputs: bit for bit
         for s in act:
             assert np.array_equal(inputs.widen(conv_after[s]), ref["conv"][s]), f"window of slot {s}"

@@ -72,7 +72,9 @@ def _check_pool(p, pool_before: np.ndarray, pool_after: torch.Tensor, ref, commi
         for s in act:
             for h in range(p.HV):
                 worst = max(worst, rel_l2(inputs.widen(after[s, h]), ref["final"][s][h]))
-        assert worst <= TOL[p.io_dtype], f"committed state relL2 {worst}"
+        # a committed slot is stored in the pool's dtype: a bf16 pool holds the state to bf16's bar
+        tol = TOL["bf16"] if p.pool_dtype == "bf16" else TOL[p.io_dtype]
+        assert worst <= tol, f"committed state relL2 {worst}"
 
 
 def _check_ibuf(p, ib: torch.Tensor, ref):
@@ -92,7 +94,8 @@ def _check_ibuf(p, ib: torch.Tensor, ref):
         for t in range(L):
             for h in range(p.HV):
                 worst = max(worst, rel_l2(got[t, h], ref["states"][b][t, h]))
-    assert worst <= TOL[p.io_dtype], f"intermediate state relL2 {worst}"
+    tol = TOL["bf16"] if ib.dtype == torch.bfloat16 else TOL[p.io_dtype]  # rows stored in bf16: bf16's bar
+    assert worst <= tol, f"intermediate state relL2 {worst}"
     assert np.all(raw[~written] == sent), "intermediate rows that must stay untouched changed"
 
 
