@@ -195,8 +195,9 @@ __device__ __forceinline__ int iperm(int p) {
 // c0 += A0 B'^T and c1 += A1 B'^T over KD columns (16-row tiles from LDS, as MM::nt), where B'
 // is B with every column multiplied by f[column] (fp32, physical column order; NULL: none).  The
 // two products share the scaled B operand, and every operand read is issued before the first
-// product.  With TWO = false only c0 is formed (a1 is not read).
-template <typename MT, int KD, bool TWO = true>
+// product.  With TWO = false only c0 is formed (a1 is not read).  With TR the products are formed
+// transposed (B' A^T): lane (g, i) then holds row i of A's tile, columns 4g .. 4g+3 of B's.
+template <typename MT, int KD, bool TWO = true, bool TR = false>
 __device__ __forceinline__ void nt2_bscaled(f32x4_t& c0, const typename MM<MT>::S* a0, f32x4_t& c1,
                                             const typename MM<MT>::S* a1, int lda, const typename MM<MT>::S* b,
                                             int ldb, const float* f) {
@@ -231,8 +232,13 @@ __device__ __forceinline__ void nt2_bscaled(f32x4_t& c0, const typename MM<MT>::
                 w.w = pack_bf16x2(__uint_as_float(w.w << 16) * f1[s][2], __uint_as_float(w.w & 0xFFFF0000u) * f1[s][3]);
             }
             const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, w);
-            c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va0[s], bv, c0, 0, 0, 0);
-            if constexpr (TWO) c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va1[s], bv, c1, 0, 0, 0);
+            if constexpr (TR) {
+                c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bv, va0[s], c0, 0, 0, 0);
+                if constexpr (TWO) c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bv, va1[s], c1, 0, 0, 0);
+            } else {
+                c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va0[s], bv, c0, 0, 0, 0);
+                if constexpr (TWO) c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va1[s], bv, c1, 0, 0, 0);
+            }
         }
         }
     } else {
@@ -247,8 +253,13 @@ __device__ __forceinline__ void nt2_bscaled(f32x4_t& c0, const typename MM<MT>::
         }
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-            c0 = __builtin_amdgcn_mfma_f32_16x16x4f32(va0[s], vb[s], c0, 0, 0, 0);
-            if constexpr (TWO) c1 = __builtin_amdgcn_mfma_f32_16x16x4f32(va1[s], vb[s], c1, 0, 0, 0);
+            if constexpr (TR) {
+                c0 = __builtin_amdgcn_mfma_f32_16x16x4f32(vb[s], va0[s], c0, 0, 0, 0);
+                if constexpr (TWO) c1 = __builtin_amdgcn_mfma_f32_16x16x4f32(vb[s], va1[s], c1, 0, 0, 0);
+            } else {
+                c0 = __builtin_amdgcn_mfma_f32_16x16x4f32(va0[s], vb[s], c0, 0, 0, 0);
+                if constexpr (TWO) c1 = __builtin_amdgcn_mfma_f32_16x16x4f32(va1[s], vb[s], c1, 0, 0, 0);
+            }
         }
     }
 }
@@ -721,6 +732,15 @@ __device__ __forceinline__ void st8_perm(typename MM<MT>::S* row, int c8, const 
         x.get(f);
         MM<MT>::st8(row + c8, f);
     }
+}
+
+// Four fp32 values into four adjacent elements (natural column order) of the operand type.
+template <typename MT>
+__device__ __forceinline__ void st4f(typename MM<MT>::S* p, const float* f) {
+    if constexpr (sizeof(typename MM<MT>::S) == 2)
+        *reinterpret_cast<uint2*>(p) = uint2{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3])};
+    else
+        *reinterpret_cast<f32x4_t*>(p) = f32x4_t{f[0], f[1], f[2], f[3]};
 }
 
 // Four fp32 values of logical columns c4 .. c4+3 (c4 a multiple of 4) into an operand row, in the
@@ -1331,29 +1351,37 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
                 auto do_pair = [&](int I, int J) {
                     const int fi = J == I ? I : J == I - 1 ? -1 : (I == 2 ? 4 : (J == 0 ? 5 : 6));
                     f32x4_t cl = {0.f, 0.f, 0.f, 0.f}, cp = {0.f, 0.f, 0.f, 0.f};
+                    // transposed products: lane (g, i) holds row 16I + i, columns 16J + 4g .. +3, so each
+                    // lane writes its four entries of L and of P with one store each
                     if (want_o)
-                        nt2_bscaled<MT, K>(cl, sK + 16 * I * LDK, cp, sQ + 16 * I * LDK, LDK, sRG + 16 * J * LDK, LDK,
-                                           fi >= 0 ? fperm + fi * K : nullptr);
+                        nt2_bscaled<MT, K, true, true>(cl, sK + 16 * I * LDK, cp, sQ + 16 * I * LDK, LDK,
+                                                       sRG + 16 * J * LDK, LDK, fi >= 0 ? fperm + fi * K : nullptr);
                     else  // no outputs: P is not needed
-                        nt2_bscaled<MT, K, false>(cl, sK + 16 * I * LDK, cp, sQ + 16 * I * LDK, LDK, sRG + 16 * J * LDK,
-                                                  LDK, fi >= 0 ? fperm + fi * K : nullptr);
+                        nt2_bscaled<MT, K, false, true>(cl, sK + 16 * I * LDK, cp, sQ + 16 * I * LDK, LDK,
+                                                        sRG + 16 * J * LDK, LDK, fi >= 0 ? fperm + fi * K : nullptr);
+                    const int r = 16 * I + lr, c4 = 4 * g4;
+                    const float br = sb[r];
+                    float lv[4], pv[4];
+                    if (J < I) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int rr = 4 * g4 + e, r = 16 * I + rr, j = 16 * J + lr;
-                        if (J < I) {
-                            sLo[r * LDO + j] = M::cvt(-sb[r] * cl[e]);
-                            if (want_o) sP[r * LDT + perm<MT>(j)] = M::cvt(cp[e]);
-                        } else {  // diagonal blocks: L in fp32, strictly lower, for the inversion; P lower
-                            sLd[I * 16 * LDN + rr * LDN + lr] = (lr < rr) ? sb[r] * cl[e] : 0.0f;
-                            if (want_o) {
-                                float pv = (lr <= rr) ? cp[e] : 0.0f;
-                                if (lr == rr) {  // q_r . k_r from the unscaled rows
-                                    pv = sdg[r];
+                        for (int e = 0; e < 4; ++e) lv[e] = -br * cl[e];
+                        st4f<MT>(sLo + r * LDO + 16 * J + c4, lv);
+                        if (want_o) {
 #pragma unroll
-                                    for (int b = 1; b < K / 64; ++b) pv += sdg[b * CH + r];
-                                }
-                                sP[r * LDT + perm<MT>(j)] = M::cvt(pv);
-                            }
+                            for (int e = 0; e < 4; ++e) pv[e] = cp[e];
+                            st4f_perm<MT>(sP + r * LDT, 16 * J + c4, pv);
+                        }
+                    } else {  // diagonal blocks: L in fp32, strictly lower, for the inversion; P lower
+                        *reinterpret_cast<f32x4_t*>(sLd + I * 16 * LDN + lr * LDN + c4) =
+                            f32x4_t{c4 < lr ? br * cl[0] : 0.0f, c4 + 1 < lr ? br * cl[1] : 0.0f,
+                                    c4 + 2 < lr ? br * cl[2] : 0.0f, c4 + 3 < lr ? br * cl[3] : 0.0f};
+                        if (want_o) {
+                            float dg = sdg[r];  // q_r . k_r from the unscaled rows
+#pragma unroll
+                            for (int b = 1; b < K / 64; ++b) dg += sdg[b * CH + r];
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) pv[e] = c4 + e == lr ? dg : c4 + e < lr ? cp[e] : 0.0f;
+                            st4f_perm<MT>(sP + r * LDT, 16 * I + c4, pv);
                         }
                     }
                 };
