@@ -1149,39 +1149,45 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
         // ===== B/C: L = beta (K K^T) decay (strictly lower), P = (Q K^T) decay (lower incl. diag);
         //       waves 0-3 also invert the diagonal block of L they computed =====
         if constexpr (!PER_K) {
-            // L(I, J) and P(I, J) share their right operand K_J: they are computed as pairs,
-            // with every operand read issued before the first product
+            // L(I, J) and P(I, J) share their right operand K_J: they are computed as pairs, with every
+            // operand read issued before the first product, and transposed (K_J as the left operand):
+            // lane (g, i) then holds row 16I + i, columns 16J + 4g .. +3, and writes them with one store
             auto pair = [&](int I, int J, f32x4_t& cl, f32x4_t& cp) {
                 cl = f32x4_t{0.f, 0.f, 0.f, 0.f};
                 cp = f32x4_t{0.f, 0.f, 0.f, 0.f};
                 if (want_o)
-                    M::template nt2<K>(cl, sK + 16 * I * LDK, sK + 16 * J * LDK, cp, sQ + 16 * I * LDK,
-                                       sK + 16 * J * LDK, LDK);
+                    M::template nt2<K>(cl, sK + 16 * J * LDK, sK + 16 * I * LDK, cp, sK + 16 * J * LDK,
+                                       sQ + 16 * I * LDK, LDK);
                 else  // P only feeds the output
-                    M::nt(cl, sK + 16 * I * LDK, LDK, sK + 16 * J * LDK, LDK, K);
+                    M::nt(cl, sK + 16 * J * LDK, LDK, sK + 16 * I * LDK, LDK, K);
             };
-            auto store_p_diag = [&](int I, const f32x4_t& acc) {  // element-wise decay, masked
-                const f32x4_t gr = *reinterpret_cast<const f32x4_t*>(sg + 16 * I + 4 * g4);
-                const float gj = sg[16 * I + lr];
+            auto store_p_diag = [&](int I, const f32x4_t& acc) {  // element-wise decay, masked (transposed tile)
+                const int r = 16 * I + lr;
+                const float gr = sg[r];
+                const f32x4_t gj = *reinterpret_cast<const f32x4_t*>(sg + 16 * I + 4 * g4);
+                float x[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int r = 16 * I + 4 * g4 + e, j = 16 * I + lr;
-                    const float x = exp_f32(gr[e] - gj) * acc[e];  // inf above the diagonal is discarded
-                    sP[r * LDT + perm<MT>(j)] = M::cvt((r >= j) ? x : 0.0f);
+                    const float v = exp_f32(gr - gj[e]) * acc[e];  // inf above the diagonal is discarded
+                    x[e] = (lr >= 4 * g4 + e) ? v : 0.0f;
                 }
+                st4f_perm<MT>(sP + r * LDT, 16 * I + 4 * g4, x);
             };
-            // off-diagonal blocks (I > J): decay from the per-row factor tables
+            // off-diagonal blocks (I > J): decay from the per-row factor tables (transposed tiles)
             auto store_off = [&](int I, int J, const f32x4_t& cl, const f32x4_t& cp) {
-                const f32x4_t fa = *reinterpret_cast<const f32x4_t*>(FP(Lay::g_fa) + J * CH + 16 * I + 4 * g4);
-                const f32x4_t br = *reinterpret_cast<const f32x4_t*>(sb + 16 * I + 4 * g4);
-                const float fb = FP(Lay::g_fb)[16 * J + lr];
+                const int r = 16 * I + lr;
+                const float fa = FP(Lay::g_fa)[J * CH + r];
+                const float br = sb[r];
+                const f32x4_t fb = *reinterpret_cast<const f32x4_t*>(FP(Lay::g_fb) + 16 * J + 4 * g4);
+                float lx[4], px[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int r = 16 * I + 4 * g4 + e, j = 16 * J + lr;
-                    const float d = fa[e] * fb;
-                    sLo[r * LDO + j] = M::cvt(-br[e] * d * cl[e]);
-                    if (want_o) sP[r * LDT + perm<MT>(j)] = M::cvt(d * cp[e]);
+                    const float d = fa * fb[e];
+                    lx[e] = -br * d * cl[e];
+                    px[e] = d * cp[e];
                 }
+                st4f<MT>(sLo + r * LDO + 16 * J + 4 * g4, lx);
+                if (want_o) st4f_perm<MT>(sP + r * LDT, 16 * J + 4 * g4, px);
             };
             auto off_pair = [&](int q) {  // q-th of the pairs (1,0),(2,0),(2,1),(3,0),(3,1),(3,2)
                 int I, J;
@@ -1200,16 +1206,18 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
                 } else {
                     pair(w, w, cl, cp);
                 }
+                // (K_w K_w^T is symmetric: the tile reads as transposed like the pairs)
                 float* sN = sLd + w * 16 * LDN;
-                const f32x4_t gr = *reinterpret_cast<const f32x4_t*>(sg + 16 * w + 4 * g4);
-                const f32x4_t br = *reinterpret_cast<const f32x4_t*>(sb + 16 * w + 4 * g4);
-                const float gj = sg[16 * w + lr];
+                const float gr = sg[16 * w + lr];
+                const float br = sb[16 * w + lr];
+                const f32x4_t gj = *reinterpret_cast<const f32x4_t*>(sg + 16 * w + 4 * g4);
+                f32x4_t xn;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int rr = 4 * g4 + e;
-                    const float x = br[e] * exp_f32(gr[e] - gj) * cl[e];
-                    sN[rr * LDN + lr] = (rr > lr) ? x : 0.0f;
+                    const float x = br * exp_f32(gr - gj[e]) * cl[e];
+                    xn[e] = (lr > 4 * g4 + e) ? x : 0.0f;
                 }
+                *reinterpret_cast<f32x4_t*>(sN + lr * LDN + 4 * g4) = xn;
                 if constexpr (NW == 4) {
                     if (want_o) store_p_diag(w, cp);
                 }
@@ -1226,8 +1234,8 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
                     } else if (want_o) {  // waves 6 and 7: diagonal P tiles (I, I), I = 2 (w - 6), 2 (w - 6) + 1
                         const int I0 = 2 * (w - 6);
                         f32x4_t c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
-                        M::template nt2<K>(c0, sQ + 16 * I0 * LDK, sK + 16 * I0 * LDK, c1, sQ + 16 * (I0 + 1) * LDK,
-                                           sK + 16 * (I0 + 1) * LDK, LDK);
+                        M::template nt2<K>(c0, sK + 16 * I0 * LDK, sQ + 16 * I0 * LDK, c1, sK + 16 * (I0 + 1) * LDK,
+                                           sQ + 16 * (I0 + 1) * LDK, LDK);
                         store_p_diag(I0, c0);
                         store_p_diag(I0 + 1, c1);
                     }
