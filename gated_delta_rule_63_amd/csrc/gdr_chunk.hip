@@ -275,8 +275,9 @@ __device__ __forceinline__ uint32_t pack_tile_hi(const f32x4_t& t) { return pack
 // perm()-ordered A row; for an fp32 step (t, e) position l/16 is index 16t + 4*(l/16) + e.
 // With LOWER, A is lower triangular (A[r][j] = 0 for j > r): reduction steps entirely above the
 // diagonal of a 16-row tile are skipped.  The A reads of two k-steps are issued together, before
-// their products.
-template <typename MT, int NP, int NI, bool LOWER = false>
+// their products.  With TR the tiles are formed transposed (lane (g, i) holds row 16*tile + i,
+// columns 4g .. 4g+3 of B's 16).
+template <typename MT, int NP, int NI, bool LOWER = false, bool TR = false>
 __device__ __forceinline__ void gemm_regs(f32x4_t* acc, const typename MM<MT>::S* sA, int lda, const f32x4_t* Bt) {
     const int l = threadIdx.x & 63, g4 = l >> 4, lr = l & 15;
     if constexpr (sizeof(typename MM<MT>::S) == 2) {
@@ -299,7 +300,8 @@ __device__ __forceinline__ void gemm_regs(f32x4_t* acc, const typename MM<MT>::S
 #pragma unroll
                 for (int i = 0; i < NI; ++i) {
                     if (LOWER && 32 * (m0 + m) > 16 * i + 15) continue;
-                    acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[m][i], bv, acc[i], 0, 0, 0);
+                    if constexpr (TR) acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bv, av[m][i], acc[i], 0, 0, 0);
+                    else acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[m][i], bv, acc[i], 0, 0, 0);
                 }
             }
         }
@@ -312,7 +314,8 @@ __device__ __forceinline__ void gemm_regs(f32x4_t* acc, const typename MM<MT>::S
                 for (int i = 0; i < NI; ++i) {
                     if (LOWER && t > i) continue;
                     const float av = sA[(16 * i + lr) * lda + 16 * t + 4 * g4 + e];
-                    acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, Bt[t][e], acc[i], 0, 0, 0);
+                    if constexpr (TR) acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(Bt[t][e], av, acc[i], 0, 0, 0);
+                    else acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, Bt[t][e], acc[i], 0, 0, 0);
                 }
             }
         }
@@ -347,8 +350,9 @@ __device__ __forceinline__ void gemm_regs_2b(f32x4_t* acc0, const f32x4_t* Bt0, 
 }
 
 // acc0[i] += A0[16*i + .., :] B and acc1[i] += A1[16*i + .., :] B (gemm_regs for two left operands with
-// one right operand): each packing of B feeds both, and the two accumulator chains interleave.
-template <typename MT, int NP, int NI>
+// one right operand): each packing of B feeds both, and the two accumulator chains interleave.  With
+// TR1 the acc1 tiles are formed transposed (as gemm_regs with TR).
+template <typename MT, int NP, int NI, bool TR1 = false>
 __device__ __forceinline__ void gemm_regs2(f32x4_t* acc0, const typename MM<MT>::S* sA0, f32x4_t* acc1,
                                            const typename MM<MT>::S* sA1, int lda, const f32x4_t* Bt) {
     if constexpr (sizeof(typename MM<MT>::S) == 2) {
@@ -368,12 +372,13 @@ __device__ __forceinline__ void gemm_regs2(f32x4_t* acc0, const typename MM<MT>:
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
                 acc0[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[i], bv, acc0[i], 0, 0, 0);
-                acc1[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[i], bv, acc1[i], 0, 0, 0);
+                if constexpr (TR1) acc1[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bv, a1[i], acc1[i], 0, 0, 0);
+                else acc1[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[i], bv, acc1[i], 0, 0, 0);
             }
         }
     } else {
         gemm_regs<MT, NP, NI>(acc0, sA0, lda, Bt);
-        gemm_regs<MT, NP, NI>(acc1, sA1, lda, Bt);
+        gemm_regs<MT, NP, NI, false, TR1>(acc1, sA1, lda, Bt);
     }
 }
 
@@ -1650,31 +1655,35 @@ __global__ __launch_bounds__(4 * BV) void chunk_fused_kernel(const ChunkArgs a) 
             __syncthreads();
             continue;
         }
+        // the output tiles are formed transposed: lane (g, i) holds token 16t + i, value columns
+        // 16w + 4g .. +3, written to the staging area with one store per tile
         f32x4_t oa[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) oa[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        if (want_o) gemm_regs2<MT, K, 4>(nu, sW, oa, SP(PER_K ? Lay::k_qt : Lay::g_q), LDK, hs);
+        if (want_o) gemm_regs2<MT, K, 4, true>(nu, sW, oa, SP(PER_K ? Lay::k_qt : Lay::g_q), LDK, hs);
         else gemm_regs<MT, K, 4>(nu, sW, LDK, hs);
         if (ci + 1 < nc) load_vgb(ci + 1);
         if (want_o) {
         if constexpr (!PER_K) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const f32x4_t f = *reinterpret_cast<const f32x4_t*>(FP(Lay::g_eg) + 16 * i + 4 * g4);
+                const float f = FP(Lay::g_eg)[16 * i + lr];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) oa[i][e] *= f[e];
+                for (int e = 0; e < 4; ++e) oa[i][e] *= f;
             }
         }
-        gemm_regs<MT, CH, 4, true>(oa, sP, LDT, nu);
+        gemm_regs<MT, CH, 4, true, true>(oa, sP, LDT, nu);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * i + 4 * g4 + e, c = 16 * w + lr;
+            {
+                const int r = 16 * i + lr, c = 16 * w + 4 * g4;  // four adjacent columns, inside one granule
                 if constexpr (std::is_same<IO, float>::value)
-                    *reinterpret_cast<float*>(so + OS::off(r, c)) = a.scale * oa[i][e];
+                    *reinterpret_cast<f32x4_t*>(so + OS::off(r, c)) =
+                        f32x4_t{a.scale * oa[i][0], a.scale * oa[i][1], a.scale * oa[i][2], a.scale * oa[i][3]};
                 else
-                    *reinterpret_cast<uint16_t*>(so + OS::off(r, c)) = f32_to_bf16(a.scale * oa[i][e]);
+                    *reinterpret_cast<uint2*>(so + OS::off(r, c)) =
+                        uint2{pack_bf16x2(a.scale * oa[i][0], a.scale * oa[i][1]),
+                              pack_bf16x2(a.scale * oa[i][2], a.scale * oa[i][3])};
             }
         }
         }
